@@ -1,0 +1,511 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties one oracle step to something other than itself: a library routine, a closed form,
+a brute-force enumeration on a tiny input, or a hand-worked fixture under tests/golden.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.spatial.distance as ssd
+import scipy.special as ssp
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _blobs(rng, n, d, centres, spread=0.3, scale=5.0):
+    c = rng.normal(size=(centres, d)) * scale
+    lab = rng.integers(0, centres, n)
+    return c[lab] + spread * rng.normal(size=(n, d)), lab
+
+
+# ------------------------------------------------------------------------------------ RNG
+def test_splitmix64_reference_outputs():
+    for case in _golden("splitmix64.json")["cases"]:
+        s = case["seed"]
+        for want in case["outputs"]:
+            s, out = O.splitmix64_next(s)
+            assert out == int(want)
+
+
+def test_kpp_uniform_is_first_output_scaled():
+    # u_m = (first SplitMix64 output seeded with the stream key) >> 11, times 2^-53
+    first = int(_golden("splitmix64.json")["cases"][1]["outputs"][0])
+    assert O.kpp_uniform(0, 0, 0, 0) == (first >> 11) * 2.0 ** -53
+    u = [O.kpp_uniform(7, h, s, m) for h in range(3) for s in range(2) for m in range(50)]
+    assert all(0.0 <= x < 1.0 for x in u)
+    assert len(set(u)) == len(u)
+
+
+# ------------------------------------------------------------------------------------ rounding
+def test_round_bf16_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(size=20000) * 10.0 ** rng.integers(-5, 5, 20000),
+                        # exact halfway cases: low 16 bits 0x8000, both parities of the kept lsb
+                        (np.arange(1, 2001, dtype=np.uint32) << 16 | 0x8000).view(np.float32).astype(np.float64),
+                        -(np.arange(1, 2001, dtype=np.uint32) << 16 | 0x8000).view(np.float32).astype(np.float64)])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x), want)
+
+
+def test_round_f32_matches_numpy_cast():
+    x = np.random.default_rng(1).normal(size=1000) * 1e3
+    np.testing.assert_array_equal(O.round_f32(x), x.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------------------------------------------ metric
+def test_qrkc_metric_is_mean_squared_qk_score_difference():
+    """P9: sum_{t,u} (q.k - q.c)^2 / (N Nk) == sum_u (k-c)^T M (k-c) / Nk for M = qrkc_metric(Q)."""
+    rng = np.random.default_rng(2)
+    Q = rng.normal(size=(40, 6)) + 1.5  # non-zero mean: a centred covariance would fail
+    K = rng.normal(size=(30, 6))
+    Cn = rng.normal(size=(5, 6))
+    lab = rng.integers(0, 5, 30)
+    M = O.qrkc_metric(Q)
+    lhs = O.qk_score_sq_error(Q, K, lab, Cn)
+    rhs = np.mean([O.metric_distance(K[u:u + 1], Cn[lab[u]], M)[0] for u in range(30)])
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+    # brute force over explicit pairs
+    bf = np.mean([(Q[t] @ K[u] - Q[t] @ Cn[lab[u]]) ** 2 for t in range(40) for u in range(30)])
+    assert abs(bf - lhs) <= 1e-10 * max(1.0, abs(bf))
+
+
+def test_metric_distance_matches_scipy_mahalanobis():
+    rng = np.random.default_rng(3)
+    A = rng.normal(size=(7, 5))
+    M = A.T @ A / 7
+    P = rng.normal(size=(20, 5))
+    c = rng.normal(size=5)
+    want = ssd.cdist(P, c[None, :], "mahalanobis", VI=M)[:, 0] ** 2
+    np.testing.assert_allclose(O.metric_distance(P, c, M), want, rtol=1e-12, atol=1e-12)
+    want_e = ssd.cdist(P, c[None, :], "sqeuclidean")[:, 0]
+    np.testing.assert_allclose(O.metric_distance(P, c), want_e, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ init
+def test_candidate_rows():
+    np.testing.assert_array_equal(O.candidate_rows(10, 2), np.arange(10))
+    r = O.candidate_rows(75600, 500)
+    assert r.size == 4096 and r[0] == 0 and r[-1] == (4095 * 75600) // 4096
+    assert O.candidate_rows(219600, 1000).size == 8000
+    assert np.all(np.diff(r) > 0)
+
+
+@pytest.mark.parametrize("case", _golden("kmeanspp_hand.json")["cases"], ids=lambda c: c["name"])
+def test_kmeanspp_hand_worked(case):
+    X = np.asarray(case["X"], dtype=np.float64)
+    M = None if case["M"] is None else np.asarray(case["M"], dtype=np.float64)
+    draws = case["draws"]
+    cent, chosen, _ = O.kmeanspp(X, case["C"], M, draws=lambda m: draws[m], return_trace=True)
+    np.testing.assert_array_equal(chosen, case["chosen"])
+    np.testing.assert_array_equal(cent, np.asarray(case["centres"], dtype=np.float64))
+
+
+def test_kmeanspp_c_equals_n_picks_every_point_once():
+    """P11: with C = N distinct points every point is chosen exactly once."""
+    X = np.random.default_rng(4).normal(size=(50, 3))
+    _, chosen, _ = O.kmeanspp(X, 50, None, seed=3, return_trace=True)
+    assert sorted(chosen.tolist()) == list(range(50))
+    _, chosen, _ = O.kmeanspp(X, 50, O.qrkc_metric(X), seed=5, return_trace=True)
+    assert sorted(chosen.tolist()) == list(range(50))
+
+
+def test_kmeanspp_duplicates_fall_back_to_lowest_unchosen():
+    X = np.zeros((6, 2))
+    X[3] = 1.0
+    _, chosen, _ = O.kmeanspp(X, 4, None, draws=lambda m: 0.0, return_trace=True)
+    # first 0; then only row 3 has mass; then all D2 = 0 -> lowest unchosen rows 1
+    assert chosen.tolist() == [0, 3, 1, 2]
+
+
+def test_kmeanspp_sampling_frequencies_follow_d2():
+    """Second centre is drawn with probability D^2 / sum D^2 (checked over many seeds)."""
+    X = np.array([[0.0], [1.0], [2.0], [4.0]])
+    counts = np.zeros(4)
+    for s in range(4000):
+        _, chosen, _ = O.kmeanspp(X, 2, None, draws=lambda m, s=s: 0.0 if m == 0 else O.kpp_uniform(s, 0, 0, 1),
+                                  return_trace=True)
+        counts[chosen[1]] += 1
+    p = np.array([0, 1, 4, 16]) / 21.0
+    assert np.all(np.abs(counts / 4000 - p) < 0.03)
+
+
+# ------------------------------------------------------------------------------------ Lloyd
+def _sk_lloyd(X, init, iters):
+    from sklearn.cluster import KMeans
+    km = KMeans(n_clusters=init.shape[0], init=init, n_init=1, max_iter=iters, tol=0.0, algorithm="lloyd")
+    km.fit(X)
+    return km.labels_, km.cluster_centers_
+
+
+def test_assign_matches_scipy_argmin():
+    rng = np.random.default_rng(5)
+    X = rng.normal(size=(500, 8))
+    C = rng.normal(size=(13, 8))
+    g, b = O.consumed_centroids(C, O.EUCLID, None, bf16=False)
+    d = ssd.cdist(X, O.round_f32(C), "sqeuclidean")
+    np.testing.assert_array_equal(O.assign(X, g, b), np.argmin(d, axis=1))
+    M = O.qrkc_metric(rng.normal(size=(60, 8)) + 0.5)
+    g, b = O.consumed_centroids(C, O.QRKC, M, bf16=False)
+    dm = ssd.cdist(X, O.round_f32(C), "mahalanobis", VI=M) ** 2
+    srt = np.sort(dm, axis=1)
+    clear = (srt[:, 1] - srt[:, 0]) > 1e-6 * (1 + srt[:, 0])
+    assert clear.mean() > 0.95
+    np.testing.assert_array_equal(O.assign(X, g, b)[clear], np.argmin(dm, axis=1)[clear])
+
+
+def test_assign_ties_go_to_lowest_index():
+    X = np.array([[0.0, 0.0], [1.0, 0.0]])
+    C = np.array([[1.0, 1.0], [1.0, -1.0], [1.0, 1.0]])
+    g, b = O.consumed_centroids(C, O.EUCLID, None, bf16=False)
+    assert O.assign(X, g, b).tolist() == [0, 0]
+
+
+def test_consumed_centroids_bf16_rules():
+    rng = np.random.default_rng(6)
+    C = rng.normal(size=(4, 8)).astype(np.float32).astype(np.float64)
+    g, b = O.consumed_centroids(C, O.EUCLID, None, bf16=True)
+    gt = torch.from_numpy(C.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(g, gt)
+    np.testing.assert_array_equal(b, (gt * gt).sum(1).astype(np.float32).astype(np.float64))
+    M = O.round_f32(O.qrkc_metric(rng.normal(size=(30, 8))))
+    g, b = O.consumed_centroids(C, O.QRKC, M, bf16=True)
+    y = C @ M  # M symmetric
+    np.testing.assert_array_equal(g, torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy())
+    np.testing.assert_allclose(b, np.einsum("ij,jk,ik->i", C, M, C), rtol=1e-7)
+
+
+def test_lloyd_euclid_matches_sklearn():
+    rng = np.random.default_rng(7)
+    X, _ = _blobs(rng, 600, 5, 8)
+    init = X[rng.choice(600, 8, replace=False)]
+    for iters in (1, 3, 30):
+        lab, c = O.lloyd(X, init, iters, O.EUCLID, None, bf16=False)
+        sl, sc = _sk_lloyd(X, O.round_f32(init), iters)
+        np.testing.assert_allclose(c, sc, rtol=1e-6, atol=1e-6)
+        if iters == 30:  # converged: sklearn's final relabel agrees with the last assignment
+            np.testing.assert_array_equal(lab, sl)
+
+
+def test_lloyd_qrkc_is_euclidean_kmeans_on_whitened_keys():
+    """QRKC K-means == Euclidean K-means on y = L^T x with M = L L^T (library K-means)."""
+    rng = np.random.default_rng(8)
+    K, _ = _blobs(rng, 500, 4, 6, spread=0.4)
+    Q = rng.normal(size=(200, 4)) * np.array([3.0, 1.0, 0.5, 0.2]) + 0.3
+    M = O.round_f32(O.qrkc_metric(Q))
+    L = np.linalg.cholesky(M)
+    init = K[rng.choice(500, 6, replace=False)]
+    lab, c = O.lloyd(K, init, 25, O.QRKC, M, bf16=False)
+    sl, sc = _sk_lloyd(K @ L, O.round_f32(init) @ L, 25)
+    np.testing.assert_array_equal(lab, sl)
+    np.testing.assert_allclose(c, sc @ np.linalg.inv(L), rtol=1e-5, atol=1e-5)
+
+
+def test_qrkc_equals_euclid_when_metric_is_isotropic():
+    """P8: M = a*I (queries = scaled orthogonal rows) -> identical labels and centroids."""
+    rng = np.random.default_rng(9)
+    d = 8
+    Q = np.vstack([np.eye(d) * 2.0, -np.eye(d) * 2.0])
+    M = O.qrkc_metric(Q)
+    np.testing.assert_allclose(M, np.eye(d) * 4.0 * 2 / (2 * d) * 1.0, atol=0)
+    X, _ = _blobs(rng, 300, d, 5)
+    # fp32 consumption: M = I/2 scales every b_j - 2 x.g_j by exactly 1/2
+    ce = O.cluster(X, 5, 6, O.EUCLID, None, seed=1, side=O.SIDE_K, bf16=False)
+    cm = O.cluster(X, 5, 6, O.QRKC, M, seed=1, side=O.SIDE_K, bf16=False)
+    np.testing.assert_array_equal(ce["labels"], cm["labels"])
+    np.testing.assert_array_equal(ce["centroids"], cm["centroids"])
+
+
+def test_lloyd_objective_non_increasing():
+    """P10: the K-means objective never rises from one iteration to the next (fp64 data)."""
+    rng = np.random.default_rng(10)
+    X = rng.normal(size=(800, 6))
+    for metric, M in ((O.EUCLID, None), (O.QRKC, O.round_f32(O.qrkc_metric(rng.normal(size=(100, 6)) + 1)))):
+        trace = []
+        O.lloyd(X, X[:20], 12, metric, M, bf16=False, trace=trace)
+        obj = []
+        for lab, c in trace:
+            obj.append(sum(O.metric_distance(X[lab == j], c[j], M).sum() for j in range(20)))
+        assert all(b <= a * (1 + 1e-9) for a, b in zip(obj, obj[1:]))
+
+
+def test_update_keeps_empty_clusters():
+    X = np.array([[1.0, 2.0], [3.0, 4.0]])
+    prev = np.array([[9.0, 9.0], [0.0, 0.0], [5.0, -5.0]])
+    c = O.update(X, np.array([1, 1]), 3, prev)
+    np.testing.assert_array_equal(c, [[9.0, 9.0], [2.0, 3.0], [5.0, -5.0]])
+
+
+def test_cluster_order_is_stable_argsort():
+    rng = np.random.default_rng(11)
+    lab = rng.integers(0, 17, 3000)
+    lab[lab == 5] = 6  # an empty cluster
+    perm, off = O.cluster_order(lab, 17)
+    np.testing.assert_array_equal(perm, np.argsort(lab, kind="stable"))
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(lab, minlength=17))]))
+    assert off[5] == off[6]
+
+
+# ------------------------------------------------------------------------------------ PAMA
+def test_pama_hand_worked():
+    g = _golden("pama_hand.json")
+    perm, off = O.cluster_order(np.array(g["q_labels"]), g["cq"])
+    A = O.pama(np.array(g["Q"]), perm, off, np.array(g["k_cent"]), np.array(g["k_sizes"]), g["scale"])
+    np.testing.assert_allclose(A, np.array(g["map"]), rtol=0, atol=1e-15)
+
+
+def _toy_head(rng, n=120, d=8):
+    Q = rng.normal(size=(n, d)) + 0.5
+    K = rng.normal(size=(n, d)) + 0.5
+    V = rng.normal(size=(n, d))
+    return Q, K, V
+
+
+def test_pama_rows_sum_to_one():
+    """P1."""
+    rng = np.random.default_rng(12)
+    Q, K, _ = _toy_head(rng)
+    ql = rng.integers(0, 7, 120)
+    ql[ql == 3] = 4  # empty query block -> zero row
+    kl = rng.integers(0, 9, 120)
+    kl[kl == 2] = 1  # empty key block
+    perm, off = O.cluster_order(ql, 7)
+    kc = np.stack([K[kl == j].mean(0) if (kl == j).any() else np.zeros(8) for j in range(9)])
+    A = O.pama(Q, perm, off, kc, np.bincount(kl, minlength=9), 0.35)
+    live = np.diff(off) > 0
+    np.testing.assert_allclose(A[live].sum(1), 1.0, atol=1e-12)
+    assert np.all(A[~live] == 0) and np.all(A[:, 2] == 0)
+
+
+def test_pama_singleton_key_clusters_equal_full_estimate():
+    """P5: Ck = N singletons -> PAMA == exact block mass of the dense softmax (scipy softmax)."""
+    rng = np.random.default_rng(13)
+    Q, K, _ = _toy_head(rng, 60)
+    ql = rng.integers(0, 5, 60)
+    perm, off = O.cluster_order(ql, 5)
+    s = 0.4
+    A = O.pama(Q, perm, off, K, np.ones(60, dtype=np.int64), s)
+    P = ssp.softmax(s * Q @ K.T, axis=1)
+    for i in range(5):
+        np.testing.assert_allclose(A[i], P[ql == i].mean(0), atol=1e-13)
+
+
+def test_pama_singleton_queries_and_keys_is_each_query_softmax():
+    """P6: Cq = Ck = N -> every map row is one query's own softmax over the keys."""
+    rng = np.random.default_rng(14)
+    Q, K, _ = _toy_head(rng, 40)
+    ident = np.arange(40)
+    A = O.pama(Q, ident, np.arange(41), K, np.ones(40, dtype=np.int64), 0.3)
+    np.testing.assert_allclose(A, ssp.softmax(0.3 * Q @ K.T, axis=1), atol=1e-13)
+
+
+def test_pama_size_weighting_exact_for_identical_keys():
+    """P7: keys equal inside each cluster -> size-weighted centroid softmax equals the exact
+    block mass (dropping the ln n term fails this)."""
+    rng = np.random.default_rng(15)
+    base = rng.normal(size=(6, 8))
+    kl = np.repeat(np.arange(6), [1, 2, 3, 5, 8, 13])
+    K = base[kl]
+    Q = rng.normal(size=(30, 8))
+    ql = rng.integers(0, 4, 30)
+    perm, off = O.cluster_order(ql, 4)
+    A = O.pama(Q, perm, off, base, np.bincount(kl), 0.5)
+    P = ssp.softmax(0.5 * Q @ K.T, axis=1)
+    FF = np.stack([P[:, kl == j].sum(1) for j in range(6)], axis=1)
+    for i in range(4):
+        np.testing.assert_allclose(A[i], FF[ql == i].mean(0), atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------ top-p
+def test_topp_hand_worked():
+    g = _golden("topp_hand.json")
+    A = np.array(g["map"])
+    ks = np.array(g["k_sizes"])
+    for case in g["cases"]:
+        mask, counts, cols, keys = O.select_topp(A, ks, case["p"])
+        assert [c.tolist() for c in cols] == case["cols"], case["p"]
+        assert keys.tolist() == case["keys"]
+        assert counts.tolist() == [len(c) for c in case["cols"]]
+        assert np.array_equal(mask, np.array([[j in c for j in range(5)] for c in case["cols"]]))
+
+
+def test_topp_is_minimal_max_mass_set_bruteforce():
+    """P2 by enumeration: the kept set reaches p, no smaller set does, and among sets of its size it
+    has the largest mass (ties broken toward lower indices)."""
+    rng = np.random.default_rng(16)
+    for trial in range(300):
+        ck = int(rng.integers(1, 7))
+        row = rng.dirichlet(np.ones(ck) * 0.7)
+        if trial % 5 == 0:
+            row = np.round(row * 8) / 8  # exact ties and exact hits of p
+            if row.sum() == 0:
+                continue
+            row = row / row.sum()
+        p = float(rng.choice([0.3, 0.5, 0.75, 0.9, 0.95]))
+        mask, _, cols, _ = O.select_topp(row[None, :], np.ones(ck, dtype=np.int64), p)
+        sel = tuple(cols[0].tolist())
+        best = None
+        for k in range(1, ck + 1):
+            cands = [c for c in itertools.combinations(range(ck), k) if row[list(c)].sum() >= p]
+            if cands:
+                top = max(row[list(c)].sum() for c in cands)
+                best = [c for c in cands if row[list(c)].sum() == top]
+                break
+        if best is None:  # rounding: the whole row is below p
+            assert sel == tuple(np.flatnonzero(row > 0))
+            continue
+        assert len(sel) == len(best[0])
+        assert row[list(sel)].sum() == row[list(best[0])].sum()
+        assert sel == min(best)  # lexicographically smallest among equal-mass sets
+
+
+# ------------------------------------------------------------------------------------ attention
+def _selection(rng, cq, ck, k_sizes, density=0.5):
+    cols = []
+    for _ in range(cq):
+        c = np.flatnonzero((rng.random(ck) < density) & (k_sizes > 0))
+        if c.size == 0:
+            c = np.flatnonzero(k_sizes > 0)[:1]
+        cols.append(c.astype(np.int32))
+    return cols
+
+
+def test_sparse_attention_matches_torch_sdpa_with_block_mask():
+    rng = np.random.default_rng(17)
+    n, d = 150, 16
+    Q, K, V = (rng.normal(size=(n, d)) for _ in range(3))
+    ql = rng.integers(0, 6, n)
+    kl = rng.integers(0, 9, n)
+    kl[kl == 4] = 5
+    qp, qo = O.cluster_order(ql, 6)
+    kp, ko = O.cluster_order(kl, 9)
+    cols = _selection(rng, 6, 9, np.diff(ko))
+    s = 0.3
+    Os, lse = O.sparse_attention(Q, K, V, qp, qo, kp, ko, cols, s)
+    allowed = np.zeros((n, n), dtype=bool)
+    for t in range(n):
+        allowed[t] = np.isin(kl, cols[ql[t]])
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        attn_mask=torch.from_numpy(allowed)[None], scale=s)[0].numpy()
+    np.testing.assert_allclose(Os, want, atol=1e-12)
+    sc = torch.from_numpy(s * Q @ K.T).masked_fill(~torch.from_numpy(allowed), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=1).numpy(), atol=1e-12)
+
+
+def test_dense_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(18)
+    Q, K, V = (rng.normal(size=(70, 8)) for _ in range(3))
+    Od, lse = O.dense_attention(Q, K, V, 0.25, block=16)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], scale=0.25)[0].numpy()
+    np.testing.assert_allclose(Od, want, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(torch.from_numpy(0.25 * Q @ K.T), 1).numpy(), atol=1e-12)
+
+
+def test_p_one_sparse_equals_dense():
+    """P3: top-p with p = 1 keeps all non-empty key clusters, so sparse == dense."""
+    rng = np.random.default_rng(19)
+    Q, K, V = _toy_head(rng, 100)
+    r = O.retrieve(Q, K, 6, 10, 3, 1.0, 0.3, bf16=False)
+    Os, ls = O.sparse_attention(Q, K, V, r["q"]["perm"], r["q"]["offsets"], r["k"]["perm"],
+                                r["k"]["offsets"], r["cols"], 0.3)
+    Od, ld = O.dense_attention(Q, K, V, 0.3)
+    np.testing.assert_allclose(Os, Od, atol=1e-12)
+    np.testing.assert_allclose(ls, ld, atol=1e-12)
+
+
+def test_identity_values_return_the_masked_softmax():
+    """P16: with V = I the attention output is the masked softmax matrix itself."""
+    rng = np.random.default_rng(20)
+    n = 64
+    Q, K = rng.normal(size=(n, n)), rng.normal(size=(n, n))
+    ql, kl = rng.integers(0, 4, n), rng.integers(0, 5, n)
+    qp, qo = O.cluster_order(ql, 4)
+    kp, ko = O.cluster_order(kl, 5)
+    cols = _selection(rng, 4, 5, np.diff(ko))
+    Os, _ = O.sparse_attention(Q, K, np.eye(n), qp, qo, kp, ko, cols, 0.125)
+    for t in range(n):
+        sel = np.isin(kl, cols[ql[t]])
+        want = np.zeros(n)
+        want[sel] = ssp.softmax(0.125 * Q[t] @ K[sel].T)
+        np.testing.assert_allclose(Os[t], want, atol=1e-13)
+
+
+def test_recall_from_lse_equals_bruteforce_softmax_mass():
+    """P13: exp(LSE_sel - LSE_dense) == the dense softmax mass on the selected keys."""
+    rng = np.random.default_rng(21)
+    Q, K, V = _toy_head(rng, 90)
+    ql, kl = rng.integers(0, 5, 90), rng.integers(0, 7, 90)
+    qp, qo = O.cluster_order(ql, 5)
+    kp, ko = O.cluster_order(kl, 7)
+    cols = _selection(rng, 5, 7, np.diff(ko), 0.4)
+    _, ls = O.sparse_attention(Q, K, V, qp, qo, kp, ko, cols, 0.3)
+    _, ld = O.dense_attention(Q, K, V, 0.3)
+    r = O.recall(ls, ld)
+    P = ssp.softmax(0.3 * Q @ K.T, axis=1)
+    want = np.array([P[t, np.isin(kl, cols[ql[t]])].sum() for t in range(90)])
+    np.testing.assert_allclose(r, want, atol=1e-13)
+
+
+def test_full_full_topp_recall_reaches_p():
+    """P4 (Table 1 Full/Full rows: worst recall just above p): selecting blocks by the exact
+    block mass gives every query block a mean recall >= p."""
+    rng = np.random.default_rng(22)
+    Q, K, V = _toy_head(rng, 200, 8)
+    r = O.retrieve(Q, K, 8, 16, 4, 0.9, 0.35, bf16=False)
+    ql, kl = r["q"]["labels"], r["k"]["labels"]
+    est = O.estimator_maps(Q, K, ql, kl, r["q"]["centroids"], r["k"]["centroids"], 0.35)
+    qp, qo = r["q"]["perm"], r["q"]["offsets"]
+    A_ff = np.stack([est["FF"][qp[qo[i]:qo[i + 1]]].mean(0) if qo[i + 1] > qo[i] else np.zeros(16)
+                     for i in range(8)])
+    _, _, cols, _ = O.select_topp(A_ff, np.diff(r["k"]["offsets"]), 0.9)
+    _, ls = O.sparse_attention(Q, K, V, qp, qo, r["k"]["perm"], r["k"]["offsets"], cols, 0.35)
+    _, ld = O.dense_attention(Q, K, V, 0.35)
+    rec = O.recall(ls, ld)
+    for i in range(8):
+        t = qp[qo[i]:qo[i + 1]]
+        if t.size:
+            assert rec[t].mean() >= 0.9 - 1e-12
+    # and the FC (PAMA) rows are the per-query rows of the FC estimator, averaged
+    A_fc = O.pama(Q, qp, qo, r["k"]["centroids"], np.diff(r["k"]["offsets"]), 0.35)
+    for i in range(8):
+        t = qp[qo[i]:qo[i + 1]]
+        if t.size:
+            np.testing.assert_allclose(A_fc[i], est["FC"][t].mean(0), atol=1e-13)
+
+
+def test_key_runs_merge_adjacent_clusters():
+    off = np.array([0, 3, 3, 7, 9, 12])
+    assert O.key_runs([0, 1, 2], off) == [(0, 7)]
+    assert O.key_runs([0, 3, 4], off) == [(0, 3), (7, 12)]
+    assert O.key_runs([1], off) == []
+
+
+def test_density_definitions():
+    mask = np.array([[1, 0], [1, 1]], dtype=bool)
+    b, t = O.density(mask, [2, 3], [1, 4])
+    assert b == 3 / 4
+    assert t == (2 * 1 + 3 * 1 + 3 * 4) / 25
+
+
+def test_tv_zero_for_full_and_estimators_are_distributions():
+    rng = np.random.default_rng(23)
+    Q, K, _ = _toy_head(rng, 80)
+    r = O.retrieve(Q, K, 5, 8, 3, 0.9, 0.35, bf16=False)
+    est = O.estimator_maps(Q, K, r["q"]["labels"], r["k"]["labels"], r["q"]["centroids"],
+                           r["k"]["centroids"], 0.35)
+    assert O.tv_to_full(est["FF"], est["FF"]) == 0.0
+    for v in est.values():
+        np.testing.assert_allclose(v.sum(1), 1.0, atol=1e-12)
