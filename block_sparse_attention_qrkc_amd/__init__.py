@@ -1,0 +1,174 @@
+"""PARK block retrieval + block-sparse attention for MI355X (gfx950).
+
+Thin Python layer over the C ABI of ``libpark.so`` (see ``include/park.h``). Functions take and
+return torch tensors on the ROCm device and enqueue on the current stream; the computation runs
+entirely in the library's HIP kernels.
+
+Method: "PARK: Accurate Block Retrieval for Sparse Attention in Video Diffusion Transformers"
+(Figure 2 caption and abstract): Euclidean K-means on queries, query-aware (QRKC) K-means on keys,
+cluster-contiguous token order, the PAMA block-importance map, top-p selection (Table 1 caption)
+and attention restricted to the selected blocks.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, PARK_BF16, PARK_EHIP, PARK_EINVAL, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_CLUSTER_Q,
+    PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN,
+    PARK_EUCLID, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_F32, PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_OK,
+    PARK_QRKC, PARK_SIDE_K, PARK_SIDE_Q, ParkError, Workspace, lib, make_params, make_shape, park_forward_outputs,
+    park_params, park_shape, workspace_bytes,
+)
+from ._lib import _check, _ptr, _stream, _ws
+
+__all__ = [
+    "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_select_topp", "park_sparse_attn",
+    "park_permute_rows", "park_unpermute_rows", "park_forward", "park_version", "ParkError", "lib",
+]
+
+
+def park_version() -> str:
+    return lib().park_version().decode()
+
+
+def park_qrkc_metric(q, out=None, ws=None, stream=None):
+    """M_h = (1/n) sum_t q_t q_t^T per head, float32 [heads, d, d]."""
+    sh = make_shape(q)
+    M = out if out is not None else torch.empty(sh.heads, sh.d, sh.d, dtype=torch.float32, device=q.device)
+    wp, wn = _ws(PARK_ENTRY_METRIC, sh, None, q.device, ws)
+    _check(lib().park_qrkc_metric(ctypes.byref(sh), _ptr(q), _ptr(M), wp, wn, _stream(stream)))
+    return M
+
+
+def park_cluster(x, n_clusters, iters, metric=PARK_EUCLID, qmetric=None, init=PARK_INIT_KMEANSPP, seed=0,
+                 side=PARK_SIDE_Q, centroids=None, ws=None, stream=None):
+    """K-means of one token side. Returns dict(centroids, labels, perm, offsets).
+
+    With ``init=PARK_INIT_WARM`` the given ``centroids`` [heads, C, d] float32 are the start (and are
+    updated in place)."""
+    sh = make_shape(x)
+    H, N, D = sh.heads, sh.n, sh.d
+    dev = x.device
+    if centroids is None:
+        if init == PARK_INIT_WARM:
+            raise ValueError("warm start needs centroids")
+        centroids = torch.empty(H, n_clusters, D, dtype=torch.float32, device=dev)
+    labels = torch.empty(H, N, dtype=torch.int32, device=dev) if iters > 0 else None
+    perm = torch.empty(H, N, dtype=torch.int32, device=dev) if iters > 0 else None
+    offsets = torch.empty(H, n_clusters + 1, dtype=torch.int32, device=dev) if iters > 0 else None
+    prm = make_params(cq=n_clusters, ck=n_clusters)
+    entry = PARK_ENTRY_CLUSTER_Q
+    wp, wn = _ws(entry, sh, prm, dev, ws)
+    _check(lib().park_cluster(ctypes.byref(sh), _ptr(x), int(metric), _ptr(qmetric), int(n_clusters), int(iters),
+                              int(init), int(seed) & ((1 << 64) - 1), int(side), _ptr(centroids), _ptr(labels),
+                              _ptr(perm), _ptr(offsets), wp, wn, _stream(stream)))
+    return {"centroids": centroids, "labels": labels, "perm": perm, "offsets": offsets}
+
+
+def park_retrieve_map(q, q_perm, q_offsets, k_centroids, k_offsets, scale=0.0, out=None, ws=None, stream=None):
+    """PAMA map [heads, cq, ck] float32."""
+    sh = make_shape(q)
+    cq = q_offsets.shape[1] - 1
+    ck = k_offsets.shape[1] - 1
+    M = out if out is not None else torch.empty(sh.heads, cq, ck, dtype=torch.float32, device=q.device)
+    prm = make_params(cq=cq, ck=ck)
+    wp, wn = _ws(PARK_ENTRY_RETRIEVE_MAP, sh, prm, q.device, ws)
+    _check(lib().park_retrieve_map(ctypes.byref(sh), _ptr(q), _ptr(q_perm), _ptr(q_offsets), cq, _ptr(k_centroids),
+                                   _ptr(k_offsets), ck, float(scale), _ptr(M), wp, wn, _stream(stream)))
+    return M
+
+
+def park_select_topp(map, k_offsets, p, stream=None):
+    """Top-p cut of every map row. Returns dict(mask, counts, cols, sel_keys)."""
+    H, cq, ck = map.shape
+    dev = map.device
+    mask = torch.empty(H, cq, ck, dtype=torch.uint8, device=dev)
+    counts = torch.empty(H, cq, dtype=torch.int32, device=dev)
+    cols = torch.empty(H, cq, ck, dtype=torch.int32, device=dev)
+    sel = torch.empty(H, cq, dtype=torch.int64, device=dev)
+    _check(lib().park_select_topp(_ptr(map), H, cq, ck, _ptr(k_offsets), float(p), _ptr(mask), _ptr(counts),
+                                  _ptr(cols), _ptr(sel), _stream(stream)))
+    return {"mask": mask, "counts": counts, "cols": cols, "sel_keys": sel}
+
+
+def park_sparse_attn(q, k, v, q_perm, q_offsets, k_perm, k_offsets, counts, cols, scale=0.0, out=None, lse=True,
+                     ws=None, stream=None):
+    """Attention over the selected blocks. Returns (out [heads, n, d], lse [heads, n] or None)."""
+    sh = make_shape(q)
+    cq = q_offsets.shape[1] - 1
+    ck = k_offsets.shape[1] - 1
+    o = out if out is not None else torch.empty_like(q)
+    L = None
+    if lse is True:
+        L = torch.empty(sh.heads, sh.n, dtype=torch.float32, device=q.device)
+    elif isinstance(lse, torch.Tensor):
+        L = lse
+    prm = make_params(cq=cq, ck=ck)
+    wp, wn = _ws(PARK_ENTRY_SPARSE_ATTN, sh, prm, q.device, ws)
+    _check(lib().park_sparse_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(q_perm), _ptr(q_offsets), cq,
+                                  _ptr(k_perm), _ptr(k_offsets), ck, _ptr(counts), _ptr(cols), float(scale), _ptr(o),
+                                  _ptr(L), wp, wn, _stream(stream)))
+    return o, L
+
+
+def park_permute_rows(x, perm, out=None, stream=None):
+    """out[h, p] = x[h, perm[h, p]]."""
+    sh = make_shape(x)
+    o = out if out is not None else torch.empty_like(x)
+    _check(lib().park_permute_rows(ctypes.byref(sh), _ptr(x), _ptr(perm), _ptr(o), _stream(stream)))
+    return o
+
+
+def park_unpermute_rows(x, perm, out=None, stream=None):
+    """out[h, perm[h, p]] = x[h, p]."""
+    sh = make_shape(x)
+    o = out if out is not None else torch.empty_like(x)
+    _check(lib().park_unpermute_rows(ctypes.byref(sh), _ptr(x), _ptr(perm), _ptr(o), _stream(stream)))
+    return o
+
+
+_FWD_FIELDS = {
+    "metric": lambda H, N, D, cq, ck: ((H, D, D), torch.float32),
+    "q_labels": lambda H, N, D, cq, ck: ((H, N), torch.int32),
+    "q_perm": lambda H, N, D, cq, ck: ((H, N), torch.int32),
+    "q_offsets": lambda H, N, D, cq, ck: ((H, cq + 1), torch.int32),
+    "k_labels": lambda H, N, D, cq, ck: ((H, N), torch.int32),
+    "k_perm": lambda H, N, D, cq, ck: ((H, N), torch.int32),
+    "k_offsets": lambda H, N, D, cq, ck: ((H, ck + 1), torch.int32),
+    "map": lambda H, N, D, cq, ck: ((H, cq, ck), torch.float32),
+    "mask": lambda H, N, D, cq, ck: ((H, cq, ck), torch.uint8),
+    "counts": lambda H, N, D, cq, ck: ((H, cq), torch.int32),
+    "cols": lambda H, N, D, cq, ck: ((H, cq, ck), torch.int32),
+    "sel_keys": lambda H, N, D, cq, ck: ((H, cq), torch.int64),
+    "lse": lambda H, N, D, cq, ck: ((H, N), torch.float32),
+}
+
+
+def park_forward(q, k, v, cq, ck, iters, p, scale=0.0, seed=0, kmetric=PARK_QRKC, init=PARK_INIT_KMEANSPP,
+                 q_centroids=None, k_centroids=None, outputs=(), out=None, ws=None, stream=None):
+    """The whole path for one layer. ``outputs`` names intermediates to return (see
+    park_forward_outputs); q_centroids / k_centroids are caller state for warm starts."""
+    sh = make_shape(q)
+    H, N, D = sh.heads, sh.n, sh.d
+    dev = q.device
+    if q_centroids is None:
+        q_centroids = torch.empty(H, cq, D, dtype=torch.float32, device=dev)
+    if k_centroids is None:
+        k_centroids = torch.empty(H, ck, D, dtype=torch.float32, device=dev)
+    o = out if out is not None else torch.empty_like(q)
+    res = {}
+    fo = park_forward_outputs()
+    for name in outputs:
+        shp, dt = _FWD_FIELDS[name](H, N, D, cq, ck)
+        t = torch.empty(shp, dtype=dt, device=dev)
+        res[name] = t
+        setattr(fo, name, t.data_ptr())
+    prm = make_params(cq, ck, iters, p, scale, seed, kmetric, init)
+    wp, wn = _ws(PARK_ENTRY_FORWARD, sh, prm, dev, ws)
+    _check(lib().park_forward(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(o), ctypes.byref(prm),
+                              _ptr(q_centroids), _ptr(k_centroids), ctypes.byref(fo), wp, wn, _stream(stream)))
+    res.update(out=o, q_centroids=q_centroids, k_centroids=k_centroids)
+    return res

@@ -1,0 +1,306 @@
+// PAMA block-importance map (PARK page, Figure 2 caption and abstract): every original query keeps
+// its own softmax over the key centroids (logit scale*q.c_j + ln n_j), and the distributions are
+// averaged within each query cluster.
+//
+// Work item = up to 256 consecutive cluster-ordered queries of one query cluster. bf16 data: four
+// waves, each handling four 16-query tiles with 16x16x32 MFMA (queries = A rows, centroids = B
+// columns), so every centroid fragment loaded feeds four MFMAs.
+// Pass 1 keeps a running (max, sum) per query with one exp per logit; pass 2 recomputes the
+// logits and adds exp(l - max) / sum into per-wave column sums in LDS. Partial column sums of each
+// work item are then summed per cluster in fixed order in fp64 and divided by the cluster size.
+#include "park_common.h"
+#include "park_internal.h"
+
+namespace park {
+
+namespace {
+
+// Per head: chunk_base[i] = work items of query clusters before i; chunk_base[cq] = total.
+__global__ __launch_bounds__(1024) void pama_chunks(const int32_t* __restrict__ q_offsets, int cq,
+                                                    int32_t* __restrict__ chunk_base) {
+  __shared__ int scratch[17];
+  const int h = blockIdx.x;
+  const int32_t* off = q_offsets + (int64_t)h * (cq + 1);
+  int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
+  const int per = (cq + 1023) / 1024;
+  const int i0 = threadIdx.x * per;
+  int local = 0;
+  for (int k = 0; k < per; ++k)
+    if (i0 + k < cq) local += (off[i0 + k + 1] - off[i0 + k] + kPamaRows - 1) / kPamaRows;
+  int total;
+  int run = block_exclusive_scan(local, scratch, &total);
+  for (int k = 0; k < per; ++k) {
+    if (i0 + k < cq) {
+      cb[i0 + k] = run;
+      run += (off[i0 + k + 1] - off[i0 + k] + kPamaRows - 1) / kPamaRows;
+    }
+  }
+  if (threadIdx.x == 0) cb[cq] = total;
+}
+
+// Consumed key centroids (bf16-rounded) and ln n_j (-inf for empty clusters).
+__global__ __launch_bounds__(256) void pama_prep(const float* __restrict__ k_cent, const int32_t* __restrict__ k_off,
+                                                 int ck, int D, uint16_t* __restrict__ khat,
+                                                 float* __restrict__ logn) {
+  const int h = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tot = (int64_t)ck * D;
+  if (e < tot) khat[(int64_t)h * tot + e] = (uint16_t)f32_to_bf16_bits(k_cent[(int64_t)h * tot + e]);
+  if (e < ck) {
+    const int n = k_off[(int64_t)h * (ck + 1) + e + 1] - k_off[(int64_t)h * (ck + 1) + e];
+    logn[(int64_t)h * ck + e] = n > 0 ? logf((float)n) : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ int find_item(const int32_t* cb, int cq, int c) {
+  // largest i with cb[i] <= c and cb[i+1] > c
+  int lo = 0, hi = cq;  // cb[lo] <= c < cb[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cb[mid] <= c)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q, int64_t N,
+                                                 const int32_t* __restrict__ q_perm,
+                                                 const int32_t* __restrict__ q_off, int cq,
+                                                 const uint16_t* __restrict__ khat, const float* __restrict__ logn,
+                                                 int ck, float scale, const int32_t* __restrict__ chunk_base,
+                                                 int max_chunks, float* __restrict__ partial) {
+  constexpr int KS = D / 32;
+  constexpr int TW = 4;  // 16-query tiles per wave: each centroid fragment feeds TW MFMAs
+  __shared__ float colsum[4][kMaxClusters];
+  const int h = blockIdx.y;
+  const int c = blockIdx.x;
+  const int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
+  if (c >= cb[cq]) return;
+  const int i = find_item(cb, cq, c);
+  const int32_t* off = q_off + (int64_t)h * (cq + 1);
+  const int row0 = off[i] + (c - cb[i]) * kPamaRows;
+  const int row_end = min(row0 + kPamaRows, off[i + 1]);
+  const int l = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int g = l / 16;  // lane group: rows g*4 .. g*4+3 of a tile
+  const uint16_t* Qh = Q + (int64_t)h * N * D;
+  const int32_t* ph = q_perm + (int64_t)h * N;
+  const uint16_t* kh = khat + (int64_t)h * ck * D;
+  const float* lnh = logn + (int64_t)h * ck;
+  const int nct = (ck + 15) / 16;
+  for (int j = threadIdx.x; j < 4 * kMaxClusters; j += 256) (&colsum[0][0])[j] = 0.f;
+  __syncthreads();
+
+  const int w0 = row0 + w * 16 * TW;  // this wave's first row
+  if (w0 < row_end) {
+    // A operands: query row w0 + t*16 + l%16, dims kk*32 + g*8 .. +7
+    u32x4_t qa[TW][KS];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int r = w0 + t * 16 + l % 16;
+      const bool ok = r < row_end;
+      const uint16_t* qrow = Qh + (int64_t)(ok ? ph[r] : 0) * D;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4_t*>(qrow + kk * 32 + g * 8);
+        qa[t][kk] = v;
+      }
+    }
+    // pass 1: per-lane running (max, sum) of rows t*16 + g*4 + e over this lane's centroid column
+    float m[TW][4], s[TW][4];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[t][e] = -INFINITY;
+        s[t][e] = 0.f;
+      }
+    for (int ct = 0; ct < nct; ++ct) {
+      const int j = ct * 16 + l % 16;
+      const bool jok = j < ck;
+      u32x4_t bv[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (jok) v = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)j * D + kk * 32 + g * 8);
+        bv[kk] = v;
+      }
+      const float ln = jok ? lnh[j] : -INFINITY;
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lg = acc[e] * scale + ln;
+          if (lg > m[t][e]) {
+            s[t][e] = s[t][e] * __expf(m[t][e] - lg) + 1.f;
+            m[t][e] = lg;
+          } else if (lg > -INFINITY) {
+            s[t][e] += __expf(lg - m[t][e]);
+          }
+        }
+      }
+    }
+    // merge (max, sum) across the 16 lanes of each group; 1/sum per row
+    float inv[TW][4];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float mo = __shfl_xor(m[t][e], o, kWave);
+          const float so = __shfl_xor(s[t][e], o, kWave);
+          const float mn = fmaxf(m[t][e], mo);
+          float sn = 0.f;
+          if (mn > -INFINITY) sn = s[t][e] * __expf(m[t][e] - mn) + so * __expf(mo - mn);
+          m[t][e] = mn;
+          s[t][e] = sn;
+        }
+        const bool ok = (w0 + t * 16 + g * 4 + e) < row_end && s[t][e] > 0.f;
+        inv[t][e] = ok ? 1.f / s[t][e] : 0.f;
+        if (!ok) m[t][e] = 0.f;
+      }
+    }
+    // pass 2: accumulate normalised weights into the wave's column sums
+    for (int ct = 0; ct < nct; ++ct) {
+      const int j = ct * 16 + l % 16;
+      const bool jok = j < ck;
+      u32x4_t bv[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (jok) v = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)j * D + kk * 32 + g * 8);
+        bv[kk] = v;
+      }
+      const float ln = jok ? lnh[j] : -INFINITY;
+      float cs = 0.f;
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
+        float ct_sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lg = acc[e] * scale + ln;
+          ct_sum += (inv[t][e] > 0.f && lg > -INFINITY) ? __expf(lg - m[t][e]) * inv[t][e] : 0.f;
+        }
+        cs += ct_sum;
+      }
+      cs += __shfl_xor(cs, 16, kWave);
+      cs += __shfl_xor(cs, 32, kWave);
+      if (g == 0 && jok) colsum[w][j] = cs;
+    }
+  }
+  __syncthreads();
+  float* out = partial + ((int64_t)h * max_chunks + c) * ck;
+  for (int j = threadIdx.x; j < ck; j += 256) out[j] = ((colsum[0][j] + colsum[1][j]) + colsum[2][j]) + colsum[3][j];
+}
+
+// fp32 data: one thread per query row, fp64 logits and weights, block-wide column sums.
+template <int D>
+__global__ __launch_bounds__(256) void pama_f32(const float* __restrict__ Q, int64_t N,
+                                                const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off,
+                                                int cq, const float* __restrict__ k_cent,
+                                                const int32_t* __restrict__ k_off, int ck, float scale,
+                                                const int32_t* __restrict__ chunk_base, int max_chunks,
+                                                float* __restrict__ partial) {
+  __shared__ double red[4];
+  const int h = blockIdx.y;
+  const int c = blockIdx.x;
+  const int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
+  if (c >= cb[cq]) return;
+  const int i = find_item(cb, cq, c);
+  const int32_t* off = q_off + (int64_t)h * (cq + 1);
+  const int r = off[i] + (c - cb[i]) * kPamaRows + threadIdx.x;
+  const bool ok = r < off[i + 1];
+  const float* q = Q + ((int64_t)h * N + (ok ? q_perm[(int64_t)h * N + r] : 0)) * D;
+  const float* kc = k_cent + (int64_t)h * ck * D;
+  const int32_t* ko = k_off + (int64_t)h * (ck + 1);
+  double m = -INFINITY, s = 0.0;
+  for (int j = 0; j < ck; ++j) {
+    const int n = ko[j + 1] - ko[j];
+    if (n == 0) continue;
+    double dot = 0.0;
+    for (int a = 0; a < D; ++a) dot += (double)q[a] * (double)kc[j * D + a];
+    const double lg = (double)scale * dot + log((double)n);
+    if (lg > m) {
+      s = s * exp(m - lg) + 1.0;
+      m = lg;
+    } else {
+      s += exp(lg - m);
+    }
+  }
+  float* out = partial + ((int64_t)h * max_chunks + c) * ck;
+  for (int j = 0; j < ck; ++j) {
+    const int n = ko[j + 1] - ko[j];
+    double wv = 0.0;
+    if (ok && n > 0) {
+      double dot = 0.0;
+      for (int a = 0; a < D; ++a) dot += (double)q[a] * (double)kc[j * D + a];
+      wv = exp((double)scale * dot + log((double)n) - m) / s;
+    }
+    wv = wave_sum_f64(wv);
+    if (lane_id() == 0) red[threadIdx.x / kWave] = wv;
+    __syncthreads();
+    if (threadIdx.x == 0) out[j] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void pama_reduce(const float* __restrict__ partial, const int32_t* __restrict__ q_off,
+                                                   const int32_t* __restrict__ chunk_base, int cq, int ck,
+                                                   int max_chunks, float* __restrict__ map) {
+  const int h = blockIdx.y;
+  const int i = blockIdx.x;
+  const int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
+  const int n = q_off[(int64_t)h * (cq + 1) + i + 1] - q_off[(int64_t)h * (cq + 1) + i];
+  float* row = map + ((int64_t)h * cq + i) * ck;
+  for (int j = threadIdx.x; j < ck; j += 256) {
+    double s = 0.0;
+    for (int c = cb[i]; c < cb[i + 1]; ++c) s += (double)partial[((int64_t)h * max_chunks + c) * ck + j];
+    row[j] = n > 0 ? (float)(s / (double)n) : 0.f;
+  }
+}
+
+}  // namespace
+
+int64_t pama_max_chunks(const Dims& s, int cq) { return ceil_div(s.N, kPamaRows) + cq; }
+
+hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, const int32_t* q_offsets, int cq,
+                       const float* k_cent, const int32_t* k_offsets, int ck, float scale, float* map, void* khat,
+                       float* logn, int32_t* chunk_base, float* partial, hipStream_t st) {
+  const int maxc = (int)pama_max_chunks(s, cq);
+  pama_chunks<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, chunk_base);
+  const dim3 grid((unsigned)maxc, (unsigned)s.H);
+  if (s.bf16) {
+    const dim3 pg((unsigned)ceil_div((int64_t)ck * s.D, 256), (unsigned)s.H);
+    pama_prep<<<pg, 256, 0, st>>>(k_cent, k_offsets, ck, (int)s.D, static_cast<uint16_t*>(khat), logn);
+    if (s.D == 128)
+      pama_bf16<128><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+                                           static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base, maxc,
+                                           partial);
+    else
+      pama_bf16<64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+                                          static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base, maxc,
+                                          partial);
+  } else {
+    if (s.D == 128)
+      pama_f32<128><<<grid, 256, 0, st>>>(static_cast<const float*>(q), s.N, q_perm, q_offsets, cq, k_cent,
+                                          k_offsets, ck, scale, chunk_base, maxc, partial);
+    else
+      pama_f32<64><<<grid, 256, 0, st>>>(static_cast<const float*>(q), s.N, q_perm, q_offsets, cq, k_cent,
+                                         k_offsets, ck, scale, chunk_base, maxc, partial);
+  }
+  pama_reduce<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(partial, q_offsets, chunk_base, cq, ck, maxc, map);
+  return hipGetLastError();
+}
+
+}  // namespace park

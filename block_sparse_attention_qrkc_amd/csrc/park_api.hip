@@ -1,0 +1,498 @@
+// C ABI of the library: host-side validation, workspace carving and launch sequencing.
+// Nothing is enqueued before every argument has been checked; no exception leaves this file.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/park.h"
+#include "park_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+park_status fail(park_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+park_status fail(park_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+park_status ok() {
+  g_last_error.clear();
+  return PARK_OK;
+}
+
+park_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PARK_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Bump allocator over the caller's workspace; with a null base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+park_status check_shape(const park_shape* s, park::Dims* out) {
+  if (!s) return fail(PARK_EINVAL, "shape is NULL");
+  if (s->heads < 1 || s->heads > 65535) return fail(PARK_EINVAL, "heads must be in [1, 65535], got %lld", (long long)s->heads);
+  if (s->n < 1 || s->n >= (int64_t(1) << 24)) return fail(PARK_EINVAL, "n must be in [1, 2^24), got %lld", (long long)s->n);
+  if (s->d != 64 && s->d != 128) return fail(PARK_EUNSUPPORTED, "d must be 64 or 128, got %lld", (long long)s->d);
+  if (s->dtype != PARK_F32 && s->dtype != PARK_BF16) return fail(PARK_EUNSUPPORTED, "dtype must be PARK_F32 or PARK_BF16");
+  *out = park::Dims{s->heads, s->n, s->d, s->dtype == PARK_BF16 ? 1 : 0};
+  return PARK_OK;
+}
+
+park_status check_clusters(const park::Dims& s, int64_t c, const char* name) {
+  if (c < 1 || c > park::kMaxClusters || c > s.N)
+    return fail(PARK_EINVAL, "%s must be in [1, min(n, %d)], got %lld", name, park::kMaxClusters, (long long)c);
+  return PARK_OK;
+}
+
+park_status check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(PARK_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(PARK_EINVAL, "%s must be %zu-byte aligned", name, align);
+  return PARK_OK;
+}
+
+#define PARK_TRY(expr)               \
+  do {                               \
+    park_status _st = (expr);        \
+    if (_st != PARK_OK) return _st;  \
+  } while (0)
+
+float resolve_scale(float scale, int64_t d) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)d); }
+
+// ---------------------------------------------------------------------------------------------
+// Workspace plans (shared by the size query and the carving)
+// ---------------------------------------------------------------------------------------------
+
+struct MetricWs {
+  double* partial;
+};
+MetricWs plan_metric(Carver& cv, const park::Dims& s) {
+  MetricWs w;
+  w.partial = cv.take<double>(s.bf16 ? park::metric_partial_count(s) : 1);
+  return w;
+}
+
+struct ClusterWs {
+  double* cand_norm;
+  int32_t* table;
+  void* g;
+  float* b;
+};
+ClusterWs plan_cluster(Carver& cv, const park::Dims& s, int C) {
+  ClusterWs w;
+  w.cand_norm = cv.take<double>((size_t)s.H * park::kpp_candidates(s.N, C));
+  w.table = cv.take<int32_t>(park::sort_table_ints(s, C));
+  w.g = s.bf16 ? (void*)cv.take<uint16_t>((size_t)(s.H * C * s.D)) : (void*)cv.take<float>((size_t)(s.H * C * s.D));
+  w.b = cv.take<float>((size_t)(s.H * C));
+  return w;
+}
+
+struct MapWs {
+  uint16_t* khat;
+  float* logn;
+  int32_t* chunk_base;
+  float* partial;
+};
+MapWs plan_map(Carver& cv, const park::Dims& s, int cq, int ck) {
+  MapWs w;
+  w.khat = cv.take<uint16_t>((size_t)(s.H * ck * s.D));
+  w.logn = cv.take<float>((size_t)(s.H * ck));
+  w.chunk_base = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
+  w.partial = cv.take<float>((size_t)(s.H * park::pama_max_chunks(s, cq) * ck));
+  return w;
+}
+
+struct AttnWs {
+  int32_t* tile_base;
+  int32_t* runs;
+};
+AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck) {
+  AttnWs w;
+  w.tile_base = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
+  w.runs = cv.take<int32_t>((size_t)(s.H * cq * (2 * ck + 3)));
+  return w;
+}
+
+struct ForwardWs {
+  float* metric;
+  int32_t *q_labels, *q_perm, *q_offsets, *k_labels, *k_perm, *k_offsets;
+  float* map;
+  int32_t *counts, *cols;
+  int64_t* sel_keys;
+  MetricWs mt;
+  ClusterWs qc, kc;
+  MapWs mw;
+  AttnWs aw;
+};
+ForwardWs plan_forward(Carver& cv, const park::Dims& s, const park_params& p) {
+  ForwardWs w;
+  const size_t hn = (size_t)(s.H * s.N);
+  w.metric = cv.take<float>((size_t)(s.H * s.D * s.D));
+  w.q_labels = cv.take<int32_t>(hn);
+  w.q_perm = cv.take<int32_t>(hn);
+  w.q_offsets = cv.take<int32_t>((size_t)(s.H * (p.cq + 1)));
+  w.k_labels = cv.take<int32_t>(hn);
+  w.k_perm = cv.take<int32_t>(hn);
+  w.k_offsets = cv.take<int32_t>((size_t)(s.H * (p.ck + 1)));
+  w.map = cv.take<float>((size_t)(s.H * p.cq * p.ck));
+  w.counts = cv.take<int32_t>((size_t)(s.H * p.cq));
+  w.cols = cv.take<int32_t>((size_t)(s.H * p.cq * p.ck));
+  w.sel_keys = cv.take<int64_t>((size_t)(s.H * p.cq));
+  w.mt = plan_metric(cv, s);
+  w.qc = plan_cluster(cv, s, p.cq);
+  w.kc = plan_cluster(cv, s, p.ck);
+  w.mw = plan_map(cv, s, p.cq, p.ck);
+  w.aw = plan_attn(cv, s, p.cq, p.ck);
+  return w;
+}
+
+park_status check_params(const park::Dims& s, const park_params* p, bool need_iters) {
+  if (!p) return fail(PARK_EINVAL, "params is NULL");
+  PARK_TRY(check_clusters(s, p->cq, "cq"));
+  PARK_TRY(check_clusters(s, p->ck, "ck"));
+  if (p->iters < (need_iters ? 1 : 0) || p->iters > 100000)
+    return fail(PARK_EINVAL, "iters must be in [%d, 100000], got %d", need_iters ? 1 : 0, p->iters);
+  if (!(p->p > 0.0 && p->p <= 1.0)) return fail(PARK_EINVAL, "p must be in (0, 1], got %g", p->p);
+  if (p->kmetric != PARK_EUCLID && p->kmetric != PARK_QRKC) return fail(PARK_EINVAL, "kmetric must be PARK_EUCLID or PARK_QRKC");
+  if (p->init != PARK_INIT_KMEANSPP && p->init != PARK_INIT_WARM) return fail(PARK_EINVAL, "init must be PARK_INIT_KMEANSPP or PARK_INIT_WARM");
+  if (std::isnan(p->scale)) return fail(PARK_EINVAL, "scale is NaN");
+  return PARK_OK;
+}
+
+park_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return PARK_OK;
+  if (ws_bytes < need) return fail(PARK_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  if (!ws) return fail(PARK_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(PARK_EINVAL, "workspace must be 256-byte aligned");
+  return PARK_OK;
+}
+
+size_t forward_ws_bytes(const park::Dims& s, const park_params& p) {
+  Carver cv(nullptr);
+  plan_forward(cv, s, p);
+  return cv.off;
+}
+
+// Clustering sequence shared by park_cluster and park_forward.
+hipError_t run_cluster(const park::Dims& s, const void* x, const float* metric, int C, int iters, int init,
+                       uint64_t seed, int side, float* cent, int32_t* labels, int32_t* perm, int32_t* offsets,
+                       const ClusterWs& w, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (init == PARK_INIT_KMEANSPP) {
+    e = park::launch_kpp(s, x, metric, C, seed, side, cent, w.cand_norm, st);
+    if (e != hipSuccess) return e;
+  }
+  if (iters == 0) return e;
+  e = park::launch_consume(s, x, C, nullptr, nullptr, cent, 0, metric, w.g, w.b, st);
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    e = park::launch_assign(s, x, C, w.g, w.b, labels, st);
+    if (e == hipSuccess) e = park::launch_sort(s, C, labels, w.table, perm, offsets, st);
+    if (e == hipSuccess) e = park::launch_consume(s, x, C, perm, offsets, cent, 1, metric, w.g, w.b, st);
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* park_version(void) { return "park-mi355x 0.1.0 (gfx950)"; }
+
+const char* park_status_string(int32_t status) {
+  switch (status) {
+    case PARK_OK: return "PARK_OK";
+    case PARK_EINVAL: return "PARK_EINVAL";
+    case PARK_EUNSUPPORTED: return "PARK_EUNSUPPORTED";
+    case PARK_EWORKSPACE: return "PARK_EWORKSPACE";
+    case PARK_EHIP: return "PARK_EHIP";
+    default: return "PARK_UNKNOWN";
+  }
+}
+
+const char* park_last_error(void) { return g_last_error.c_str(); }
+
+size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_params* params) {
+  try {
+    park::Dims s;
+    if (check_shape(shape, &s) != PARK_OK) return 0;
+    Carver cv(nullptr);
+    switch (entry) {
+      case PARK_ENTRY_METRIC:
+        plan_metric(cv, s);
+        return cv.off;
+      case PARK_ENTRY_CLUSTER_Q:
+      case PARK_ENTRY_CLUSTER_K: {
+        if (!params) return 0;
+        const int C = entry == PARK_ENTRY_CLUSTER_Q ? params->cq : params->ck;
+        if (check_clusters(s, C, "clusters") != PARK_OK) return 0;
+        plan_cluster(cv, s, C);
+        return cv.off;
+      }
+      case PARK_ENTRY_RETRIEVE_MAP:
+        if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
+        plan_map(cv, s, params->cq, params->ck);
+        return cv.off;
+      case PARK_ENTRY_SELECT_TOPP:
+        return 0;
+      case PARK_ENTRY_SPARSE_ATTN:
+        if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
+        plan_attn(cv, s, params->cq, params->ck);
+        return cv.off;
+      case PARK_ENTRY_FORWARD:
+        if (check_params(s, params, true) != PARK_OK) return 0;
+        return forward_ws_bytes(s, *params);
+      default:
+        return 0;
+    }
+  } catch (...) {
+    return 0;
+  }
+}
+
+park_status park_qrkc_metric(const park_shape* shape, const void* q, float* metric, void* ws, size_t ws_bytes,
+                             void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(q, "q", 16));
+    PARK_TRY(check_ptr(metric, "metric", 4));
+    Carver meas(nullptr);
+    plan_metric(meas, s);
+    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+    Carver cv(ws);
+    MetricWs w = plan_metric(cv, s);
+    return hip_check(park::launch_metric(s, q, metric, w.partial, (hipStream_t)stream), "park_qrkc_metric");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_qrkc_metric: internal error");
+  }
+}
+
+park_status park_cluster(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
+                         int32_t n_clusters, int32_t iters, int32_t init, uint64_t seed, int32_t side, float* centroids,
+                         int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(x, "x", 16));
+    PARK_TRY(check_clusters(s, n_clusters, "n_clusters"));
+    if (metric != PARK_EUCLID && metric != PARK_QRKC) return fail(PARK_EINVAL, "metric must be PARK_EUCLID or PARK_QRKC");
+    if (metric == PARK_QRKC) PARK_TRY(check_ptr(qmetric, "qmetric", 4));
+    if (iters < 0 || iters > 100000) return fail(PARK_EINVAL, "iters must be in [0, 100000], got %d", iters);
+    if (init != PARK_INIT_KMEANSPP && init != PARK_INIT_WARM) return fail(PARK_EINVAL, "init must be PARK_INIT_KMEANSPP or PARK_INIT_WARM");
+    if (side != PARK_SIDE_Q && side != PARK_SIDE_K) return fail(PARK_EINVAL, "side must be PARK_SIDE_Q or PARK_SIDE_K");
+    PARK_TRY(check_ptr(centroids, "centroids", 4));
+    if (iters > 0) {
+      PARK_TRY(check_ptr(labels, "labels", 4));
+      PARK_TRY(check_ptr(perm, "perm", 4));
+      PARK_TRY(check_ptr(offsets, "offsets", 4));
+    }
+    Carver meas(nullptr);
+    plan_cluster(meas, s, n_clusters);
+    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+    Carver cv(ws);
+    ClusterWs w = plan_cluster(cv, s, n_clusters);
+    const float* mp = metric == PARK_QRKC ? qmetric : nullptr;
+    return hip_check(run_cluster(s, x, mp, n_clusters, iters, init, seed, side, centroids, labels, perm, offsets, w,
+                                 (hipStream_t)stream),
+                     "park_cluster");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_cluster: internal error");
+  }
+}
+
+park_status park_retrieve_map(const park_shape* shape, const void* q, const int32_t* q_perm, const int32_t* q_offsets,
+                              int32_t cq, const float* k_centroids, const int32_t* k_offsets, int32_t ck, float scale,
+                              float* map, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(q, "q", 16));
+    PARK_TRY(check_ptr(q_perm, "q_perm", 4));
+    PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
+    PARK_TRY(check_ptr(k_centroids, "k_centroids", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(map, "map", 4));
+    PARK_TRY(check_clusters(s, cq, "cq"));
+    PARK_TRY(check_clusters(s, ck, "ck"));
+    if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
+    Carver meas(nullptr);
+    plan_map(meas, s, cq, ck);
+    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+    Carver cv(ws);
+    MapWs w = plan_map(cv, s, cq, ck);
+    return hip_check(park::launch_pama(s, q, q_perm, q_offsets, cq, k_centroids, k_offsets, ck,
+                                       resolve_scale(scale, s.D), map, w.khat, w.logn, w.chunk_base, w.partial,
+                                       (hipStream_t)stream),
+                     "park_retrieve_map");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_retrieve_map: internal error");
+  }
+}
+
+park_status park_select_topp(const float* map, int64_t heads, int32_t cq, int32_t ck, const int32_t* k_offsets,
+                             double p, uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys,
+                             void* stream) {
+  try {
+    if (heads < 1 || heads > 65535) return fail(PARK_EINVAL, "heads must be in [1, 65535]");
+    if (cq < 1 || cq > park::kMaxClusters) return fail(PARK_EINVAL, "cq must be in [1, %d]", park::kMaxClusters);
+    if (ck < 1 || ck > park::kMaxClusters) return fail(PARK_EINVAL, "ck must be in [1, %d]", park::kMaxClusters);
+    if (!(p > 0.0 && p <= 1.0)) return fail(PARK_EINVAL, "p must be in (0, 1], got %g", p);
+    PARK_TRY(check_ptr(map, "map", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(counts, "counts", 4));
+    PARK_TRY(check_ptr(cols, "cols", 4));
+    if (sel_keys) PARK_TRY(check_ptr(sel_keys, "sel_keys", 8));
+    return hip_check(park::launch_select_topp(map, heads, cq, ck, k_offsets, p, mask, counts, cols, sel_keys,
+                                              (hipStream_t)stream),
+                     "park_select_topp");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_select_topp: internal error");
+  }
+}
+
+park_status park_sparse_attn(const park_shape* shape, const void* q, const void* k, const void* v, const int32_t* q_perm,
+                             const int32_t* q_offsets, int32_t cq, const int32_t* k_perm, const int32_t* k_offsets,
+                             int32_t ck, const int32_t* counts, const int32_t* cols, float scale, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(q, "q", 16));
+    PARK_TRY(check_ptr(k, "k", 16));
+    PARK_TRY(check_ptr(v, "v", 16));
+    PARK_TRY(check_ptr(out, "out", 16));
+    PARK_TRY(check_ptr(q_perm, "q_perm", 4));
+    PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
+    PARK_TRY(check_ptr(k_perm, "k_perm", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(counts, "counts", 4));
+    PARK_TRY(check_ptr(cols, "cols", 4));
+    if (lse) PARK_TRY(check_ptr(lse, "lse", 4));
+    PARK_TRY(check_clusters(s, cq, "cq"));
+    PARK_TRY(check_clusters(s, ck, "ck"));
+    if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
+    Carver meas(nullptr);
+    plan_attn(meas, s, cq, ck);
+    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+    Carver cv(ws);
+    AttnWs w = plan_attn(cv, s, cq, ck);
+    return hip_check(park::launch_sparse_attn(s, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts, cols,
+                                              resolve_scale(scale, s.D), out, lse, w.tile_base, w.runs,
+                                              (hipStream_t)stream),
+                     "park_sparse_attn");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_sparse_attn: internal error");
+  }
+}
+
+park_status park_permute_rows(const park_shape* shape, const void* x, const int32_t* perm, void* out, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(x, "x", 16));
+    PARK_TRY(check_ptr(perm, "perm", 4));
+    PARK_TRY(check_ptr(out, "out", 16));
+    if (x == out) return fail(PARK_EINVAL, "x and out must not overlap");
+    return hip_check(park::launch_permute(s, x, perm, out, 0, (hipStream_t)stream), "park_permute_rows");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_permute_rows: internal error");
+  }
+}
+
+park_status park_unpermute_rows(const park_shape* shape, const void* x, const int32_t* perm, void* out, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(x, "x", 16));
+    PARK_TRY(check_ptr(perm, "perm", 4));
+    PARK_TRY(check_ptr(out, "out", 16));
+    if (x == out) return fail(PARK_EINVAL, "x and out must not overlap");
+    return hip_check(park::launch_permute(s, x, perm, out, 1, (hipStream_t)stream), "park_unpermute_rows");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_unpermute_rows: internal error");
+  }
+}
+
+park_status park_forward(const park_shape* shape, const void* q, const void* k, const void* v, void* out,
+                         const park_params* params, float* q_centroids, float* k_centroids,
+                         const park_forward_outputs* outputs, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_params(s, params, true));
+    PARK_TRY(check_ptr(q, "q", 16));
+    PARK_TRY(check_ptr(k, "k", 16));
+    PARK_TRY(check_ptr(v, "v", 16));
+    PARK_TRY(check_ptr(out, "out", 16));
+    PARK_TRY(check_ptr(q_centroids, "q_centroids", 4));
+    PARK_TRY(check_ptr(k_centroids, "k_centroids", 4));
+    park_forward_outputs o;
+    std::memset(&o, 0, sizeof(o));
+    if (outputs) o = *outputs;
+    const void* opt[] = {o.metric, o.q_labels, o.q_perm, o.q_offsets, o.k_labels, o.k_perm, o.k_offsets,
+                         o.map, o.counts, o.cols, o.lse};
+    for (const void* ptr : opt)
+      if (ptr && !aligned(ptr, 4)) return fail(PARK_EINVAL, "forward outputs must be 4-byte aligned");
+    if (o.sel_keys && !aligned(o.sel_keys, 8)) return fail(PARK_EINVAL, "sel_keys must be 8-byte aligned");
+    const park_params& p = *params;
+    PARK_TRY(check_ws(ws, ws_bytes, forward_ws_bytes(s, p)));
+    Carver cv(ws);
+    ForwardWs w = plan_forward(cv, s, p);
+    hipStream_t st = (hipStream_t)stream;
+    float* M = o.metric ? o.metric : w.metric;
+    int32_t* ql = o.q_labels ? o.q_labels : w.q_labels;
+    int32_t* qp = o.q_perm ? o.q_perm : w.q_perm;
+    int32_t* qo = o.q_offsets ? o.q_offsets : w.q_offsets;
+    int32_t* kl = o.k_labels ? o.k_labels : w.k_labels;
+    int32_t* kp = o.k_perm ? o.k_perm : w.k_perm;
+    int32_t* ko = o.k_offsets ? o.k_offsets : w.k_offsets;
+    float* map = o.map ? o.map : w.map;
+    int32_t* counts = o.counts ? o.counts : w.counts;
+    int32_t* cols = o.cols ? o.cols : w.cols;
+    int64_t* sk = o.sel_keys ? o.sel_keys : w.sel_keys;
+    const float scale = resolve_scale(p.scale, s.D);
+    const bool qrkc = p.kmetric == PARK_QRKC;
+
+    hipError_t e = hipSuccess;
+    if (qrkc) e = park::launch_metric(s, q, M, w.mt.partial, st);
+    if (e == hipSuccess)
+      e = run_cluster(s, q, nullptr, p.cq, p.iters, p.init, p.seed, PARK_SIDE_Q, q_centroids, ql, qp, qo, w.qc, st);
+    if (e == hipSuccess)
+      e = run_cluster(s, k, qrkc ? M : nullptr, p.ck, p.iters, p.init, p.seed, PARK_SIDE_K, k_centroids, kl, kp, ko,
+                      w.kc, st);
+    if (e == hipSuccess)
+      e = park::launch_pama(s, q, qp, qo, p.cq, k_centroids, ko, p.ck, scale, map, w.mw.khat, w.mw.logn,
+                            w.mw.chunk_base, w.mw.partial, st);
+    if (e == hipSuccess)
+      e = park::launch_select_topp(map, s.H, p.cq, p.ck, ko, p.p, o.mask, counts, cols, sk, st);
+    if (e == hipSuccess)
+      e = park::launch_sparse_attn(s, q, k, v, qp, qo, p.cq, kp, ko, p.ck, counts, cols, scale, out, o.lse,
+                                   w.aw.tile_base, w.aw.runs, st);
+    return hip_check(e, "park_forward");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_forward: internal error");
+  }
+}
+
+}  // extern "C"

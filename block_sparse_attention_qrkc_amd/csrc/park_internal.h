@@ -1,0 +1,66 @@
+// Internal launcher interface between the C ABI layer and the kernels. Every launcher enqueues
+// on `stream` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace park {
+
+struct Dims {
+  int64_t H, N, D;
+  int bf16;  // 1: bf16 data, 0: fp32 data
+};
+
+constexpr int kMaxClusters = 2048;
+constexpr int kMetricChunk = 4096;  // tokens per partial second-moment block
+constexpr int kSortChunk = 1024;    // tokens per counting-sort chunk (one wave)
+constexpr int kPamaRows = 256;      // query rows per PAMA work item
+constexpr int kAttnBM = 128;        // query rows per attention work item
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int kpp_candidates(int64_t n, int c) {
+  int64_t s = 8 * (int64_t)c;
+  if (s < 4096) s = 4096;
+  return (int)(s < n ? s : n);
+}
+
+// metric.hip
+hipError_t launch_metric(const Dims& s, const void* q, float* metric, double* partial, hipStream_t st);
+size_t metric_partial_count(const Dims& s);
+
+// kmeans.hip
+hipError_t launch_kpp(const Dims& s, const void* x, const float* metric, int C, uint64_t seed, int side,
+                      float* cent, double* cand_norm, hipStream_t st);
+hipError_t launch_consume(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets,
+                          float* cent, int do_update, const float* metric, void* g, float* b,
+                          hipStream_t st);
+hipError_t launch_assign(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
+                         hipStream_t st);
+hipError_t launch_sort(const Dims& s, int C, const int32_t* labels, int32_t* table, int32_t* perm,
+                       int32_t* offsets, hipStream_t st);
+size_t sort_table_ints(const Dims& s, int C);
+
+// pama.hip
+hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, const int32_t* q_offsets, int cq,
+                       const float* k_cent, const int32_t* k_offsets, int ck, float scale, float* map,
+                       void* khat, float* logn, int32_t* chunk_base, float* partial, hipStream_t st);
+int64_t pama_max_chunks(const Dims& s, int cq);
+
+// select.hip
+hipError_t launch_select_topp(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double p,
+                              uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st);
+
+// attn.hip
+hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
+                              const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
+                              int ck, const int32_t* counts, const int32_t* cols, float scale, void* out,
+                              float* lse, int32_t* tile_base, int32_t* runs, hipStream_t st);
+int64_t attn_max_tiles(const Dims& s, int cq);
+
+// permute.hip
+hipError_t launch_permute(const Dims& s, const void* x, const int32_t* perm, void* out, int inverse,
+                          hipStream_t st);
+
+}  // namespace park

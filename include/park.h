@@ -1,0 +1,220 @@
+/*
+ * park.h - C ABI of the MI355X (gfx950) PARK block retrieval + block-sparse attention library.
+ *
+ * Method: "PARK: Accurate Block Retrieval for Sparse Attention in Video Diffusion Transformers".
+ * Per attention head: cluster queries with Euclidean K-means and keys with K-means under a metric
+ * derived from the current queries (QRKC), order tokens cluster by cluster, build the PAMA
+ * block-importance map (every query's softmax over the key centroids, averaged within its query
+ * cluster), cut each map row at top-p cumulative mass, and run attention only over the selected
+ * (query cluster, key cluster) pairs.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are device pointers to dense row-major arrays; X of a park_shape is [heads, n, d].
+ *   - The caller owns every buffer, including the workspace (size from park_workspace_bytes).
+ *     The library allocates no device memory and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before anything is enqueued; on error nothing is
+ *     enqueued and park_last_error() holds a message. Device faults surface at the caller's next
+ *     synchronisation. No C++ exception crosses this interface.
+ *   - Supported: d in {64, 128}; dtype PARK_F32 or PARK_BF16; 1 <= clusters <= min(n, 2048);
+ *     1 <= n < 2^24; all pointers 16-byte aligned.
+ *   - Ties and reductions are resolved in a fixed order: results are deterministic run to run.
+ */
+#ifndef PARK_H
+#define PARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PARK_OK = 0,
+  PARK_EINVAL = 1,       /* bad argument (null pointer, size out of range, misalignment) */
+  PARK_EUNSUPPORTED = 2, /* valid but not supported here (d, dtype) */
+  PARK_EWORKSPACE = 3,   /* workspace smaller than park_workspace_bytes() */
+  PARK_EHIP = 4          /* a HIP launch or runtime call failed */
+} park_status;
+
+typedef enum { PARK_F32 = 0, PARK_BF16 = 1 } park_dtype;
+typedef enum { PARK_EUCLID = 0, PARK_QRKC = 1 } park_metric;
+typedef enum { PARK_INIT_KMEANSPP = 0, PARK_INIT_WARM = 1 } park_init;
+typedef enum { PARK_SIDE_Q = 0, PARK_SIDE_K = 1 } park_side;
+
+typedef struct {
+  int64_t heads; /* independent attention heads */
+  int64_t n;     /* tokens per head */
+  int64_t d;     /* head dimension: 64 or 128 */
+  int32_t dtype; /* park_dtype of Q, K, V and the attention output */
+} park_shape;
+
+typedef struct {
+  int32_t cq;      /* query clusters (NQ on the PARK pages, Tables 7-8) */
+  int32_t ck;      /* key clusters (NK) */
+  int32_t iters;   /* Lloyd iterations per clustering, >= 1 for park_forward */
+  double p;        /* top-p threshold, 0 < p <= 1 (PARK page, Table 1: p = 0.9) */
+  float scale;     /* softmax scale; <= 0 selects 1/sqrt(d) */
+  uint64_t seed;   /* k-means++ seed */
+  int32_t kmetric; /* park_metric of the key clustering: PARK_QRKC (default) or PARK_EUCLID */
+  int32_t init;    /* park_init: PARK_INIT_KMEANSPP, or PARK_INIT_WARM to start from the
+                      centroids already in the caller's centroid buffers */
+} park_params;
+
+/* Entry identifiers for park_workspace_bytes. */
+enum {
+  PARK_ENTRY_METRIC = 0,
+  PARK_ENTRY_CLUSTER_Q = 1, /* park_cluster with cq clusters, Euclidean */
+  PARK_ENTRY_CLUSTER_K = 2, /* park_cluster with ck clusters, metric kmetric */
+  PARK_ENTRY_RETRIEVE_MAP = 3,
+  PARK_ENTRY_SELECT_TOPP = 4,
+  PARK_ENTRY_SPARSE_ATTN = 5,
+  PARK_ENTRY_FORWARD = 6
+};
+
+/* Workspace bytes an entry needs for this shape and these parameters (0 on invalid input). */
+size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_params* params);
+
+/* Human-readable name of a status code (static string). */
+const char* park_status_string(int32_t status);
+
+/* Detail of the last error on the calling thread ("" when none). */
+const char* park_last_error(void);
+
+/* Library version string. */
+const char* park_version(void);
+
+/*
+ * QRKC key metric. PARK page, Figure 2 caption and abstract: keys are transformed with a metric
+ * derived from the current queries so that keys with similar QK scores group together. Reading:
+ * M_h = (1/n) sum_t q_t q_t^T, so (k - c)^T M (k - c) is the mean over the current queries of the
+ * squared QK-score difference (q.k - q.c)^2.
+ *   q      [heads, n, d] of shape->dtype
+ *   metric [heads, d, d] float32 output (symmetric)
+ */
+park_status park_qrkc_metric(const park_shape* shape, const void* q, float* metric, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * K-means clustering of one token side (PARK page, Figure 2 caption: queries with Euclidean
+ * K-means, keys with the query-derived metric).
+ *   x          [heads, n, d] of shape->dtype: queries or keys
+ *   metric     PARK_EUCLID, or PARK_QRKC with qmetric = [heads, d, d] float32 from
+ *              park_qrkc_metric (NULL for PARK_EUCLID)
+ *   n_clusters C, 1 <= C <= min(n, 2048)
+ *   iters      Lloyd iterations (assign, then update) >= 0
+ *   init       PARK_INIT_KMEANSPP: seeded k-means++ over the strided candidate rows
+ *              floor(i*n/S), S = min(n, max(4096, 8C)), draws from the SplitMix64 counter stream
+ *              (seed, head, side); PARK_INIT_WARM: start from the values in `centroids`
+ *   side       park_side, selects the random stream
+ *   centroids  [heads, C, d] float32, output (input too for PARK_INIT_WARM): after the last
+ *              update each centroid is the mean of its members; empty clusters keep their value
+ *   labels     [heads, n] int32: cluster of each token from the last assignment
+ *   perm       [heads, n] int32: token at each cluster-ordered position (stable: tokens of one
+ *              cluster keep their original order)
+ *   offsets    [heads, C + 1] int32: cluster j occupies positions offsets[j] .. offsets[j+1]-1
+ * Assignment: label(x) = argmin_j b_j - 2 x.g_j, lowest j on ties, with (g_j, b_j) the consumed
+ * centroid: Euclidean g_j = c_j (bf16-rounded for bf16 data), b_j = |g_j|^2; QRKC g_j = M c_j
+ * (fp32, then bf16 for bf16 data), b_j = c_j^T M c_j. With iters == 0 only the centroids are
+ * written and labels/perm/offsets may be NULL.
+ */
+park_status park_cluster(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
+                         int32_t n_clusters, int32_t iters, int32_t init, uint64_t seed, int32_t side,
+                         float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * PAMA block-importance map (PARK page, Figure 2 caption and abstract: each original query keeps
+ * its own softmax over the key centroids; the distributions are averaged within each query block).
+ *   q            [heads, n, d] queries in original token order
+ *   q_perm, q_offsets  query clustering from park_cluster (cq clusters)
+ *   k_centroids  [heads, ck, d] float32 key centroids (bf16-rounded on use for bf16 data)
+ *   k_offsets    [heads, ck + 1] key cluster offsets (sizes n_j)
+ *   scale        softmax scale (<= 0 selects 1/sqrt(d))
+ *   map          [heads, cq, ck] float32 output: A[i, j] = mean over queries t of block i of
+ *                softmax_j(scale * q_t.c_j + ln n_j); empty key clusters get 0; empty query
+ *                blocks give a zero row.
+ */
+park_status park_retrieve_map(const park_shape* shape, const void* q, const int32_t* q_perm,
+                              const int32_t* q_offsets, int32_t cq, const float* k_centroids,
+                              const int32_t* k_offsets, int32_t ck, float scale, float* map, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Row-wise top-p cut of the map (PARK page, Table 1 caption: top-p block retrieval, p = 0.9).
+ * Per row: order key clusters by importance (descending, ties to the lower index) and keep the
+ * shortest prefix whose cumulative importance (summed in fp64) reaches p. p >= 1 keeps every
+ * non-empty key cluster; a row whose total stays below p keeps every block with positive
+ * importance; empty key clusters are never kept; an all-zero row keeps nothing.
+ *   map       [heads, cq, ck] float32
+ *   k_offsets [heads, ck + 1]
+ *   mask      [heads, cq, ck] uint8 output (1 = kept), may be NULL
+ *   counts    [heads, cq] int32 output: kept clusters per row
+ *   cols      [heads, cq, ck] int32 output: kept cluster ids of row i in ascending order in
+ *             cols[h, i, 0 .. counts[h, i]-1] (row-padded layout)
+ *   sel_keys  [heads, cq] int64 output: keys row i attends to (sum of kept cluster sizes), may be NULL
+ */
+park_status park_select_topp(const float* map, int64_t heads, int32_t cq, int32_t ck,
+                             const int32_t* k_offsets, double p, uint8_t* mask, int32_t* counts,
+                             int32_t* cols, int64_t* sel_keys, void* stream);
+
+/*
+ * Attention over the selected blocks only (PARK abstract: attention computed only within the
+ * retrieved blocks). Every query of cluster i attends to the keys of the clusters in
+ * cols[h, i, 0 .. counts[h, i]-1]; the softmax is renormalised over those keys.
+ *   q, k, v    [heads, n, d] in original token order (fp32 data is rounded to bf16 on load;
+ *              the products run on bf16 MFMA with fp32 accumulation)
+ *   q_perm/q_offsets, k_perm/k_offsets  clusterings from park_cluster
+ *   out        [heads, n, d] of shape->dtype, original token order
+ *   lse        [heads, n] float32 log-sum-exp of the scaled scores over the selected keys, or NULL
+ */
+park_status park_sparse_attn(const park_shape* shape, const void* q, const void* k, const void* v,
+                             const int32_t* q_perm, const int32_t* q_offsets, int32_t cq,
+                             const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
+                             const int32_t* counts, const int32_t* cols, float scale, void* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Cluster-contiguous gather and its inverse (the "Clustered" token ordering of PARK Tables 1/10).
+ *   park_permute_rows:   out[h, p, :] = x[h, perm[h, p], :]
+ *   park_unpermute_rows: out[h, perm[h, p], :] = x[h, p, :]
+ * x and out are [heads, n, d] of shape->dtype and must not overlap.
+ */
+park_status park_permute_rows(const park_shape* shape, const void* x, const int32_t* perm, void* out,
+                              void* stream);
+park_status park_unpermute_rows(const park_shape* shape, const void* x, const int32_t* perm, void* out,
+                                void* stream);
+
+/* Optional outputs of park_forward (any field may be NULL; then the value stays in the workspace). */
+typedef struct {
+  float* metric;       /* [heads, d, d] */
+  int32_t* q_labels;   /* [heads, n] */
+  int32_t* q_perm;     /* [heads, n] */
+  int32_t* q_offsets;  /* [heads, cq + 1] */
+  int32_t* k_labels;   /* [heads, n] */
+  int32_t* k_perm;     /* [heads, n] */
+  int32_t* k_offsets;  /* [heads, ck + 1] */
+  float* map;          /* [heads, cq, ck] */
+  uint8_t* mask;       /* [heads, cq, ck] */
+  int32_t* counts;     /* [heads, cq] */
+  int32_t* cols;       /* [heads, cq, ck] */
+  int64_t* sel_keys;   /* [heads, cq] */
+  float* lse;          /* [heads, n] */
+} park_forward_outputs;
+
+/*
+ * The whole path for one layer: QRKC metric, both clusterings (seeded or warm), PAMA map, top-p,
+ * block-sparse attention. q_centroids [heads, cq, d] and k_centroids [heads, ck, d] are caller
+ * state: outputs, and inputs for PARK_INIT_WARM (a later denoising step reusing the previous
+ * step's centroids). The query side uses side stream PARK_SIDE_Q, the key side PARK_SIDE_K.
+ */
+park_status park_forward(const park_shape* shape, const void* q, const void* k, const void* v, void* out,
+                         const park_params* params, float* q_centroids, float* k_centroids,
+                         const park_forward_outputs* outputs, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARK_H */

@@ -1,0 +1,308 @@
+"""HIP path vs the fp64 oracle, stage by stage, on the same seeded inputs (lock-step: every oracle
+stage is fed exactly what the GPU stage consumed). Sizes span several tiles with ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_qrkc_amd as bsa
+import oracle as O
+from gpu_helpers import (ATTN_MAX_ABS, ATTN_MEAN_ABS, MAP_ABS, SMALL, TAU, attn_view, check_topp_rows, cols_list,
+                         inputs, np_i, to64)
+
+pytestmark = pytest.mark.gpu
+
+WL = ["small", "small64", "tiny"]
+
+
+def _bf(w):
+    return w.dtype == "bf16"
+
+
+@pytest.fixture(scope="module", params=WL)
+def case(request):
+    w = SMALL[request.param]
+    Q, K, V = inputs(w)
+    M = bsa.park_qrkc_metric(Q)
+    torch.cuda.synchronize()
+    print(f"\n[case] {w.name}: H={w.heads} N={w.n} d={w.d} {w.dtype} cq={w.cq} ck={w.ck}", flush=True)
+    return w, Q, K, V, M
+
+
+def test_qrkc_metric(case):
+    w, Q, K, V, M = case
+    Mg = to64(M)
+    for h in range(w.heads):
+        Mo = O.qrkc_metric(to64(Q[h]))
+        rel = np.abs(Mg[h] - Mo).max() / np.abs(Mo).max()
+        assert rel <= (2e-6 if _bf(w) else 1e-7), rel
+        np.testing.assert_array_equal(Mg[h], Mg[h].T)
+
+
+@pytest.mark.parametrize("side", ["q", "k"])
+def test_kmeanspp_seeding(case, side):
+    w, Q, K, V, M = case
+    X = Q if side == "q" else K
+    C = w.cq if side == "q" else w.ck
+    metric = bsa.PARK_EUCLID if side == "q" else bsa.PARK_QRKC
+    sd = bsa.PARK_SIDE_Q if side == "q" else bsa.PARK_SIDE_K
+    res = bsa.park_cluster(X, C, 0, metric, M if side == "k" else None, seed=11, side=sd)
+    cg = to64(res["centroids"])
+    near = 0
+    for h in range(w.heads):
+        Mh = to64(M[h]) if side == "k" else None
+        co, chosen, margins = O.kmeanspp(to64(X[h]), C, Mh, seed=11, head=h, side=sd, return_trace=True)
+        diff = np.flatnonzero(np.any(cg[h] != co, axis=1))
+        if diff.size:
+            m = diff[0]
+            assert margins[m] <= TAU, f"head {h}: seeding differs at step {m} (margin {margins[m]:.3g})"
+            near += 1
+    print(f"[kmeans++ {side}] near-ties: {near}")
+
+
+@pytest.mark.parametrize("side", ["q", "k"])
+def test_lloyd_lockstep(case, side):
+    w, Q, K, V, M = case
+    X = Q if side == "q" else K
+    C = w.cq if side == "q" else w.ck
+    metric = bsa.PARK_EUCLID if side == "q" else bsa.PARK_QRKC
+    sd = bsa.PARK_SIDE_Q if side == "q" else bsa.PARK_SIDE_K
+    Mp = M if side == "k" else None
+    cent = bsa.park_cluster(X, C, 0, metric, Mp, seed=5, side=sd)["centroids"]
+    Xs = [to64(X[h]) for h in range(w.heads)]
+    xmax = max(np.abs(x).max() for x in Xs)
+    near = 0
+    for it in range(3):
+        prev = to64(cent)
+        res = bsa.park_cluster(X, C, 1, metric, Mp, init=bsa.PARK_INIT_WARM, side=sd, centroids=cent)
+        lab, perm, off, new = np_i(res["labels"]), np_i(res["perm"]), np_i(res["offsets"]), to64(res["centroids"])
+        for h in range(w.heads):
+            Mh = to64(M[h]) if side == "k" else None
+            g, b = O.consumed_centroids(prev[h], metric, Mh, bf16=_bf(w))
+            n_near, bad = O.assign_near_tie(Xs[h], g, b, lab[h], TAU)
+            assert bad.size == 0, f"iter {it} head {h}: {bad.size} labels differ beyond near-ties, e.g. {bad[:5]}"
+            near += n_near
+            po, oo = O.cluster_order(lab[h], C)
+            np.testing.assert_array_equal(perm[h], po)
+            np.testing.assert_array_equal(off[h], oo)
+            co = O.update(Xs[h], lab[h], C, prev[h])
+            err = np.abs(new[h] - co).max()
+            assert err <= 1e-6 * xmax, err
+    print(f"[lloyd {side}] assignment near-ties over 3 iterations: {near}")
+
+
+@pytest.fixture(scope="module")
+def clustered(case):
+    w, Q, K, V, M = case
+    qc = bsa.park_cluster(Q, w.cq, 3, bsa.PARK_EUCLID, None, seed=1, side=bsa.PARK_SIDE_Q)
+    kc = bsa.park_cluster(K, w.ck, 3, bsa.PARK_QRKC, M, seed=1, side=bsa.PARK_SIDE_K)
+    return w, Q, K, V, M, qc, kc
+
+
+def test_pama_map(clustered):
+    w, Q, K, V, M, qc, kc = clustered
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    Ag = to64(A)
+    for h in range(w.heads):
+        kcent = to64(kc["centroids"][h])
+        khat = O.round_bf16(kcent) if _bf(w) else kcent
+        sizes = np.diff(np_i(kc["offsets"][h]))
+        Ao = O.pama(to64(Q[h]), np_i(qc["perm"][h]), np_i(qc["offsets"][h]), khat, sizes, w.scale)
+        err = np.abs(Ag[h] - Ao).max()
+        assert err <= MAP_ABS, err
+        live = np.diff(np_i(qc["offsets"][h])) > 0
+        assert np.abs(Ag[h][live].sum(1) - 1).max() <= MAP_ABS
+        assert np.all(Ag[h][~live] == 0)
+        assert np.all(Ag[h][:, sizes == 0] == 0)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.95, 1.0])
+def test_select_topp(clustered, p):
+    w, Q, K, V, M, qc, kc = clustered
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    sel = bsa.park_select_topp(A, kc["offsets"], p)
+    Ag = to64(A)
+    mask, counts, cols, keys = np_i(sel["mask"]), np_i(sel["counts"]), np_i(sel["cols"]), np_i(sel["sel_keys"])
+    near = 0
+    for h in range(w.heads):
+        sizes = np.diff(np_i(kc["offsets"][h]))
+        n_near, bad = check_topp_rows(Ag[h], sizes, p, counts[h], cols[h], keys[h])
+        assert not bad, f"head {h} rows {bad}"
+        near += n_near
+        for i in range(w.cq):
+            c = cols[h, i, :counts[h, i]]
+            assert np.all(np.diff(c) > 0)
+            assert np.array_equal(np.flatnonzero(mask[h, i]), c)
+            assert keys[h, i] == sizes[c].sum()
+            if Ag[h, i].sum() > 0 and p < 1:
+                mass = Ag[h, i, c].sum()
+                assert mass >= p - 1e-6  # P2: the kept mass reaches p
+                assert mass - Ag[h, i, c].min() < p + 1e-6  # and the kept set is minimal
+            if p >= 1 and Ag[h, i].sum() > 0:
+                assert np.array_equal(c, np.flatnonzero(sizes > 0))
+    print(f"[top-p {p}] near-ties: {near}")
+
+
+def test_select_topp_hand_fixture():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "topp_hand.json")))
+    A = torch.tensor(g["map"], dtype=torch.float32, device="cuda")[None].contiguous()
+    ko = torch.tensor([np.concatenate([[0], np.cumsum(g["k_sizes"])]).tolist()], dtype=torch.int32, device="cuda")
+    for case in g["cases"]:
+        sel = bsa.park_select_topp(A, ko, case["p"])
+        counts, cols, keys = np_i(sel["counts"])[0], np_i(sel["cols"])[0], np_i(sel["sel_keys"])[0]
+        assert [cols[i, :counts[i]].tolist() for i in range(3)] == case["cols"]
+        assert keys.tolist() == case["keys"]
+
+
+def _attn_check(w, Q, K, V, qp, qo, kp, ko, counts, cols, out, lse, heads=None):
+    worst, mean_acc, n = 0.0, 0.0, 0
+    for h in (range(w.heads) if heads is None else heads):
+        Oo, Lo = O.sparse_attention(attn_view(w, Q[h]), attn_view(w, K[h]), attn_view(w, V[h]), np_i(qp[h]),
+                                    np_i(qo[h]), np_i(kp[h]), np_i(ko[h]), cols_list(np_i(counts[h]), np_i(cols[h])),
+                                    w.scale)
+        Og, Lg = to64(out[h]), to64(lse[h])
+        e = np.abs(Og - Oo)
+        worst = max(worst, e.max())
+        mean_acc += e.sum()
+        n += e.size
+        fin = np.isfinite(Lo)
+        np.testing.assert_array_equal(np.isfinite(Lg), fin)
+        assert np.abs(Lg[fin] - Lo[fin]).max() <= 1e-3
+    assert worst <= ATTN_MAX_ABS, worst
+    assert mean_acc / n <= ATTN_MEAN_ABS, mean_acc / n
+    return worst, mean_acc / n
+
+
+@pytest.mark.parametrize("p", [0.9, 1.0])
+def test_sparse_attention(clustered, p):
+    w, Q, K, V, M, qc, kc = clustered
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    sel = bsa.park_select_topp(A, kc["offsets"], p)
+    out, lse = bsa.park_sparse_attn(Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"], sel["counts"],
+                                    sel["cols"])
+    worst, mean = _attn_check(w, Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"], sel["counts"],
+                              sel["cols"], out, lse)
+    print(f"[attention p={p}] max-abs {worst:.2e} mean-abs {mean:.2e}")
+    if p == 1.0:  # P3: top-p = 1 reproduces dense attention
+        for h in range(w.heads):
+            Od, Ld = O.dense_attention(attn_view(w, Q[h]), attn_view(w, K[h]), attn_view(w, V[h]), w.scale)
+            e = np.abs(to64(out[h]) - Od)
+            assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS
+            assert np.abs(to64(lse[h]) - Ld).max() <= 1e-3
+
+
+def test_sparse_attention_edge_selections():
+    """Hand-built clusterings and selections: singleton and empty clusters, empty rows, runs that
+    merge across adjacent clusters, and key clusters that are selected but empty."""
+    w = SMALL["small"]
+    rng = np.random.default_rng(3)
+    Q, K, V = inputs(w)
+    H, N = w.heads, w.n
+    cq, ck = 37, 61
+    qps, qos, kps, kos, cnts, colss = [], [], [], [], [], []
+    for h in range(H):
+        ql = rng.integers(0, cq, N)
+        ql[ql == 5] = 6              # empty query cluster
+        ql[:3] = 7                   # cluster 7 is small
+        ql[ql == 7] = 8
+        ql[100] = 7                  # singleton query cluster
+        kl = rng.integers(0, ck, N)
+        kl[kl == 9] = 10             # empty key cluster
+        kl[kl == 11] = 12
+        kl[200] = 11                 # singleton key cluster
+        qp, qo = O.cluster_order(ql, cq)
+        kp, ko = O.cluster_order(kl, ck)
+        cols = np.zeros((cq, ck), dtype=np.int32)
+        cnt = np.zeros(cq, dtype=np.int32)
+        for i in range(cq):
+            if i == 3:
+                sel = np.array([], dtype=np.int64)        # a query cluster that selected nothing
+            elif i == 4:
+                sel = np.arange(ck)                       # everything, including the empty cluster
+            elif i == 8:
+                sel = np.array([9, 11])                   # an empty and a singleton key cluster
+            else:
+                sel = np.flatnonzero(rng.random(ck) < 0.3)
+            cnt[i] = sel.size
+            cols[i, :sel.size] = sel
+        qps.append(qp); qos.append(qo); kps.append(kp); kos.append(ko); cnts.append(cnt); colss.append(cols)
+    T = lambda a: torch.tensor(np.stack(a), dtype=torch.int32, device="cuda").contiguous()
+    qp, qo, kp, ko, counts, cols = map(T, (qps, qos, kps, kos, cnts, colss))
+    out, lse = bsa.park_sparse_attn(Q, K, V, qp, qo, kp, ko, counts, cols)
+    _attn_check(w, Q, K, V, qp, qo, kp, ko, counts, cols, out, lse)
+    # the cluster that selected nothing gets zero output and -inf log-sum-exp
+    for h in range(H):
+        rows = np_i(qp[h])[np_i(qo[h])[3]:np_i(qo[h])[4]]
+        assert np.all(to64(out[h])[rows] == 0) and np.all(np.isneginf(to64(lse[h])[rows]))
+
+
+def test_permute_roundtrip(case):
+    """P12: gather then scatter is the identity; the gather matches the permutation."""
+    w, Q, K, V, M = case
+    qc = bsa.park_cluster(Q, w.cq, 2, bsa.PARK_EUCLID, None, seed=2)
+    Qp = bsa.park_permute_rows(Q, qc["perm"])
+    back = bsa.park_unpermute_rows(Qp, qc["perm"])
+    assert torch.equal(back, Q)
+    for h in range(w.heads):
+        assert torch.equal(Qp[h], Q[h][qc["perm"][h].long()])
+
+
+ALL_OUT = ("metric", "q_labels", "q_perm", "q_offsets", "k_labels", "k_perm", "k_offsets", "map", "mask", "counts",
+           "cols", "sel_keys", "lse")
+
+
+def test_forward_matches_entry_points_and_oracle(case):
+    w, Q, K, V, M = case
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=3, outputs=ALL_OUT)
+    # the fused entry equals the separate entry points, bit for bit
+    qc = bsa.park_cluster(Q, w.cq, w.iters, bsa.PARK_EUCLID, None, seed=3, side=bsa.PARK_SIDE_Q)
+    kc = bsa.park_cluster(K, w.ck, w.iters, bsa.PARK_QRKC, r["metric"], seed=3, side=bsa.PARK_SIDE_K)
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    sel = bsa.park_select_topp(A, kc["offsets"], w.p)
+    out, lse = bsa.park_sparse_attn(Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"], sel["counts"],
+                                    sel["cols"])
+    assert torch.equal(r["metric"], M)
+    assert torch.equal(r["q_perm"], qc["perm"]) and torch.equal(r["k_perm"], kc["perm"])
+    assert torch.equal(r["q_centroids"], qc["centroids"]) and torch.equal(r["k_centroids"], kc["centroids"])
+    assert torch.equal(r["map"], A) and torch.equal(r["counts"], sel["counts"])
+    assert torch.equal(r["out"], out) and torch.equal(r["lse"], lse)
+    # lock-step oracle on the forward's own intermediates
+    for h in range(w.heads):
+        sizes = np.diff(np_i(r["k_offsets"][h]))
+        kcent = to64(r["k_centroids"][h])
+        Ao = O.pama(to64(Q[h]), np_i(r["q_perm"][h]), np_i(r["q_offsets"][h]),
+                    O.round_bf16(kcent) if _bf(w) else kcent, sizes, w.scale)
+        assert np.abs(to64(r["map"][h]) - Ao).max() <= MAP_ABS
+        _, bad = check_topp_rows(to64(r["map"][h]), sizes, w.p, np_i(r["counts"][h]), np_i(r["cols"][h]),
+                                 np_i(r["sel_keys"][h]))
+        assert not bad
+    _attn_check(w, Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], r["counts"], r["cols"],
+                r["out"], r["lse"])
+    # determinism: a second run is bitwise identical
+    r2 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=3, outputs=("map", "lse"))
+    assert torch.equal(r2["out"], r["out"]) and torch.equal(r2["map"], r["map"]) and torch.equal(r2["lse"], r["lse"])
+
+
+def test_forward_free_running_vs_oracle_tiny():
+    """The tiny workload end to end against the oracle run on its own (no lock-step): labels agree
+    up to near-tie cascades and the recall of both stays above the dense-mass bound."""
+    w = SMALL["tiny"]
+    Q, K, V = inputs(w)
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=ALL_OUT)
+    q, k, v = to64(Q[0]), to64(K[0]), to64(V[0])
+    ro = O.forward(q, k, v, w.cq, w.ck, w.iters, w.p, w.scale, seed=0, bf16=False)
+    agree_q = (np_i(r["q_labels"][0]) == ro["q"]["labels"]).mean()
+    agree_k = (np_i(r["k_labels"][0]) == ro["k"]["labels"]).mean()
+    _, ld = O.dense_attention(*(O.round_bf16(x) for x in (q, k, v)), w.scale)
+    rec_g = O.recall(to64(r["lse"][0]), ld).mean()
+    rec_o = O.recall(ro["lse"], ld).mean()
+    print(f"[tiny free-running] label agreement q={agree_q:.4f} k={agree_k:.4f}; recall gpu={rec_g:.4f} "
+          f"oracle={rec_o:.4f}")
+    assert agree_q > 0.99 and agree_k > 0.99
+    assert abs(rec_g - rec_o) < 0.01
+    # p = 1: dense equivalence through the fused entry
+    r1 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, 1.0, seed=0)
+    Od, _ = O.dense_attention(*(O.round_bf16(x) for x in (q, k, v)), w.scale)
+    e = np.abs(to64(r1["out"][0]) - Od)
+    assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS
