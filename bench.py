@@ -1,0 +1,193 @@
+"""Benchmark of the PARK path on one MI355X: retrieval + block-sparse attention per layer.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan] [--no-cpu]
+
+A step is one park_forward call (QRKC metric, seeded K-means on queries and keys, PAMA map, top-p,
+block-sparse attention) over one synthetic layer already resident in HBM. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import synth
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "retrieval+sparse-attn ms/layer; effective TFLOP/s & MFMA % at N=75,600, p=0.9"
+
+
+def _events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_call(fn, reps, warmup=1):
+    """Mean ms of fn() over `reps` calls, timed with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    a, b = _events()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline(w, Q, K, V, seed):
+    """The oracle as it stands on a bounded sample of the workload, scaled to ms per layer.
+
+    Sample: the whole retrieval of head 0 (metric, both seedings and clusterings, PAMA, top-p) and
+    the sparse attention of the first `na` query clusters of head 0; scaled by heads and by
+    query clusters respectively."""
+    import oracle as O
+    q, k, v = (x[0].to(torch.float64).cpu().numpy() for x in (Q, K, V))
+    t0 = time.perf_counter()
+    r = O.retrieve(q, k, w.cq, w.ck, w.iters, w.p, w.scale, seed=seed, head=0, bf16=(w.dtype == "bf16"))
+    t_ret = time.perf_counter() - t0
+    na = 2
+    qp, qo = r["q"]["perm"], r["q"]["offsets"]
+    rows = [i for i in range(w.cq) if qo[i + 1] > qo[i]][:na]
+    t0 = time.perf_counter()
+    O.sparse_attention(q, k, v, qp, qo, r["k"]["perm"], r["k"]["offsets"], r["cols"], w.scale, rows=rows)
+    t_att = time.perf_counter() - t0
+    n_live = sum(1 for i in range(w.cq) if qo[i + 1] > qo[i])
+    ms = 1e3 * (t_ret * w.heads + t_att * (n_live / max(len(rows), 1)) * w.heads)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": ms, "unit": "ms/layer", "cores": cores, "kind": "oracle",
+            "sample": f"head 0 retrieval ({t_ret:.1f} s) x {w.heads} heads + sparse attention of {len(rows)} of "
+                      f"{n_live} query clusters of head 0 ({t_att:.1f} s) scaled to all clusters and heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "heads shard across GPUs with no exchange inside the path, so per-GPU throughput is the N=1 figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import block_sparse_attention_qrkc_amd as bsa
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready: {w.name} H={w.heads} N={w.n} d={w.d}")
+    ws = bsa.Workspace()
+    qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
+    kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
+    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse", "map", "metric")
+
+    def step():
+        return bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed, q_centroids=qcent,
+                                k_centroids=kcent, outputs=outs, ws=ws)
+
+    for _ in range(args.warmup):
+        r = step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    t0 = time.perf_counter()
+    a, b = _events()
+    a.record()
+    for _ in range(args.steps):
+        r = step()
+    b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = a.elapsed_time(b) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    # selection statistics of the last step
+    qsz = torch.diff(r["q_offsets"], dim=1).to(torch.float64)
+    ksel = r["sel_keys"].to(torch.float64)
+    n = w.n
+    computed_flops = 4.0 * w.d * float((qsz * ksel).sum())
+    dense_flops = 4.0 * w.d * n * n * w.heads
+    density = computed_flops / dense_flops
+
+    res = {"metric": METRIC, "value": round(ms_step, 3), "unit": "ms/layer", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": w.name, "heads": w.heads, "n": n, "d": w.d, "cq": w.cq, "ck": w.ck,
+                      "iters": w.iters, "p": w.p, "grid": list(w.grid)}}
+    res["host_wall_ms_per_step"] = round(wall, 3)
+    res["token_density"] = round(density, 5)
+
+    if not args.no_stages:
+        M = r["metric"]
+        st = {}
+        st["metric"] = time_call(lambda: bsa.park_qrkc_metric(Q, out=M, ws=ws), 3)
+        st["cluster_q"] = time_call(lambda: bsa.park_cluster(Q, w.cq, w.iters, bsa.PARK_EUCLID, None, seed=args.seed,
+                                                             side=bsa.PARK_SIDE_Q, ws=ws), 2)
+        st["cluster_k"] = time_call(lambda: bsa.park_cluster(K, w.ck, w.iters, bsa.PARK_QRKC, M, seed=args.seed,
+                                                             side=bsa.PARK_SIDE_K, ws=ws), 2)
+        qc = bsa.park_cluster(Q, w.cq, w.iters, bsa.PARK_EUCLID, None, seed=args.seed, side=bsa.PARK_SIDE_Q, ws=ws)
+        kc = bsa.park_cluster(K, w.ck, w.iters, bsa.PARK_QRKC, M, seed=args.seed, side=bsa.PARK_SIDE_K, ws=ws)
+        A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"], ws=ws)
+        st["pama"] = time_call(lambda: bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"],
+                                                             kc["offsets"], out=A, ws=ws), 5)
+        sel = bsa.park_select_topp(A, kc["offsets"], w.p)
+        st["select"] = time_call(lambda: bsa.park_select_topp(A, kc["offsets"], w.p), 5)
+        out = torch.empty_like(Q)
+        lse = torch.empty(w.heads, n, dtype=torch.float32, device=dev)
+        args_attn = (Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"])
+        st["sparse_attn"] = time_call(lambda: bsa.park_sparse_attn(*args_attn, sel["counts"], sel["cols"], out=out,
+                                                                   lse=lse, ws=ws), 3)
+        dsel = bsa.park_select_topp(A, kc["offsets"], 1.0)
+        lse_d = torch.empty_like(lse)
+        st["dense_attn"] = time_call(lambda: bsa.park_sparse_attn(*args_attn, dsel["counts"], dsel["cols"], out=out,
+                                                                  lse=lse_d, ws=ws), 2)
+        bsa.park_sparse_attn(*args_attn, sel["counts"], sel["cols"], out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        rec = torch.exp(lse.double() - lse_d.double()).mean(dim=1).cpu().numpy()
+        qsz2 = torch.diff(qc["offsets"], dim=1).to(torch.float64)
+        flops_sel = 4.0 * w.d * float((qsz2 * sel["sel_keys"].to(torch.float64)).sum())
+        retrieval = st["metric"] + st["cluster_q"] + st["cluster_k"] + st["pama"] + st["select"]
+        res["stages_ms"] = {k: round(v, 3) for k, v in st.items()}
+        res["retrieval_ms"] = round(retrieval, 3)
+        res["sparse_attn_ms"] = round(st["sparse_attn"], 3)
+        res["dense_attn_ms"] = round(st["dense_attn"], 3)
+        res["retrieval_over_dense"] = round(retrieval / st["dense_attn"], 4)
+        res["effective_tflops_dense_equiv"] = round(dense_flops / (ms_step * 1e9), 2)
+        res["computed_tflops"] = round(computed_flops / (ms_step * 1e9), 2)
+        res["mfma_frac_whole_path"] = round(computed_flops / (ms_step * 1e9) / PEAK_BF16_TFLOPS, 4)
+        res["dense_attn_tflops"] = round(dense_flops / (st["dense_attn"] * 1e9), 2)
+        res["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
+                         "worst": round(float(rec.min()), 4)}
+        ach = flops_sel / (st["sparse_attn"] * 1e9)
+        log(f"stages: {res['stages_ms']}")
+        res["roofline"] = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": round(ach, 2),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "traffic": None,
+                           "work": f"4*d*sum_i n_q(i)*L(i) = {flops_sel / 1e12:.3f} TFLOP per launch"}
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle sample)")
+        res["cpu_baseline"] = cpu_baseline(w, Q, K, V, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

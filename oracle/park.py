@@ -107,7 +107,7 @@ def metric_distance(P, c, M=None):
     diff = np.asarray(P, dtype=np.float64) - np.asarray(c, dtype=np.float64)[None, :]
     if M is None:
         return np.einsum("ij,ij->i", diff, diff)
-    return np.einsum("ij,jk,ik->i", diff, np.asarray(M, dtype=np.float64), diff)
+    return ((diff @ np.asarray(M, dtype=np.float64)) * diff).sum(axis=1)
 
 
 # --------------------------------------------------------------------------------------------
