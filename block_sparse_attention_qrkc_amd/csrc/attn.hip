@@ -323,6 +323,262 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   }
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// bf16 kernel: key/value tiles are copied HBM -> LDS with gfx950 direct loads (no register staging),
+// double-buffered so the copy of tile t+1 overlaps the MFMA work on tile t. Rows stay row-major in
+// LDS with their 16-byte chunks XOR-swizzled by row (bank spread); V^T operands come from the
+// transposing LDS read (each lane of a 16-lane group receives 4 keys of one column).
+// ------------------------------------------------------------------------------------------------
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+#define PARK_LDS __attribute__((address_space(3)))
+
+template <int CPR>
+__device__ __forceinline__ int chunk_swz(int r) {
+  return CPR == 16 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (r & 7);
+}
+
+// vmcnt(0): wait until this wave's vector-memory operations (including LDS-direct loads) are done
+#define PARK_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+template <int D>
+struct AttnTileLoader {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;         // bytes per row
+  static constexpr int TILEB = kBN * ROWB;   // bytes per K (or V) tile
+  static constexpr int RPB = 1024 / ROWB;    // rows per 1 KB wave load
+  static constexpr int LOADS = TILEB / 4096; // wave loads per wave per tile (4 waves)
+};
+
+constexpr int kAttnMaxRuns = 1024;  // runs kept in LDS by the direct-load kernel
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __restrict__ Q,
+                                                           const uint16_t* __restrict__ K,
+                                                           const uint16_t* __restrict__ V, int64_t N,
+                                                           const int32_t* __restrict__ q_perm,
+                                                           const int32_t* __restrict__ q_off, int cq,
+                                                           const int32_t* __restrict__ k_perm,
+                                                           const int32_t* __restrict__ tile_base,
+                                                           const int32_t* __restrict__ runs, int ck, float scale,
+                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
+  using TL = AttnTileLoader<D>;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPR = TL::CPR;
+  constexpr int ROWB = TL::ROWB;
+  constexpr int TILEB = TL::TILEB;
+  constexpr int RPB = TL::RPB;
+  constexpr int LOADS = TL::LOADS;
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILEB];
+  __shared__ int32_t run_v[kAttnMaxRuns + 1];
+  __shared__ int32_t run_k[kAttnMaxRuns];
+
+  const int h = blockIdx.y;
+  const int c = blockIdx.x;
+  const int32_t* tb = tile_base + (int64_t)h * (cq + 1);
+  if (c >= tb[cq]) return;
+  const int i = find_tile(tb, cq, c);
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int hl = l / 32;
+  const int32_t* qo = q_off + (int64_t)h * (cq + 1);
+  const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
+  const int qend = min(qbeg + kAttnBM, qo[i + 1]);
+  const int32_t* rec = runs + ((int64_t)h * cq + i) * (2 * ck + 3);
+  const int nr = rec[0];
+  for (int e = threadIdx.x; e <= nr; e += 256) run_v[e] = rec[1 + e];
+  for (int e = threadIdx.x; e < nr; e += 256) run_k[e] = rec[ck + 2 + e];
+  const uint16_t* Qh = Q + (int64_t)h * N * D;
+  const uint16_t* Kh = K + (int64_t)h * N * D;
+  const uint16_t* Vh = V + (int64_t)h * N * D;
+  const int32_t* kp = k_perm + (int64_t)h * N;
+
+  const int qpos = qbeg + w * 32 + l % 32;
+  const bool qok = qpos < qend;
+  const int qrow = qok ? q_perm[(int64_t)h * N + qpos] : 0;
+  u32x4_t qb[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (qok) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qrow * D + kk * 16 + hl * 8);
+    qb[kk] = v;
+  }
+  __syncthreads();
+  const int L = run_v[nr];
+
+  // load slots: slot q of this lane copies tile row trow[q], logical chunk lchunk[q], into physical
+  // chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
+  int trow[LOADS], cur[LOADS], lchunk[LOADS], nrow[LOADS];
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) {
+    trow[q] = (w * LOADS + q) * RPB + l / CPR;
+    cur[q] = 0;
+    lchunk[q] = (l % CPR) ^ chunk_swz<CPR>(trow[q]);
+  }
+  // rows of the keys of tile starting at v0 (keys past the end read row 0: finite, masked)
+  auto fetch_rows = [&](int v0) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const int v = v0 + trow[q];
+      int pos = -1;
+      if (v < L) {
+        while (run_v[cur[q] + 1] <= v) ++cur[q];
+        pos = run_k[cur[q]] + (v - run_v[cur[q]]);
+      }
+      nrow[q] = pos >= 0 ? kp[pos] : 0;
+    }
+  };
+  auto issue = [&](uint8_t* kbuf, uint8_t* vbuf) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const int64_t goff = (int64_t)nrow[q] * D + lchunk[q] * 8;
+      const int boff = (w * LOADS + q) * 1024;
+      __builtin_amdgcn_global_load_lds(Kh + goff, (PARK_LDS void*)(kbuf + boff), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vh + goff, (PARK_LDS void*)(vbuf + boff), 16, 0, 0);
+    }
+  };
+
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  const float sl2 = scale * 1.4426950408889634f;
+  // softmax reference: the running max is only raised when a score exceeds it by more than
+  // 8 / sl2 (p stays below 2^8), which skips almost every rescale of O
+  const float thresh = 8.0f / sl2;
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  const int r = l % 32;
+  const int prow = ((r / 4) % 2) * 16 + (r / 8) * 4 + r % 4;
+  const int g16 = l / 16, i16 = l % 16;
+
+  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int v0) {
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int R = st * 32 + prow;
+      const uint8_t* krow = kt + R * ROWB;
+      const int sw = chunk_swz<CPR>(R);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + ((2 * kk + hl) ^ sw) * 16);
+        sacc[st] = mfma32(a, qb[kk], sacc[st]);
+      }
+    }
+    const int nvalid = L - v0;
+    if (nvalid < kBN) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (st * 32 + hl * 16 + e >= nvalid) sacc[st][e] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const bool raise = mx > m_ref + thresh;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      m_ref = m_new;
+    }
+    const float mb = m_ref * sl2;
+    u32x4_t pb[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float pv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][e], sl2, -mb));
+        l_run += pv[e];
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pb[st][kh][q] = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int D0 = dt * 32 + 16 * (g16 & 1);
+      const int cc = (D0 + 4 * (i16 % 4)) / 8;
+      const int half = (i16 % 4) & 1;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int R1 = st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4;
+          const int R2 = R1 + 4;
+          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (PARK_LDS s16x4_t*)(vt + R1 * ROWB + (cc ^ chunk_swz<CPR>(R1)) * 16 + half * 8));
+          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (PARK_LDS s16x4_t*)(vt + R2 * ROWB + (cc ^ chunk_swz<CPR>(R2)) * 16 + half * 8));
+          const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
+          const u32x2_t a2 = __builtin_bit_cast(u32x2_t, t2);
+          const u32x4_t a = {a1[0], a1[1], a2[0], a2[1]};
+          o[dt] = mfma32(a, pb[st][kh], o[dt]);
+        }
+    }
+  };
+
+  // pipeline: rows of tile t+2 are fetched while tile t+1 is copied and tile t is computed
+  const int nt = (L + kBN - 1) / kBN;
+  if (nt > 0) {
+    fetch_rows(0);
+    issue(kb0, vb0);
+    if (nt > 1) fetch_rows(kBN);
+  }
+  for (int t = 0; t < nt; t += 2) {
+    PARK_WAIT_VMEM();
+    __syncthreads();
+    if (t + 1 < nt) {
+      issue(kb1, vb1);
+      if (t + 2 < nt) fetch_rows((t + 2) * kBN);
+    }
+    compute(kb0, vb0, t * kBN);
+    if (t + 1 < nt) {
+      PARK_WAIT_VMEM();
+      __syncthreads();
+      if (t + 2 < nt) {
+        issue(kb0, vb0);
+        if (t + 3 < nt) fetch_rows((t + 3) * kBN);
+      }
+      compute(kb1, vb1, (t + 1) * kBN);
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (qok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = out + ((int64_t)h * N + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dt * 32 + g4 * 8 + hl * 4;
+        store_out4<uint16_t>(orow + d0, o[dt][g4 * 4] * inv, o[dt][g4 * 4 + 1] * inv, o[dt][g4 * 4 + 2] * inv,
+                             o[dt][g4 * 4 + 3] * inv);
+      }
+    if (lse != nullptr && hl == 0)
+      lse[(int64_t)h * N + qrow] = l_tot > 0.f ? m_ref * scale + logf(l_tot) : -INFINITY;
+  }
+}
+
 }  // namespace
 
 int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, kAttnBM) + cq; }
@@ -338,12 +594,24 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
                                                  static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, k_perm, \
                                                  tile_base, runs, ck, scale, static_cast<T*>(out), lse);
-  if (s.bf16) {
+  if (s.bf16 && ck > kAttnMaxRuns) {
+    // more selectable clusters than the direct-load kernel keeps runs for: register-staged kernel
     if (s.D == 128) {
       PARK_ATTN(uint16_t, 128)
     } else {
       PARK_ATTN(uint16_t, 64)
     }
+  } else if (s.bf16) {
+    const uint16_t* qh = static_cast<const uint16_t*>(q);
+    const uint16_t* kh = static_cast<const uint16_t*>(k);
+    const uint16_t* vh = static_cast<const uint16_t*>(v);
+    uint16_t* oh = static_cast<uint16_t*>(out);
+    if (s.D == 128)
+      sparse_attn_bf16<128><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, k_perm, tile_base, runs, ck,
+                                                   scale, oh, lse);
+    else
+      sparse_attn_bf16<64><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, k_perm, tile_base, runs, ck,
+                                                  scale, oh, lse);
   } else {
     if (s.D == 128) {
       PARK_ATTN(float, 128)
