@@ -59,8 +59,8 @@ def park_cluster(x, n_clusters, iters, metric=PARK_EUCLID, qmetric=None, init=PA
     labels = torch.empty(H, N, dtype=torch.int32, device=dev) if iters > 0 else None
     perm = torch.empty(H, N, dtype=torch.int32, device=dev) if iters > 0 else None
     offsets = torch.empty(H, n_clusters + 1, dtype=torch.int32, device=dev) if iters > 0 else None
-    prm = make_params(cq=n_clusters, ck=n_clusters)
-    entry = PARK_ENTRY_CLUSTER_Q
+    prm = make_params(cq=n_clusters, ck=n_clusters, kmetric=metric)
+    entry = PARK_ENTRY_CLUSTER_K if metric == PARK_QRKC else PARK_ENTRY_CLUSTER_Q
     wp, wn = _ws(entry, sh, prm, dev, ws)
     _check(lib().park_cluster(ctypes.byref(sh), _ptr(x), int(metric), _ptr(qmetric), int(n_clusters), int(iters),
                               int(init), int(seed) & ((1 << 64) - 1), int(side), _ptr(centroids), _ptr(labels),

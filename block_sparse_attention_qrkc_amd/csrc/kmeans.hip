@@ -29,200 +29,260 @@ __device__ __forceinline__ double kpp_uniform(uint64_t seed, int head, int side,
   return (double)(splitmix_first(key) >> 11) * 0x1.0p-53;
 }
 
-__device__ __forceinline__ int64_t cand_row(int i, int S, int64_t N) { return ((int64_t)i * N) / S; }
-
-// Squared norm of every candidate: |x|^2 (Euclidean) or x^T M x (QRKC), fp64.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void kpp_cand_norm(const T* __restrict__ X, int64_t N, int S,
-                                                     const float* __restrict__ M, double* __restrict__ out) {
-  const int h = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= S) return;
-  const T* x = X + ((int64_t)h * N + cand_row(i, S, N)) * D;
-  float xv[D];
-#pragma unroll
-  for (int a0 = 0; a0 < D; a0 += 8) load8_f32(x + a0, xv + a0);
-  double s = 0.0;
-  if (M == nullptr) {
-#pragma unroll
-    for (int a = 0; a < D; ++a) s += (double)xv[a] * (double)xv[a];
-  } else {
-    const float* Mh = M + (int64_t)h * D * D;
-    for (int a = 0; a < D; ++a) {
-      double y = 0.0;
-#pragma unroll 16
-      for (int b = 0; b < D; ++b) y += (double)Mh[a * D + b] * (double)xv[b];
-      s += (double)xv[a] * y;
-    }
-  }
-  out[(int64_t)h * S + i] = s;
+// floor(i * N / S): i * N < 2^53 is exact in fp64, and the quotient's fractional part is at least 1/S,
+// far above the division's rounding error, so the truncated fp64 quotient is the exact floor.
+__device__ __forceinline__ int64_t cand_row(int i, int S, int64_t N) {
+  return (int64_t)(((double)i * (double)N) / (double)S);
 }
 
-constexpr int kKppThreads = 1024;
-constexpr int kKppMaxPer = 16;  // candidates per thread (S <= 16384)
-
-// One workgroup per head. Thread t owns candidates [t*P, t*P + P). D2 is kept in registers.
+// Per candidate i: xx_i = |x_i|^2 (Euclidean) or x_i^T M x_i (QRKC); for QRKC also y_i = M x_i,
+// the vector later steps dot the candidates against. Block = 64 candidates, 4 threads each (a
+// quarter of the outputs per thread); M and the rows are staged in LDS; fp32 products, fp64 sums
+// of the quarters.
 template <typename T, int D>
-__global__ __launch_bounds__(kKppThreads) void kpp_seed(const T* __restrict__ X, int64_t N, int S, int C,
-                                                        const float* __restrict__ M,
-                                                        const double* __restrict__ cand_norm, uint64_t seed,
-                                                        int side, float* __restrict__ cent) {
-  __shared__ double cvec[D];
-  __shared__ double yvec[D];
-  __shared__ double red[kKppThreads / kWave];
-  __shared__ double scan_scratch[17];
-  __shared__ double cc_shared;
-  __shared__ int pick;
-  __shared__ int fallback;
+__global__ __launch_bounds__(256) void kpp_prep(const T* __restrict__ X, int64_t N, int S, const float* __restrict__ M,
+                                                double* __restrict__ xx, float* __restrict__ y) {
+  constexpr int XS = D + 1;       // padded row stride (floats)
+  extern __shared__ float kpp_lds[];
+  float* xs = kpp_lds;            // [64][XS]
+  float* ms = kpp_lds + 64 * XS;  // [D][D] (QRKC only)
+  __shared__ double part_s[4][64];
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * D; e += 256) {
+    const int ci = i0 + e / D;
+    xs[(e / D) * XS + e % D] = ci < S ? load_f32(X + ((int64_t)h * N + cand_row(ci, S, N)) * D, e % D) : 0.f;
+  }
+  if (M != nullptr)
+    for (int e = threadIdx.x; e < D * D; e += 256) ms[e] = M[(int64_t)h * D * D + e];
+  __syncthreads();
+  const int c = threadIdx.x % 64;  // candidate within the block
+  const int q4 = threadIdx.x / 64;  // quarter of the outputs (uniform per wave)
+  constexpr int AQ = D / 4;
+  const float* x = xs + c * XS;
+  double acc = 0.0;
+  if (M == nullptr) {
+    for (int a = q4 * AQ; a < q4 * AQ + AQ; ++a) acc += (double)x[a] * (double)x[a];
+  } else {
+    for (int a = q4 * AQ; a < q4 * AQ + AQ; ++a) {
+      const float* mr = ms + a * D;  // wave-uniform row: broadcast reads
+      float ya = 0.f;
+#pragma unroll 16
+      for (int b = 0; b < D; ++b) ya = __builtin_fmaf(mr[b], x[b], ya);
+      acc += (double)x[a] * (double)ya;
+      if (i0 + c < S) y[((int64_t)h * S + i0 + c) * D + a] = ya;
+    }
+  }
+  part_s[q4][c] = acc;
+  __syncthreads();
+  if (threadIdx.x < 64 && i0 + threadIdx.x < S)
+    xx[(int64_t)h * S + i0 + threadIdx.x] =
+        ((part_s[0][threadIdx.x] + part_s[1][threadIdx.x]) + part_s[2][threadIdx.x]) + part_s[3][threadIdx.x];
+}
 
+struct KppSide {
+  const void* x;      // [H, N, D] data of this side
+  const double* xx;   // [H, S] candidate norms
+  const float* y;     // [H, S, D] candidate metric products (NULL: Euclidean, y = x)
+  float* cent;        // [H, C, D] output
+  int C, S, side;
+};
+
+constexpr int kKppThreads = 1024;
+constexpr int kKppWaves = kKppThreads / kWave;
+
+// Sum over aligned groups of G lanes (G = 8, 16 or 32); every lane of a group gets the group sum.
+// Groups of 16 use DPP row rotations, groups of 8 a half-row mirror and quad permutations.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G == 16) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+    return v;
+  } else if constexpr (G == 8) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    return v;
+  } else {
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+  }
+}
+
+// One workgroup per (head, side); blockIdx.y selects the side. D^2 of the S candidates live in LDS.
+// Per step: a block-wide prefix over D^2 (thread t owns candidates [t*P, t*P + P)) finds the sampled
+// candidate; then every D^2 is lowered by the distance to the new centre,
+// dist = xx_i - 2 x_i.y_t + xx_t. For the dot products LPR lanes read one candidate row together
+// (16 bytes each, one cache line per 8 lanes), accumulate in fp32 and add across the group.
+template <typename T, int D>
+__global__ __launch_bounds__(kKppThreads) void kpp_seed(KppSide s0, KppSide s1, int64_t N, uint64_t seed) {
+  constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+  constexpr int LPR = D / EPC;             // lanes per candidate row
+  constexpr int RPW = kWave / LPR;         // candidate rows per wave per round
+  constexpr int RPB = kKppWaves * RPW;     // candidate rows per round
+  constexpr int BATCH = 8;                 // rounds whose loads are in flight together
+  extern __shared__ double d2s[];          // [S]
+  __shared__ __attribute__((aligned(16))) float yf[D];
+  __shared__ double wtot[kKppWaves];
+  __shared__ double cc_s;
+  __shared__ int pick;
+  __shared__ uint32_t taken[16384 / 32];
+
+  const KppSide sd = blockIdx.y == 0 ? s0 : s1;
   const int h = blockIdx.x;
+  const int C = sd.C, S = sd.S;
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int w = tid / kWave;
   const int P = (S + kKppThreads - 1) / kKppThreads;
   const int base = tid * P;
-  const T* Xh = X + (int64_t)h * N * D;
-  const float* Mh = M ? M + (int64_t)h * D * D : nullptr;
-  const double* xx = cand_norm + (int64_t)h * S;
-
-  double d2[kKppMaxPer];
-  double own_xx[kKppMaxPer];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int k = 0; k < kKppMaxPer; ++k) {
-    d2[k] = 0.0;
-    own_xx[k] = (k < P && base + k < S) ? xx[base + k] : 0.0;
-  }
+  const T* Xh = static_cast<const T*>(sd.x) + (int64_t)h * N * D;
+  const double* xxh = sd.xx + (int64_t)h * S;
+  const float* yh = sd.y ? sd.y + (int64_t)h * S * D : nullptr;
+  for (int q = tid; q < 16384 / 32; q += kKppThreads) taken[q] = 0u;
+  const int rounds = (S + RPB - 1) / RPB;
+  const int my_chunk = l % LPR;
+  const int my_row_in_wave = l / LPR;
 
   for (int m = 0; m < C; ++m) {
-    // ---- choose candidate t
     if (m == 0) {
       if (tid == 0) {
-        int t0 = (int)(kpp_uniform(seed, h, side, 0) * (double)S);
+        const int t0 = (int)(kpp_uniform(seed, h, sd.side, 0) * (double)S);
         pick = t0 < S ? t0 : S - 1;
       }
       __syncthreads();
     } else {
       double local = 0.0;
+      for (int k = 0; k < P; ++k)
+        if (base + k < S) local += d2s[base + k];
+      const double inc = wave_inclusive_scan(local);
+      if (l == kWave - 1) wtot[w] = inc;
+      __syncthreads();  // A
+      double total = 0.0;
 #pragma unroll
-      for (int k = 0; k < kKppMaxPer; ++k)
-        if (k < P) local += d2[k];
-      double total;
-      const double ex = block_exclusive_scan(local, scan_scratch, &total);
-      if (tid == 0) {
-        pick = S;
-        fallback = 0;
-      }
-      __syncthreads();
+      for (int q = 0; q < kKppWaves; ++q) total += wtot[q];
       if (total > 0.0) {
-        const double v = kpp_uniform(seed, h, side, m) * total;
-        // owner: the first thread whose range reaches past v
-        if (ex + local > v) atomicMin(&pick, tid);
-        __syncthreads();
-        const int owner = pick;
-        __syncthreads();
-        if (owner >= kKppThreads && tid == 0) fallback = S + 1;  // rounding left v past every range
-        if (tid == owner) {
-          double run = ex;
-          int found = -1, last_pos = -1;
+        const double v = kpp_uniform(seed, h, sd.side, m) * total;
+        int owner_w = -1;
+        double owner_pre = 0.0, run = 0.0;
 #pragma unroll
-          for (int k = 0; k < kKppMaxPer; ++k) {
-            if (k < P && found < 0 && d2[k] > 0.0) {
-              last_pos = k;
-              run += d2[k];
-              if (run > v) found = k;
-            }
+        for (int q = 0; q < kKppWaves; ++q) {
+          if (owner_w < 0 && run + wtot[q] > v) {
+            owner_w = q;
+            owner_pre = run;
           }
-          if (found < 0) found = last_pos;
-          if (found >= 0)
-            pick = base + found;
-          else
-            fallback = owner * P + 1;  // no mass in the owner's range: take the last one before it
+          run += wtot[q];
         }
+        if (owner_w < 0) {  // v rounded onto the total: the last wave with mass
+          run = 0.0;
+          for (int q = 0; q < kKppWaves; ++q) {
+            if (wtot[q] > 0.0) {
+              owner_w = q;
+              owner_pre = run;
+            }
+            run += wtot[q];
+          }
+        }
+        if (w == owner_w) {
+          const uint64_t hit = __ballot(owner_pre + inc > v);
+          const int owner_l = hit ? __ffsll((unsigned long long)hit) - 1 : kWave - 1;
+          if (l == owner_l) {
+            double r2 = owner_pre + inc - local;
+            int found = -1, last_pos = -1;
+            for (int k = 0; k < P && base + k < S; ++k) {
+              const double dk = d2s[base + k];
+              if (dk > 0.0) {
+                last_pos = k;
+                r2 += dk;
+                if (r2 > v) {
+                  found = k;
+                  break;
+                }
+              }
+            }
+            if (found < 0) found = last_pos;
+            pick = found >= 0 ? base + found : -1;
+          }
+        }
+      } else if (tid == 0) {
+        pick = -1;
+      }
+      __syncthreads();  // B
+      if (pick < 0) {
+        // rounding left the sampler without a candidate: the last candidate with mass; or every
+        // D^2 is zero: the lowest candidate not chosen yet
+        const bool any_mass = total > 0.0;
         __syncthreads();
-        if (fallback) {
-          const int limit = fallback - 1;
-          if (tid == 0) pick = -1;
-          __syncthreads();
-          int lastk = -1;
-#pragma unroll
-          for (int k = 0; k < kKppMaxPer; ++k)
-            if (k < P && base + k < limit && d2[k] > 0.0) lastk = base + k;
-          if (lastk >= 0) atomicMax(&pick, lastk);
-          __syncthreads();
-          if (tid == 0 && pick < 0) pick = 0;
-          __syncthreads();
+        if (tid == 0) pick = any_mass ? -1 : S;
+        __syncthreads();
+        for (int i = tid; i < S; i += kKppThreads) {
+          if (any_mass) {
+            if (d2s[i] > 0.0) atomicMax(&pick, i);
+          } else if (!((taken[i >> 5] >> (i & 31)) & 1u)) {
+            atomicMin(&pick, i);
+          }
         }
-      } else {
-        // every D^2 is zero: lowest candidate not yet chosen
-        int first = S;
-#pragma unroll
-        for (int k = kKppMaxPer - 1; k >= 0; --k)
-          if (k < P && base + k < S && !((taken >> k) & 1u)) first = base + k;
-        if (first < S) atomicMin(&pick, first);
         __syncthreads();
       }
     }
     const int t = pick;
-    const int64_t row = cand_row(t, S, N);
-    // ---- centre c = x_t, y = M c (or c), cc = c.y
-    for (int a = tid; a < D; a += kKppThreads) {
-      const float cv = load_f32(Xh + row * D, a);
-      cvec[a] = (double)cv;
-      cent[((int64_t)h * C + m) * D + a] = cv;
-    }
-    __syncthreads();
-    if (Mh != nullptr) {
-      // thread (a, part): 8 threads per output row, 16 products each for D = 128
-      constexpr int kParts = 8;
-      const int a = tid / kParts;
-      const int part = tid % kParts;
-      double y = 0.0;
-      if (a < D) {
-        const int b0 = part * (D / kParts);
-#pragma unroll
-        for (int b = 0; b < D / kParts; ++b) y += (double)Mh[a * D + b0 + b] * cvec[b0 + b];
-      }
-#pragma unroll
-      for (int o = 1; o < kParts; o <<= 1) y += __shfl_xor(y, o, kWave);
-      if (a < D && part == 0) yvec[a] = y;
-    } else {
-      for (int a = tid; a < D; a += kKppThreads) yvec[a] = cvec[a];
-    }
-    __syncthreads();
+    // centre: y = M x_t (or x_t); cc = xx_t
     {
-      double s = (tid < D) ? cvec[tid] * yvec[tid] : 0.0;
-      s = wave_sum_f64(s);
-      if (l == 0) red[w] = s;
-      __syncthreads();
-      if (tid == 0) {
-        double c2 = 0.0;
-        for (int q = 0; q < kKppThreads / kWave; ++q) c2 += red[q];
-        cc_shared = c2;
+      if (tid == 0) taken[t >> 5] |= 1u << (t & 31);
+      const T* xt = Xh + cand_row(t, S, N) * D;
+      for (int a = tid; a < D; a += kKppThreads) {
+        const float xa = load_f32(xt, a);
+        yf[a] = yh ? yh[(int64_t)t * D + a] : xa;
+        sd.cent[((int64_t)h * C + m) * D + a] = xa;
       }
-      __syncthreads();
+      if (tid == 0) cc_s = xxh[t];
     }
-    const double cc = cc_shared;
-    // ---- D^2 update: dist = xx - 2 x.y + cc
+    __syncthreads();  // C
+    const double cc = cc_s;
+    float yc[EPC];
 #pragma unroll
-    for (int k = 0; k < kKppMaxPer; ++k) {
-      if (k < P && base + k < S) {
-        const int i = base + k;
-        if (i == t) {
-          taken |= 1u << k;
-          d2[k] = 0.0;
-        } else if (!((taken >> k) & 1u)) {
-          const T* x = Xh + cand_row(i, S, N) * D;
-          double dot = 0.0;
-          for (int a0 = 0; a0 < D; a0 += 8) {
-            float xv[8];
-            load8_f32(x + a0, xv);
+    for (int e = 0; e < EPC; ++e) yc[e] = yf[my_chunk * EPC + e];
+    for (int r0 = 0; r0 < rounds; r0 += BATCH) {
+      u32x4_t xv[BATCH];
+      double xxv[BATCH];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dot += (double)xv[e] * yvec[a0 + e];
+      for (int b = 0; b < BATCH; ++b) {
+        const int i = (r0 + b) * RPB + w * RPW + my_row_in_wave;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        double n2 = 0.0;
+        if (r0 + b < rounds && i < S) {
+          v = *reinterpret_cast<const u32x4_t*>(Xh + cand_row(i, S, N) * D + my_chunk * EPC);
+          n2 = xxh[i];
+        }
+        xv[b] = v;
+        xxv[b] = n2;
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        float acc = 0.f;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc = __builtin_fmaf(__uint_as_float(xv[b][q] << 16), yc[2 * q], acc);
+            acc = __builtin_fmaf(__uint_as_float(xv[b][q] & 0xFFFF0000u), yc[2 * q + 1], acc);
           }
-          double dist = own_xx[k] - 2.0 * dot + cc;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(__uint_as_float(xv[b][q]), yc[q], acc);
+        }
+        acc = group_sum<LPR>(acc);
+        const int i = (r0 + b) * RPB + w * RPW + my_row_in_wave;
+        if (my_chunk == 0 && r0 + b < rounds && i < S) {
+          double dist = xxv[b] - 2.0 * (double)acc + cc;
           dist = dist > 0.0 ? dist : 0.0;
-          d2[k] = (m == 0 || dist < d2[k]) ? dist : d2[k];
+          if (i == t)
+            d2s[i] = 0.0;
+          else if (m == 0 || dist < d2s[i])
+            d2s[i] = dist;
         }
       }
     }
@@ -231,88 +291,449 @@ __global__ __launch_bounds__(kKppThreads) void kpp_seed(const T* __restrict__ X,
 }
 
 // ------------------------------------------------------------------------------------------------
-// Update (optional) + consumed centroid form
+// Cooperative k-means++ (bf16 data): the candidates of one (head, side) are split over G
+// co-resident workgroups, each holding its share on chip for the whole seeding (one row per thread
+// in registers, the rest in LDS), so a step touches no off-chip candidate data. Per step the parts
+// publish their D^2 sums, the part holding the sampled prefix position finds the candidate and
+// publishes it, and every part lowers its D^2 against the new centre. Launched cooperatively
+// (all workgroups resident); every wait is bounded.
 // ------------------------------------------------------------------------------------------------
 
-// One workgroup per (cluster, head). With do_update, c_j = fp32(fp64 mean of members in sorted
-// order); empty clusters keep their value. Then g_j, b_j for the next assignment:
-//   Euclidean: g = c (bf16-rounded for bf16 data), b = fp32(sum g^2)
-//   QRKC:      y = M c (fp64), g = fp32(y) (then bf16), b = fp32(c.y)
+constexpr int kCoopMaxParts = 16;
+constexpr int kCoopThreads = 512;  // 2 waves per SIMD: room for one candidate row per thread
+constexpr int kCoopWaves = kCoopThreads / kWave;
+constexpr long long kSpinLimit = 1ll << 20;  // ~30 ms per wait; a normal wait takes microseconds
+
+struct CoopSide {
+  const uint16_t* x;  // [H, N, D]
+  const double* xx;   // [H, S]
+  const float* y;     // [H, S, D] or NULL (Euclidean)
+  float* cent;        // [H, C, D]
+  double* psum;       // [H, C, kCoopMaxParts, 2]: per part (D^2 sum, first untaken candidate)
+  int* sync;          // [H, C, 3]: arrivals, chosen candidate, chosen flag; then one failure flag
+  int C, S, side, G, SP;
+};
+
+// Wait until *p >= want: relaxed polling (no cache maintenance per poll), then one acquire fence.
+// A wait that runs out sets *fail, after which every wait of the launch returns at once, so a
+// broken launch still ends promptly (with wrong centroids) instead of hanging.
+__device__ __forceinline__ void spin_until(int* p, int want, int* fail) {
+  long long n = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+    if (__hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    if (++n >= kSpinLimit) {
+      __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int D>
+__global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s1, int H, int64_t N, uint64_t seed) {
+  constexpr int ROW_U32 = D / 2;
+  extern __shared__ uint32_t lrows[];  // [SP - threads][D / 2] bf16 pairs of the LDS-resident rows
+  __shared__ __attribute__((aligned(16))) uint32_t yhi[D / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t ylo[D / 2];
+  __shared__ double wred[kCoopWaves];
+  __shared__ double wred2[kCoopWaves];
+  __shared__ int wmin[kCoopWaves];
+  __shared__ double pre_s, v_s, cc_s;
+  __shared__ int owner_s, pick_s;
+
+  // decode (side, head, part)
+  int b = blockIdx.x;
+  const bool second = b >= H * s0.G;
+  const CoopSide sd = second ? s1 : s0;
+  if (second) b -= H * s0.G;
+  const int h = b / sd.G;
+  const int part = b % sd.G;
+  const int C = sd.C, S = sd.S, G = sd.G, SP = sd.SP;
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int w = tid / kWave;
+  const int c0 = part * SP;                   // first candidate of this part
+  const int cnt = min(SP, S - c0);            // candidates of this part
+  const int nreg = min(cnt, kCoopThreads);     // register-resident (thread tid: c0 + tid)
+  const int nlds = cnt - nreg;                // LDS-resident (thread tid: c0 + 1024 + tid)
+  const uint16_t* Xh = sd.x + (int64_t)h * N * D;
+  const double* xxh = sd.xx + (int64_t)h * S;
+  const float* yh = sd.y ? sd.y + (int64_t)h * S * D : nullptr;
+  double* psum = sd.psum + (int64_t)h * C * kCoopMaxParts * 2;
+  int* sync = sd.sync + (int64_t)h * C * 3;
+  int* fail = sd.sync + (int64_t)H * C * 3;
+
+  // on-chip candidate rows
+  const bool has_r = tid < nreg;
+  const bool has_l = tid < nlds;
+  uint32_t xr[ROW_U32];
+  {
+    const int i = c0 + tid;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(Xh + (has_r ? cand_row(i, S, N) : 0) * D);
+#pragma unroll
+    for (int q = 0; q < ROW_U32; q += 4) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (has_r) v = *reinterpret_cast<const u32x4_t*>(src + q);
+      xr[q] = v[0];
+      xr[q + 1] = v[1];
+      xr[q + 2] = v[2];
+      xr[q + 3] = v[3];
+    }
+  }
+  for (int e = tid; e < nlds * (ROW_U32 / 4); e += kCoopThreads) {
+    const int r = e / (ROW_U32 / 4), q = (e % (ROW_U32 / 4)) * 4;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(Xh + cand_row(c0 + kCoopThreads + r, S, N) * D);
+    *reinterpret_cast<u32x4_t*>(&lrows[r * ROW_U32 + q]) = *reinterpret_cast<const u32x4_t*>(src + q);
+  }
+  const double xx_r = has_r ? xxh[c0 + tid] : 0.0;
+  const double xx_l = has_l ? xxh[c0 + kCoopThreads + tid] : 0.0;
+  double d2r = 0.0, d2l = 0.0;
+  bool taken_r = false, taken_l = false;
+  __syncthreads();
+
+  for (int m = 0; m < C; ++m) {
+    int t;
+    if (m == 0) {
+      const int t0 = (int)(kpp_uniform(seed, h, sd.side, 0) * (double)S);
+      t = t0 < S ? t0 : S - 1;
+    } else {
+      // ---- this part's D^2 sum and first untaken candidate
+      const double loc = d2r + d2l;
+      double ws = wave_sum_f64(loc);
+      int fu = has_r && !taken_r ? c0 + tid : (has_l && !taken_l ? c0 + kCoopThreads + tid : 0x7FFFFFFF);
+      // lowest untaken: reg candidates precede LDS ones in candidate order
+      const int fu_r = has_r && !taken_r ? c0 + tid : 0x7FFFFFFF;
+      const int fu_l = has_l && !taken_l ? c0 + kCoopThreads + tid : 0x7FFFFFFF;
+      fu = fu_r < fu_l ? fu_r : fu_l;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const int f2 = __shfl_xor(fu, o, kWave);
+        fu = f2 < fu ? f2 : fu;
+      }
+      if (l == 0) {
+        wred[w] = ws;
+        wmin[w] = fu;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double pt = 0.0;
+        int pf = 0x7FFFFFFF;
+        for (int q = 0; q < kCoopWaves; ++q) {
+          pt += wred[q];
+          pf = wmin[q] < pf ? wmin[q] : pf;
+        }
+        psum[((int64_t)m * kCoopMaxParts + part) * 2] = pt;
+        psum[((int64_t)m * kCoopMaxParts + part) * 2 + 1] = (double)pf;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(&sync[m * 3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        spin_until(&sync[m * 3], G, fail);
+        // every part reads the same G values in the same order
+        double total = 0.0;
+        for (int q = 0; q < G; ++q) total += __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2],
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int owner = -1;
+        double pre = 0.0;
+        double v = 0.0;
+        if (total > 0.0) {
+          v = kpp_uniform(seed, h, sd.side, m) * total;
+          double run = 0.0;
+          for (int q = 0; q < G; ++q) {
+            const double pq = __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            if (owner < 0 && run + pq > v) {
+              owner = q;
+              pre = run;
+            }
+            run += pq;
+          }
+          if (owner < 0) {  // v rounded onto the total: the last part with mass
+            run = 0.0;
+            for (int q = 0; q < G; ++q) {
+              const double pq = __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+              if (pq > 0.0) {
+                owner = q;
+                pre = run;
+              }
+              run += pq;
+            }
+          }
+          pick_s = -1;
+        } else {
+          // every D^2 is zero: the lowest candidate not chosen yet, over all parts
+          int best = 0x7FFFFFFF;
+          for (int q = 0; q < G; ++q) {
+            const int fq = (int)__hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2 + 1], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            best = fq < best ? fq : best;
+          }
+          pick_s = best < S ? best : 0;
+        }
+        owner_s = owner;
+        pre_s = pre;
+        v_s = v;
+      }
+      __syncthreads();
+      const int owner = owner_s;
+      if (owner >= 0) {
+        if (owner == part) {
+          // prefix over this part's candidates in candidate order: registers rows, then LDS rows
+          const double v = v_s;
+          const double incr = wave_inclusive_scan(d2r);
+          const double incl = wave_inclusive_scan(d2l);
+          if (l == kWave - 1) {
+            wred[w] = incr;
+            wred2[w] = incl;
+          }
+          __syncthreads();
+          double pr = pre_s, pl;
+          for (int q = 0; q < w; ++q) pr += wred[q];
+          double totr = pre_s;
+          for (int q = 0; q < kCoopWaves; ++q) totr += wred[q];
+          pl = totr;
+          for (int q = 0; q < w; ++q) pl += wred2[q];
+          // first candidate whose running sum exceeds v
+          int hit = 0x7FFFFFFF;
+          if (d2r > 0.0 && pr + incr > v) hit = c0 + tid;
+          else if (d2l > 0.0 && pl + incl > v) hit = c0 + kCoopThreads + tid;
+          if (d2r > 0.0 && pr + incr > v) hit = c0 + tid;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) {
+            const int h2 = __shfl_xor(hit, o, kWave);
+            hit = h2 < hit ? h2 : hit;
+          }
+          if (l == 0) wmin[w] = hit;
+          // fallback (rounding only): the last candidate of this part with mass
+          int lastm = -1;
+          if (d2r > 0.0) lastm = c0 + tid;
+          if (d2l > 0.0) lastm = c0 + kCoopThreads + tid;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) {
+            const int l2 = __shfl_xor(lastm, o, kWave);
+            lastm = l2 > lastm ? l2 : lastm;
+          }
+          __syncthreads();
+          if (l == 0) wred[w] = (double)lastm;
+          __syncthreads();
+          if (tid == 0) {
+            int best = 0x7FFFFFFF, lastbest = -1;
+            for (int q = 0; q < kCoopWaves; ++q) {
+              best = wmin[q] < best ? wmin[q] : best;
+              lastbest = (int)wred[q] > lastbest ? (int)wred[q] : lastbest;
+            }
+            if (best == 0x7FFFFFFF) best = lastbest >= 0 ? lastbest : c0;
+            sync[m * 3 + 1] = best;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(&sync[m * 3 + 2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pick_s = best;
+          }
+        } else if (tid == 0) {
+          spin_until(&sync[m * 3 + 2], 1, fail);
+          pick_s = __hip_atomic_load(&sync[m * 3 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+      }
+      t = pick_s;
+    }
+    // ---- centre y_t as bf16 pairs (high part, remainder); part 0 writes the output centroid
+    for (int a2 = tid; a2 < D / 2; a2 += kCoopThreads) {
+      const uint16_t* xt = Xh + cand_row(t, S, N) * D;
+      const float x0 = bf16_bits_to_f32(xt[2 * a2]), x1 = bf16_bits_to_f32(xt[2 * a2 + 1]);
+      const float y0 = yh ? yh[(int64_t)t * D + 2 * a2] : x0;
+      const float y1 = yh ? yh[(int64_t)t * D + 2 * a2 + 1] : x1;
+      const uint32_t h0 = f32_to_bf16_bits(y0), h1 = f32_to_bf16_bits(y1);
+      yhi[a2] = h0 | (h1 << 16);
+      ylo[a2] = f32_to_bf16_bits(y0 - bf16_bits_to_f32(h0)) | (f32_to_bf16_bits(y1 - bf16_bits_to_f32(h1)) << 16);
+      if (part == 0) {
+        sd.cent[((int64_t)h * C + m) * D + 2 * a2] = x0;
+        sd.cent[((int64_t)h * C + m) * D + 2 * a2 + 1] = x1;
+      }
+    }
+    if (tid == 0) cc_s = xxh[t];
+    __syncthreads();
+    const double cc = cc_s;
+    // ---- lower D^2 against the new centre. Dot products on packed bf16 pairs (v_dot2_f32_bf16,
+    // fp32 accumulation) against y split into a bf16 high part and a bf16 remainder.
+    {
+      float accr = 0.f, accl = 0.f;
+      const uint32_t* lrow = lrows + tid * ROW_U32;
+#pragma unroll
+      for (int q = 0; q < ROW_U32; q += 4) {
+        const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(&yhi[q]);
+        const u32x4_t lv = *reinterpret_cast<const u32x4_t*>(&ylo[q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t xe = xr[q + e], he = hv[e], le = lv[e];
+          accr = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(he), accr, false);
+          accr = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accr, false);
+        }
+        if (has_l) {
+          const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(lrow + q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t xe = xv[e], he = hv[e], le = lv[e];
+            accl = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(he), accl, false);
+            accl = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accl, false);
+          }
+        }
+      }
+      if (has_r) {
+        if (c0 + tid == t) {
+          taken_r = true;
+          d2r = 0.0;
+        } else if (!taken_r) {
+          double dist = xx_r - 2.0 * (double)accr + cc;
+          dist = dist > 0.0 ? dist : 0.0;
+          d2r = (m == 0 || dist < d2r) ? dist : d2r;
+        }
+      }
+      if (has_l) {
+        if (c0 + kCoopThreads + tid == t) {
+          taken_l = true;
+          d2l = 0.0;
+        } else if (!taken_l) {
+          double dist = xx_l - 2.0 * (double)accl + cc;
+          dist = dist > 0.0 ? dist : 0.0;
+          d2l = (m == 0 || dist < d2l) ? dist : d2l;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void fill_i32(int* p, int64_t n, int v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Update: member means, then the consumed centroid form (g, b) for the next assignment
+// ------------------------------------------------------------------------------------------------
+
+// One workgroup per (cluster, head). With do_update, c_j = fp32(fp64 mean of the members, summed
+// in cluster order); empty clusters keep their value. Euclidean sides also write g_j (c_j, bf16-
+// rounded for bf16 data) and b_j = fp32(sum g_j^2); QRKC sides get (g, b) from consume_qrkc.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void update_consume(const T* __restrict__ X, int64_t N, int C,
-                                                      const int32_t* __restrict__ perm,
-                                                      const int32_t* __restrict__ offsets, float* __restrict__ cent,
-                                                      int do_update, const float* __restrict__ M, void* g_out,
-                                                      float* __restrict__ b_out, int bf16) {
-  constexpr int TPR = D / 2;        // threads per row (2 dims each)
-  constexpr int RG = 256 / TPR;     // row groups
+__global__ __launch_bounds__(256) void centroid_mean(const T* __restrict__ X, int64_t N, int C,
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ offsets, float* __restrict__ cent,
+                                                     int do_update, int euclid, void* g_out, float* __restrict__ b_out,
+                                                     int bf16) {
+  constexpr int CPR = D / 8;     // 8-element pieces per row
+  constexpr int RG = 256 / CPR;  // row groups
   __shared__ double part[RG][D];
-  __shared__ float cvec[D];
   __shared__ double red[4];
   const int j = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int l = lane_id();
   float* cj = cent + ((int64_t)h * C + j) * D;
+  float c = 0.f;
   int n = 0;
   if (do_update) {
     const int beg = offsets[(int64_t)h * (C + 1) + j];
     const int end = offsets[(int64_t)h * (C + 1) + j + 1];
     n = end - beg;
     if (n > 0) {
-      const int dp = tid % TPR;
-      const int rg = tid / TPR;
+      const int pc = tid % CPR;
+      const int rg = tid / CPR;
       const T* Xh = X + (int64_t)h * N * D;
       const int32_t* ph = perm + (int64_t)h * N;
-      double s0 = 0.0, s1 = 0.0;
+      double acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0;
       for (int r = beg + rg; r < end; r += RG) {
-        const T* x = Xh + (int64_t)ph[r] * D + 2 * dp;
-        s0 += (double)load_f32(x, 0);
-        s1 += (double)load_f32(x, 1);
+        float xv[8];
+        load8_f32(Xh + (int64_t)ph[r] * D + pc * 8, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (double)xv[e];
       }
-      part[rg][2 * dp] = s0;
-      part[rg][2 * dp + 1] = s1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[rg][pc * 8 + e] = acc[e];
       __syncthreads();
       if (tid < D) {
-        double s = 0.0;
+        double sum = 0.0;
 #pragma unroll
-        for (int q = 0; q < RG; ++q) s += part[q][tid];
-        const float c = (float)(s / (double)n);
+        for (int q = 0; q < RG; ++q) sum += part[q][tid];
+        c = (float)(sum / (double)n);
         cj[tid] = c;
-        cvec[tid] = c;
       }
     }
   }
-  if (n == 0 && tid < D) cvec[tid] = cj[tid];
-  __syncthreads();
+  if (!euclid) return;
+  if (n == 0 && tid < D) c = cj[tid];
   double term = 0.0;
   if (tid < D) {
     const int64_t gi = ((int64_t)h * C + j) * D + tid;
-    float gv;
-    if (M == nullptr) {
-      gv = cvec[tid];
-      if (bf16) gv = bf16_bits_to_f32(f32_to_bf16_bits(gv));
-      term = (double)gv * (double)gv;
-    } else {
-      const float* Mr = M + (int64_t)h * D * D + (int64_t)tid * D;
-      double y = 0.0;
-      for (int b = 0; b < D; ++b) y += (double)Mr[b] * (double)cvec[b];
-      gv = (float)y;
-      if (bf16) gv = bf16_bits_to_f32(f32_to_bf16_bits(gv));
-      term = (double)cvec[tid] * y;
-    }
-    if (bf16)
+    float gv = c;
+    if (bf16) {
+      gv = bf16_bits_to_f32(f32_to_bf16_bits(gv));
       static_cast<uint16_t*>(g_out)[gi] = (uint16_t)(__float_as_uint(gv) >> 16);
-    else
+    } else {
       static_cast<float*>(g_out)[gi] = gv;
+    }
+    term = (double)gv * (double)gv;
   }
   term = wave_sum_f64(term);
-  if (l == 0) red[tid / kWave] = term;
+  if (lane_id() == 0) red[tid / kWave] = term;
   __syncthreads();
-  if (tid == 0) {
-    double s = 0.0;
-    for (int q = 0; q < 4; ++q) s += red[q];
-    b_out[(int64_t)h * C + j] = (float)s;
+  if (tid == 0) b_out[(int64_t)h * C + j] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
+}
+
+// QRKC consumed form for 32 centroids per block: y_j = M c_j (fp64 sums of fp64 products; M
+// staged in LDS as fp32 and read along columns, which M's symmetry makes equal to rows),
+// g_j = fp32(y_j) (then bf16), b_j = fp32(c_j . y_j). Thread = (output dim a, 16 centroids).
+template <int D>
+__global__ __launch_bounds__(256) void consume_qrkc(const float* __restrict__ cent, int C, const float* __restrict__ M,
+                                                    void* g_out, float* __restrict__ b_out, int bf16) {
+  constexpr int JB = 32;                  // centroids per block
+  constexpr int JT = JB * D / 256;        // centroids per thread (16 for D = 128, 8 for D = 64)
+  extern __shared__ float cq_lds[];
+  float* ms = cq_lds;                              // [D][D]
+  double* cs = reinterpret_cast<double*>(cq_lds + D * D);  // [JB][D]
+  __shared__ double bred[JB][256 / 64];
+  const int h = blockIdx.y;
+  const int j0 = blockIdx.x * JB;
+  for (int e = threadIdx.x; e < D * D; e += 256) ms[e] = M[(int64_t)h * D * D + e];
+  for (int e = threadIdx.x; e < JB * D; e += 256) {
+    const int jj = j0 + e / D;
+    cs[e] = jj < C ? (double)cent[((int64_t)h * C + jj) * D + e % D] : 0.0;
+  }
+  __syncthreads();
+  const int a = threadIdx.x % D;
+  const int jg = threadIdx.x / D;  // which group of JT centroids
+  double acc[JT];
+#pragma unroll
+  for (int q = 0; q < JT; ++q) acc[q] = 0.0;
+  for (int b = 0; b < D; ++b) {
+    const double m = (double)ms[b * D + a];  // M[b][a] == M[a][b]
+#pragma unroll
+    for (int q = 0; q < JT; ++q) acc[q] += m * cs[(jg * JT + q) * D + b];
+  }
+  // g and the per-thread terms of b_j = sum_a c_ja y_ja
+#pragma unroll
+  for (int q = 0; q < JT; ++q) {
+    const int jl = jg * JT + q;
+    const int j = j0 + jl;
+    double term = cs[jl * D + a] * acc[q];
+    if (j < C) {
+      const int64_t gi = ((int64_t)h * C + j) * D + a;
+      const float gv = (float)acc[q];
+      if (bf16)
+        static_cast<uint16_t*>(g_out)[gi] = (uint16_t)f32_to_bf16_bits(gv);
+      else
+        static_cast<float*>(g_out)[gi] = gv;
+    }
+    term = wave_sum_f64(term);
+    if (lane_id() == 0) bred[jl][(threadIdx.x % D) / 64] = term;
+  }
+  __syncthreads();
+  if (threadIdx.x < JB && j0 + threadIdx.x < C) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) t += bred[threadIdx.x][w];
+    b_out[(int64_t)h * C + j0 + threadIdx.x] = (float)t;
   }
 }
 
@@ -551,51 +972,182 @@ __global__ __launch_bounds__(64) void sort_scatter(const int32_t* __restrict__ l
 // Launchers
 // ------------------------------------------------------------------------------------------------
 
-hipError_t launch_kpp(const Dims& s, const void* x, const float* metric, int C, uint64_t seed, int side,
-                      float* cent, double* cand_norm, hipStream_t st) {
-  const int S = kpp_candidates(s.N, C);
-  const dim3 g1((unsigned)ceil_div(S, 256), (unsigned)s.H);
-#define PARK_KPP(T, D)                                                                                 \
-  kpp_cand_norm<T, D><<<g1, 256, 0, st>>>(static_cast<const T*>(x), s.N, S, metric, cand_norm);       \
-  kpp_seed<T, D><<<(unsigned)s.H, kKppThreads, 0, st>>>(static_cast<const T*>(x), s.N, S, C, metric, \
-                                                         cand_norm, seed, side, cent);
+// Single-workgroup seeding (any dtype): candidate norms, then one workgroup per (head, side).
+static hipError_t launch_kpp_single(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
+  KppSide ks[2];
+  int smax = 0;
+  for (int q = 0; q < nsides; ++q) {
+    const KppArgs& a = sides[q];
+    const int S = kpp_candidates(s.N, a.C);
+    smax = S > smax ? S : smax;
+    ks[q] = KppSide{a.x, a.xx, a.metric ? a.y : nullptr, a.cent, a.C, S, a.side};
+  }
+  if (nsides == 1) ks[1] = ks[0];
+  const dim3 grid((unsigned)s.H, (unsigned)nsides);
+  const size_t lds = (size_t)smax * sizeof(double);
+#define PARK_SEED(T, D) kpp_seed<T, D><<<grid, kKppThreads, lds, st>>>(ks[0], ks[1], s.N, seed);
   if (s.bf16) {
     if (s.D == 128) {
-      PARK_KPP(uint16_t, 128)
+      PARK_SEED(uint16_t, 128)
     } else {
-      PARK_KPP(uint16_t, 64)
+      PARK_SEED(uint16_t, 64)
     }
   } else {
     if (s.D == 128) {
-      PARK_KPP(float, 128)
+      PARK_SEED(float, 128)
     } else {
-      PARK_KPP(float, 64)
+      PARK_SEED(float, 64)
     }
   }
-#undef PARK_KPP
+#undef PARK_SEED
   return hipGetLastError();
 }
 
-hipError_t launch_consume(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets,
-                          float* cent, int do_update, const float* metric, void* g, float* b, hipStream_t st) {
-  const dim3 grid((unsigned)C, (unsigned)s.H);
-#define PARK_UPD(T, D)                                                                                         \
-  update_consume<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(x), s.N, C, perm, offsets, cent, do_update, \
-                                             metric, g, b, s.bf16);
-  if (s.bf16) {
-    if (s.D == 128) {
-      PARK_UPD(uint16_t, 128)
-    } else {
-      PARK_UPD(uint16_t, 64)
+// Parts per side for the cooperative seeding within `budget` workgroups per head; false if the
+// candidates cannot be held on chip with that budget.
+static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budget, int* G) {
+  const int lmax = (140 * 1024) / (int)(s.D * 2);  // LDS-resident rows per part
+  const int cap = kCoopThreads + lmax;
+  int used = 0;
+  double work[2];
+  for (int q = 0; q < nsides; ++q) {
+    const int S = kpp_candidates(s.N, sides[q].C);
+    G[q] = (int)ceil_div(S, cap);
+    if (G[q] > kCoopMaxParts) return false;
+    used += G[q];
+    work[q] = (double)sides[q].C * S;
+  }
+  if (used > budget) return false;
+  // spare workgroups go where the per-part work is largest
+  while (used < budget) {
+    int best = -1;
+    double bw = 0.0;
+    for (int q = 0; q < nsides; ++q) {
+      const int S = kpp_candidates(s.N, sides[q].C);
+      if (G[q] >= kCoopMaxParts || ceil_div(S, G[q] + 1) < 256) continue;
+      const double wq = work[q] / G[q];
+      if (wq > bw) {
+        bw = wq;
+        best = q;
+      }
     }
-  } else {
-    if (s.D == 128) {
-      PARK_UPD(float, 128)
+    if (best < 0) break;
+    ++G[best];
+    ++used;
+  }
+  return true;
+}
+
+static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nsides, const int* G, uint64_t seed,
+                                  hipStream_t st) {
+  CoopSide cs[2];
+  size_t lds = 0;
+  int64_t total = 0;
+  for (int q = 0; q < nsides; ++q) {
+    const KppArgs& a = sides[q];
+    const int S = kpp_candidates(s.N, a.C);
+    const int SP = (int)ceil_div(S, G[q]);
+    cs[q] = CoopSide{static_cast<const uint16_t*>(a.x), a.xx, a.metric ? a.y : nullptr, a.cent, a.psum, a.sync,
+                     a.C, S, a.side, G[q], SP};
+    const size_t l = (size_t)(SP > kCoopThreads ? SP - kCoopThreads : 0) * (size_t)s.D * 2;
+    lds = l > lds ? l : lds;
+    total += s.H * G[q];
+    const int64_t nsync = s.H * (int64_t)a.C * 3 + 1;
+    fill_i32<<<(unsigned)ceil_div(nsync, 256), 256, 0, st>>>(a.sync, nsync, 0);
+  }
+  if (nsides == 1) {
+    cs[1] = cs[0];
+    cs[1].G = 0;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int H = (int)s.H;
+  int64_t N = s.N;
+  void* args[] = {&cs[0], &cs[1], &H, &N, &seed};
+  const void* fn = s.D == 128 ? (const void*)kpp_coop<128> : (const void*)kpp_coop<64>;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)total), dim3(kCoopThreads), args, (unsigned)lds, st);
+}
+
+hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
+  // candidate norms (and metric products) for every side
+  for (int q = 0; q < nsides; ++q) {
+    const KppArgs& a = sides[q];
+    const int S = kpp_candidates(s.N, a.C);
+    const dim3 g1((unsigned)ceil_div(S, 64), (unsigned)s.H);
+    const size_t lds = (size_t)(64 * (s.D + 1) + (a.metric ? s.D * s.D : 0)) * sizeof(float);
+#define PARK_PREP(T, D) \
+  kpp_prep<T, D><<<g1, 256, lds, st>>>(static_cast<const T*>(a.x), s.N, S, a.metric, a.xx, a.metric ? a.y : nullptr);
+    if (s.bf16) {
+      if (s.D == 128) {
+        PARK_PREP(uint16_t, 128)
+      } else {
+        PARK_PREP(uint16_t, 64)
+      }
     } else {
-      PARK_UPD(float, 64)
+      if (s.D == 128) {
+        PARK_PREP(float, 128)
+      } else {
+        PARK_PREP(float, 64)
+      }
+    }
+#undef PARK_PREP
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s.bf16) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && cus > 0) {
+      const int budget = cus / (int)s.H;
+      int G[2];
+      if (budget > 0 && plan_parts(s, sides, nsides, budget, G)) {
+        if (launch_kpp_coop(s, sides, nsides, G, seed, st) == hipSuccess) return hipSuccess;
+        (void)hipGetLastError();
+      } else if (nsides == 2 && budget > 0 && plan_parts(s, sides, 1, budget, G) &&
+                 plan_parts(s, sides + 1, 1, budget, G + 1)) {
+        // both sides do not fit at once: one launch per side
+        if (launch_kpp_coop(s, sides, 1, G, seed, st) == hipSuccess &&
+            launch_kpp_coop(s, sides + 1, 1, G + 1, seed, st) == hipSuccess)
+          return hipSuccess;
+        (void)hipGetLastError();
+      }
     }
   }
-#undef PARK_UPD
+  return launch_kpp_single(s, sides, nsides, seed, st);
+}
+
+hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets, float* cent,
+                         int do_update, const float* metric, void* g, float* b, hipStream_t st) {
+  const dim3 grid((unsigned)C, (unsigned)s.H);
+  const int euclid = metric == nullptr;
+  if (do_update || euclid) {
+#define PARK_MEAN(T, D)                                                                                    \
+  centroid_mean<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(x), s.N, C, perm, offsets, cent, do_update, \
+                                            euclid, g, b, s.bf16);
+    if (s.bf16) {
+      if (s.D == 128) {
+        PARK_MEAN(uint16_t, 128)
+      } else {
+        PARK_MEAN(uint16_t, 64)
+      }
+    } else {
+      if (s.D == 128) {
+        PARK_MEAN(float, 128)
+      } else {
+        PARK_MEAN(float, 64)
+      }
+    }
+#undef PARK_MEAN
+  }
+  if (!euclid) {
+    const dim3 g2((unsigned)ceil_div(C, 32), (unsigned)s.H);
+    const size_t lds = (size_t)s.D * s.D * sizeof(float) + (size_t)32 * s.D * sizeof(double);
+    if (s.D == 128)
+      consume_qrkc<128><<<g2, 256, lds, st>>>(cent, C, metric, g, b, s.bf16);
+    else
+      consume_qrkc<64><<<g2, 256, lds, st>>>(cent, C, metric, g, b, s.bf16);
+  }
   return hipGetLastError();
 }
 

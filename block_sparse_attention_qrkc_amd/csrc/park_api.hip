@@ -95,13 +95,20 @@ MetricWs plan_metric(Carver& cv, const park::Dims& s) {
 
 struct ClusterWs {
   double* cand_norm;
+  float* cand_y;
+  double* kpp_psum;
+  int32_t* kpp_sync;
   int32_t* table;
   void* g;
   float* b;
 };
-ClusterWs plan_cluster(Carver& cv, const park::Dims& s, int C) {
+ClusterWs plan_cluster(Carver& cv, const park::Dims& s, int C, bool qrkc) {
   ClusterWs w;
-  w.cand_norm = cv.take<double>((size_t)s.H * park::kpp_candidates(s.N, C));
+  const size_t S = (size_t)park::kpp_candidates(s.N, C);
+  w.cand_norm = cv.take<double>((size_t)s.H * S);
+  w.cand_y = qrkc ? cv.take<float>((size_t)s.H * S * s.D) : nullptr;
+  w.kpp_psum = cv.take<double>((size_t)s.H * C * 16 * 2);
+  w.kpp_sync = cv.take<int32_t>((size_t)s.H * C * 3 + 1);
   w.table = cv.take<int32_t>(park::sort_table_ints(s, C));
   w.g = s.bf16 ? (void*)cv.take<uint16_t>((size_t)(s.H * C * s.D)) : (void*)cv.take<float>((size_t)(s.H * C * s.D));
   w.b = cv.take<float>((size_t)(s.H * C));
@@ -160,8 +167,8 @@ ForwardWs plan_forward(Carver& cv, const park::Dims& s, const park_params& p) {
   w.cols = cv.take<int32_t>((size_t)(s.H * p.cq * p.ck));
   w.sel_keys = cv.take<int64_t>((size_t)(s.H * p.cq));
   w.mt = plan_metric(cv, s);
-  w.qc = plan_cluster(cv, s, p.cq);
-  w.kc = plan_cluster(cv, s, p.ck);
+  w.qc = plan_cluster(cv, s, p.cq, false);
+  w.kc = plan_cluster(cv, s, p.ck, p.kmetric == PARK_QRKC);
   w.mw = plan_map(cv, s, p.cq, p.ck);
   w.aw = plan_attn(cv, s, p.cq, p.ck);
   return w;
@@ -194,23 +201,22 @@ size_t forward_ws_bytes(const park::Dims& s, const park_params& p) {
   return cv.off;
 }
 
-// Clustering sequence shared by park_cluster and park_forward.
-hipError_t run_cluster(const park::Dims& s, const void* x, const float* metric, int C, int iters, int init,
-                       uint64_t seed, int side, float* cent, int32_t* labels, int32_t* perm, int32_t* offsets,
-                       const ClusterWs& w, hipStream_t st) {
-  hipError_t e = hipSuccess;
-  if (init == PARK_INIT_KMEANSPP) {
-    e = park::launch_kpp(s, x, metric, C, seed, side, cent, w.cand_norm, st);
-    if (e != hipSuccess) return e;
-  }
-  if (iters == 0) return e;
-  e = park::launch_consume(s, x, C, nullptr, nullptr, cent, 0, metric, w.g, w.b, st);
+// Lloyd iterations shared by park_cluster and park_forward: (g, b) of the current centroids, then
+// per iteration assign -> stable sort -> update (which also prepares (g, b) for the next one).
+hipError_t run_lloyd(const park::Dims& s, const void* x, const float* metric, int C, int iters, float* cent,
+                     int32_t* labels, int32_t* perm, int32_t* offsets, const ClusterWs& w, hipStream_t st) {
+  if (iters == 0) return hipSuccess;
+  hipError_t e = park::launch_update(s, x, C, nullptr, nullptr, cent, 0, metric, w.g, w.b, st);
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
     e = park::launch_assign(s, x, C, w.g, w.b, labels, st);
     if (e == hipSuccess) e = park::launch_sort(s, C, labels, w.table, perm, offsets, st);
-    if (e == hipSuccess) e = park::launch_consume(s, x, C, perm, offsets, cent, 1, metric, w.g, w.b, st);
+    if (e == hipSuccess) e = park::launch_update(s, x, C, perm, offsets, cent, 1, metric, w.g, w.b, st);
   }
   return e;
+}
+
+park::KppArgs kpp_args(const void* x, const float* metric, int C, int side, float* cent, const ClusterWs& w) {
+  return park::KppArgs{x, metric, C, side, cent, w.cand_norm, w.cand_y, w.kpp_psum, w.kpp_sync};
 }
 
 }  // namespace
@@ -246,7 +252,7 @@ size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_p
         if (!params) return 0;
         const int C = entry == PARK_ENTRY_CLUSTER_Q ? params->cq : params->ck;
         if (check_clusters(s, C, "clusters") != PARK_OK) return 0;
-        plan_cluster(cv, s, C);
+        plan_cluster(cv, s, C, entry == PARK_ENTRY_CLUSTER_K && params->kmetric == PARK_QRKC);
         return cv.off;
       }
       case PARK_ENTRY_RETRIEVE_MAP:
@@ -308,14 +314,19 @@ park_status park_cluster(const park_shape* shape, const void* x, int32_t metric,
       PARK_TRY(check_ptr(offsets, "offsets", 4));
     }
     Carver meas(nullptr);
-    plan_cluster(meas, s, n_clusters);
+    plan_cluster(meas, s, n_clusters, metric == PARK_QRKC);
     PARK_TRY(check_ws(ws, ws_bytes, meas.off));
     Carver cv(ws);
-    ClusterWs w = plan_cluster(cv, s, n_clusters);
+    ClusterWs w = plan_cluster(cv, s, n_clusters, metric == PARK_QRKC);
     const float* mp = metric == PARK_QRKC ? qmetric : nullptr;
-    return hip_check(run_cluster(s, x, mp, n_clusters, iters, init, seed, side, centroids, labels, perm, offsets, w,
-                                 (hipStream_t)stream),
-                     "park_cluster");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (init == PARK_INIT_KMEANSPP) {
+      const park::KppArgs a = kpp_args(x, mp, n_clusters, side, centroids, w);
+      e = park::launch_kpp(s, &a, 1, seed, st);
+    }
+    if (e == hipSuccess) e = run_lloyd(s, x, mp, n_clusters, iters, centroids, labels, perm, offsets, w, st);
+    return hip_check(e, "park_cluster");
   } catch (...) {
     return fail(PARK_EHIP, "park_cluster: internal error");
   }
@@ -476,11 +487,14 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
 
     hipError_t e = hipSuccess;
     if (qrkc) e = park::launch_metric(s, q, M, w.mt.partial, st);
-    if (e == hipSuccess)
-      e = run_cluster(s, q, nullptr, p.cq, p.iters, p.init, p.seed, PARK_SIDE_Q, q_centroids, ql, qp, qo, w.qc, st);
-    if (e == hipSuccess)
-      e = run_cluster(s, k, qrkc ? M : nullptr, p.ck, p.iters, p.init, p.seed, PARK_SIDE_K, k_centroids, kl, kp, ko,
-                      w.kc, st);
+    if (e == hipSuccess && p.init == PARK_INIT_KMEANSPP) {
+      // both sides seeded in one launch (one workgroup per head and side)
+      const park::KppArgs a[2] = {kpp_args(q, nullptr, p.cq, PARK_SIDE_Q, q_centroids, w.qc),
+                                  kpp_args(k, qrkc ? M : nullptr, p.ck, PARK_SIDE_K, k_centroids, w.kc)};
+      e = park::launch_kpp(s, a, 2, p.seed, st);
+    }
+    if (e == hipSuccess) e = run_lloyd(s, q, nullptr, p.cq, p.iters, q_centroids, ql, qp, qo, w.qc, st);
+    if (e == hipSuccess) e = run_lloyd(s, k, qrkc ? M : nullptr, p.ck, p.iters, k_centroids, kl, kp, ko, w.kc, st);
     if (e == hipSuccess)
       e = park::launch_pama(s, q, qp, qo, p.cq, k_centroids, ko, p.ck, scale, map, w.mw.khat, w.mw.logn,
                             w.mw.chunk_base, w.mw.partial, st);

@@ -26,6 +26,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
+// A 32-bit word as a pair of bfloat16. Takes the word by value: bit-casting an element of a vector
+// register in place has been seen to read the wrong element, so callers pass a scalar copy.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
 // Two floats to packed bfloat16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};

@@ -31,11 +31,22 @@ hipError_t launch_metric(const Dims& s, const void* q, float* metric, double* pa
 size_t metric_partial_count(const Dims& s);
 
 // kmeans.hip
-hipError_t launch_kpp(const Dims& s, const void* x, const float* metric, int C, uint64_t seed, int side,
-                      float* cent, double* cand_norm, hipStream_t st);
-hipError_t launch_consume(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets,
-                          float* cent, int do_update, const float* metric, void* g, float* b,
-                          hipStream_t st);
+struct KppArgs {
+  const void* x;        // [H, N, D] data of the side
+  const float* metric;  // [H, D, D] query metric (QRKC side) or NULL (Euclidean)
+  int C;                // clusters
+  int side;             // random stream id
+  float* cent;          // [H, C, D] output centroids
+  double* xx;           // workspace [H, S] candidate norms
+  float* y;             // workspace [H, S, D] candidate metric products (QRKC side)
+  double* psum;         // workspace [H, C, 16, 2] per-part sums of the cooperative seeding
+  int* sync;            // workspace [H, C, 3] step flags of the cooperative seeding
+};
+// k-means++ seeding of one or two sides in a single launch.
+hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st);
+// Centroid means (do_update) and the consumed form (g, b) of the centroids for the next assignment.
+hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets, float* cent,
+                         int do_update, const float* metric, void* g, float* b, hipStream_t st);
 hipError_t launch_assign(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
                          hipStream_t st);
 hipError_t launch_sort(const Dims& s, int C, const int32_t* labels, int32_t* table, int32_t* perm,
