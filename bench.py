@@ -70,6 +70,31 @@ def cpu_baseline(w, Q, K, V, seed):
                       f"{n_live} query clusters of head 0 ({t_att:.1f} s) scaled to all clusters and heads"}
 
 
+def kernel_only(args, w, Q, K, V, step, bsa, ws, log):
+    r = step()
+    torch.cuda.synchronize()
+    if args.kernel_only == "sparse_attn":
+        out = torch.empty_like(Q)
+        lse = torch.empty(w.heads, w.n, dtype=torch.float32, device=Q.device)
+        fn = lambda: bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"],
+                                          r["counts"], r["cols"], out=out, lse=lse, ws=ws)
+    elif args.kernel_only == "assign":
+        fn = lambda: bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, r["metric"], init=bsa.PARK_INIT_WARM,
+                                      side=bsa.PARK_SIDE_K, centroids=r["k_centroids"].clone(), ws=ws)
+    else:
+        A = torch.empty(w.heads, w.cq, w.ck, dtype=torch.float32, device=Q.device)
+        kc = r["k_centroids"]
+        fn = lambda: bsa.park_retrieve_map(Q, r["q_perm"], r["q_offsets"], kc, r["k_offsets"], out=A, ws=ws)
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=Q.device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"ran {args.kernel_only} x{args.steps} and a 1 GiB copy")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +104,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown")
+    ap.add_argument("--kernel-only", choices=["sparse_attn", "assign", "pama"], default=None,
+                    help="profiling aid: prepare one layer, then launch only this stage --steps times, followed "
+                         "by a 1 GiB device copy (reference for byte counters); prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -99,11 +127,16 @@ def main():
     qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
     kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
     outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse", "map", "metric")
+    if args.kernel_only:
+        outs = outs + ("k_labels",)
 
     def step():
         return bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed, q_centroids=qcent,
                                 k_centroids=kcent, outputs=outs, ws=ws)
 
+    if args.kernel_only:
+        kernel_only(args, w, Q, K, V, step, bsa, ws, log)
+        return
     for _ in range(args.warmup):
         r = step()
     torch.cuda.synchronize()

@@ -1,15 +1,15 @@
 // Block-sparse attention over the selected (query cluster, key cluster) pairs (PARK abstract:
 // attention is computed only within the retrieved blocks).
 //
-// Schedule: a work item is one 128-query tile of one query cluster. The key clusters a query
-// cluster selected are merged into runs of contiguous cluster-ordered key positions, and the runs
-// are concatenated into one virtual key sequence, so key tiles of 64 are full MFMA tiles except the
-// last one of each item, however small the individual clusters are.
+// Schedule: a work item is one 128-query tile of one query cluster. The original key rows of the
+// key clusters a query cluster selected are gathered once into one list (the cluster's virtual key
+// sequence), so key tiles of 64 are full MFMA tiles except the last one of each item, however small
+// the individual clusters are.
 //
-// Kernel: four waves x 32 queries. Per 64-key tile, keys and values are gathered through the key
-// permutation into LDS (values transposed), S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16
-// MFMA with fp32 accumulation, and an online softmax in exp2 form keeps one running max and sum per
-// query. Outputs are written straight to the queries' original rows.
+// Kernel: four waves x 32 queries. Per 64-key tile, keys and values are copied into LDS through the
+// gather list, S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA with fp32 accumulation,
+// and an online softmax in exp2 form keeps one reference max and sum per query. Outputs are written
+// straight to the queries' original rows.
 #include "park_common.h"
 #include "park_internal.h"
 
@@ -40,70 +40,57 @@ __global__ __launch_bounds__(1024) void attn_tiles(const int32_t* __restrict__ q
   if (threadIdx.x == 0) tb[cq] = total;
 }
 
-// Per (query cluster, head): runs of contiguous key positions. Layout of one row's record
-// (stride 2*ck + 3 ints): [0] = number of runs R, [1 .. R+1] = virtual starts (the last one is the
-// total key count), [ck + 2 .. ck + 2 + R) = key-position starts.
-__global__ __launch_bounds__(256) void attn_runs(const int32_t* __restrict__ counts, const int32_t* __restrict__ cols,
-                                                 const int32_t* __restrict__ k_offsets, int cq, int ck,
-                                                 int32_t* __restrict__ runs) {
-  __shared__ int iscratch[17];
-  __shared__ int iscratch2[17];
+// Per (query cluster, head): the original key rows of the selected key clusters, concatenated in
+// selection order: gather[(h * cq + i) * N + v] for v < glen[h * cq + i]. Column entries outside
+// [0, ck) or with offsets outside [0, N] contribute nothing; the list is cut at N keys.
+__global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ cols,
+                                                   const int32_t* __restrict__ k_offsets,
+                                                   const int32_t* __restrict__ k_perm, int64_t N, int cq, int ck,
+                                                   int32_t* __restrict__ gather, int32_t* __restrict__ glen) {
+  __shared__ int scratch[17];
+  __shared__ int c_start[256], c_len[256], c_dst[256];
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int w = tid / kWave;
   int cnt = counts[(int64_t)h * cq + i];
   cnt = cnt < 0 ? 0 : (cnt > ck ? ck : cnt);
   const int32_t* crow = cols + ((int64_t)h * cq + i) * ck;
   const int32_t* ko = k_offsets + (int64_t)h * (ck + 1);
-  int32_t* rec = runs + ((int64_t)h * cq + i) * (2 * ck + 3);
-  const int per = (cnt + 255) / 256;
-  const int m0 = tid * per;
-  int nflag = 0, len = 0;
-  for (int e = 0; e < per; ++e) {
-    const int m = m0 + e;
+  const int32_t* kp = k_perm + (int64_t)h * N;
+  int32_t* dst = gather + ((int64_t)h * cq + i) * N;
+  int64_t base = 0;
+  for (int m0 = 0; m0 < cnt; m0 += 256) {
+    const int m = m0 + tid;
+    int a = 0, len = 0;
     if (m < cnt) {
       const int j = crow[m];
-      const bool jok = j >= 0 && j < ck;
-      const int a = jok ? ko[j] : 0, b = jok ? ko[j + 1] : 0;
-      if (b > a) {
-        len += b - a;
-        bool start = true;
-        if (m > 0) {
-          const int jp = crow[m - 1];
-          if (jp >= 0 && jp < ck && ko[jp + 1] > ko[jp] && ko[jp + 1] == a) start = false;
+      if (j >= 0 && j < ck) {
+        const int64_t lo = ko[j], hi = ko[j + 1];
+        if (lo >= 0 && hi > lo && hi <= N) {
+          a = (int)lo;
+          len = (int)(hi - lo);
         }
-        nflag += start;
       }
     }
-  }
-  int nruns, total_len;
-  int rid = block_exclusive_scan(nflag, iscratch, &nruns);
-  int vpos = block_exclusive_scan(len, iscratch2, &total_len);
-  for (int e = 0; e < per; ++e) {
-    const int m = m0 + e;
-    if (m < cnt) {
-      const int j = crow[m];
-      const bool jok = j >= 0 && j < ck;
-      const int a = jok ? ko[j] : 0, b = jok ? ko[j + 1] : 0;
-      if (b > a) {
-        bool start = true;
-        if (m > 0) {
-          const int jp = crow[m - 1];
-          if (jp >= 0 && jp < ck && ko[jp + 1] > ko[jp] && ko[jp + 1] == a) start = false;
-        }
-        if (start) {
-          rec[1 + rid] = vpos;
-          rec[ck + 2 + rid] = a;
-          ++rid;
-        }
-        vpos += b - a;
-      }
+    int tot;
+    const int pre = block_exclusive_scan(len, scratch, &tot);
+    c_start[tid] = a;
+    c_len[tid] = len;
+    c_dst[tid] = (int)min<int64_t>(base + pre, N);
+    __syncthreads();
+    const int nloc = min(256, cnt - m0);
+    for (int e = w; e < nloc; e += 4) {
+      const int s0 = c_start[e], d0 = c_dst[e];
+      const int ln = (int)min<int64_t>(c_len[e], N - d0);
+      for (int u = l; u < ln; u += kWave) dst[d0 + u] = kp[s0 + u];
     }
+    base += tot;
+    __syncthreads();
   }
-  if (tid == 0) {
-    rec[0] = nruns;
-    rec[1 + nruns] = total_len;
-  }
+  if (tid == 0) glen[(int64_t)h * cq + i] = (int)min<int64_t>(base, N);
 }
 
 __device__ __forceinline__ int find_tile(const int32_t* tb, int cq, int c) {
@@ -121,7 +108,7 @@ __device__ __forceinline__ int find_tile(const int32_t* tb, int cq, int c) {
 template <typename T>
 __device__ __forceinline__ void store_out4(T* p, float a, float b, float c, float d);
 template <>
-__device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+[[maybe_unused]] __device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
   u32x2_t v;
   v[0] = pack_bf16x2(a, b);
   v[1] = pack_bf16x2(c, d);
@@ -140,9 +127,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
                                                           const T* __restrict__ V, int64_t N,
                                                           const int32_t* __restrict__ q_perm,
                                                           const int32_t* __restrict__ q_off, int cq,
-                                                          const int32_t* __restrict__ k_perm,
                                                           const int32_t* __restrict__ tile_base,
-                                                          const int32_t* __restrict__ runs, int ck, float scale,
+                                                          const int32_t* __restrict__ gather,
+                                                          const int32_t* __restrict__ glen, float scale,
                                                           T* __restrict__ out, float* __restrict__ lse) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
@@ -151,8 +138,6 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint16_t ks[kBN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VSTR];
   __shared__ int32_t krow[kBN];
-  __shared__ int32_t run_v[kMaxClusters + 1];
-  __shared__ int32_t run_k[kMaxClusters];
 
   const int h = blockIdx.y;
   const int c = blockIdx.x;
@@ -166,14 +151,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
   const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
   const int qend = min(qbeg + kAttnBM, qo[i + 1]);
-  const int32_t* rec = runs + ((int64_t)h * cq + i) * (2 * ck + 3);
-  const int nr = rec[0];
-  for (int e = tid; e <= nr; e += 256) run_v[e] = rec[1 + e];
-  for (int e = tid; e < nr; e += 256) run_k[e] = rec[ck + 2 + e];
+  const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
+  const int L = glen[(int64_t)h * cq + i];
   const T* Qh = Q + (int64_t)h * N * D;
   const T* Kh = K + (int64_t)h * N * D;
   const T* Vh = V + (int64_t)h * N * D;
-  const int32_t* kp = k_perm + (int64_t)h * N;
 
   // B operand of S^T = K Q^T: query column l%32, dims kk*16 + hl*8 .. +7
   const int qpos = qbeg + w * 32 + l % 32;
@@ -194,8 +176,6 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   const float sl2 = scale * 1.4426950408889634f;
   float m_run = -INFINITY;  // running max of raw scores
   float l_run = 0.f;        // this lane's share of the running sum
-  __syncthreads();
-  const int L = run_v[nr];
   // A-operand row of S^T held by lane l: physical key of MFMA row l%32 (see below)
   const int r = l % 32;
   const int prow = ((r / 4) % 2) * 16 + (r / 8) * 4 + r % 4;
@@ -203,19 +183,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   for (int v0 = 0; v0 < L; v0 += kBN) {
     if (tid < kBN) {
       const int v = v0 + tid;
-      int row = -1;
-      if (v < L) {
-        int lo = 0, hi = nr;  // run_v[lo] <= v < run_v[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (run_v[mid] <= v)
-            lo = mid;
-          else
-            hi = mid;
-        }
-        row = kp[run_k[lo] + (v - run_v[lo])];
-      }
-      krow[tid] = row;
+      krow[tid] = v < L ? rows[v] : -1;
     }
     __syncthreads();
     // K tile, row-major
@@ -334,9 +302,38 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 #define PARK_LDS __attribute__((address_space(3)))
 
+// Chunk swizzle of LDS row r. Two read patterns must be bank-conflict free:
+//  - K (ds_read_b128): a 16-lane group reads one logical chunk of rows {0-3, 16-19, 4-7, 20-23}
+//    (or the same set + 8), so those 16 rows need distinct swizzles (and, for 8-lane phases,
+//    distinct low 3 bits within {0-3, 16-19} and within {4-7, 20-23});
+//  - V (ds_read_b64_tr_b16): a half-wave reads an aligned group of four chunks from four
+//    consecutive rows 4a..4a+3 (a quarter-wave: two chunks), so bits 2-3 (and bits 1-2) of the
+//    swizzle must differ across those four rows.
+// D = 128 (16 chunks per row): sw = 2 (g ^ 2g) ^ ((r >> 2) & 1) * 2 ^ ((r >> 4) & 1), g = r & 3,
+// i.e. {0, 6, 12, 10} by r & 3 with the bit-0/bit-1 flips separating the row quartets.
+// D = 64 (8 chunks, two rows per 256-byte bank sweep): rows of equal parity in a K group need
+// distinct swizzles, rows r and r + 2 of a V quartet need different bit 2.
 template <int CPR>
 __device__ __forceinline__ int chunk_swz(int r) {
-  return CPR == 16 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (r & 7);
+  if constexpr (CPR == 16) {
+    const int g = r & 3;
+    return (2 * (g ^ (g << 1))) ^ (((r >> 2) & 1) << 1) ^ ((r >> 4) & 1);
+  } else {
+    return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+  }
+}
+
+// Work-group -> tile mapping that keeps neighbouring tiles (the tiles of one query cluster read
+// the same key/value rows) on one XCD: work-groups are dealt to the 8 XCDs round-robin, so XCD x
+// receives ids x, x + 8, ...; those are given the x-th contiguous range of tiles.
+[[maybe_unused]] __device__ __forceinline__ void xcd_tile(int& h, int& c) {
+  const int nx = gridDim.x;
+  const int G = nx * gridDim.y;
+  const int b = blockIdx.x + blockIdx.y * nx;
+  const int x = b & 7, per = G >> 3, rem = G & 7;
+  const int L = x * per + min(x, rem) + (b >> 3);
+  h = L / nx;
+  c = L - h * nx;
 }
 
 // vmcnt(0): wait until this wave's vector-memory operations (including LDS-direct loads) are done
@@ -351,19 +348,21 @@ struct AttnTileLoader {
   static constexpr int LOADS = TILEB / 4096; // wave loads per wave per tile (4 waves)
 };
 
-constexpr int kAttnMaxRuns = 1024;  // runs kept in LDS by the direct-load kernel
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V, int64_t N,
                                                            const int32_t* __restrict__ q_perm,
                                                            const int32_t* __restrict__ q_off, int cq,
-                                                           const int32_t* __restrict__ k_perm,
                                                            const int32_t* __restrict__ tile_base,
-                                                           const int32_t* __restrict__ runs, int ck, float scale,
+                                                           const int32_t* __restrict__ gather,
+                                                           const int32_t* __restrict__ glen, float scale,
                                                            uint16_t* __restrict__ out, float* __restrict__ lse) {
+  // device-only body: the buffer-resource builtins have no host form, and the host pass needs only
+  // the signature for the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
   using TL = AttnTileLoader<D>;
+  constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw (untyped) access
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CPR = TL::CPR;
@@ -375,11 +374,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILEB];
-  __shared__ int32_t run_v[kAttnMaxRuns + 1];
-  __shared__ int32_t run_k[kAttnMaxRuns];
 
-  const int h = blockIdx.y;
-  const int c = blockIdx.x;
+  int h, c;
+  xcd_tile(h, c);
   const int32_t* tb = tile_base + (int64_t)h * (cq + 1);
   if (c >= tb[cq]) return;
   const int i = find_tile(tb, cq, c);
@@ -389,14 +386,14 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
   const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
   const int qend = min(qbeg + kAttnBM, qo[i + 1]);
-  const int32_t* rec = runs + ((int64_t)h * cq + i) * (2 * ck + 3);
-  const int nr = rec[0];
-  for (int e = threadIdx.x; e <= nr; e += 256) run_v[e] = rec[1 + e];
-  for (int e = threadIdx.x; e < nr; e += 256) run_k[e] = rec[ck + 2 + e];
+  const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
+  const int L = glen[(int64_t)h * cq + i];
   const uint16_t* Qh = Q + (int64_t)h * N * D;
-  const uint16_t* Kh = K + (int64_t)h * N * D;
-  const uint16_t* Vh = V + (int64_t)h * N * D;
-  const int32_t* kp = k_perm + (int64_t)h * N;
+  // per-head buffer resources: 32-bit row offsets, and reads past the head's rows return zero
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
 
   const int qpos = qbeg + w * 32 + l % 32;
   const bool qok = qpos < qend;
@@ -408,38 +405,31 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
     if (qok) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qrow * D + kk * 16 + hl * 8);
     qb[kk] = v;
   }
-  __syncthreads();
-  const int L = run_v[nr];
 
   // load slots: slot q of this lane copies tile row trow[q], logical chunk lchunk[q], into physical
   // chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
-  int trow[LOADS], cur[LOADS], lchunk[LOADS], nrow[LOADS];
+  int trow[LOADS], lbyte[LOADS], voff[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
     trow[q] = (w * LOADS + q) * RPB + l / CPR;
-    cur[q] = 0;
-    lchunk[q] = (l % CPR) ^ chunk_swz<CPR>(trow[q]);
+    lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
+    voff[q] = 0;
   }
-  // rows of the keys of tile starting at v0 (keys past the end read row 0: finite, masked)
+  // byte offsets of the rows of the tile starting at v0 (keys past the end read row 0: finite, masked)
   auto fetch_rows = [&](int v0) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       const int v = v0 + trow[q];
-      int pos = -1;
-      if (v < L) {
-        while (run_v[cur[q] + 1] <= v) ++cur[q];
-        pos = run_k[cur[q]] + (v - run_v[cur[q]]);
-      }
-      nrow[q] = pos >= 0 ? kp[pos] : 0;
+      const uint32_t row = v < L ? (uint32_t)rows[v] : 0u;
+      voff[q] = (int)(row * ROWB + lbyte[q]);
     }
   };
   auto issue = [&](uint8_t* kbuf, uint8_t* vbuf) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
-      const int64_t goff = (int64_t)nrow[q] * D + lchunk[q] * 8;
       const int boff = (w * LOADS + q) * 1024;
-      __builtin_amdgcn_global_load_lds(Kh + goff, (PARK_LDS void*)(kbuf + boff), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vh + goff, (PARK_LDS void*)(vbuf + boff), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(kbuf + boff), 16, voff[q], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(vbuf + boff), 16, voff[q], 0, 0, 0);
     }
   };
 
@@ -449,14 +439,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   const float sl2 = scale * 1.4426950408889634f;
-  // softmax reference: the running max is only raised when a score exceeds it by more than
-  // 8 / sl2 (p stays below 2^8), which skips almost every rescale of O
-  const float thresh = 8.0f / sl2;
+  // Softmax reference: m_ref is set from the first tile's scores and only raised when a tile's
+  // weights 2^(sl2 (s - m_ref)) would exceed 2^40 in one lane's sum; any reference works for the
+  // final O / l and the fp32 accumulators have range to spare, so almost no tile rescales O.
+  constexpr float kRaise = 1099511627776.0f;  // 2^40
   float m_ref = -INFINITY;
   float l_run = 0.f;
   const int r = l % 32;
   const int prow = ((r / 4) % 2) * 16 + (r / 8) * 4 + r % 4;
   const int g16 = l / 16, i16 = l % 16;
+  const bf16x2_t ones = as_bf16x2(0x3F803F80u);
 
   auto compute = [&](const uint8_t* kt, const uint8_t* vt, int v0) {
     f32x16_t sacc[2];
@@ -481,15 +473,40 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
         for (int e = 0; e < 16; ++e)
           if (st * 32 + hl * 16 + e >= nvalid) sacc[st][e] = -INFINITY;
     }
-    float mx = sacc[0][0];
+    auto tile_max = [&]() {
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const bool raise = mx > m_ref + thresh;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mx : m_ref;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
+      return fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    };
+    if (v0 == 0) m_ref = tile_max();
+    u32x4_t pb[2][2];
+    float ps;
+    auto weights = [&]() {
+      const float mb = m_ref * sl2;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float pv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][e], sl2, -mb));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t pk = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
+            pb[st][kh][q] = pk;
+            s4[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, s4[q], false);
+          }
+      }
+      ps = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    weights();
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
+      const float mx = tile_max();
+      const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
       l_run *= alpha;
 #pragma unroll
@@ -497,22 +514,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
       m_ref = m_new;
+      weights();
     }
-    const float mb = m_ref * sl2;
-    u32x4_t pb[2][2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      float pv[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][e], sl2, -mb));
-        l_run += pv[e];
-      }
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pb[st][kh][q] = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
-    }
+    l_run += ps;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int D0 = dt * 32 + 16 * (g16 & 1);
@@ -577,40 +581,38 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
     if (lse != nullptr && hl == 0)
       lse[(int64_t)h * N + qrow] = l_tot > 0.f ? m_ref * scale + logf(l_tot) : -INFINITY;
   }
+#endif
 }
 
 }  // namespace
 
 int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, kAttnBM) + cq; }
 
+size_t attn_gather_ints(const Dims& s, int cq) { return (size_t)(s.H * cq) * (size_t)(s.N + 1); }
+
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
                               const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
                               int ck, const int32_t* counts, const int32_t* cols, float scale, void* out, float* lse,
-                              int32_t* tile_base, int32_t* runs, hipStream_t st) {
+                              int32_t* tile_base, int32_t* gather, hipStream_t st) {
+  int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
   attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, tile_base);
-  attn_runs<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, cq, ck, runs);
+  attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, gather,
+                                                                glen);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
 #define PARK_ATTN(T, D)                                                                                          \
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
-                                                 static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, k_perm, \
-                                                 tile_base, runs, ck, scale, static_cast<T*>(out), lse);
-  if (s.bf16 && ck > kAttnMaxRuns) {
-    // more selectable clusters than the direct-load kernel keeps runs for: register-staged kernel
-    if (s.D == 128) {
-      PARK_ATTN(uint16_t, 128)
-    } else {
-      PARK_ATTN(uint16_t, 64)
-    }
-  } else if (s.bf16) {
+                                                 static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, tile_base, \
+                                                 gather, glen, scale, static_cast<T*>(out), lse);
+  if (s.bf16) {
     const uint16_t* qh = static_cast<const uint16_t*>(q);
     const uint16_t* kh = static_cast<const uint16_t*>(k);
     const uint16_t* vh = static_cast<const uint16_t*>(v);
     uint16_t* oh = static_cast<uint16_t*>(out);
     if (s.D == 128)
-      sparse_attn_bf16<128><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, k_perm, tile_base, runs, ck,
+      sparse_attn_bf16<128><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
                                                    scale, oh, lse);
     else
-      sparse_attn_bf16<64><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, k_perm, tile_base, runs, ck,
+      sparse_attn_bf16<64><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
                                                   scale, oh, lse);
   } else {
     if (s.D == 128) {

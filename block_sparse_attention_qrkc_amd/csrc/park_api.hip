@@ -132,12 +132,12 @@ MapWs plan_map(Carver& cv, const park::Dims& s, int cq, int ck) {
 
 struct AttnWs {
   int32_t* tile_base;
-  int32_t* runs;
+  int32_t* gather;
 };
 AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck) {
   AttnWs w;
   w.tile_base = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
-  w.runs = cv.take<int32_t>((size_t)(s.H * cq * (2 * ck + 3)));
+  w.gather = cv.take<int32_t>(park::attn_gather_ints(s, cq));
   return w;
 }
 
@@ -409,7 +409,7 @@ park_status park_sparse_attn(const park_shape* shape, const void* q, const void*
     Carver cv(ws);
     AttnWs w = plan_attn(cv, s, cq, ck);
     return hip_check(park::launch_sparse_attn(s, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts, cols,
-                                              resolve_scale(scale, s.D), out, lse, w.tile_base, w.runs,
+                                              resolve_scale(scale, s.D), out, lse, w.tile_base, w.gather,
                                               (hipStream_t)stream),
                      "park_sparse_attn");
   } catch (...) {
@@ -502,7 +502,7 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
       e = park::launch_select_topp(map, s.H, p.cq, p.ck, ko, p.p, o.mask, counts, cols, sk, st);
     if (e == hipSuccess)
       e = park::launch_sparse_attn(s, q, k, v, qp, qo, p.cq, kp, ko, p.ck, counts, cols, scale, out, o.lse,
-                                   w.aw.tile_base, w.aw.runs, st);
+                                   w.aw.tile_base, w.aw.gather, st);
     return hip_check(e, "park_forward");
   } catch (...) {
     return fail(PARK_EHIP, "park_forward: internal error");

@@ -8,6 +8,11 @@ import synth
 TAU = 1e-5  # near-tie threshold: decisions closer than this to their boundary are counted, not failed
 ATTN_MAX_ABS = 2e-2
 ATTN_MEAN_ABS = 2e-3
+# log-sum-exp: the attention weights are rounded to bf16 before they meet V on the MFMA, and the
+# normaliser is the sum of those same rounded weights, so l carries a relative error of up to
+# 2^-8 (bf16 unit roundoff, 8 significant bits) on top of fp32 rounding:
+# |d lse| <= log(1 + 2^-8) + fp32 terms < 4e-3
+LSE_ABS = 4e-3
 MAP_ABS = 1e-5
 
 

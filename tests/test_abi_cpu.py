@@ -43,6 +43,15 @@ def test_library_exports_every_declared_symbol(L):
     assert lib.park_version().decode().startswith("park-mi355x")
 
 
+def test_library_has_no_unresolved_symbols_of_its_own():
+    """Every kernel launch stub and helper is defined in the library (a kernel whose host pass was
+    dropped shows up as an undefined park:: symbol and the library would fail to load)."""
+    from block_sparse_attention_qrkc_amd import _lib
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert not [ln for ln in out.splitlines() if "park" in ln]
+    ctypes.CDLL(_lib.LIB_PATH)
+
+
 def test_status_strings(L):
     lib = L.lib()
     assert lib.park_status_string(0) == b"PARK_OK"
