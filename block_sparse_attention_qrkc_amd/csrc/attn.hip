@@ -408,28 +408,27 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
 
   // load slots: slot q of this lane copies tile row trow[q], logical chunk lchunk[q], into physical
   // chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
-  int trow[LOADS], lbyte[LOADS], voff[LOADS];
+  int trow[LOADS], lbyte[LOADS], nrow[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
     trow[q] = (w * LOADS + q) * RPB + l / CPR;
     lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
-    voff[q] = 0;
+    nrow[q] = 0;
   }
-  // byte offsets of the rows of the tile starting at v0 (keys past the end read row 0: finite, masked)
+  // rows of the tile starting at v0 (keys past the end read the last row: finite, masked). The index
+  // load is unconditional (clamped) and its value is only used in issue(), after the next wait for
+  // all copies, so nothing forces an early wait on it or on the tile copies issued before it.
   auto fetch_rows = [&](int v0) {
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-      const int v = v0 + trow[q];
-      const uint32_t row = v < L ? (uint32_t)rows[v] : 0u;
-      voff[q] = (int)(row * ROWB + lbyte[q]);
-    }
+    for (int q = 0; q < LOADS; ++q) nrow[q] = rows[min(v0 + trow[q], L - 1)];
   };
   auto issue = [&](uint8_t* kbuf, uint8_t* vbuf) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       const int boff = (w * LOADS + q) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(kbuf + boff), 16, voff[q], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(vbuf + boff), 16, voff[q], 0, 0, 0);
+      const int voff = (int)((uint32_t)nrow[q] * ROWB + lbyte[q]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(kbuf + boff), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(vbuf + boff), 16, voff, 0, 0, 0);
     }
   };
 
