@@ -53,7 +53,7 @@ def cpu_baseline(w, Q, K, V, seed):
     t0 = time.perf_counter()
     r = O.retrieve(q, k, w.cq, w.ck, w.iters, w.p, w.scale, seed=seed, head=0, bf16=(w.dtype == "bf16"))
     t_ret = time.perf_counter() - t0
-    na = 2
+    na = 12
     qp, qo = r["q"]["perm"], r["q"]["offsets"]
     rows = [i for i in range(w.cq) if qo[i + 1] > qo[i]][:na]
     t0 = time.perf_counter()

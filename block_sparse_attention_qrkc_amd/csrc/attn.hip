@@ -1,15 +1,16 @@
 // Block-sparse attention over the selected (query cluster, key cluster) pairs (PARK abstract:
 // attention is computed only within the retrieved blocks).
 //
-// Schedule: a work item is one 128-query tile of one query cluster. The original key rows of the
-// key clusters a query cluster selected are gathered once into one list (the cluster's virtual key
-// sequence), so key tiles of 64 are full MFMA tiles except the last one of each item, however small
-// the individual clusters are.
+// Schedule: a work item is one tile of 256 (bf16) or 128 (fp32) queries of one query cluster. The
+// original key rows of the key clusters a query cluster selected are gathered once into one list
+// (the cluster's virtual key sequence), so key tiles are full MFMA tiles except the last one of each
+// item, however small the individual clusters are.
 //
-// Kernel: four waves x 32 queries. Per 64-key tile, keys and values are copied into LDS through the
-// gather list, S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA with fp32 accumulation,
-// and an online softmax in exp2 form keeps one reference max and sum per query. Outputs are written
-// straight to the queries' original rows.
+// Per wave of 32 queries and key tile: S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA with
+// fp32 accumulation, and an online softmax in exp2 form keeps one reference max and sum per query.
+// Outputs are written straight to the queries' original rows.
+#include <type_traits>
+
 #include "park_common.h"
 #include "park_internal.h"
 
@@ -17,8 +18,8 @@ namespace park {
 
 namespace {
 
-// Per head: tile_base[i] = tiles of query clusters before i; tile_base[cq] = total.
-__global__ __launch_bounds__(1024) void attn_tiles(const int32_t* __restrict__ q_offsets, int cq,
+// Per head: tile_base[i] = bm-query tiles of query clusters before i; tile_base[cq] = total.
+__global__ __launch_bounds__(1024) void attn_tiles(const int32_t* __restrict__ q_offsets, int cq, int bm,
                                                    int32_t* __restrict__ tile_base) {
   __shared__ int scratch[17];
   const int h = blockIdx.x;
@@ -28,13 +29,13 @@ __global__ __launch_bounds__(1024) void attn_tiles(const int32_t* __restrict__ q
   const int i0 = threadIdx.x * per;
   int local = 0;
   for (int k = 0; k < per; ++k)
-    if (i0 + k < cq) local += (off[i0 + k + 1] - off[i0 + k] + kAttnBM - 1) / kAttnBM;
+    if (i0 + k < cq) local += (off[i0 + k + 1] - off[i0 + k] + bm - 1) / bm;
   int total;
   int run = block_exclusive_scan(local, scratch, &total);
   for (int k = 0; k < per; ++k) {
     if (i0 + k < cq) {
       tb[i0 + k] = run;
-      run += (off[i0 + k + 1] - off[i0 + k] + kAttnBM - 1) / kAttnBM;
+      run += (off[i0 + k + 1] - off[i0 + k] + bm - 1) / bm;
     }
   }
   if (threadIdx.x == 0) tb[cq] = total;
@@ -293,10 +294,10 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
 
 
 // ------------------------------------------------------------------------------------------------
-// bf16 kernel: key/value tiles are copied HBM -> LDS with gfx950 direct loads (no register staging),
-// double-buffered so the copy of tile t+1 overlaps the MFMA work on tile t. Rows stay row-major in
-// LDS with their 16-byte chunks XOR-swizzled by row (bank spread); V^T operands come from the
-// transposing LDS read (each lane of a 16-lane group receives 4 keys of one column).
+// bf16 kernel: key/value tiles are copied HBM -> LDS with gfx950 direct buffer loads (no register
+// staging) into a ring of stages, so copies run several tiles ahead of the MFMA work. Rows stay
+// row-major in LDS with their 16-byte chunks XOR-swizzled by row (bank spread); V^T operands come
+// from the transposing LDS read (each lane of a 16-lane group receives 4 keys of one column).
 // ------------------------------------------------------------------------------------------------
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -336,44 +337,62 @@ __device__ __forceinline__ int chunk_swz(int r) {
   c = L - h * nx;
 }
 
-// vmcnt(0): wait until this wave's vector-memory operations (including LDS-direct loads) are done
-#define PARK_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)
+// 256-query tiles: eight waves x 32 queries share one work-group per CU (two waves per SIMD), so
+// each key/value tile copied to LDS serves 256 queries. Tiles of 32 keys (d = 128; 64 for d = 64,
+// so each wave copies 1 KB of K and of V per tile) stream through a ring of four stages, copied
+// three tiles ahead; a wave waits only for the copies of the tile it is about to read (a counted
+// vmcnt, then a plain barrier: a fenced barrier would also wait for the copies still in flight).
+constexpr int kW8BM = 256;  // queries per work item
+[[maybe_unused]] constexpr int kW8BN = 32;   // keys per tile for d = 128
+[[maybe_unused]] constexpr int kW8NST = 4;   // LDS stages of one tile (K and V)
+
+// vmcnt(n) & lgkmcnt(0), then a plain workgroup barrier
+template <int VM>
+__device__ __forceinline__ void w8_wait_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (0x7 << 4) | ((VM >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// f(integral_constant<I>) for I = B .. E-1 in order while it returns true
+template <int B, int E, typename F>
+__device__ __forceinline__ bool w8_unroll(F&& f) {
+  if constexpr (B < E) {
+    if (!f(std::integral_constant<int, B>{})) return false;
+    return w8_unroll<B + 1, E>(f);
+  } else {
+    return true;
+  }
+}
 
 template <int D>
-struct AttnTileLoader {
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;         // bytes per row
-  static constexpr int TILEB = kBN * ROWB;   // bytes per K (or V) tile
-  static constexpr int RPB = 1024 / ROWB;    // rows per 1 KB wave load
-  static constexpr int LOADS = TILEB / 4096; // wave loads per wave per tile (4 waves)
-};
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __restrict__ Q,
-                                                           const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V, int64_t N,
-                                                           const int32_t* __restrict__ q_perm,
-                                                           const int32_t* __restrict__ q_off, int cq,
-                                                           const int32_t* __restrict__ tile_base,
-                                                           const int32_t* __restrict__ gather,
-                                                           const int32_t* __restrict__ glen, float scale,
-                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
-  // device-only body: the buffer-resource builtins have no host form, and the host pass needs only
-  // the signature for the launch stub
+__global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restrict__ Q,
+                                                         const uint16_t* __restrict__ K,
+                                                         const uint16_t* __restrict__ V, int64_t N,
+                                                         const int32_t* __restrict__ q_perm,
+                                                         const int32_t* __restrict__ q_off, int cq,
+                                                         const int32_t* __restrict__ tile_base,
+                                                         const int32_t* __restrict__ gather,
+                                                         const int32_t* __restrict__ glen, float scale,
+                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using TL = AttnTileLoader<D>;
+  constexpr int NW = 8;
+  constexpr int NST = kW8NST;
   constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw (untyped) access
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int CPR = TL::CPR;
-  constexpr int ROWB = TL::ROWB;
-  constexpr int TILEB = TL::TILEB;
-  constexpr int RPB = TL::RPB;
-  constexpr int LOADS = TL::LOADS;
-  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILEB];
+  constexpr int CPR = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int BN = D == 64 ? 64 : kW8BN;
+  constexpr int NSUB = BN / 32;                 // 32-key sub-tiles
+  constexpr int TILEB = BN * ROWB;              // one K (or V) tile
+  constexpr int STAGEB = 2 * TILEB;             // K then V
+  constexpr int RPB = 1024 / ROWB;              // rows per 1 KB wave load
+  constexpr int LOADS = TILEB / (1024 * NW);    // 1 KB loads per wave per tile, for K and for V
+  static_assert(LOADS >= 1, "tile smaller than one load per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[NST * STAGEB];
 
   int h, c;
   xcd_tile(h, c);
@@ -384,12 +403,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hl = l / 32;
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
-  const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
-  const int qend = min(qbeg + kAttnBM, qo[i + 1]);
+  const int qbeg = qo[i] + (c - tb[i]) * kW8BM;
+  const int qend = min(qbeg + kW8BM, qo[i + 1]);
+  const bool active = qbeg + w * 32 < qend;  // this wave has at least one query
   const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
   const int L = glen[(int64_t)h * cq + i];
   const uint16_t* Qh = Q + (int64_t)h * N * D;
-  // per-head buffer resources: 32-bit row offsets, and reads past the head's rows return zero
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv =
@@ -397,38 +416,41 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
 
   const int qpos = qbeg + w * 32 + l % 32;
   const bool qok = qpos < qend;
-  const int qrow = qok ? q_perm[(int64_t)h * N + qpos] : 0;
+  const int qrow = q_perm[(int64_t)h * N + min(qpos, qend - 1)];
   u32x4_t qb[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (qok) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qrow * D + kk * 16 + hl * 8);
-    qb[kk] = v;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qrow * D + kk * 16 + hl * 8);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    qb[kk] = qok ? v : z;
   }
 
-  // load slots: slot q of this lane copies tile row trow[q], logical chunk lchunk[q], into physical
-  // chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
-  int trow[LOADS], lbyte[LOADS], nrow[LOADS];
+  // load slots: slot q of this lane copies tile row trow[q], logical chunk (l % CPR) ^ swizzle, into
+  // physical chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
+  int trow[LOADS], lbyte[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
     trow[q] = (w * LOADS + q) * RPB + l / CPR;
     lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
-    nrow[q] = 0;
   }
-  // rows of the tile starting at v0 (keys past the end read the last row: finite, masked). The index
-  // load is unconditional (clamped) and its value is only used in issue(), after the next wait for
-  // all copies, so nothing forces an early wait on it or on the tile copies issued before it.
-  auto fetch_rows = [&](int v0) {
+  const int nt = (L + BN - 1) / BN;
+  int nrow[NST][LOADS];  // gather-list rows of tile x live in set x % NST from iteration x - 2 NST + 1 on
+  auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
+    // read through a pointer the compiler cannot see through, so the loads stay between the barriers
+    // of their iteration (the wait counts below count every vector-memory operation of one)
+    const int32_t* rp = rows;
+    asm volatile("" : "+s"(rp));
+    const __attribute__((address_space(1))) int32_t* gp = (const __attribute__((address_space(1))) int32_t*)rp;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) nrow[q] = rows[min(v0 + trow[q], L - 1)];
+    for (int q = 0; q < LOADS; ++q) nrow[set][q] = gp[min(tile * BN + trow[q], L - 1)];
   };
-  auto issue = [&](uint8_t* kbuf, uint8_t* vbuf) {
+  auto issue = [&](int set, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
-      const int boff = (w * LOADS + q) * 1024;
-      const int voff = (int)((uint32_t)nrow[q] * ROWB + lbyte[q]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(kbuf + boff), 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(vbuf + boff), 16, voff, 0, 0, 0);
+      const int boff = slot * STAGEB + (w * LOADS + q) * 1024;
+      const int voff = (int)((uint32_t)nrow[set][q] * ROWB + lbyte[q]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
     }
   };
 
@@ -449,45 +471,67 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
   const int g16 = l / 16, i16 = l % 16;
   const bf16x2_t ones = as_bf16x2(0x3F803F80u);
 
-  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int v0) {
-    f32x16_t sacc[2];
+  // per-lane byte offsets of the LDS operand reads within a K (V) tile, computed once
+  int kofs[NSUB][KS], vofs[DT][NSUB][2][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int R = st * 32 + prow;
-      const uint8_t* krow = kt + R * ROWB;
-      const int sw = chunk_swz<CPR>(R);
+  for (int st = 0; st < NSUB; ++st) {
+    const int R = st * 32 + prow;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kofs[st][kk] = R * ROWB + ((2 * kk + hl) ^ chunk_swz<CPR>(R)) * 16;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int D0 = dt * 32 + 16 * (g16 & 1);
+    const int cc = (D0 + 4 * (i16 % 4)) / 8;
+    const int half = (i16 % 4) & 1;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int R1 = st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4;
+        const int R2 = R1 + 4;
+        vofs[dt][st][kh][0] = R1 * ROWB + (cc ^ chunk_swz<CPR>(R1)) * 16 + half * 8;
+        vofs[dt][st][kh][1] = R2 * ROWB + (cc ^ chunk_swz<CPR>(R2)) * 16 + half * 8;
+      }
+  }
+
+  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int v0) __attribute__((always_inline)) {
+    f32x16_t sacc[NSUB];
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
+      // all K operands of the sub-tile are read before its MFMAs, so LDS latency is paid once
+      u32x4_t ka[KS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + ((2 * kk + hl) ^ sw) * 16);
-        sacc[st] = mfma32(a, qb[kk], sacc[st]);
-      }
+      for (int kk = 0; kk < KS; ++kk) ka[kk] = *reinterpret_cast<const u32x4_t*>(kt + kofs[st][kk]);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) sacc[st] = mfma32(ka[kk], qb[kk], sacc[st]);
     }
     const int nvalid = L - v0;
-    if (nvalid < kBN) {
+    if (nvalid < BN) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NSUB; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (st * 32 + hl * 16 + e >= nvalid) sacc[st][e] = -INFINITY;
     }
-    auto tile_max = [&]() {
+    auto tile_max = [&]() __attribute__((always_inline)) {
       float mx = sacc[0][0];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NSUB; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
       return fmaxf(mx, __shfl_xor(mx, 32, kWave));
     };
     if (v0 == 0) m_ref = tile_max();
-    u32x4_t pb[2][2];
+    u32x4_t pb[NSUB][2];
     float ps;
-    auto weights = [&]() {
+    auto weights = [&]() __attribute__((always_inline)) {
       const float mb = m_ref * sl2;
       float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NSUB; ++st) {
         float pv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][e], sl2, -mb));
@@ -516,54 +560,62 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16(const uint16_t* __res
       weights();
     }
     l_run += ps;
+    // V^T operands of all head-dim blocks are read before the PV MFMAs
+    u32x4_t va[DT][NSUB][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int D0 = dt * 32 + 16 * (g16 & 1);
-      const int cc = (D0 + 4 * (i16 % 4)) / 8;
-      const int half = (i16 % 4) & 1;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NSUB; ++st)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const int R1 = st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4;
-          const int R2 = R1 + 4;
-          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (PARK_LDS s16x4_t*)(vt + R1 * ROWB + (cc ^ chunk_swz<CPR>(R1)) * 16 + half * 8));
-          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (PARK_LDS s16x4_t*)(vt + R2 * ROWB + (cc ^ chunk_swz<CPR>(R2)) * 16 + half * 8));
+          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(vt + vofs[dt][st][kh][0]));
+          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(vt + vofs[dt][st][kh][1]));
           const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
           const u32x2_t a2 = __builtin_bit_cast(u32x2_t, t2);
-          const u32x4_t a = {a1[0], a1[1], a2[0], a2[1]};
-          o[dt] = mfma32(a, pb[st][kh], o[dt]);
+          va[dt][st][kh] = u32x4_t{a1[0], a1[1], a2[0], a2[1]};
         }
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) o[dt] = mfma32(va[dt][st][kh], pb[st][kh], o[dt]);
   };
 
-  // pipeline: rows of tile t+2 are fetched while tile t+1 is copied and tile t is computed
-  const int nt = (L + kBN - 1) / kBN;
   if (nt > 0) {
-    fetch_rows(0);
-    issue(kb0, vb0);
-    if (nt > 1) fetch_rows(kBN);
+    // prologue: tiles 0 .. NST-2 into stages 0 .. NST-2, rows of tiles NST-1 .. 2 NST-2 into their sets
+#pragma unroll
+    for (int x = 0; x < NST - 1; ++x) load_idx(x, x);
+#pragma unroll
+    for (int x = 0; x < NST - 1; ++x) issue(x, x);
+#pragma unroll
+    for (int x = NST - 1; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
   }
-  for (int t = 0; t < nt; t += 2) {
-    PARK_WAIT_VMEM();
-    __syncthreads();
-    if (t + 1 < nt) {
-      issue(kb1, vb1);
-      if (t + 2 < nt) fetch_rows((t + 2) * kBN);
-    }
-    compute(kb0, vb0, t * kBN);
-    if (t + 1 < nt) {
-      PARK_WAIT_VMEM();
-      __syncthreads();
-      if (t + 2 < nt) {
-        issue(kb0, vb0);
-        if (t + 3 < nt) fetch_rows((t + 3) * kBN);
-      }
-      compute(kb1, vb1, (t + 1) * kBN);
-    }
+  // iteration t (stage SL = t % NST): tile t landed, tile t + NST - 1 goes into the stage tile t - 1
+  // used, then tile t is computed. Tile t was copied in iteration t - NST + 1 (or the prologue); each
+  // of the NST - 2 iterations since issued 3 LOADS operations (copies and index loads stay within
+  // their iteration; the index loads of iteration t - NST + 1 may precede its copies, so they are not
+  // counted). In the prologue only the copies of later tiles are counted.
+  for (int t = 0; t < nt; t += NST) {
+    const bool go_on = w8_unroll<0, NST>([&](auto SLc) __attribute__((always_inline)) {
+      constexpr int SL = decltype(SLc)::value;
+      constexpr int XS = (SL + NST - 1) % NST;
+      const int tt = t + SL;
+      if (tt >= nt) return false;
+      if (tt < NST - 1)
+        w8_wait_barrier<(NST - 2) * 2 * LOADS>();
+      else
+        w8_wait_barrier<3 * LOADS * (NST - 2)>();
+      issue(XS, XS);
+      load_idx(XS, tt + 2 * NST - 1);
+      if (active) compute(stages + SL * STAGEB, stages + SL * STAGEB + TILEB, tt * BN);
+      return true;
+    });
+    if (!go_on) break;
   }
+  // drain the copies still in flight before the work-group's LDS can be handed to another
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (qok) {
@@ -594,7 +646,7 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
                               int ck, const int32_t* counts, const int32_t* cols, float scale, void* out, float* lse,
                               int32_t* tile_base, int32_t* gather, hipStream_t st) {
   int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
-  attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, tile_base);
+  attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, s.bf16 ? kW8BM : kAttnBM, tile_base);
   attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, gather,
                                                                 glen);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
@@ -608,11 +660,11 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
     const uint16_t* vh = static_cast<const uint16_t*>(v);
     uint16_t* oh = static_cast<uint16_t*>(out);
     if (s.D == 128)
-      sparse_attn_bf16<128><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
-                                                   scale, oh, lse);
+      sparse_attn_w8<128><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
+                                                 scale, oh, lse);
     else
-      sparse_attn_bf16<64><<<grid, 256, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
-                                                  scale, oh, lse);
+      sparse_attn_w8<64><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
+                                                scale, oh, lse);
   } else {
     if (s.D == 128) {
       PARK_ATTN(float, 128)
