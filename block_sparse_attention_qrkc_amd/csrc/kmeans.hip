@@ -681,59 +681,70 @@ __global__ __launch_bounds__(256) void centroid_mean(const T* __restrict__ X, in
   if (tid == 0) b_out[(int64_t)h * C + j] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
 }
 
-// QRKC consumed form for 32 centroids per block: y_j = M c_j (fp64 sums of fp64 products; M
-// staged in LDS as fp32 and read along columns, which M's symmetry makes equal to rows),
-// g_j = fp32(y_j) (then bf16), b_j = fp32(c_j . y_j). Thread = (output dim a, 16 centroids).
+// QRKC consumed form for 32 centroids per block: y_j = M c_j (fp64 sums of fp64 products of the
+// fp32 values; M staged in LDS as fp32 and read along columns, which M's symmetry makes equal to
+// rows), g_j = fp32(y_j) (then bf16), b_j = fp32(c_j . y_j). Register tiles: thread t computes
+// y_ja for the 4 centroids j = 4 (t / 32) + 0..3 and the D / 32 dims a = (t % 32) + 32 i, so per b
+// it reads D / 32 values of M and 4 of c (the latter shared by the 32 threads of a half-wave).
 template <int D>
 __global__ __launch_bounds__(256) void consume_qrkc(const float* __restrict__ cent, int C, const float* __restrict__ M,
                                                     void* g_out, float* __restrict__ b_out, int bf16) {
-  constexpr int JB = 32;                  // centroids per block
-  constexpr int JT = JB * D / 256;        // centroids per thread (16 for D = 128, 8 for D = 64)
+  constexpr int JB = 32;      // centroids per block
+  constexpr int AT = D / 32;  // dims per thread
   extern __shared__ float cq_lds[];
-  float* ms = cq_lds;                              // [D][D]
-  double* cs = reinterpret_cast<double*>(cq_lds + D * D);  // [JB][D]
-  __shared__ double bred[JB][256 / 64];
+  float* ms = cq_lds;           // [D][D]
+  float* cs = cq_lds + D * D;   // [JB][D]
   const int h = blockIdx.y;
   const int j0 = blockIdx.x * JB;
-  for (int e = threadIdx.x; e < D * D; e += 256) ms[e] = M[(int64_t)h * D * D + e];
-  for (int e = threadIdx.x; e < JB * D; e += 256) {
+  for (int e = threadIdx.x * 4; e < D * D; e += 256 * 4)
+    *reinterpret_cast<f32x4_t*>(ms + e) = *reinterpret_cast<const f32x4_t*>(M + (int64_t)h * D * D + e);
+  for (int e = threadIdx.x * 4; e < JB * D; e += 256 * 4) {
     const int jj = j0 + e / D;
-    cs[e] = jj < C ? (double)cent[((int64_t)h * C + jj) * D + e % D] : 0.0;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (jj < C) v = *reinterpret_cast<const f32x4_t*>(cent + ((int64_t)h * C + jj) * D + e % D);
+    *reinterpret_cast<f32x4_t*>(cs + e) = v;
   }
   __syncthreads();
-  const int a = threadIdx.x % D;
-  const int jg = threadIdx.x / D;  // which group of JT centroids
-  double acc[JT];
+  const int ai = threadIdx.x % 32;
+  const int jg = threadIdx.x / 32;  // centroids 4 jg .. 4 jg + 3
+  double acc[4][AT];
 #pragma unroll
-  for (int q = 0; q < JT; ++q) acc[q] = 0.0;
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < AT; ++i) acc[q][i] = 0.0;
   for (int b = 0; b < D; ++b) {
-    const double m = (double)ms[b * D + a];  // M[b][a] == M[a][b]
+    double m[AT], c[4];
 #pragma unroll
-    for (int q = 0; q < JT; ++q) acc[q] += m * cs[(jg * JT + q) * D + b];
+    for (int i = 0; i < AT; ++i) m[i] = (double)ms[b * D + ai + 32 * i];  // M[b][a] == M[a][b]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = (double)cs[(4 * jg + q) * D + b];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < AT; ++i) acc[q][i] = __builtin_fma(m[i], c[q], acc[q][i]);
   }
-  // g and the per-thread terms of b_j = sum_a c_ja y_ja
 #pragma unroll
-  for (int q = 0; q < JT; ++q) {
-    const int jl = jg * JT + q;
+  for (int q = 0; q < 4; ++q) {
+    const int jl = 4 * jg + q;
     const int j = j0 + jl;
-    double term = cs[jl * D + a] * acc[q];
-    if (j < C) {
-      const int64_t gi = ((int64_t)h * C + j) * D + a;
-      const float gv = (float)acc[q];
-      if (bf16)
-        static_cast<uint16_t*>(g_out)[gi] = (uint16_t)f32_to_bf16_bits(gv);
-      else
-        static_cast<float*>(g_out)[gi] = gv;
-    }
-    term = wave_sum_f64(term);
-    if (lane_id() == 0) bred[jl][(threadIdx.x % D) / 64] = term;
-  }
-  __syncthreads();
-  if (threadIdx.x < JB && j0 + threadIdx.x < C) {
-    double t = 0.0;
+    double term = 0.0;
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) t += bred[threadIdx.x][w];
-    b_out[(int64_t)h * C + j0 + threadIdx.x] = (float)t;
+    for (int i = 0; i < AT; ++i) {
+      const int a = ai + 32 * i;
+      term += (double)cs[jl * D + a] * acc[q][i];
+      if (j < C) {
+        const int64_t gi = ((int64_t)h * C + j) * D + a;
+        const float gv = (float)acc[q][i];
+        if (bf16)
+          static_cast<uint16_t*>(g_out)[gi] = (uint16_t)f32_to_bf16_bits(gv);
+        else
+          static_cast<float*>(g_out)[gi] = gv;
+      }
+    }
+    // the 32 threads of this half-wave hold the dims of centroid j
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) term += __shfl_xor(term, o, kWave);
+    if (ai == 0 && j < C) b_out[(int64_t)h * C + j] = (float)term;
   }
 }
 
@@ -930,8 +941,11 @@ __global__ __launch_bounds__(1024) void sort_scan(int32_t* __restrict__ table, i
   }
 }
 
-// One wave per chunk: tokens are placed in order, 64 at a time; lanes with equal labels are
-// ranked by lane index, which keeps the original order inside each cluster.
+// One wave per chunk: tokens are placed in order, 64 at a time. A lane's peers (lanes with the same
+// label) come from one ballot per label bit; its rank among them is the number of lower peer lanes,
+// which keeps the original order inside each cluster, and the lowest peer advances the cluster's
+// cursor. A single wave's LDS accesses complete in program order, so no barrier is needed between
+// reading and advancing the cursors.
 __global__ __launch_bounds__(64) void sort_scatter(const int32_t* __restrict__ labels, int64_t N, int C,
                                                    int nchunk, const int32_t* __restrict__ table,
                                                    int32_t* __restrict__ perm) {
@@ -945,24 +959,25 @@ __global__ __launch_bounds__(64) void sort_scatter(const int32_t* __restrict__ l
   const int32_t* lh = labels + (int64_t)h * N;
   int32_t* ph = perm + (int64_t)h * N;
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  constexpr int kLabelBits = 11;  // labels < kMaxClusters = 2^11
+  static_assert((1 << kLabelBits) >= kMaxClusters, "label bits");
   for (int r = 0; r < kSortChunk / 64; ++r) {
     const int64_t t = (int64_t)ch * kSortChunk + r * 64 + l;
     const bool valid = t < N;
-    const int lab = valid ? lh[t] : -1;
-    uint64_t active = __ballot(valid);
-    int pos = 0;
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int lead_lab = __shfl(lab, leader, kWave);
-      const uint64_t same = __ballot(lab == lead_lab) & active;
-      const int c0 = cursor[lead_lab];
-      if (lab == lead_lab && valid) pos = c0 + __popcll(same & lt_mask);
-      __syncthreads();  // every lane has read cursor before the leader advances it
-      if (l == leader) cursor[lead_lab] = c0 + __popcll(same);
-      __syncthreads();
-      active &= ~same;
+    const int lab = valid ? lh[t] : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int k = 0; k < kLabelBits; ++k) {
+      const bool bit = (lab >> k) & 1;
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
     }
-    if (valid) ph[pos] = (int32_t)t;
+    if (valid) {
+      const int c0 = cursor[lab];
+      const int pos = c0 + __popcll(peers & lt_mask);
+      ph[pos] = (int32_t)t;
+      if ((peers & lt_mask) == 0) cursor[lab] = c0 + __popcll(peers);
+    }
   }
 }
 
@@ -1142,7 +1157,7 @@ hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* per
   }
   if (!euclid) {
     const dim3 g2((unsigned)ceil_div(C, 32), (unsigned)s.H);
-    const size_t lds = (size_t)s.D * s.D * sizeof(float) + (size_t)32 * s.D * sizeof(double);
+    const size_t lds = (size_t)s.D * s.D * sizeof(float) + (size_t)32 * s.D * sizeof(float);
     if (s.D == 128)
       consume_qrkc<128><<<g2, 256, lds, st>>>(cent, C, metric, g, b, s.bf16);
     else
