@@ -310,7 +310,7 @@ struct CoopSide {
   const float* y;     // [H, S, D] or NULL (Euclidean)
   float* cent;        // [H, C, D]
   double* psum;       // [H, C, kCoopMaxParts, 2]: per part (D^2 sum, first untaken candidate)
-  int* sync;          // [H, C, 3]: arrivals, chosen candidate, chosen flag; then one failure flag
+  int* sync;          // [H, C, 3]: arrivals, (unused), chosen candidate + 1; then one failure flag
   int C, S, side, G, SP;
 };
 
@@ -328,6 +328,21 @@ __device__ __forceinline__ void spin_until(int* p, int want, int* fail) {
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Wait until *p != 0 and return it (same limits as spin_until).
+__device__ __forceinline__ int spin_nonzero(int* p, int* fail) {
+  long long n = 0;
+  int v;
+  while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+    if (__hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    if (++n >= kSpinLimit) {
+      __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return v;
 }
 
 template <int D>
@@ -416,63 +431,64 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
         wmin[w] = fu;
       }
       __syncthreads();
-      if (tid == 0) {
-        double pt = 0.0;
-        int pf = 0x7FFFFFFF;
-        for (int q = 0; q < kCoopWaves; ++q) {
-          pt += wred[q];
-          pf = wmin[q] < pf ? wmin[q] : pf;
+      if (w == 0) {
+        if (l == 0) {
+          double pt = 0.0;
+          int pf = 0x7FFFFFFF;
+          for (int q = 0; q < kCoopWaves; ++q) {
+            pt += wred[q];
+            pf = wmin[q] < pf ? wmin[q] : pf;
+          }
+          psum[((int64_t)m * kCoopMaxParts + part) * 2] = pt;
+          psum[((int64_t)m * kCoopMaxParts + part) * 2 + 1] = (double)pf;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __hip_atomic_fetch_add(&sync[m * 3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          spin_until(&sync[m * 3], G, fail);
         }
-        psum[((int64_t)m * kCoopMaxParts + part) * 2] = pt;
-        psum[((int64_t)m * kCoopMaxParts + part) * 2 + 1] = (double)pf;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(&sync[m * 3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        spin_until(&sync[m * 3], G, fail);
-        // every part reads the same G values in the same order
-        double total = 0.0;
-        for (int q = 0; q < G; ++q) total += __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2],
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // the G part sums are read at once (lane q: part q) and folded in the same order by every
+        // part (a lane scan)
+        const double pq = l < G ? __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + l) * 2], __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.0;
+        const int fq = l < G ? (int)__hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + l) * 2 + 1],
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0x7FFFFFFF;
+        double run = pq;  // inclusive prefix over parts
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const double u = __shfl_up(run, o, kWave);
+          if (l >= o) run += u;
+        }
+        const double total = __shfl(run, G - 1, kWave);
+        const double run_prev = __shfl_up(run, 1, kWave);
+        const double pre_q = l == 0 ? 0.0 : run_prev;  // exclusive prefix of part l
         int owner = -1;
-        double pre = 0.0;
         double v = 0.0;
         if (total > 0.0) {
           v = kpp_uniform(seed, h, sd.side, m) * total;
-          double run = 0.0;
-          for (int q = 0; q < G; ++q) {
-            const double pq = __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2], __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-            if (owner < 0 && run + pq > v) {
-              owner = q;
-              pre = run;
-            }
-            run += pq;
+          const uint64_t over = __ballot(l < G && run > v);
+          if (over) {
+            owner = __ffsll((unsigned long long)over) - 1;
+          } else {  // v rounded onto the total: the last part with mass
+            const uint64_t mass = __ballot(l < G && pq > 0.0);
+            owner = 63 - __clzll((unsigned long long)mass);
           }
-          if (owner < 0) {  // v rounded onto the total: the last part with mass
-            run = 0.0;
-            for (int q = 0; q < G; ++q) {
-              const double pq = __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2], __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-              if (pq > 0.0) {
-                owner = q;
-                pre = run;
-              }
-              run += pq;
-            }
-          }
-          pick_s = -1;
-        } else {
-          // every D^2 is zero: the lowest candidate not chosen yet, over all parts
-          int best = 0x7FFFFFFF;
-          for (int q = 0; q < G; ++q) {
-            const int fq = (int)__hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + q) * 2 + 1], __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-            best = fq < best ? fq : best;
-          }
-          pick_s = best < S ? best : 0;
         }
-        owner_s = owner;
-        pre_s = pre;
-        v_s = v;
+        int best = fq;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const int f2 = __shfl_xor(best, o, kWave);
+          best = f2 < best ? f2 : best;
+        }
+        const double pre = owner >= 0 ? __shfl(pre_q, owner, kWave) : 0.0;
+        if (l == 0) {
+          owner_s = owner;
+          pre_s = pre;
+          v_s = v;
+          // every D^2 is zero: the lowest candidate not chosen yet, over all parts
+          pick_s = owner < 0 ? (best < S ? best : 0) : -1;
+        }
       }
       __syncthreads();
       const int owner = owner_s;
@@ -523,14 +539,13 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
               lastbest = (int)wred[q] > lastbest ? (int)wred[q] : lastbest;
             }
             if (best == 0x7FFFFFFF) best = lastbest >= 0 ? lastbest : c0;
-            sync[m * 3 + 1] = best;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __hip_atomic_store(&sync[m * 3 + 2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the flag carries the pick (+1, so that 0 means not yet)
+            __hip_atomic_store(&sync[m * 3 + 2], best + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pick_s = best;
           }
         } else if (tid == 0) {
-          spin_until(&sync[m * 3 + 2], 1, fail);
-          pick_s = __hip_atomic_load(&sync[m * 3 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int f = spin_nonzero(&sync[m * 3 + 2], fail);
+          pick_s = f > 0 ? f - 1 : 0;  // 0 only after a failed wait (then the result is wrong anyway)
         }
         __syncthreads();
       }
