@@ -1,6 +1,8 @@
 """Benchmark of the PARK path on one MI355X: retrieval + block-sparse attention per layer.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan] [--no-cpu] [--no-stages]
+python bench.py --sweep        # p x Ck grid on the Wan-shaped layer (one JSON document)
+python bench.py --schedule     # the long clip's 10-step schedule: full K-means at anchors, warm starts
 
 A step is one park_forward call (QRKC metric, seeded K-means on queries and keys, PAMA map, top-p,
 block-sparse attention) over one synthetic layer already resident in HBM. Prints one JSON line.
@@ -49,11 +51,16 @@ def cpu_baseline(w, Q, K, V, seed):
     the sparse attention of the first `na` query clusters of head 0; scaled by heads and by
     query clusters respectively."""
     import oracle as O
-    q, k, v = (x[0].to(torch.float64).cpu().numpy() for x in (Q, K, V))
+    nh = min(4, w.heads)
     t0 = time.perf_counter()
-    r = O.retrieve(q, k, w.cq, w.ck, w.iters, w.p, w.scale, seed=seed, head=0, bf16=(w.dtype == "bf16"))
-    t_ret = time.perf_counter() - t0
-    na = 12
+    for hh in range(nh):
+        qh, kh = (x[hh].to(torch.float64).cpu().numpy() for x in (Q, K))
+        rh = O.retrieve(qh, kh, w.cq, w.ck, w.iters, w.p, w.scale, seed=seed, head=hh, bf16=(w.dtype == "bf16"))
+        if hh == 0:
+            r = rh
+    t_ret = (time.perf_counter() - t0) / nh
+    q, k, v = (x[0].to(torch.float64).cpu().numpy() for x in (Q, K, V))
+    na = 50
     qp, qo = r["q"]["perm"], r["q"]["offsets"]
     rows = [i for i in range(w.cq) if qo[i + 1] > qo[i]][:na]
     t0 = time.perf_counter()
@@ -66,8 +73,9 @@ def cpu_baseline(w, Q, K, V, seed):
     except AttributeError:
         cores = os.cpu_count()
     return {"value": ms, "unit": "ms/layer", "cores": cores, "kind": "oracle",
-            "sample": f"head 0 retrieval ({t_ret:.1f} s) x {w.heads} heads + sparse attention of {len(rows)} of "
-                      f"{n_live} query clusters of head 0 ({t_att:.1f} s) scaled to all clusters and heads"}
+            "sample": f"retrieval of heads 0-{nh - 1} ({t_ret:.1f} s per head) x {w.heads} heads + sparse attention "
+                      f"of {len(rows)} of {n_live} query clusters of head 0 ({t_att:.1f} s) scaled to all clusters "
+                      f"and heads"}
 
 
 def kernel_only(args, w, Q, K, V, step, bsa, ws, log):
@@ -95,15 +103,153 @@ def kernel_only(args, w, Q, K, V, step, bsa, ws, log):
     log(f"ran {args.kernel_only} x{args.steps} and a 1 GiB copy")
 
 
+PROFILE_PMC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sparse_attn_w8_wan_pmc.md")
+ATTN_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_qrkc_amd", "csrc",
+                        "attn.hip")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on the
+    attention source as it is now (else None)."""
+    import hashlib
+    import re
+    try:
+        txt = open(PROFILE_PMC).read()
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch = ([0-9.eE+]+) \(attn.hip sha256 prefix ([0-9a-f]+)\)", txt)
+    if m and m.group(2) == sha:
+        return float(m.group(1))
+    return None
+
+
+def ceilings(dev):
+    """Measured ceilings on this GPU: a large bf16 GEMM (vendor library) and a device copy."""
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    ms = time_call(lambda: torch.mm(a, b), 10, warmup=3)
+    gemm = 2 * 8192 ** 3 / (ms * 1e9)
+    del a, b
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = time_call(lambda: dst.copy_(src), 10, warmup=2)
+    copy = 2 * (1 << 31) / (ms * 1e6)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_tflops": round(gemm, 1), "copy_gbs": round(copy, 1)}
+
+
+def selection_stats(w, r):
+    """Token density, computed and padded FLOPs of one layer's selection."""
+    qsz = torch.diff(r["q_offsets"], dim=1).to(torch.float64)
+    ksel = r["sel_keys"].to(torch.float64)
+    computed = 4.0 * w.d * float((qsz * ksel).sum())
+    # the kernel runs whole 32-query blocks and whole 32-key tiles (64 for d = 64)
+    bn = 64 if w.d == 64 else 32
+    padded = 4.0 * w.d * float((torch.ceil(qsz / 32) * 32 * torch.ceil(ksel / bn) * bn).sum())
+    dense = 4.0 * w.d * w.n * w.n * w.heads
+    return computed, padded, dense
+
+
+def run_sweep(args, bsa, w0, dev, log):
+    """p x Ck grid on the Wan-shaped layer: density, recall, retrieval and attention ms."""
+    out = {"sweep": "p x ck on " + w0.name, "points": []}
+    Q, K, V = synth.make_qkv(w0, seed=args.seed, device=dev)
+    ws = bsa.Workspace()
+    for ck in synth.SWEEP_CK:
+        M = bsa.park_qrkc_metric(Q, ws=ws)
+        qc = bsa.park_cluster(Q, w0.cq, w0.iters, bsa.PARK_EUCLID, None, seed=args.seed, side=bsa.PARK_SIDE_Q, ws=ws)
+        kc = bsa.park_cluster(K, ck, w0.iters, bsa.PARK_QRKC, M, seed=args.seed, side=bsa.PARK_SIDE_K, ws=ws)
+        A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"], ws=ws)
+        t_ret = (time_call(lambda: bsa.park_cluster(K, ck, w0.iters, bsa.PARK_QRKC, M, seed=args.seed,
+                                                    side=bsa.PARK_SIDE_K, ws=ws), 1)
+                 + time_call(lambda: bsa.park_cluster(Q, w0.cq, w0.iters, bsa.PARK_EUCLID, None, seed=args.seed,
+                                                      side=bsa.PARK_SIDE_Q, ws=ws), 1)
+                 + time_call(lambda: bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"],
+                                                          kc["offsets"], out=A, ws=ws), 1))
+        args_attn = (Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"])
+        dsel = bsa.park_select_topp(A, kc["offsets"], 1.0)
+        _, lse_d = bsa.park_sparse_attn(*args_attn, dsel["counts"], dsel["cols"], ws=ws)
+        for p in synth.SWEEP_P:
+            sel = bsa.park_select_topp(A, kc["offsets"], p)
+            out_t = torch.empty_like(Q)
+            lse = torch.empty(w0.heads, w0.n, dtype=torch.float32, device=dev)
+            t_att = time_call(lambda: bsa.park_sparse_attn(*args_attn, sel["counts"], sel["cols"], out=out_t,
+                                                           lse=lse, ws=ws), 2)
+            rec = torch.exp(lse.double() - lse_d.double()).mean(dim=1).cpu().numpy()
+            r = {"q_offsets": qc["offsets"], "sel_keys": sel["sel_keys"]}
+            computed, padded, dense = selection_stats(w0, r)
+            pt = {"p": p, "ck": ck, "token_density": round(computed / dense, 5), "sparse_attn_ms": round(t_att, 3),
+                  "retrieval_ms": round(t_ret, 3), "computed_tflops": round(computed / (t_att * 1e9), 1),
+                  "padded_over_computed": round(padded / max(computed, 1.0), 4),
+                  "recall": {"mean": round(float(rec.mean()), 4), "worst": round(float(rec.min()), 4)}}
+            out["points"].append(pt)
+            log(f"sweep {pt}")
+    print(json.dumps(out), flush=True)
+
+
+def run_schedule(args, bsa, w, dev, log):
+    """The long clip's denoising schedule: inputs drift every step; full K-means (k-means++ and
+    ``iters`` iterations) at the anchor steps, warm start from the previous centroids with
+    ``warm_iters`` iterations otherwise."""
+    Q, K, V, Qm, Km = synth.make_qkv(w, seed=args.seed, device=dev, keep_fp32=True)
+    ws = bsa.Workspace()
+    qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
+    kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
+    steps = []
+    for t in range(w.steps):
+        if t > 0:
+            Q.copy_(synth.drift_step(w, Qm, args.seed, t, 0))
+            K.copy_(synth.drift_step(w, Km, args.seed, t, 1))
+        full = t in w.anchors
+        init = bsa.PARK_INIT_KMEANSPP if full else bsa.PARK_INIT_WARM
+        iters = w.iters if full else w.warm_iters
+        fn = lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, iters, w.p, seed=args.seed, init=init,
+                                      q_centroids=qcent, k_centroids=kcent, outputs=("q_offsets", "sel_keys"),
+                                      ws=ws)
+        if full:
+            r = fn()  # also the warm start of the next steps
+            torch.cuda.synchronize()
+            a, b = _events()
+            a.record()
+            r = bsa.park_forward(Q, K, V, w.cq, w.ck, iters, w.p, seed=args.seed, init=init, q_centroids=qcent,
+                                 k_centroids=kcent, outputs=("q_offsets", "sel_keys"), ws=ws)
+            b.record()
+        else:
+            qs, ks = qcent.clone(), kcent.clone()
+            r = fn()
+            torch.cuda.synchronize()
+            qcent.copy_(qs)
+            kcent.copy_(ks)
+            a, b = _events()
+            a.record()
+            r = fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        computed, padded, dense = selection_stats(w, r)
+        steps.append({"step": t, "full_kmeans": full, "iters": iters, "ms": round(ms, 3),
+                      "token_density": round(computed / dense, 5)})
+        log(f"schedule {steps[-1]}")
+    tot = sum(x["ms"] for x in steps)
+    print(json.dumps({"schedule": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "steps": steps,
+                      "total_ms": round(tot, 3), "ms_per_step": round(tot / len(steps), 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured GEMM / copy ceilings")
+    ap.add_argument("--sweep", action="store_true", help="p x Ck grid on the Wan-shaped layer (own JSON document)")
+    ap.add_argument("--schedule", action="store_true",
+                    help="the long clip's multi-step schedule with warm starts (own JSON document)")
     ap.add_argument("--kernel-only", choices=["sparse_attn", "assign", "pama"], default=None,
                     help="profiling aid: prepare one layer, then launch only this stage --steps times, followed "
                          "by a 1 GiB device copy (reference for byte counters); prints no JSON line")
@@ -120,6 +266,12 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    if args.sweep:
+        run_sweep(args, bsa, synth.WORKLOADS["wan"], dev, log)
+        return
+    if args.schedule:
+        run_schedule(args, bsa, synth.WORKLOADS["long"], dev, log)
+        return
     Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready: {w.name} H={w.heads} N={w.n} d={w.d}")
@@ -142,22 +294,23 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
     t0 = time.perf_counter()
+    evs = [_events() for _ in range(args.steps)]
     a, b = _events()
     a.record()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        evs[k][0].record()
         r = step()
+        evs[k][1].record()
     b.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_step = a.elapsed_time(b) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (median {per[len(per) // 2]:.3f}, min {per[0]:.3f})")
 
     # selection statistics of the last step
-    qsz = torch.diff(r["q_offsets"], dim=1).to(torch.float64)
-    ksel = r["sel_keys"].to(torch.float64)
     n = w.n
-    computed_flops = 4.0 * w.d * float((qsz * ksel).sum())
-    dense_flops = 4.0 * w.d * n * n * w.heads
+    computed_flops, padded_flops, dense_flops = selection_stats(w, r)
     density = computed_flops / dense_flops
 
     res = {"metric": METRIC, "value": round(ms_step, 3), "unit": "ms/layer", "n_gpus": 1, "steps": args.steps,
@@ -166,7 +319,10 @@ def main():
            "config": {"workload": w.name, "heads": w.heads, "n": n, "d": w.d, "cq": w.cq, "ck": w.ck,
                       "iters": w.iters, "p": w.p, "grid": list(w.grid)}}
     res["host_wall_ms_per_step"] = round(wall, 3)
+    res["step_ms_median"] = round(per[len(per) // 2], 3)
+    res["step_ms_min"] = round(per[0], 3)
     res["token_density"] = round(density, 5)
+    res["padded_over_computed_flops"] = round(padded_flops / computed_flops, 4)
 
     if not args.no_stages:
         M = r["metric"]
@@ -211,10 +367,16 @@ def main():
                          "worst": round(float(rec.min()), 4)}
         ach = flops_sel / (st["sparse_attn"] * 1e9)
         log(f"stages: {res['stages_ms']}")
-        res["roofline"] = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": round(ach, 2),
+        traffic = measured_traffic() if w.name == "wan" else None
+        res["roofline"] = {"kernel": "sparse_attn_w8", "bound": "mfma", "achieved": round(ach, 2),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                           "traffic": None,
-                           "work": f"4*d*sum_i n_q(i)*L(i) = {flops_sel / 1e12:.3f} TFLOP per launch"}
+                           "traffic": traffic,
+                           "work": f"4*d*sum_i n_q(i)*L(i) = {flops_sel / 1e12:.3f} TFLOP per launch",
+                           "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from "
+                                           "profiles/sparse_attn_w8_wan_pmc.md; null when the kernel source changed"}
+        if not args.no_ceilings:
+            res["ceilings"] = ceilings(dev)
+            res["roofline"]["frac_of_measured_gemm"] = round(ach / res["ceilings"]["gemm_bf16_tflops"], 4)
 
     if not args.no_cpu:
         log("cpu baseline (oracle sample)")
