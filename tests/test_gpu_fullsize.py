@@ -1,0 +1,257 @@
+"""The HIP path at the full layer sizes, in the launch configuration the benchmark times (one
+park_forward call per layer, workspace reused), checked against the fp64 oracle on sampled heads,
+query blocks and tokens, and through properties that hold at any size on every head.
+
+Workloads: the Wan-shaped layer (40 heads, N = 75,600, Cq = 100, Ck = 500), the HunyuanVideo-shaped
+layer (24 heads, N = 118,800, Cq = 128, Ck = 512) and the long clip (40 heads, N = 219,600,
+Cq = 200, Ck = 1000), all d = 128, bf16, 10 iterations, p = 0.9; plus one warm-started step of the
+long clip's drifting schedule."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_qrkc_amd as bsa
+import oracle as O
+import synth
+from gpu_helpers import (ATTN_MAX_ABS, ATTN_MEAN_ABS, LSE_ABS, MAP_ABS, TAU, check_topp_rows, cols_list, np_i,
+                         to64)
+
+pytestmark = pytest.mark.gpu
+
+ALL_OUT = ("metric", "q_labels", "q_perm", "q_offsets", "k_labels", "k_perm", "k_offsets", "map", "mask", "counts",
+           "cols", "sel_keys", "lse")
+SAMPLE_TOKENS = 16384  # tokens per sampled head for the assignment check
+SAMPLE_BLOCKS = 3      # query blocks per sampled head for the map and attention checks
+
+
+def _heads(w):
+    return sorted({0, w.heads // 2, w.heads - 1})
+
+
+@pytest.fixture(scope="module", params=["wan", "hunyuan", "long"])
+def full(request):
+    w = synth.WORKLOADS[request.param]
+    print(f"\n[full] {w.name}: H={w.heads} N={w.n} d={w.d} cq={w.cq} ck={w.ck} iters={w.iters} p={w.p}", flush=True)
+    Q, K, V = synth.make_qkv(w, seed=0, device="cuda")
+    ws = bsa.Workspace()
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=ALL_OUT, ws=ws)
+    torch.cuda.synchronize()
+    yield w, Q, K, V, r, ws
+    del Q, K, V, r, ws
+    torch.cuda.empty_cache()
+
+
+def _sample_blocks(off, rng):
+    live = np.flatnonzero(np.diff(off) > 0)
+    return sorted(rng.choice(live, size=min(SAMPLE_BLOCKS, live.size), replace=False).tolist())
+
+
+def test_full_metric(full):
+    w, Q, K, V, r, ws = full
+    Mg = to64(r["metric"])
+    for h in _heads(w):
+        Mo = O.qrkc_metric(to64(Q[h]))
+        rel = np.abs(Mg[h] - Mo).max() / np.abs(Mo).max()
+        assert rel <= 2e-6, (h, rel)
+    assert np.array_equal(Mg, Mg.transpose(0, 2, 1))
+
+
+def test_full_cluster_order_and_means(full):
+    """Every head: perm / offsets are the stable counting sort of the returned labels (bit-exact),
+    and every non-empty centroid is the member mean of the returned labels (the labels come from
+    the last assignment and the centroids from the update that follows it)."""
+    w, Q, K, V, r, ws = full
+    for side, X, C in (("q", Q, w.cq), ("k", K, w.ck)):
+        lab, perm, off = np_i(r[f"{side}_labels"]), np_i(r[f"{side}_perm"]), np_i(r[f"{side}_offsets"])
+        cent = to64(r[f"{side}_centroids"])
+        assert lab.min() >= 0 and lab.max() < C
+        for h in range(w.heads):
+            po, oo = O.cluster_order(lab[h], C)
+            np.testing.assert_array_equal(perm[h], po)
+            np.testing.assert_array_equal(off[h], oo)
+        for h in _heads(w):
+            x = to64(X[h])
+            co = O.update(x, lab[h], C, cent[h])
+            err = np.abs(cent[h] - co).max()
+            assert err <= 1e-6 * np.abs(x).max(), (side, h, err)
+
+
+@pytest.mark.parametrize("side", ["q", "k"])
+def test_full_seeding(full, side):
+    w, Q, K, V, r, ws = full
+    X = Q if side == "q" else K
+    C = w.cq if side == "q" else w.ck
+    metric = bsa.PARK_EUCLID if side == "q" else bsa.PARK_QRKC
+    sd = bsa.PARK_SIDE_Q if side == "q" else bsa.PARK_SIDE_K
+    M = r["metric"] if side == "k" else None
+    cg = to64(bsa.park_cluster(X, C, 0, metric, M, seed=0, side=sd, ws=ws)["centroids"])
+    near = 0
+    for h in _heads(w):
+        Mh = to64(M[h]) if side == "k" else None
+        co, chosen, margins = O.kmeanspp(to64(X[h]), C, Mh, seed=0, head=h, side=sd, return_trace=True)
+        diff = np.flatnonzero(np.any(cg[h] != co, axis=1))
+        if diff.size:
+            m = diff[0]
+            assert margins[m] <= TAU, f"head {h}: seeding differs at step {m} (margin {margins[m]:.3g})"
+            near += 1
+    print(f"[full seeding {side}] near-ties: {near}")
+
+
+@pytest.mark.parametrize("side", ["q", "k"])
+def test_full_lloyd_step(full, side):
+    """One more iteration warm-started from the layer's final centroids: sampled labels against the
+    fp64 argmin over the consumed centroids (near-ties counted), the order bit-exact on every head,
+    the new centroids against the fp64 member means on sampled heads."""
+    w, Q, K, V, r, ws = full
+    X = Q if side == "q" else K
+    C = w.cq if side == "q" else w.ck
+    metric = bsa.PARK_EUCLID if side == "q" else bsa.PARK_QRKC
+    sd = bsa.PARK_SIDE_Q if side == "q" else bsa.PARK_SIDE_K
+    M = r["metric"] if side == "k" else None
+    prev = r[f"{side}_centroids"].clone()
+    res = bsa.park_cluster(X, C, 1, metric, M, init=bsa.PARK_INIT_WARM, side=sd, centroids=prev.clone(), ws=ws)
+    lab, perm, off, new = np_i(res["labels"]), np_i(res["perm"]), np_i(res["offsets"]), to64(res["centroids"])
+    prev = to64(prev)
+    rng = np.random.default_rng(7)
+    near = 0
+    for h in range(w.heads):
+        po, oo = O.cluster_order(lab[h], C)
+        np.testing.assert_array_equal(perm[h], po)
+        np.testing.assert_array_equal(off[h], oo)
+    for h in _heads(w):
+        x = to64(X[h])
+        Mh = to64(M[h]) if side == "k" else None
+        g, b = O.consumed_centroids(prev[h], metric, Mh, bf16=True)
+        t = rng.choice(w.n, size=SAMPLE_TOKENS, replace=False)
+        n_near, bad = O.assign_near_tie(x[t], g, b, lab[h][t], TAU)
+        assert bad.size == 0, f"head {h}: {bad.size} sampled labels differ beyond near-ties"
+        near += n_near
+        co = O.update(x, lab[h], C, prev[h])
+        assert np.abs(new[h] - co).max() <= 1e-6 * np.abs(x).max()
+    print(f"[full lloyd {side}] near-ties among sampled tokens: {near}")
+
+
+def test_full_map(full):
+    w, Q, K, V, r, ws = full
+    A = to64(r["map"])
+    qo_all, ko_all = np_i(r["q_offsets"]), np_i(r["k_offsets"])
+    for h in range(w.heads):  # P1 on every head: live rows sum to 1, the rest is zero
+        live = np.diff(qo_all[h]) > 0
+        assert np.abs(A[h][live].sum(1) - 1).max() <= MAP_ABS
+        assert np.all(A[h][~live] == 0)
+        assert np.all(A[h][:, np.diff(ko_all[h]) == 0] == 0)
+    rng = np.random.default_rng(11)
+    for h in _heads(w):
+        qo, ko = qo_all[h], ko_all[h]
+        rows = _sample_blocks(qo, rng)
+        khat = O.round_bf16(to64(r["k_centroids"][h]))
+        Ao = O.pama(to64(Q[h]), np_i(r["q_perm"][h]), qo, khat, np.diff(ko), w.scale, rows=rows)
+        err = np.abs(A[h][rows] - Ao[rows]).max()
+        assert err <= MAP_ABS, (h, rows, err)
+
+
+def test_full_select(full):
+    w, Q, K, V, r, ws = full
+    A = to64(r["map"])
+    counts, cols, keys, mask = np_i(r["counts"]), np_i(r["cols"]), np_i(r["sel_keys"]), np_i(r["mask"])
+    near = 0
+    for h in range(w.heads):
+        sizes = np.diff(np_i(r["k_offsets"][h]))
+        n_near, bad = check_topp_rows(A[h], sizes, w.p, counts[h], cols[h], keys[h])
+        assert not bad, f"head {h} rows {bad}"
+        near += n_near
+        for i in range(w.cq):
+            c = cols[h, i, :counts[h, i]]
+            assert np.array_equal(np.flatnonzero(mask[h, i]), c)
+    print(f"[full top-p] near-ties: {near}")
+
+
+def test_full_attention_sampled(full):
+    """Sampled query blocks of sampled heads against the fp64 masked softmax over the selected keys;
+    recall from the kernel's log-sum-exp against the brute-force dense softmax share."""
+    w, Q, K, V, r, ws = full
+    rng = np.random.default_rng(13)
+    worst, tot, n, rec_err = 0.0, 0.0, 0, 0.0
+    for h in _heads(w):
+        qp, qo = np_i(r["q_perm"][h]), np_i(r["q_offsets"][h])
+        kp, ko = np_i(r["k_perm"][h]), np_i(r["k_offsets"][h])
+        rows = _sample_blocks(qo, rng)
+        q, k, v = to64(Q[h]), to64(K[h]), to64(V[h])
+        Oo, Lo = O.sparse_attention(q, k, v, qp, qo, kp, ko, cols_list(np_i(r["counts"][h]), np_i(r["cols"][h])),
+                                    w.scale, rows=rows)
+        t = np.concatenate([qp[qo[i]:qo[i + 1]] for i in rows])
+        Og, Lg = to64(r["out"][h])[t], to64(r["lse"][h])[t]
+        e = np.abs(Og - Oo[t])
+        worst = max(worst, e.max())
+        tot += e.sum()
+        n += e.size
+        assert np.abs(Lg - Lo[t]).max() <= LSE_ABS
+        # recall of 256 of these tokens: kernel LSE vs the oracle's selected / dense log-mass
+        tt = rng.choice(t, size=min(256, t.size), replace=False)
+        _, Ld = O.dense_attention(q, k, v, w.scale, rows=tt)
+        rg = O.recall(to64(r["lse"][h])[tt], Ld[tt])
+        ro = O.recall(Lo[tt], Ld[tt])
+        # |exp(a) - exp(b)| <= exp(b) * expm1(|a - b|) with exp(b) <= 1: the LSE bound carries over
+        assert np.all(rg <= 1 + np.expm1(LSE_ABS)) and np.abs(rg - ro).max() <= np.expm1(LSE_ABS)
+        rec_err = max(rec_err, np.abs(rg - ro).mean())
+    assert worst <= ATTN_MAX_ABS, worst
+    assert tot / n <= ATTN_MEAN_ABS, tot / n
+    assert rec_err <= 1e-3, rec_err
+    print(f"[full attention] max-abs {worst:.2e} mean-abs {tot / n:.2e}; recall mean-abs error {rec_err:.2e}")
+
+
+def test_full_output_everywhere(full):
+    """Every token of every head gets a finite output (every live query block selects at least one
+    non-empty key block at p < 1), and a second call is bitwise identical."""
+    w, Q, K, V, r, ws = full
+    assert torch.isfinite(r["out"].float()).all()
+    assert torch.isfinite(r["lse"]).all()
+    live = np.diff(np_i(r["q_offsets"]), axis=1) > 0
+    assert np.all(np_i(r["counts"])[live] > 0)
+    r2 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=("map", "lse"), ws=ws)
+    assert torch.equal(r2["out"], r["out"]) and torch.equal(r2["map"], r["map"]) and torch.equal(r2["lse"], r["lse"])
+
+
+def test_long_warm_step():
+    """One drifted step of the long clip's schedule: warm start from the previous step's centroids,
+    two iterations; the first of them checked in lock-step against the oracle on a sampled head."""
+    w = synth.WORKLOADS["long"]
+    print(f"\n[full] long warm step: H={w.heads} N={w.n}", flush=True)
+    Q, K, V, Qm, Km = synth.make_qkv(w, seed=0, device="cuda", keep_fp32=True)
+    ws = bsa.Workspace()
+    r0 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, ws=ws)
+    qc, kc = r0["q_centroids"], r0["k_centroids"]
+    Q = synth.drift_step(w, Qm, 0, 1, 0)
+    K = synth.drift_step(w, Km, 0, 1, 1)
+    del Qm, Km
+    q_prev, k_prev = qc.clone(), kc.clone()
+    r1 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.warm_iters, w.p, seed=0, init=bsa.PARK_INIT_WARM,
+                          q_centroids=qc, k_centroids=kc, outputs=ALL_OUT, ws=ws)
+    # the same two iterations through the clustering entry point, starting from the saved centroids
+    one = bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, r1["metric"], init=bsa.PARK_INIT_WARM, side=bsa.PARK_SIDE_K,
+                           centroids=k_prev.clone(), ws=ws)
+    two = bsa.park_cluster(K, w.ck, w.warm_iters, bsa.PARK_QRKC, r1["metric"], init=bsa.PARK_INIT_WARM,
+                           side=bsa.PARK_SIDE_K, centroids=k_prev.clone(), ws=ws)
+    assert torch.equal(two["centroids"], r1["k_centroids"]) and torch.equal(two["perm"], r1["k_perm"])
+    h = w.heads - 1
+    x = to64(K[h])
+    g, b = O.consumed_centroids(to64(k_prev[h]), O.QRKC, to64(r1["metric"][h]), bf16=True)
+    t = np.random.default_rng(5).choice(w.n, size=SAMPLE_TOKENS, replace=False)
+    n_near, bad = O.assign_near_tie(x[t], g, b, np_i(one["labels"][h])[t], TAU)
+    assert bad.size == 0
+    co = O.update(x, np_i(one["labels"][h]), w.ck, to64(k_prev[h]))
+    assert np.abs(to64(one["centroids"][h]) - co).max() <= 1e-6 * np.abs(x).max()
+    # the warm step's selection and attention on a sampled block
+    A = to64(r1["map"][h])
+    sizes = np.diff(np_i(r1["k_offsets"][h]))
+    _, bad = check_topp_rows(A, sizes, w.p, np_i(r1["counts"][h]), np_i(r1["cols"][h]), np_i(r1["sel_keys"][h]))
+    assert not bad
+    qp, qo = np_i(r1["q_perm"][h]), np_i(r1["q_offsets"][h])
+    rows = _sample_blocks(qo, np.random.default_rng(3))[:1]
+    Oo, Lo = O.sparse_attention(to64(Q[h]), x, to64(V[h]), qp, qo, np_i(r1["k_perm"][h]), np_i(r1["k_offsets"][h]),
+                                cols_list(np_i(r1["counts"][h]), np_i(r1["cols"][h])), w.scale, rows=rows)
+    tt = qp[qo[rows[0]]:qo[rows[0] + 1]]
+    e = np.abs(to64(r1["out"][h])[tt] - Oo[tt])
+    assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS
+    assert np.abs(to64(r1["lse"][h])[tt] - Lo[tt]).max() <= LSE_ABS
+    print(f"[long warm step] sampled near-ties {n_near}")
