@@ -2,10 +2,13 @@
 // under the query-derived metric M):
 //   * k-means++ seeding (Arthur & Vassilvitskii 2007) over strided candidate rows, in fp64, with
 //     draws from a SplitMix64 counter stream (Steele, Lea & Flood 2014);
-//   * assignment: label = argmin_j b_j - 2 x.g_j on bf16 MFMA (fp32 accumulation), lowest j on ties;
+//   * assignment: label = argmin_j b_j - 2 x.g_j on bf16 MFMA (fp32 accumulation), lowest j on ties
+//     (bf16 data: scores compared in their top 20 bits, see asg_key);
 //   * stable counting sort of the labels into cluster-contiguous order;
 //   * update: fixed-order fp64 member means stored as fp32, followed by the consumed form (g, b)
 //     of every centroid for the next assignment.
+#include <cfloat>
+
 #include "park_common.h"
 #include "park_internal.h"
 
@@ -35,49 +38,126 @@ __device__ __forceinline__ int64_t cand_row(int i, int S, int64_t N) {
   return (int64_t)(((double)i * (double)N) / (double)S);
 }
 
-// Per candidate i: xx_i = |x_i|^2 (Euclidean) or x_i^T M x_i (QRKC); for QRKC also y_i = M x_i,
-// the vector later steps dot the candidates against. Block = 64 candidates, 4 threads each (a
-// quarter of the outputs per thread); M and the rows are staged in LDS; fp32 products, fp64 sums
-// of the quarters.
+// Euclidean candidate norms xx_i = |x_i|^2 (fp64 sums of fp64 squares): block = 64 candidates,
+// 4 threads each (a quarter of the dims per thread); rows staged in LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void kpp_prep(const T* __restrict__ X, int64_t N, int S, const float* __restrict__ M,
-                                                double* __restrict__ xx, float* __restrict__ y) {
-  constexpr int XS = D + 1;       // padded row stride (floats)
-  extern __shared__ float kpp_lds[];
-  float* xs = kpp_lds;            // [64][XS]
-  float* ms = kpp_lds + 64 * XS;  // [D][D] (QRKC only)
+__global__ __launch_bounds__(256) void kpp_prep(const T* __restrict__ X, int64_t N, int S, double* __restrict__ xx) {
+  constexpr int XS = D + 1;  // padded row stride (floats)
+  __shared__ float xs[64 * XS];
   __shared__ double part_s[4][64];
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * D; e += 256) {
-    const int ci = i0 + e / D;
-    xs[(e / D) * XS + e % D] = ci < S ? load_f32(X + ((int64_t)h * N + cand_row(ci, S, N)) * D, e % D) : 0.f;
+  // rows staged 8 elements per load, all loads of a thread in flight together
+#pragma unroll
+  for (int k = 0; k < 64 * D / 8 / 256; ++k) {
+    const int e = threadIdx.x + k * 256;
+    const int r = e / (D / 8), a0 = (e % (D / 8)) * 8;
+    float v[8];
+    load8_f32(X + ((int64_t)h * N + cand_row(min(i0 + r, S - 1), S, N)) * D + a0, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xs[r * XS + a0 + q] = i0 + r < S ? v[q] : 0.f;
   }
-  if (M != nullptr)
-    for (int e = threadIdx.x; e < D * D; e += 256) ms[e] = M[(int64_t)h * D * D + e];
   __syncthreads();
-  const int c = threadIdx.x % 64;  // candidate within the block
-  const int q4 = threadIdx.x / 64;  // quarter of the outputs (uniform per wave)
+  const int c = threadIdx.x % 64;   // candidate within the block
+  const int q4 = threadIdx.x / 64;  // quarter of the dims (uniform per wave)
   constexpr int AQ = D / 4;
   const float* x = xs + c * XS;
   double acc = 0.0;
-  if (M == nullptr) {
-    for (int a = q4 * AQ; a < q4 * AQ + AQ; ++a) acc += (double)x[a] * (double)x[a];
-  } else {
-    for (int a = q4 * AQ; a < q4 * AQ + AQ; ++a) {
-      const float* mr = ms + a * D;  // wave-uniform row: broadcast reads
-      float ya = 0.f;
-#pragma unroll 16
-      for (int b = 0; b < D; ++b) ya = __builtin_fmaf(mr[b], x[b], ya);
-      acc += (double)x[a] * (double)ya;
-      if (i0 + c < S) y[((int64_t)h * S + i0 + c) * D + a] = ya;
-    }
-  }
+  for (int a = q4 * AQ; a < q4 * AQ + AQ; ++a) acc += (double)x[a] * (double)x[a];
   part_s[q4][c] = acc;
   __syncthreads();
   if (threadIdx.x < 64 && i0 + threadIdx.x < S)
     xx[(int64_t)h * S + i0 + threadIdx.x] =
         ((part_s[0][threadIdx.x] + part_s[1][threadIdx.x]) + part_s[2][threadIdx.x]) + part_s[3][threadIdx.x];
+}
+
+// QRKC candidate products with register tiles (y = M x and xx = x . y for 64 candidates per block):
+// thread t computes the D / 16 outputs a = (D / 16) (t % 16) + {0 .. D / 16 - 1} of the four
+// candidates 4 (t / 16) + {0..3}, accumulating over b = 0 .. D - 1 in order (fp32 FMA
+// chains), reading 3 LDS vectors per 4 * D / 16 FMAs. xx: fp64 sums of fp64 products over the
+// thread's outputs, then over the 16 output groups.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kpp_prep_tiled(const T* __restrict__ X, int64_t N, int S,
+                                                      const float* __restrict__ M, double* __restrict__ xx,
+                                                      float* __restrict__ y) {
+  constexpr int OA = D / 16;  // outputs per thread
+  extern __shared__ float kpt_lds[];
+  float* ms = kpt_lds;          // [D][D]
+  constexpr int XT = 68;         // padded stride of xs (16-byte aligned rows, fewer bank conflicts)
+  float* xs = kpt_lds + D * D;  // [D][XT]: xs[b * XT + c] = x_c[b]
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * 64;
+  // all staging loads of a thread are issued before their LDS stores
+  float v[64 * D / 8 / 256][8];
+#pragma unroll
+  for (int k = 0; k < 64 * D / 8 / 256; ++k) {
+    const int e = threadIdx.x + k * 256;
+    load8_f32(X + ((int64_t)h * N + cand_row(min(i0 + e / (D / 8), S - 1), S, N)) * D + (e % (D / 8)) * 8, v[k]);
+  }
+  f32x4_t mv4[D * D / 4 / 256];
+#pragma unroll
+  for (int k = 0; k < D * D / 4 / 256; ++k)
+    mv4[k] = *reinterpret_cast<const f32x4_t*>(M + (int64_t)h * D * D + (threadIdx.x + k * 256) * 4);
+#pragma unroll
+  for (int k = 0; k < 64 * D / 8 / 256; ++k) {
+    const int e = threadIdx.x + k * 256;
+    const int c = e / (D / 8), b0 = (e % (D / 8)) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xs[(b0 + q) * XT + c] = i0 + c < S ? v[k][q] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < D * D / 4 / 256; ++k) *reinterpret_cast<f32x4_t*>(ms + (threadIdx.x + k * 256) * 4) = mv4[k];
+  __syncthreads();
+  const int og = threadIdx.x % 16;  // output group
+  const int cg = threadIdx.x / 16;  // candidate group
+  float acc[4][OA];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int o = 0; o < OA; ++o) acc[q][o] = 0.f;
+  for (int b = 0; b < D; ++b) {
+    const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xs + b * XT + cg * 4);
+    float mv[OA];  // M[b][a] == M[a][b]
+#pragma unroll
+    for (int o = 0; o < OA; o += 4) {
+      const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(ms + b * D + og * OA + o);
+      mv[o] = m4[0];
+      mv[o + 1] = m4[1];
+      mv[o + 2] = m4[2];
+      mv[o + 3] = m4[3];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int o = 0; o < OA; ++o) acc[q][o] = __builtin_fmaf(mv[o], xv[q], acc[q][o]);
+  }
+  double part[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = cg * 4 + q;
+    double sacc = 0.0;
+#pragma unroll
+    for (int o = 0; o < OA; ++o) sacc += (double)xs[(og * OA + o) * XT + c] * (double)acc[q][o];
+    part[q] = sacc;
+    if (i0 + c < S) {
+      float* yr = y + ((int64_t)h * S + i0 + c) * D + og * OA;
+#pragma unroll
+      for (int o = 0; o < OA; o += 4) {
+        const f32x4_t v = {acc[q][o], acc[q][o + 1], acc[q][o + 2], acc[q][o + 3]};
+        *reinterpret_cast<f32x4_t*>(yr + o) = v;
+      }
+    }
+  }
+  // sum over the 16 output groups (16 consecutive lanes)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) part[q] += __shfl_xor(part[q], o, kWave);
+  if (og == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i0 + cg * 4 + q < S) xx[(int64_t)h * S + i0 + cg * 4 + q] = part[q];
+  }
 }
 
 struct KppSide {
@@ -658,11 +738,21 @@ __global__ __launch_bounds__(256) void centroid_mean(const T* __restrict__ X, in
       double acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-      for (int r = beg + rg; r < end; r += RG) {
-        float xv[8];
-        load8_f32(Xh + (int64_t)ph[r] * D + pc * 8, xv);
+      // rows beg + rg + RG k in increasing k; U member indices, then U rows, in flight at a time
+      constexpr int U = 8;
+      for (int r0 = beg + rg; r0 < end; r0 += U * RG) {
+        int idx[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (double)xv[e];
+        for (int u = 0; u < U; ++u) idx[u] = ph[min(r0 + u * RG, end - 1)];
+        float xv[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load8_f32(Xh + (int64_t)idx[u] * D + pc * 8, xv[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (r0 + u * RG < end) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (double)xv[u][e];
+          }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[rg][pc * 8 + e] = acc[e];
@@ -711,12 +801,23 @@ __global__ __launch_bounds__(256) void consume_qrkc(const float* __restrict__ ce
   float* cs = cq_lds + D * D;   // [JB][D]
   const int h = blockIdx.y;
   const int j0 = blockIdx.x * JB;
-  for (int e = threadIdx.x * 4; e < D * D; e += 256 * 4)
-    *reinterpret_cast<f32x4_t*>(ms + e) = *reinterpret_cast<const f32x4_t*>(M + (int64_t)h * D * D + e);
-  for (int e = threadIdx.x * 4; e < JB * D; e += 256 * 4) {
-    const int jj = j0 + e / D;
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    if (jj < C) v = *reinterpret_cast<const f32x4_t*>(cent + ((int64_t)h * C + jj) * D + e % D);
+  // all staging loads of a thread are issued before their LDS stores
+  f32x4_t mv4[D * D / 4 / 256], cv4[JB * D / 4 / 256];
+#pragma unroll
+  for (int k = 0; k < D * D / 4 / 256; ++k)
+    mv4[k] = *reinterpret_cast<const f32x4_t*>(M + (int64_t)h * D * D + (threadIdx.x + k * 256) * 4);
+#pragma unroll
+  for (int k = 0; k < JB * D / 4 / 256; ++k) {
+    const int e = (threadIdx.x + k * 256) * 4;
+    cv4[k] = *reinterpret_cast<const f32x4_t*>(cent + ((int64_t)h * C + min(j0 + e / D, C - 1)) * D + e % D);
+  }
+#pragma unroll
+  for (int k = 0; k < D * D / 4 / 256; ++k) *reinterpret_cast<f32x4_t*>(ms + (threadIdx.x + k * 256) * 4) = mv4[k];
+#pragma unroll
+  for (int k = 0; k < JB * D / 4 / 256; ++k) {
+    const int e = (threadIdx.x + k * 256) * 4;
+    f32x4_t v = cv4[k];
+    if (j0 + e / D >= C) v = f32x4_t{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4_t*>(cs + e) = v;
   }
   __syncthreads();
@@ -769,11 +870,30 @@ __global__ __launch_bounds__(256) void consume_qrkc(const float* __restrict__ ce
 
 constexpr int kAsgChunk = 128;  // centroids staged in LDS at a time
 
+// Argmax keys. A lane holds 16 scores of one point per 32-centroid tile (slots 0..15, increasing
+// centroid index). Its key replaces the 4 low mantissa bits of the fp32 score by 15 - slot, so one
+// float max over keys finds the best score and, among scores equal in their top 20 bits, the
+// lowest slot (for non-negative scores; equal negative scores go to the highest slot). Dropping
+// 4 bits perturbs a comparison by less than 2^-19 of the scores' magnitude.
+__device__ __forceinline__ float asg_key(float s, uint32_t code) {
+  return __uint_as_float((__float_as_uint(s) & ~15u) | code);
+}
+__device__ __forceinline__ float asg_trunc(float k) { return __uint_as_float(__float_as_uint(k) & ~15u); }
+// v_max3_f32 (keys are finite, never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // bf16 data. Each wave owns PT*32 points held as MFMA B operands; centroid tiles of 32 rows are
 // the A operands. The accumulator starts at -b_j/2, so it holds x.g_j - b_j/2 and the label is the
-// argmax (lowest j on ties).
+// argmax. Per tile the lane's 16 keys are reduced with v_max3; the running best moves to a later
+// tile only when that tile's best is larger in its top 20 bits, so equal scores keep the lower
+// centroid index across tiles. Registers are capped for three waves per SIMD, so that one wave's
+// MFMAs run while the others compare.
 template <int D, int PT>
-__global__ __launch_bounds__(256) void assign_bf16(const uint16_t* __restrict__ X, int64_t N, int C,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void assign_bf16(const uint16_t* __restrict__ X, int64_t N, int C,
                                                    const uint16_t* __restrict__ G, const float* __restrict__ b,
                                                    int32_t* __restrict__ labels) {
   constexpr int KS = D / 16;
@@ -800,24 +920,43 @@ __global__ __launch_bounds__(256) void assign_bf16(const uint16_t* __restrict__ 
       xb[pt][kk] = v;
     }
   }
-  float best[PT];
-  int bidx[PT];
+  float best[PT];   // key of the best score so far
+  float bestt[PT];  // its top 20 bits
+  int btile[PT];    // its tile
 #pragma unroll
   for (int pt = 0; pt < PT; ++pt) {
-    best[pt] = -INFINITY;
-    bidx[pt] = 0;
+    best[pt] = -FLT_MAX;
+    bestt[pt] = -FLT_MAX;
+    btile[pt] = 0;
   }
-  for (int c0 = 0; c0 < C; c0 += kAsgChunk) {
-    // stage centroids [c0, c0 + 128) and -b/2
-    for (int e = threadIdx.x; e < kAsgChunk * (D / 8); e += 256) {
-      const int r = e / (D / 8);
-      const int c8 = e % (D / 8);
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c0 + r < C) v = *reinterpret_cast<const u32x4_t*>(Gh + (int64_t)(c0 + r) * D + c8 * 8);
-      *reinterpret_cast<u32x4_t*>(&gl[r * STR + c8 * 8]) = v;
+  // Centroid chunks of 128 rows pass through LDS; the next chunk is fetched into registers while
+  // the current one is in use (loads clamped to row C - 1, padding rows zeroed on the LDS store).
+  constexpr int PPT = kAsgChunk * (D / 8) / 256;  // 16-byte pieces per thread and chunk
+  u32x4_t pre[PPT];
+  float preb;
+  auto fetch = [&](int cn) {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int row = min(cn + e / (D / 8), C - 1);
+      pre[q] = *reinterpret_cast<const u32x4_t*>(Gh + (int64_t)row * D + (e % (D / 8)) * 8);
     }
-    for (int r = threadIdx.x; r < kAsgChunk; r += 256) hb[r] = (c0 + r < C) ? -0.5f * bh[c0 + r] : -INFINITY;
+    preb = bh[min(cn + (int)(threadIdx.x % kAsgChunk), C - 1)];
+  };
+  fetch(0);
+  for (int c0 = 0; c0 < C; c0 += kAsgChunk) {
+    // stage centroids [c0, c0 + 128) and -b/2 (padding rows: zero centroid, score -FLT_MAX)
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int r = e / (D / 8);
+      u32x4_t v = pre[q];
+      if (c0 + r >= C) v = u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(&gl[r * STR + (e % (D / 8)) * 8]) = v;
+    }
+    if (threadIdx.x < kAsgChunk) hb[threadIdx.x] = (c0 + (int)threadIdx.x < C) ? -0.5f * preb : -FLT_MAX;
     __syncthreads();
+    if (c0 + kAsgChunk < C) fetch(c0 + kAsgChunk);
     const int ntile = (C - c0 + 31) / 32 < kAsgChunk / 32 ? (C - c0 + 31) / 32 : kAsgChunk / 32;
     for (int ct = 0; ct < ntile; ++ct) {
       f32x16_t acc[PT];
@@ -832,15 +971,19 @@ __global__ __launch_bounds__(256) void assign_bf16(const uint16_t* __restrict__ 
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma32(a, xb[pt][kk], acc[pt]);
       }
+      const int tile = c0 / 32 + ct;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
+        float t = max3f(asg_key(acc[pt][0], 15u), asg_key(acc[pt][1], 14u), asg_key(acc[pt][2], 13u));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = c0 + ct * 32 + (i / 4) * 8 + hl * 4 + i % 4;
-          if (acc[pt][i] > best[pt]) {
-            best[pt] = acc[pt][i];
-            bidx[pt] = j;
-          }
+        for (int i = 3; i < 15; i += 2)
+          t = max3f(t, asg_key(acc[pt][i], 15u - i), asg_key(acc[pt][i + 1], 14u - i));
+        t = max3f(t, asg_key(acc[pt][15], 0u), asg_key(acc[pt][15], 0u));
+        const float tt = asg_trunc(t);
+        if (tt > bestt[pt]) {
+          best[pt] = t;
+          bestt[pt] = tt;
+          btile[pt] = tile;
         }
       }
     }
@@ -848,11 +991,14 @@ __global__ __launch_bounds__(256) void assign_bf16(const uint16_t* __restrict__ 
   }
 #pragma unroll
   for (int pt = 0; pt < PT; ++pt) {
-    const float ob = __shfl_xor(best[pt], 32, kWave);
-    const int oi = __shfl_xor(bidx[pt], 32, kWave);
-    if (ob > best[pt] || (ob == best[pt] && oi < bidx[pt])) bidx[pt] = oi;
+    const int slot = 15 - (int)(__float_as_uint(best[pt]) & 15u);
+    int bi = btile[pt] * 32 + (slot / 4) * 8 + hl * 4 + slot % 4;
+    // the other half-wave holds the other 16 centroids of every tile for the same point
+    const float ob = __shfl_xor(bestt[pt], 32, kWave);
+    const int oi = __shfl_xor(bi, 32, kWave);
+    if (ob > bestt[pt] || (ob == bestt[pt] && oi < bi)) bi = oi;
     const int64_t p = p_base + pt * 32 + l % 32;
-    if (hl == 0 && p < N) labels[(int64_t)h * N + p] = bidx[pt];
+    if (hl == 0 && p < N) labels[(int64_t)h * N + p] = bi;
   }
 }
 
@@ -898,88 +1044,116 @@ __global__ __launch_bounds__(256) void assign_f32(const float* __restrict__ X, i
 __global__ __launch_bounds__(64) void sort_hist(const int32_t* __restrict__ labels, int64_t N, int C, int nchunk,
                                                 int32_t* __restrict__ table) {
   __shared__ int cnt[kMaxClusters];
+  constexpr int R = kSortChunk / 64;
   const int h = blockIdx.y;
   const int ch = blockIdx.x;
+  const int64_t t0 = (int64_t)ch * kSortChunk + lane_id();
+  const int32_t* lh = labels + (int64_t)h * N;
+  int lab[R];  // all loads issued before the first use
+#pragma unroll
+  for (int r = 0; r < R; ++r) lab[r] = lh[min(t0 + r * 64, N - 1)];
   for (int c = threadIdx.x; c < C; c += 64) cnt[c] = 0;
   __syncthreads();
-  const int64_t t0 = (int64_t)ch * kSortChunk;
-  const int32_t* lh = labels + (int64_t)h * N;
-  for (int e = threadIdx.x; e < kSortChunk; e += 64) {
-    const int64_t t = t0 + e;
-    if (t < N) atomicAdd(&cnt[lh[t]], 1);
-  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (t0 + r * 64 < N) atomicAdd(&cnt[lab[r]], 1);
   __syncthreads();
   int32_t* out = table + ((int64_t)h * nchunk + ch) * C;
   for (int c = threadIdx.x; c < C; c += 64) out[c] = cnt[c];
 }
 
-// Per head: table[chunk][c] <- number of tokens placed before chunk's first token of cluster c
-// (offsets included); offsets[c] = tokens with label < c.
-__global__ __launch_bounds__(1024) void sort_scan(int32_t* __restrict__ table, int nchunk, int C,
-                                                  int32_t* __restrict__ offsets) {
-  __shared__ int tot[kMaxClusters];
+// Per (head, cluster c): table[chunk][c] <- tokens of cluster c in the chunks before `chunk`
+// (exclusive prefix over chunks, 16 loads in flight per thread); tot[c] <- all tokens of cluster c.
+__global__ __launch_bounds__(64) void sort_scan_chunks(int32_t* __restrict__ table, int nchunk, int C,
+                                                       int32_t* __restrict__ tot) {
+  constexpr int B = 16;
+  const int h = blockIdx.y;
+  const int c = blockIdx.x * 64 + threadIdx.x;
+  if (c >= C) return;
+  int32_t* th = table + (int64_t)h * nchunk * C + c;
+  int run = 0;
+  for (int k0 = 0; k0 < nchunk; k0 += B) {
+    int v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) v[q] = th[(int64_t)min(k0 + q, nchunk - 1) * C];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      if (k0 + q < nchunk) {
+        th[(int64_t)(k0 + q) * C] = run;
+        run += v[q];
+      }
+    }
+  }
+  tot[(int64_t)h * (C + 1) + c] = run;
+}
+
+// Per head: offsets[c] <- tokens with label < c (in place over the cluster totals), offsets[C] = N.
+__global__ __launch_bounds__(1024) void sort_scan_offsets(int32_t* __restrict__ offsets, int C) {
   __shared__ int scratch[17];
   const int h = blockIdx.x;
-  int32_t* th = table + (int64_t)h * nchunk * C;
-  for (int c = threadIdx.x; c < C; c += 1024) {
-    int run = 0;
-    for (int k = 0; k < nchunk; ++k) {
-      const int v = th[(int64_t)k * C + c];
-      th[(int64_t)k * C + c] = run;
-      run += v;
-    }
-    tot[c] = run;
-  }
-  __syncthreads();
-  // exclusive scan of tot over clusters: each thread a contiguous segment
+  int32_t* oh = offsets + (int64_t)h * (C + 1);
   const int per = (C + 1023) / 1024;
   const int c_beg = threadIdx.x * per;
+  int v[(kMaxClusters + 1023) / 1024];
   int local = 0;
-  for (int k = 0; k < per; ++k)
-    if (c_beg + k < C) local += tot[c_beg + k];
+#pragma unroll
+  for (int k = 0; k < (kMaxClusters + 1023) / 1024; ++k) {
+    v[k] = (k < per && c_beg + k < C) ? oh[c_beg + k] : 0;
+    local += v[k];
+  }
   int total;
   int run = block_exclusive_scan(local, scratch, &total);
-  for (int k = 0; k < per; ++k) {
-    const int c = c_beg + k;
-    if (c < C) {
-      const int v = tot[c];
-      tot[c] = run;
-      offsets[(int64_t)h * (C + 1) + c] = run;
-      run += v;
+#pragma unroll
+  for (int k = 0; k < (kMaxClusters + 1023) / 1024; ++k) {
+    if (k < per && c_beg + k < C) {
+      oh[c_beg + k] = run;
+      run += v[k];
     }
   }
-  if (threadIdx.x == 0) offsets[(int64_t)h * (C + 1) + C] = total;
-  __syncthreads();
-  for (int c = threadIdx.x; c < C; c += 1024) {
-    const int o = tot[c];
-    for (int k = 0; k < nchunk; ++k) th[(int64_t)k * C + c] += o;
-  }
+  if (threadIdx.x == 0) oh[C] = total;
 }
 
 // One wave per chunk: tokens are placed in order, 64 at a time. A lane's peers (lanes with the same
 // label) come from one ballot per label bit; its rank among them is the number of lower peer lanes,
 // which keeps the original order inside each cluster, and the lowest peer advances the cluster's
 // cursor. A single wave's LDS accesses complete in program order, so no barrier is needed between
-// reading and advancing the cursors.
+// reading and advancing the cursors. Cursors start at offsets[c] + table[chunk][c].
 __global__ __launch_bounds__(64) void sort_scatter(const int32_t* __restrict__ labels, int64_t N, int C,
                                                    int nchunk, const int32_t* __restrict__ table,
-                                                   int32_t* __restrict__ perm) {
+                                                   const int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
   __shared__ int cursor[kMaxClusters];
+  constexpr int R = kSortChunk / 64;
   const int h = blockIdx.y;
   const int ch = blockIdx.x;
   const int l = lane_id();
-  const int32_t* base = table + ((int64_t)h * nchunk + ch) * C;
-  for (int c = l; c < C; c += 64) cursor[c] = base[c];
-  __syncthreads();
   const int32_t* lh = labels + (int64_t)h * N;
+  const int64_t t0 = (int64_t)ch * kSortChunk + l;
+  int labs[R];  // all loads issued before the first use
+#pragma unroll
+  for (int r = 0; r < R; ++r) labs[r] = lh[min(t0 + r * 64, N - 1)];
+  const int32_t* base = table + ((int64_t)h * nchunk + ch) * C;
+  const int32_t* oh = offsets + (int64_t)h * (C + 1);
+  for (int c0 = 0; c0 < C; c0 += 8 * 64) {  // 8 clusters per lane in flight
+    int v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = min(c0 + k * 64 + l, C - 1);
+      v[k] = base[c] + oh[c];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (c0 + k * 64 + l < C) cursor[c0 + k * 64 + l] = v[k];
+  }
+  __syncthreads();
   int32_t* ph = perm + (int64_t)h * N;
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
   constexpr int kLabelBits = 11;  // labels < kMaxClusters = 2^11
   static_assert((1 << kLabelBits) >= kMaxClusters, "label bits");
-  for (int r = 0; r < kSortChunk / 64; ++r) {
-    const int64_t t = (int64_t)ch * kSortChunk + r * 64 + l;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = t0 + r * 64;
     const bool valid = t < N;
-    const int lab = valid ? lh[t] : 0;
+    const int lab = labs[r];
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int k = 0; k < kLabelBits; ++k) {
@@ -1105,9 +1279,12 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
     const KppArgs& a = sides[q];
     const int S = kpp_candidates(s.N, a.C);
     const dim3 g1((unsigned)ceil_div(S, 64), (unsigned)s.H);
-    const size_t lds = (size_t)(64 * (s.D + 1) + (a.metric ? s.D * s.D : 0)) * sizeof(float);
-#define PARK_PREP(T, D) \
-  kpp_prep<T, D><<<g1, 256, lds, st>>>(static_cast<const T*>(a.x), s.N, S, a.metric, a.xx, a.metric ? a.y : nullptr);
+    const size_t lds_t = (size_t)(68 * s.D + s.D * s.D) * sizeof(float);
+#define PARK_PREP(T, D)                                                                                     \
+  if (a.metric)                                                                                             \
+    kpp_prep_tiled<T, D><<<g1, 256, lds_t, st>>>(static_cast<const T*>(a.x), s.N, S, a.metric, a.xx, a.y); \
+  else                                                                                                      \
+    kpp_prep<T, D><<<g1, 256, 0, st>>>(static_cast<const T*>(a.x), s.N, S, a.xx);
     if (s.bf16) {
       if (s.D == 128) {
         PARK_PREP(uint16_t, 128)
@@ -1211,8 +1388,9 @@ hipError_t launch_sort(const Dims& s, int C, const int32_t* labels, int32_t* tab
   const int nchunk = (int)ceil_div(s.N, kSortChunk);
   const dim3 grid((unsigned)nchunk, (unsigned)s.H);
   sort_hist<<<grid, 64, 0, st>>>(labels, s.N, C, nchunk, table);
-  sort_scan<<<(unsigned)s.H, 1024, 0, st>>>(table, nchunk, C, offsets);
-  sort_scatter<<<grid, 64, 0, st>>>(labels, s.N, C, nchunk, table, perm);
+  sort_scan_chunks<<<dim3((unsigned)ceil_div(C, 64), (unsigned)s.H), 64, 0, st>>>(table, nchunk, C, offsets);
+  sort_scan_offsets<<<(unsigned)s.H, 1024, 0, st>>>(offsets, C);
+  sort_scatter<<<grid, 64, 0, st>>>(labels, s.N, C, nchunk, table, offsets, perm);
   return hipGetLastError();
 }
 

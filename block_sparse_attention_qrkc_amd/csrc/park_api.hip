@@ -4,6 +4,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "../../include/park.h"
@@ -213,6 +215,37 @@ hipError_t run_lloyd(const park::Dims& s, const void* x, const float* metric, in
     if (e == hipSuccess) e = park::launch_update(s, x, C, perm, offsets, cent, 1, metric, w.g, w.b, st);
   }
   return e;
+}
+
+// A helper stream per device (default priority, created on first use and kept for the process):
+// park_forward runs the query-side Lloyd iterations on it, concurrently with the key side on the
+// caller's stream (the query side streams its data from HBM while the key side's assignment is
+// bound by the matrix cores). Fork and join go through events, so the caller's stream still orders
+// every launch of the call, also under stream capture.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::map<int, SideStream> g_side;
+
+// Returns the device's helper stream with g_side_mu held by `lock`.
+hipError_t side_stream(std::unique_lock<std::mutex>& lock, SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  lock = std::unique_lock<std::mutex>(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ss = n;
+  }
+  *out = &ss;
+  return hipSuccess;
 }
 
 park::KppArgs kpp_args(const void* x, const float* metric, int C, int side, float* cent, const ClusterWs& w) {
@@ -493,8 +526,19 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
                                   kpp_args(k, qrkc ? M : nullptr, p.ck, PARK_SIDE_K, k_centroids, w.kc)};
       e = park::launch_kpp(s, a, 2, p.seed, st);
     }
-    if (e == hipSuccess) e = run_lloyd(s, q, nullptr, p.cq, p.iters, q_centroids, ql, qp, qo, w.qc, st);
-    if (e == hipSuccess) e = run_lloyd(s, k, qrkc ? M : nullptr, p.ck, p.iters, k_centroids, kl, kp, ko, w.kc, st);
+    if (e == hipSuccess) {
+      // query side on the helper stream, key side on the caller's, joined before the map
+      std::unique_lock<std::mutex> lock;
+      SideStream* ss = nullptr;
+      e = side_stream(lock, &ss);
+      if (e == hipSuccess) e = hipEventRecord(ss->fork, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+      if (e == hipSuccess) e = run_lloyd(s, q, nullptr, p.cq, p.iters, q_centroids, ql, qp, qo, w.qc, ss->stream);
+      if (e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
+      if (e == hipSuccess)
+        e = run_lloyd(s, k, qrkc ? M : nullptr, p.ck, p.iters, k_centroids, kl, kp, ko, w.kc, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
+    }
     if (e == hipSuccess)
       e = park::launch_pama(s, q, qp, qo, p.cq, k_centroids, ko, p.ck, scale, map, w.mw.khat, w.mw.logn,
                             w.mw.chunk_base, w.mw.partial, st);
