@@ -377,6 +377,10 @@ __global__ __launch_bounds__(kKppThreads) void kpp_seed(KppSide s0, KppSide s1, 
 // publish their D^2 sums, the part holding the sampled prefix position finds the candidate and
 // publishes it, and every part lowers its D^2 against the new centre. Launched cooperatively
 // (all workgroups resident); every wait is bounded.
+// Every exchanged value is its own message: a slot written once per step by one atomic store
+// (relaxed, device scope) of a word that is never zero (a D^2 sum with its sign bit set, or a
+// candidate index + 1), polled by the readers until it is non-zero. No value depends on other
+// data published in the same kernel, so no fence is needed on either side.
 // ------------------------------------------------------------------------------------------------
 
 constexpr int kCoopMaxParts = 16;
@@ -389,17 +393,18 @@ struct CoopSide {
   const double* xx;   // [H, S]
   const float* y;     // [H, S, D] or NULL (Euclidean)
   float* cent;        // [H, C, D]
-  double* psum;       // [H, C, kCoopMaxParts, 2]: per part (D^2 sum, first untaken candidate)
-  int* sync;          // [H, C, 3]: arrivals, (unused), chosen candidate + 1; then one failure flag
+  uint64_t* psum;     // [H, C, kCoopMaxParts, 2]: slot [m][part][0] = part's D^2 sum of step m, flagged
+  int* sync;          // [H, C, 3]: [m][2] = candidate chosen at step m, + 1; then one failure flag
   int C, S, side, G, SP;
 };
 
-// Wait until *p >= want: relaxed polling (no cache maintenance per poll), then one acquire fence.
-// A wait that runs out sets *fail, after which every wait of the launch returns at once, so a
-// broken launch still ends promptly (with wrong centroids) instead of hanging.
-__device__ __forceinline__ void spin_until(int* p, int want, int* fail) {
+// Wait until *p != 0 and return it: relaxed polling (no cache maintenance per poll). A wait that
+// runs out sets *fail, after which every wait of the launch returns at once (with 0), so a broken
+// launch still ends promptly (with wrong centroids) instead of hanging.
+__device__ __forceinline__ int spin_nonzero(int* p, int* fail) {
   long long n = 0;
-  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+  int v;
+  while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
     if (__hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
     if (++n >= kSpinLimit) {
       __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -407,13 +412,13 @@ __device__ __forceinline__ void spin_until(int* p, int want, int* fail) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return v;
 }
 
-// Wait until *p != 0 and return it (same limits as spin_until).
-__device__ __forceinline__ int spin_nonzero(int* p, int* fail) {
+// The same for a 64-bit slot.
+__device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
   long long n = 0;
-  int v;
+  uint64_t v;
   while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
     if (__hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
     if (++n >= kSpinLimit) {
@@ -431,9 +436,11 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
   extern __shared__ uint32_t lrows[];  // [SP - threads][D / 2] bf16 pairs of the LDS-resident rows
   __shared__ __attribute__((aligned(16))) uint32_t yhi[D / 2];
   __shared__ __attribute__((aligned(16))) uint32_t ylo[D / 2];
-  __shared__ double wred[kCoopWaves];
-  __shared__ double wred2[kCoopWaves];
+  constexpr int CPR = D / 8;           // 16-byte pieces per row
+  __shared__ double wred[kCoopWaves];   // per wave: D^2 total of its register rows
+  __shared__ double wred2[kCoopWaves];  // per wave: D^2 total of its LDS rows
   __shared__ int wmin[kCoopWaves];
+  __shared__ int wfirst[2][kCoopWaves], wlast[2][kCoopWaves];
   __shared__ double pre_s, v_s, cc_s;
   __shared__ int owner_s, pick_s;
 
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
   const uint16_t* Xh = sd.x + (int64_t)h * N * D;
   const double* xxh = sd.xx + (int64_t)h * S;
   const float* yh = sd.y ? sd.y + (int64_t)h * S * D : nullptr;
-  double* psum = sd.psum + (int64_t)h * C * kCoopMaxParts * 2;
+  uint64_t* psum = sd.psum + (int64_t)h * C * kCoopMaxParts * 2;
   int* sync = sd.sync + (int64_t)h * C * 3;
   int* fail = sd.sync + (int64_t)H * C * 3;
 
@@ -476,10 +483,13 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
       xr[q + 3] = v[3];
     }
   }
-  for (int e = tid; e < nlds * (ROW_U32 / 4); e += kCoopThreads) {
-    const int r = e / (ROW_U32 / 4), q = (e % (ROW_U32 / 4)) * 4;
+  // LDS row r keeps its 16-byte piece p at position p ^ (r % CPR), so that the threads reading
+  // their own rows piece by piece hit distinct banks
+  for (int e = tid; e < nlds * CPR; e += kCoopThreads) {
+    const int r = e / CPR, p = e % CPR;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(Xh + cand_row(c0 + kCoopThreads + r, S, N) * D);
-    *reinterpret_cast<u32x4_t*>(&lrows[r * ROW_U32 + q]) = *reinterpret_cast<const u32x4_t*>(src + q);
+    *reinterpret_cast<u32x4_t*>(&lrows[r * ROW_U32 + (p ^ (r % CPR)) * 4]) =
+        *reinterpret_cast<const u32x4_t*>(src + p * 4);
   }
   const double xx_r = has_r ? xxh[c0 + tid] : 0.0;
   const double xx_l = has_l ? xxh[c0 + kCoopThreads + tid] : 0.0;
@@ -493,9 +503,10 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
       const int t0 = (int)(kpp_uniform(seed, h, sd.side, 0) * (double)S);
       t = t0 < S ? t0 : S - 1;
     } else {
-      // ---- this part's D^2 sum and first untaken candidate
-      const double loc = d2r + d2l;
-      double ws = wave_sum_f64(loc);
+      // ---- running D^2 sums inside each wave (candidate order: register rows of waves 0..7, then
+      // LDS rows of waves 0..7), the wave totals, and this part's first untaken candidate
+      const double incr = wave_inclusive_scan(d2r);
+      const double incl = wave_inclusive_scan(d2l);
       int fu = has_r && !taken_r ? c0 + tid : (has_l && !taken_l ? c0 + kCoopThreads + tid : 0x7FFFFFFF);
       // lowest untaken: reg candidates precede LDS ones in candidate order
       const int fu_r = has_r && !taken_r ? c0 + tid : 0x7FFFFFFF;
@@ -506,12 +517,15 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
         const int f2 = __shfl_xor(fu, o, kWave);
         fu = f2 < fu ? f2 : fu;
       }
-      if (l == 0) {
-        wred[w] = ws;
-        wmin[w] = fu;
+      if (l == kWave - 1) {
+        wred[w] = incr;
+        wred2[w] = incl;
       }
+      if (l == 0) wmin[w] = fu;
       __syncthreads();
       if (w == 0) {
+        // slots of step m: [part][0] = D^2 sum with its sign bit set, [part][1] = first untaken + 1
+        uint64_t* slots = psum + (int64_t)m * kCoopMaxParts * 2;
         if (l == 0) {
           double pt = 0.0;
           int pf = 0x7FFFFFFF;
@@ -519,24 +533,25 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
             pt += wred[q];
             pf = wmin[q] < pf ? wmin[q] : pf;
           }
-          psum[((int64_t)m * kCoopMaxParts + part) * 2] = pt;
-          psum[((int64_t)m * kCoopMaxParts + part) * 2 + 1] = (double)pf;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          __hip_atomic_fetch_add(&sync[m * 3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          spin_until(&sync[m * 3], G, fail);
+          for (int q = 0; q < kCoopWaves; ++q) pt += wred2[q];
+          __hip_atomic_store(&slots[part * 2], (uint64_t)__double_as_longlong(pt) | (1ull << 63), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&slots[part * 2 + 1], (uint64_t)(uint32_t)pf + 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // the G part sums are read at once (lane q: part q) and folded in the same order by every
-        // part (a lane scan)
-        const double pq = l < G ? __hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + l) * 2], __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.0;
-        const int fq = l < G ? (int)__hip_atomic_load(&psum[((int64_t)m * kCoopMaxParts + l) * 2 + 1],
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : 0x7FFFFFFF;
-        double run = pq;  // inclusive prefix over parts
+        // part (a lane scan); a failed wait reads as an empty part
+        double pq = 0.0;
+        int fq = 0x7FFFFFFF;
+        if (l < G) {
+          const uint64_t a = spin_slot(&slots[l * 2], fail);
+          const uint64_t c = spin_slot(&slots[l * 2 + 1], fail);
+          pq = __longlong_as_double((long long)(a & ~(1ull << 63)));
+          fq = c != 0 ? (int)(c - 1u) : 0x7FFFFFFF;
+        }
+        double run = pq;  // inclusive prefix over parts (lanes < kCoopMaxParts)
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
+        for (int o = 1; o < kCoopMaxParts; o <<= 1) {
           const double u = __shfl_up(run, o, kWave);
           if (l >= o) run += u;
         }
@@ -574,51 +589,32 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
       const int owner = owner_s;
       if (owner >= 0) {
         if (owner == part) {
-          // prefix over this part's candidates in candidate order: registers rows, then LDS rows
+          // running sums in candidate order (pre: the parts before this one); per wave, the first
+          // candidate whose running sum exceeds v, and the last one with mass (rounding fallback)
           const double v = v_s;
-          const double incr = wave_inclusive_scan(d2r);
-          const double incl = wave_inclusive_scan(d2l);
-          if (l == kWave - 1) {
-            wred[w] = incr;
-            wred2[w] = incl;
-          }
-          __syncthreads();
-          double pr = pre_s, pl;
+          double pr = pre_s, pl = pre_s;
           for (int q = 0; q < w; ++q) pr += wred[q];
-          double totr = pre_s;
-          for (int q = 0; q < kCoopWaves; ++q) totr += wred[q];
-          pl = totr;
+          for (int q = 0; q < kCoopWaves; ++q) pl += wred[q];
           for (int q = 0; q < w; ++q) pl += wred2[q];
-          // first candidate whose running sum exceeds v
-          int hit = 0x7FFFFFFF;
-          if (d2r > 0.0 && pr + incr > v) hit = c0 + tid;
-          else if (d2l > 0.0 && pl + incl > v) hit = c0 + kCoopThreads + tid;
-          if (d2r > 0.0 && pr + incr > v) hit = c0 + tid;
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) {
-            const int h2 = __shfl_xor(hit, o, kWave);
-            hit = h2 < hit ? h2 : hit;
+          const uint64_t hr = __ballot(d2r > 0.0 && pr + incr > v);
+          const uint64_t hq = __ballot(d2l > 0.0 && pl + incl > v);
+          const uint64_t mr = __ballot(d2r > 0.0);
+          const uint64_t mq = __ballot(d2l > 0.0);
+          if (l == 0) {
+            const int rb = c0 + w * kWave, lb = c0 + kCoopThreads + w * kWave;
+            wfirst[0][w] = hr ? rb + __ffsll((unsigned long long)hr) - 1 : 0x7FFFFFFF;
+            wfirst[1][w] = hq ? lb + __ffsll((unsigned long long)hq) - 1 : 0x7FFFFFFF;
+            wlast[0][w] = mr ? rb + 63 - __clzll((unsigned long long)mr) : -1;
+            wlast[1][w] = mq ? lb + 63 - __clzll((unsigned long long)mq) : -1;
           }
-          if (l == 0) wmin[w] = hit;
-          // fallback (rounding only): the last candidate of this part with mass
-          int lastm = -1;
-          if (d2r > 0.0) lastm = c0 + tid;
-          if (d2l > 0.0) lastm = c0 + kCoopThreads + tid;
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) {
-            const int l2 = __shfl_xor(lastm, o, kWave);
-            lastm = l2 > lastm ? l2 : lastm;
-          }
-          __syncthreads();
-          if (l == 0) wred[w] = (double)lastm;
           __syncthreads();
           if (tid == 0) {
-            int best = 0x7FFFFFFF, lastbest = -1;
-            for (int q = 0; q < kCoopWaves; ++q) {
-              best = wmin[q] < best ? wmin[q] : best;
-              lastbest = (int)wred[q] > lastbest ? (int)wred[q] : lastbest;
-            }
-            if (best == 0x7FFFFFFF) best = lastbest >= 0 ? lastbest : c0;
+            int best = 0x7FFFFFFF, last = -1;
+            for (int k2 = 0; k2 < 2 && best == 0x7FFFFFFF; ++k2)  // register rows precede LDS rows
+              for (int q = 0; q < kCoopWaves; ++q) best = wfirst[k2][q] < best ? wfirst[k2][q] : best;
+            for (int k2 = 0; k2 < 2; ++k2)
+              for (int q = 0; q < kCoopWaves; ++q) last = wlast[k2][q] > last ? wlast[k2][q] : last;
+            if (best == 0x7FFFFFFF) best = last >= 0 ? last : c0;
             // the flag carries the pick (+1, so that 0 means not yet)
             __hip_atomic_store(&sync[m * 3 + 2], best + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pick_s = best;
@@ -651,7 +647,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
     // ---- lower D^2 against the new centre. Dot products on packed bf16 pairs (v_dot2_f32_bf16,
     // fp32 accumulation) against y split into a bf16 high part and a bf16 remainder.
     {
-      float accr = 0.f, accl = 0.f;
+      float accr = 0.f, accl = 0.f, accr2 = 0.f, accl2 = 0.f;  // high and low parts of y
       const uint32_t* lrow = lrows + tid * ROW_U32;
 #pragma unroll
       for (int q = 0; q < ROW_U32; q += 4) {
@@ -661,18 +657,20 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
         for (int e = 0; e < 4; ++e) {
           const uint32_t xe = xr[q + e], he = hv[e], le = lv[e];
           accr = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(he), accr, false);
-          accr = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accr, false);
+          accr2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accr2, false);
         }
         if (has_l) {
-          const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(lrow + q);
+          const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(lrow + (((q / 4) ^ (tid % CPR)) * 4));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t xe = xv[e], he = hv[e], le = lv[e];
             accl = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(he), accl, false);
-            accl = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accl, false);
+            accl2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xe), as_bf16x2(le), accl2, false);
           }
         }
       }
+      accr += accr2;
+      accl += accl2;
       if (has_r) {
         if (c0 + tid == t) {
           taken_r = true;
@@ -1251,13 +1249,15 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
     const KppArgs& a = sides[q];
     const int S = kpp_candidates(s.N, a.C);
     const int SP = (int)ceil_div(S, G[q]);
-    cs[q] = CoopSide{static_cast<const uint16_t*>(a.x), a.xx, a.metric ? a.y : nullptr, a.cent, a.psum, a.sync,
-                     a.C, S, a.side, G[q], SP};
+    cs[q] = CoopSide{static_cast<const uint16_t*>(a.x), a.xx, a.metric ? a.y : nullptr, a.cent,
+                     reinterpret_cast<uint64_t*>(a.psum), a.sync, a.C, S, a.side, G[q], SP};
     const size_t l = (size_t)(SP > kCoopThreads ? SP - kCoopThreads : 0) * (size_t)s.D * 2;
     lds = l > lds ? l : lds;
     total += s.H * G[q];
     const int64_t nsync = s.H * (int64_t)a.C * 3 + 1;
     fill_i32<<<(unsigned)ceil_div(nsync, 256), 256, 0, st>>>(a.sync, nsync, 0);
+    const int64_t nslot = s.H * (int64_t)a.C * kCoopMaxParts * 2 * 2;  // as int32 words
+    fill_i32<<<(unsigned)ceil_div(nslot, 256), 256, 0, st>>>(reinterpret_cast<int*>(a.psum), nslot, 0);
   }
   if (nsides == 1) {
     cs[1] = cs[0];

@@ -5,8 +5,8 @@
 // Work item = up to 256 consecutive cluster-ordered queries of one query cluster. bf16 data: four
 // waves, each handling four 16-query tiles with 16x16x32 MFMA (queries = A rows, centroids = B
 // columns), so every centroid fragment loaded feeds four MFMAs.
-// Pass 1 keeps a running (max, sum) per query with one exp per logit; pass 2 recomputes the
-// logits and adds exp(l - max) / sum into per-wave column sums in LDS. Partial column sums of each
+// Pass 1 keeps a running (reference, sum) per query with one exp2 per logit; pass 2 recomputes
+// the logits and adds the normalised weights into per-wave column sums in LDS. Partial column sums of each
 // work item are then summed per cluster in fixed order in fp64 and divided by the cluster size.
 #include "park_common.h"
 #include "park_internal.h"
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(1024) void pama_chunks(const int32_t* __restrict__ 
   if (threadIdx.x == 0) cb[cq] = total;
 }
 
-// Consumed key centroids (bf16-rounded) and ln n_j (-inf for empty clusters).
+// Consumed key centroids (bf16-rounded) and log2 n_j (-inf for empty clusters).
 __global__ __launch_bounds__(256) void pama_prep(const float* __restrict__ k_cent, const int32_t* __restrict__ k_off,
                                                  int ck, int D, uint16_t* __restrict__ khat,
                                                  float* __restrict__ logn) {
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void pama_prep(const float* __restrict__ k_cen
   if (e < tot) khat[(int64_t)h * tot + e] = (uint16_t)f32_to_bf16_bits(k_cent[(int64_t)h * tot + e]);
   if (e < ck) {
     const int n = k_off[(int64_t)h * (ck + 1) + e + 1] - k_off[(int64_t)h * (ck + 1) + e];
-    logn[(int64_t)h * ck + e] = n > 0 ? logf((float)n) : -INFINITY;
+    logn[(int64_t)h * ck + e] = n > 0 ? log2f((float)n) : -INFINITY;
   }
 }
 
@@ -63,6 +63,21 @@ __device__ __forceinline__ int find_item(const int32_t* cb, int cq, int c) {
       hi = mid;
   }
   return lo;
+}
+
+// B operand fragments of centroid tile ct (centroid ct * 16 + l % 16, dims kk * 32 + g * 8 .. +7) and
+// its log-size weight. Loads are unconditional (row clamped to ck - 1) so that they stay in flight;
+// columns past ck get weight -inf.
+template <int KS>
+__device__ __forceinline__ void fetch_centroids(const uint16_t* kh, const float* lnh, int ck, int ct, int l, int g,
+                                                u32x4_t* bv, float* ln) {
+  const int j = ct * 16 + l % 16;
+  const int jc = min(j, ck - 1);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    bv[kk] = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)jc * (KS * 32) + kk * 32 + g * 8);
+  const float v = lnh[jc];
+  *ln = j < ck ? v : -INFINITY;
 }
 
 template <int D>
@@ -110,26 +125,28 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
         qa[t][kk] = v;
       }
     }
-    // pass 1: per-lane running (max, sum) of rows t*16 + g*4 + e over this lane's centroid column
-    float m[TW][4], s[TW][4];
+    // Logits in base 2: lg2 = acc * scale * log2(e) + log2(n_j). Pass 1 keeps, per lane and row, a
+    // reference r and the sum of 2^(lg2 - r) over this lane's centroid columns. r is raised only
+    // when a logit exceeds it by more than 2^kRaise (first tile, or rarely later), so the common
+    // step is one fma, one subtraction, one exp2 and one add per logit.
+    constexpr float kRaise = 16.f;
+    const float c1 = scale * 1.4426950408889634f;
+    float r[TW][4], s[TW][4];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m[t][e] = -INFINITY;
+        r[t][e] = -1e30f;  // finite, so that an empty column (-inf) never meets -inf - -inf
         s[t][e] = 0.f;
       }
+    u32x4_t bv[KS];
+    float ln;
+    fetch_centroids<KS>(kh, lnh, ck, 0, l, g, bv, &ln);
     for (int ct = 0; ct < nct; ++ct) {
-      const int j = ct * 16 + l % 16;
-      const bool jok = j < ck;
-      u32x4_t bv[KS];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (jok) v = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)j * D + kk * 32 + g * 8);
-        bv[kk] = v;
-      }
-      const float ln = jok ? lnh[j] : -INFINITY;
+      u32x4_t bn[KS];
+      float lnn;
+      fetch_centroids<KS>(kh, lnh, ck, min(ct + 1, nct - 1), l, g, bn, &lnn);
+      float lg[TW][4], dmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -137,66 +154,70 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
         for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float lg = acc[e] * scale + ln;
-          if (lg > m[t][e]) {
-            s[t][e] = s[t][e] * __expf(m[t][e] - lg) + 1.f;
-            m[t][e] = lg;
-          } else if (lg > -INFINITY) {
-            s[t][e] += __expf(lg - m[t][e]);
-          }
+          lg[t][e] = __builtin_fmaf(acc[e], c1, ln);
+          dmax = fmaxf(dmax, lg[t][e] - r[t][e]);
         }
       }
+      if (__builtin_expect(__ballot(dmax > kRaise) != 0, 0)) {
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (lg[t][e] - r[t][e] > kRaise) {
+              s[t][e] *= __builtin_amdgcn_exp2f(r[t][e] - lg[t][e]);
+              r[t][e] = lg[t][e];
+            }
+      }
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[t][e] += __builtin_amdgcn_exp2f(lg[t][e] - r[t][e]);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) bv[kk] = bn[kk];
+      ln = lnn;
     }
-    // merge (max, sum) across the 16 lanes of each group; 1/sum per row
-    float inv[TW][4];
+    // merge (reference, sum) across the 16 lanes (columns) of each group; the row's offset
+    // off = r + log2(sum) makes 2^(lg2 - off) its normalised weight (off = +inf for rows that are
+    // out of range, whose weights are then 0)
+    float roff[TW][4];
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-          const float mo = __shfl_xor(m[t][e], o, kWave);
+          const float ro = __shfl_xor(r[t][e], o, kWave);
           const float so = __shfl_xor(s[t][e], o, kWave);
-          const float mn = fmaxf(m[t][e], mo);
-          float sn = 0.f;
-          if (mn > -INFINITY) sn = s[t][e] * __expf(m[t][e] - mn) + so * __expf(mo - mn);
-          m[t][e] = mn;
-          s[t][e] = sn;
+          const float rn = fmaxf(r[t][e], ro);
+          s[t][e] = s[t][e] * __builtin_amdgcn_exp2f(r[t][e] - rn) + so * __builtin_amdgcn_exp2f(ro - rn);
+          r[t][e] = rn;
         }
         const bool ok = (w0 + t * 16 + g * 4 + e) < row_end && s[t][e] > 0.f;
-        inv[t][e] = ok ? 1.f / s[t][e] : 0.f;
-        if (!ok) m[t][e] = 0.f;
+        roff[t][e] = ok ? r[t][e] + log2f(s[t][e]) : INFINITY;
       }
     }
-    // pass 2: accumulate normalised weights into the wave's column sums
+    // pass 2: accumulate normalised weights 2^(lg2 - off) into the wave's column sums
+    fetch_centroids<KS>(kh, lnh, ck, 0, l, g, bv, &ln);
     for (int ct = 0; ct < nct; ++ct) {
       const int j = ct * 16 + l % 16;
-      const bool jok = j < ck;
-      u32x4_t bv[KS];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (jok) v = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)j * D + kk * 32 + g * 8);
-        bv[kk] = v;
-      }
-      const float ln = jok ? lnh[j] : -INFINITY;
+      u32x4_t bn[KS];
+      float lnn;
+      fetch_centroids<KS>(kh, lnh, ck, min(ct + 1, nct - 1), l, g, bn, &lnn);
       float cs = 0.f;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
-        float ct_sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lg = acc[e] * scale + ln;
-          ct_sum += (inv[t][e] > 0.f && lg > -INFINITY) ? __expf(lg - m[t][e]) * inv[t][e] : 0.f;
-        }
-        cs += ct_sum;
+        for (int e = 0; e < 4; ++e) cs += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], c1, ln) - roff[t][e]);
       }
       cs += __shfl_xor(cs, 16, kWave);
       cs += __shfl_xor(cs, 32, kWave);
-      if (g == 0 && jok) colsum[w][j] = cs;
+      if (g == 0 && j < ck) colsum[w][j] = cs;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) bv[kk] = bn[kk];
+      ln = lnn;
     }
   }
   __syncthreads();
