@@ -384,8 +384,10 @@ __global__ __launch_bounds__(kKppThreads) void kpp_seed(KppSide s0, KppSide s1, 
 // ------------------------------------------------------------------------------------------------
 
 constexpr int kCoopMaxParts = 16;
-constexpr int kCoopThreads = 512;  // 2 waves per SIMD: room for one candidate row per thread
-constexpr int kCoopWaves = kCoopThreads / kWave;
+// Threads per part: 512 (two waves per SIMD, room for the row and the update's registers) or,
+// when a head's candidates do not fit on that many parts, 1024 (four waves per SIMD).
+constexpr int kCoopThreads = 512;
+constexpr int kCoopThreadsWide = 1024;
 constexpr long long kSpinLimit = 1ll << 20;  // ~30 ms per wait; a normal wait takes microseconds
 
 struct CoopSide {
@@ -430,8 +432,9 @@ __device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
   return v;
 }
 
-template <int D>
-__global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s1, int H, int64_t N, uint64_t seed) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, int64_t N, uint64_t seed) {
+  constexpr int kCoopWaves = NT / kWave;
   constexpr int ROW_U32 = D / 2;
   extern __shared__ uint32_t lrows[];  // [SP - threads][D / 2] bf16 pairs of the LDS-resident rows
   __shared__ __attribute__((aligned(16))) uint32_t yhi[D / 2];
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
   const int w = tid / kWave;
   const int c0 = part * SP;                   // first candidate of this part
   const int cnt = min(SP, S - c0);            // candidates of this part
-  const int nreg = min(cnt, kCoopThreads);     // register-resident (thread tid: c0 + tid)
+  const int nreg = min(cnt, NT);     // register-resident (thread tid: c0 + tid)
   const int nlds = cnt - nreg;                // LDS-resident (thread tid: c0 + 1024 + tid)
   const uint16_t* Xh = sd.x + (int64_t)h * N * D;
   const double* xxh = sd.xx + (int64_t)h * S;
@@ -485,14 +488,14 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
   }
   // LDS row r keeps its 16-byte piece p at position p ^ (r % CPR), so that the threads reading
   // their own rows piece by piece hit distinct banks
-  for (int e = tid; e < nlds * CPR; e += kCoopThreads) {
+  for (int e = tid; e < nlds * CPR; e += NT) {
     const int r = e / CPR, p = e % CPR;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(Xh + cand_row(c0 + kCoopThreads + r, S, N) * D);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(Xh + cand_row(c0 + NT + r, S, N) * D);
     *reinterpret_cast<u32x4_t*>(&lrows[r * ROW_U32 + (p ^ (r % CPR)) * 4]) =
         *reinterpret_cast<const u32x4_t*>(src + p * 4);
   }
   const double xx_r = has_r ? xxh[c0 + tid] : 0.0;
-  const double xx_l = has_l ? xxh[c0 + kCoopThreads + tid] : 0.0;
+  const double xx_l = has_l ? xxh[c0 + NT + tid] : 0.0;
   double d2r = 0.0, d2l = 0.0;
   bool taken_r = false, taken_l = false;
   __syncthreads();
@@ -507,10 +510,10 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
       // LDS rows of waves 0..7), the wave totals, and this part's first untaken candidate
       const double incr = wave_inclusive_scan(d2r);
       const double incl = wave_inclusive_scan(d2l);
-      int fu = has_r && !taken_r ? c0 + tid : (has_l && !taken_l ? c0 + kCoopThreads + tid : 0x7FFFFFFF);
+      int fu = has_r && !taken_r ? c0 + tid : (has_l && !taken_l ? c0 + NT + tid : 0x7FFFFFFF);
       // lowest untaken: reg candidates precede LDS ones in candidate order
       const int fu_r = has_r && !taken_r ? c0 + tid : 0x7FFFFFFF;
-      const int fu_l = has_l && !taken_l ? c0 + kCoopThreads + tid : 0x7FFFFFFF;
+      const int fu_l = has_l && !taken_l ? c0 + NT + tid : 0x7FFFFFFF;
       fu = fu_r < fu_l ? fu_r : fu_l;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
           const uint64_t mr = __ballot(d2r > 0.0);
           const uint64_t mq = __ballot(d2l > 0.0);
           if (l == 0) {
-            const int rb = c0 + w * kWave, lb = c0 + kCoopThreads + w * kWave;
+            const int rb = c0 + w * kWave, lb = c0 + NT + w * kWave;
             wfirst[0][w] = hr ? rb + __ffsll((unsigned long long)hr) - 1 : 0x7FFFFFFF;
             wfirst[1][w] = hq ? lb + __ffsll((unsigned long long)hq) - 1 : 0x7FFFFFFF;
             wlast[0][w] = mr ? rb + 63 - __clzll((unsigned long long)mr) : -1;
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
       t = pick_s;
     }
     // ---- centre y_t as bf16 pairs (high part, remainder); part 0 writes the output centroid
-    for (int a2 = tid; a2 < D / 2; a2 += kCoopThreads) {
+    for (int a2 = tid; a2 < D / 2; a2 += NT) {
       const uint16_t* xt = Xh + cand_row(t, S, N) * D;
       const float x0 = bf16_bits_to_f32(xt[2 * a2]), x1 = bf16_bits_to_f32(xt[2 * a2 + 1]);
       const float y0 = yh ? yh[(int64_t)t * D + 2 * a2] : x0;
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(kCoopThreads) void kpp_coop(CoopSide s0, CoopSide s
         }
       }
       if (has_l) {
-        if (c0 + kCoopThreads + tid == t) {
+        if (c0 + NT + tid == t) {
           taken_l = true;
           d2l = 0.0;
         } else if (!taken_l) {
@@ -1207,9 +1210,9 @@ static hipError_t launch_kpp_single(const Dims& s, const KppArgs* sides, int nsi
 
 // Parts per side for the cooperative seeding within `budget` workgroups per head; false if the
 // candidates cannot be held on chip with that budget.
-static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budget, int* G) {
+static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budget, int nt, int* G) {
   const int lmax = (140 * 1024) / (int)(s.D * 2);  // LDS-resident rows per part
-  const int cap = kCoopThreads + lmax;
+  const int cap = nt + lmax;
   int used = 0;
   double work[2];
   for (int q = 0; q < nsides; ++q) {
@@ -1240,8 +1243,8 @@ static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budg
   return true;
 }
 
-static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nsides, const int* G, uint64_t seed,
-                                  hipStream_t st) {
+static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nsides, const int* G, int nt,
+                                  uint64_t seed, hipStream_t st) {
   CoopSide cs[2];
   size_t lds = 0;
   int64_t total = 0;
@@ -1251,7 +1254,7 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
     const int SP = (int)ceil_div(S, G[q]);
     cs[q] = CoopSide{static_cast<const uint16_t*>(a.x), a.xx, a.metric ? a.y : nullptr, a.cent,
                      reinterpret_cast<uint64_t*>(a.psum), a.sync, a.C, S, a.side, G[q], SP};
-    const size_t l = (size_t)(SP > kCoopThreads ? SP - kCoopThreads : 0) * (size_t)s.D * 2;
+    const size_t l = (size_t)(SP > nt ? SP - nt : 0) * (size_t)s.D * 2;
     lds = l > lds ? l : lds;
     total += s.H * G[q];
     const int64_t nsync = s.H * (int64_t)a.C * 3 + 1;
@@ -1268,9 +1271,12 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
   int H = (int)s.H;
   int64_t N = s.N;
   void* args[] = {&cs[0], &cs[1], &H, &N, &seed};
-  const void* fn = s.D == 128 ? (const void*)kpp_coop<128> : (const void*)kpp_coop<64>;
+  const void* fn = nt == kCoopThreads
+                       ? (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreads> : (const void*)kpp_coop<64, kCoopThreads>)
+                       : (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreadsWide>
+                                     : (const void*)kpp_coop<64, kCoopThreadsWide>);
   (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)total), dim3(kCoopThreads), args, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)total), dim3((unsigned)nt), args, (unsigned)lds, st);
 }
 
 hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
@@ -1308,16 +1314,32 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
                                                 hipSuccess && cus > 0) {
       const int budget = cus / (int)s.H;
       int G[2];
-      if (budget > 0 && plan_parts(s, sides, nsides, budget, G)) {
-        if (launch_kpp_coop(s, sides, nsides, G, seed, st) == hipSuccess) return hipSuccess;
+      // in order: both sides in one launch with 512-thread parts; one launch per side with
+      // 512-thread parts; both sides with 1024-thread parts; per side the narrowest parts that fit
+      if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreads, G)) {
+        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreads, seed, st) == hipSuccess) return hipSuccess;
         (void)hipGetLastError();
-      } else if (nsides == 2 && budget > 0 && plan_parts(s, sides, 1, budget, G) &&
-                 plan_parts(s, sides + 1, 1, budget, G + 1)) {
-        // both sides do not fit at once: one launch per side
-        if (launch_kpp_coop(s, sides, 1, G, seed, st) == hipSuccess &&
-            launch_kpp_coop(s, sides + 1, 1, G + 1, seed, st) == hipSuccess)
+      } else if (budget > 0 && nsides == 2 && plan_parts(s, sides, 1, budget, kCoopThreads, G) &&
+                 plan_parts(s, sides + 1, 1, budget, kCoopThreads, G + 1)) {
+        if (launch_kpp_coop(s, sides, 1, G, kCoopThreads, seed, st) == hipSuccess &&
+            launch_kpp_coop(s, sides + 1, 1, G + 1, kCoopThreads, seed, st) == hipSuccess)
           return hipSuccess;
         (void)hipGetLastError();
+      } else if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreadsWide, G)) {
+        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreadsWide, seed, st) == hipSuccess) return hipSuccess;
+        (void)hipGetLastError();
+      } else if (budget > 0) {
+        int nt[2] = {0, 0};
+        for (int q = 0; q < nsides; ++q)
+          for (int w : {kCoopThreads, kCoopThreadsWide})
+            if (!nt[q] && plan_parts(s, sides + q, 1, budget, w, G + q)) nt[q] = w;
+        if (nt[0] && (nsides == 1 || nt[1])) {
+          bool ok = true;
+          for (int q = 0; q < nsides && ok; ++q)
+            ok = launch_kpp_coop(s, sides + q, 1, G + q, nt[q], seed, st) == hipSuccess;
+          if (ok) return hipSuccess;
+          (void)hipGetLastError();
+        }
       }
     }
   }
