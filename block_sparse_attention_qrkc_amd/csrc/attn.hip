@@ -509,7 +509,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       for (int kk = 0; kk < KS; ++kk) sacc[st] = mfma32(ka[kk], qb[kk], sacc[st]);
     }
     const int nvalid = L - v0;
-    if (nvalid < BN) {
+    if (__builtin_expect(nvalid < BN, 0)) {
 #pragma unroll
       for (int st = 0; st < NSUB; ++st)
 #pragma unroll
