@@ -190,14 +190,21 @@ def run_sweep(args, bsa, w0, dev, log):
 
 
 def run_schedule(args, bsa, w, dev, log):
-    """The long clip's denoising schedule: inputs drift every step; full K-means (k-means++ and
-    ``iters`` iterations) at the anchor steps, warm start from the previous centroids with
-    ``warm_iters`` iterations otherwise."""
+    """The long clip's denoising schedule (PARK-p2 Table 9: how often the retrieval is recomputed).
+    Inputs drift every step. Two policies on the same inputs:
+    * warm: full K-means (k-means++ and ``iters`` iterations) at the anchor steps, warm start from the
+      previous centroids with ``warm_iters`` iterations otherwise (HyperVAttention's anchor/subset
+      idea, with every token updated);
+    * reuse: the anchor step's clustering and block selection are kept until the next anchor; the
+      steps in between run the sparse attention only.
+    Each step reports ms, token density and recall (from the kernel's log-sum-exp against dense
+    attention of the same step)."""
     Q, K, V, Qm, Km = synth.make_qkv(w, seed=args.seed, device=dev, keep_fp32=True)
     ws = bsa.Workspace()
     qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
     kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
-    steps = []
+    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse")
+    steps, kept = [], None
     for t in range(w.steps):
         if t > 0:
             Q.copy_(synth.drift_step(w, Qm, args.seed, t, 0))
@@ -206,35 +213,53 @@ def run_schedule(args, bsa, w, dev, log):
         init = bsa.PARK_INIT_KMEANSPP if full else bsa.PARK_INIT_WARM
         iters = w.iters if full else w.warm_iters
         fn = lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, iters, w.p, seed=args.seed, init=init,
-                                      q_centroids=qcent, k_centroids=kcent, outputs=("q_offsets", "sel_keys"),
-                                      ws=ws)
-        if full:
-            r = fn()  # also the warm start of the next steps
-            torch.cuda.synchronize()
-            a, b = _events()
-            a.record()
-            r = bsa.park_forward(Q, K, V, w.cq, w.ck, iters, w.p, seed=args.seed, init=init, q_centroids=qcent,
-                                 k_centroids=kcent, outputs=("q_offsets", "sel_keys"), ws=ws)
-            b.record()
-        else:
-            qs, ks = qcent.clone(), kcent.clone()
-            r = fn()
-            torch.cuda.synchronize()
-            qcent.copy_(qs)
-            kcent.copy_(ks)
-            a, b = _events()
-            a.record()
-            r = fn()
-            b.record()
+                                      q_centroids=qcent, k_centroids=kcent, outputs=outs, ws=ws)
+        qs, ks = qcent.clone(), kcent.clone()
+        fn()  # warm-up call; the timed call repeats it from the same centroids
+        torch.cuda.synchronize()
+        qcent.copy_(qs)
+        kcent.copy_(ks)
+        a, b = _events()
+        a.record()
+        r = fn()
+        b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b)
+        if full:
+            kept = {k: r[k].clone() for k in ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols",
+                                                "sel_keys")}
+        # dense log-sum-exp of this step: every key cluster selected
+        cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+        cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+        _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
+                                     cols_all, ws=ws)
+        rec = torch.exp(r["lse"] - ld).mean(dim=1)
         computed, padded, dense = selection_stats(w, r)
-        steps.append({"step": t, "full_kmeans": full, "iters": iters, "ms": round(ms, 3),
-                      "token_density": round(computed / dense, 5)})
-        log(f"schedule {steps[-1]}")
-    tot = sum(x["ms"] for x in steps)
-    print(json.dumps({"schedule": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "steps": steps,
-                      "total_ms": round(tot, 3), "ms_per_step": round(tot / len(steps), 3)}), flush=True)
+        entry = {"step": t, "full_kmeans": full, "iters": iters,
+                 "warm": {"ms": round(ms, 3), "token_density": round(computed / dense, 5),
+                          "recall_mean": round(rec.mean().item(), 4), "recall_worst": round(rec.min().item(), 4)}}
+        if full:
+            entry["reuse"] = dict(entry["warm"])
+        else:
+            fa = lambda: bsa.park_sparse_attn(Q, K, V, kept["q_perm"], kept["q_offsets"], kept["k_perm"],
+                                              kept["k_offsets"], kept["counts"], kept["cols"], ws=ws)
+            fa()
+            torch.cuda.synchronize()
+            a, b = _events()
+            a.record()
+            _, lr = fa()
+            b.record()
+            torch.cuda.synchronize()
+            rr = torch.exp(lr - ld).mean(dim=1)
+            c2, _, d2 = selection_stats(w, kept)
+            entry["reuse"] = {"ms": round(a.elapsed_time(b), 3), "token_density": round(c2 / d2, 5),
+                              "recall_mean": round(rr.mean().item(), 4), "recall_worst": round(rr.min().item(), 4)}
+        steps.append(entry)
+        log(f"schedule {entry}")
+    tot = {k: round(sum(x[k]["ms"] for x in steps), 3) for k in ("warm", "reuse")}
+    print(json.dumps({"schedule": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "p": w.p,
+                      "anchors": list(w.anchors), "steps": steps, "total_ms": tot,
+                      "ms_per_step": {k: round(v / len(steps), 3) for k, v in tot.items()}}), flush=True)
 
 
 def main():
