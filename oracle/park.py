@@ -19,8 +19,8 @@ __all__ = [
     "round_f32", "round_bf16",
     "qrkc_metric", "metric_distance", "candidate_rows", "kmeanspp", "consumed_centroids",
     "assign", "assign_near_tie", "cluster_order", "update", "lloyd", "cluster",
-    "pama", "select_topp", "key_runs", "sparse_attention", "dense_attention",
-    "recall", "density", "estimator_maps", "tv_to_full", "raw_key_mse", "qk_score_sq_error",
+    "pama", "select_topp", "topk_count", "select_topk", "key_runs", "sparse_attention", "dense_attention",
+    "recall", "density", "estimator_maps", "estimator_block_maps", "tv_to_full", "raw_key_mse", "qk_score_sq_error",
     "centered_log_mass_error", "retrieve", "forward",
 ]
 
@@ -374,6 +374,40 @@ def select_topp(A, k_sizes, p, return_margin=False):
     return mask, counts, cols, keys
 
 
+def topk_count(k_sizes, rho):
+    """Blocks a top-k row keeps at retrieval ratio rho (PARK-p2 Table 10: top-k retrieval at a fixed
+    ratio rho = 0.1). Reading: rho is the share of the head's non-empty key blocks, rounded up,
+    k = ceil(rho * C_ne - 1e-9) clamped to [1, C_ne] (the 1e-9 keeps an exact product such as
+    0.3 * 10 from rounding up to the next integer)."""
+    c_ne = int((np.asarray(k_sizes) > 0).sum())
+    if c_ne == 0:
+        return 0
+    return int(min(max(math.ceil(rho * c_ne - 1e-9), 1), c_ne))
+
+
+def select_topk(A, k_sizes, rho):
+    """Row-wise top-k cut of the block map: every row with positive importance keeps the k
+    non-empty key blocks of highest importance (ties to the lower index), k = topk_count(rho);
+    rows without positive importance (empty query blocks) keep nothing. Returns the same
+    (mask, counts, cols, keys) as select_topp."""
+    A = np.asarray(A, dtype=np.float64)
+    k_sizes = np.asarray(k_sizes, dtype=np.int64)
+    cq, ck = A.shape
+    k = topk_count(k_sizes, rho)
+    mask = np.zeros((cq, ck), dtype=bool)
+    live = np.flatnonzero(k_sizes > 0)
+    for i in range(cq):
+        row = A[i]
+        if not (row > 0).any():
+            continue
+        order = live[np.lexsort((live, -row[live]))]
+        mask[i, order[:k]] = True
+    counts = mask.sum(axis=1).astype(np.int32)
+    cols = [np.flatnonzero(mask[i]).astype(np.int32) for i in range(cq)]
+    keys = (mask * k_sizes[None, :]).sum(axis=1).astype(np.int64)
+    return mask, counts, cols, keys
+
+
 def key_runs(cols, k_offsets):
     """Key ranges in sorted-key positions that one query block attends to: selected clusters in
     ascending order, adjacent clusters merged into one run. Returns a list of (start, end)."""
@@ -506,6 +540,34 @@ def estimator_maps(Q, K, q_labels, k_labels, q_cent, k_cent, scale):
         "CF": _block_sum(softmax(scale * qc @ K.T), k_labels, ck),
         "FC": softmax(scale * Q @ kc.T + logn[None, :]),
     }
+
+
+def estimator_block_maps(Q, K, q_perm, q_offsets, q_cent, k_perm, k_offsets, k_cent, scale):
+    """Block maps [Cq, Ck] under the four query/key representations of Table 1 (PARK-p2): each query
+    block's row is the mean over its queries of the per-query block distributions of
+    estimator_maps, so FC is the PAMA map; the centroid-query rows (CC, CF) are the same for every
+    query of a block. Centroids enter as given (the caller passes them as consumed). An empty query
+    block gets a zero row."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    cq = len(q_offsets) - 1
+    ck = len(k_offsets) - 1
+    q_labels = np.empty(Q.shape[0], dtype=np.int64)
+    for i in range(cq):
+        q_labels[np.asarray(q_perm[q_offsets[i]:q_offsets[i + 1]])] = i
+    k_labels = np.empty(K.shape[0], dtype=np.int64)
+    for j in range(ck):
+        k_labels[np.asarray(k_perm[k_offsets[j]:k_offsets[j + 1]])] = j
+    rows = estimator_maps(Q, K, q_labels, k_labels, q_cent, k_cent, scale)
+    out = {}
+    for name, R in rows.items():
+        A = np.zeros((cq, ck))
+        for i in range(cq):
+            t = np.asarray(q_perm[q_offsets[i]:q_offsets[i + 1]])
+            if t.size:
+                A[i] = R[t].mean(axis=0)
+        out[name] = A
+    return out
 
 
 def tv_to_full(est, ff):

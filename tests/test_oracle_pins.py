@@ -340,6 +340,48 @@ def test_topp_hand_worked():
         assert np.array_equal(mask, np.array([[j in c for j in range(5)] for c in case["cols"]]))
 
 
+def test_topk_hand_worked():
+    g = _golden("topk_hand.json")
+    A = np.array(g["map"])
+    ks = np.array(g["k_sizes"])
+    for case in g["cases"]:
+        assert O.topk_count(ks, case["rho"]) == case["k"]
+        mask, counts, cols, keys = O.select_topk(A, ks, case["rho"])
+        assert [c.tolist() for c in cols] == case["cols"], case["rho"]
+        assert keys.tolist() == case["keys"]
+        assert counts.tolist() == [len(c) for c in case["cols"]]
+
+
+def test_topk_count_guards_rounding():
+    assert O.topk_count([1] * 10, 0.3) == 3       # 0.3 * 10 is 3.0000000000000004 in fp64
+    assert O.topk_count([1] * 500, 0.1) == 50
+    assert O.topk_count([1] * 7, 0.1) == 1
+    assert O.topk_count([0, 0], 0.5) == 0
+
+
+def test_topk_is_max_mass_set_bruteforce():
+    """The kept set has the largest importance among all k-subsets of non-empty blocks, and is the
+    lexicographically smallest among the sets that tie with it."""
+    rng = np.random.default_rng(4)
+    for trial in range(40):
+        ck = int(rng.integers(2, 8))
+        sizes = rng.integers(0, 3, ck)
+        if not (sizes > 0).any():
+            sizes[0] = 1
+        A = np.round(rng.random((3, ck)), 1)  # coarse values: ties happen
+        A[:, sizes == 0] = 0.0
+        rho = float(rng.choice([0.1, 0.3, 0.5, 0.7, 1.0]))
+        k = O.topk_count(sizes, rho)
+        live = [j for j in range(ck) if sizes[j] > 0]
+        _, _, cols, _ = O.select_topk(A, sizes, rho)
+        for i in range(3):
+            if not (A[i] > 0).any():
+                assert cols[i].size == 0
+                continue
+            best = max(itertools.combinations(live, k), key=lambda c: (sum(A[i, list(c)]), [-x for x in c]))
+            assert cols[i].tolist() == sorted(best), (trial, i)
+
+
 def test_topp_is_minimal_max_mass_set_bruteforce():
     """P2 by enumeration: the kept set reaches p, no smaller set does, and among sets of its size it
     has the largest mass (ties broken toward lower indices)."""
@@ -498,6 +540,58 @@ def test_density_definitions():
     b, t = O.density(mask, [2, 3], [1, 4])
     assert b == 3 / 4
     assert t == (2 * 1 + 3 * 1 + 3 * 4) / 25
+
+
+def _estimator_case(rng, n=48, d=6, cq=5, ck=7):
+    Q = rng.normal(size=(n, d))
+    K = rng.normal(size=(n, d))
+    ql = rng.integers(0, cq, n)
+    kl = rng.integers(0, ck, n)
+    qp, qo = O.cluster_order(ql, cq)
+    kp, ko = O.cluster_order(kl, ck)
+    qc = np.stack([Q[ql == i].mean(0) if (ql == i).any() else np.zeros(d) for i in range(cq)])
+    kc = np.stack([K[kl == j].mean(0) if (kl == j).any() else np.zeros(d) for j in range(ck)])
+    return Q, K, qp, qo, qc, kp, ko, kc, np.diff(ko)
+
+
+def test_estimator_block_maps_fc_is_pama_and_rows_are_distributions():
+    rng = np.random.default_rng(8)
+    Q, K, qp, qo, qc, kp, ko, kc, ks = _estimator_case(rng)
+    m = O.estimator_block_maps(Q, K, qp, qo, qc, kp, ko, kc, 0.4)
+    np.testing.assert_allclose(m["FC"], O.pama(Q, qp, qo, kc, ks, 0.4), atol=1e-13)
+    live = np.diff(qo) > 0
+    for name, A in m.items():
+        np.testing.assert_allclose(A[live].sum(1), 1.0, atol=1e-12, err_msg=name)
+        assert np.all(A[~live] == 0) and np.all(A[:, ks == 0] == 0), name
+
+
+def test_estimator_block_maps_collapse_in_the_limits():
+    """Singleton key blocks make key centroids exact (FC = FF, CC = CF); singleton query blocks make
+    query centroids exact (CF = FF, CC = FC); identical keys in every block make the size-weighted
+    key-centroid softmax exact (FC = FF, CC = CF)."""
+    rng = np.random.default_rng(9)
+    n, d = 24, 5
+    Q = rng.normal(size=(n, d))
+    K = rng.normal(size=(n, d))
+    ql = rng.integers(0, 4, n)
+    qp, qo = O.cluster_order(ql, 4)
+    qc = np.stack([Q[ql == i].mean(0) for i in range(4)])
+    kp, ko = O.cluster_order(np.arange(n), n)  # one key per block
+    m = O.estimator_block_maps(Q, K, qp, qo, qc, kp, ko, K.copy(), 0.5)
+    np.testing.assert_allclose(m["FC"], m["FF"], atol=1e-13)
+    np.testing.assert_allclose(m["CC"], m["CF"], atol=1e-13)
+    kl = rng.integers(0, 5, n)
+    kp, ko = O.cluster_order(kl, 5)
+    kc = np.stack([K[kl == j].mean(0) for j in range(5)])
+    qp1, qo1 = O.cluster_order(np.arange(n), n)  # one query per block
+    m = O.estimator_block_maps(Q, K, qp1, qo1, Q.copy(), kp, ko, kc, 0.5)
+    np.testing.assert_allclose(m["CF"], m["FF"], atol=1e-13)
+    np.testing.assert_allclose(m["CC"], m["FC"], atol=1e-13)
+    base = rng.normal(size=(5, d))
+    K2 = base[kl]  # every key equals its block's centroid
+    m = O.estimator_block_maps(Q, K2, qp, qo, qc, kp, ko, base, 0.5)
+    np.testing.assert_allclose(m["FC"], m["FF"], atol=1e-12)
+    np.testing.assert_allclose(m["CC"], m["CF"], atol=1e-12)
 
 
 def test_tv_zero_for_full_and_estimators_are_distributions():
