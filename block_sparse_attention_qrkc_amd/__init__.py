@@ -17,7 +17,8 @@ import torch
 
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PARK_BF16, PARK_EHIP, PARK_EINVAL, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_CLUSTER_Q,
-    PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN,
+    PARK_ENTRY_ESTIMATOR, PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP,
+    PARK_ENTRY_SPARSE_ATTN, PARK_EST_CC, PARK_EST_CF, PARK_EST_FC, PARK_EST_FF,
     PARK_EUCLID, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_F32, PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_OK,
     PARK_QRKC, PARK_SIDE_K, PARK_SIDE_Q, ParkError, Workspace, lib, make_params, make_shape, park_forward_outputs,
     park_params, park_shape, workspace_bytes,
@@ -25,7 +26,8 @@ from ._lib import (  # noqa: F401
 from ._lib import _check, _ptr, _stream, _ws
 
 __all__ = [
-    "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_select_topp", "park_sparse_attn",
+    "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
+    "park_select_topk", "park_sparse_attn",
     "park_permute_rows", "park_unpermute_rows", "park_forward", "park_version", "ParkError", "lib",
 ]
 
@@ -92,6 +94,36 @@ def park_select_topp(map, k_offsets, p, stream=None):
     _check(lib().park_select_topp(_ptr(map), H, cq, ck, _ptr(k_offsets), float(p), _ptr(mask), _ptr(counts),
                                   _ptr(cols), _ptr(sel), _stream(stream)))
     return {"mask": mask, "counts": counts, "cols": cols, "sel_keys": sel}
+
+
+def park_select_topk(map, k_offsets, rho, stream=None):
+    """Top-k cut of every map row at retrieval ratio rho. Returns dict(mask, counts, cols, sel_keys)."""
+    H, cq, ck = map.shape
+    dev = map.device
+    mask = torch.empty(H, cq, ck, dtype=torch.uint8, device=dev)
+    counts = torch.empty(H, cq, dtype=torch.int32, device=dev)
+    cols = torch.empty(H, cq, ck, dtype=torch.int32, device=dev)
+    sel = torch.empty(H, cq, dtype=torch.int64, device=dev)
+    _check(lib().park_select_topk(_ptr(map), H, cq, ck, _ptr(k_offsets), float(rho), _ptr(mask), _ptr(counts),
+                                  _ptr(cols), _ptr(sel), _stream(stream)))
+    return {"mask": mask, "counts": counts, "cols": cols, "sel_keys": sel}
+
+
+def park_estimator_map(mode, k_offsets, q=None, k=None, q_perm=None, q_offsets=None, q_centroids=None, k_perm=None,
+                       k_centroids=None, scale=0.0, out=None, ws=None, stream=None):
+    """Block map [heads, cq, ck] float32 under a PARK_EST_* query/key representation (Table 1). The
+    shape and dtype come from q (or k when q is not given); q_offsets is read in every mode."""
+    ref = q if q is not None else k
+    sh = make_shape(ref)
+    cq = q_offsets.shape[1] - 1
+    ck = k_offsets.shape[1] - 1
+    M = out if out is not None else torch.empty(sh.heads, cq, ck, dtype=torch.float32, device=ref.device)
+    prm = make_params(cq=cq, ck=ck)
+    wp, wn = _ws(PARK_ENTRY_ESTIMATOR, sh, prm, ref.device, ws)
+    _check(lib().park_estimator_map(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(q_perm), _ptr(q_offsets), cq,
+                                    _ptr(q_centroids), _ptr(k_perm), _ptr(k_offsets), ck, _ptr(k_centroids),
+                                    int(mode), float(scale), _ptr(M), wp, wn, _stream(stream)))
+    return M
 
 
 def park_sparse_attn(q, k, v, q_perm, q_offsets, k_perm, k_offsets, counts, cols, scale=0.0, out=None, lse=True,

@@ -80,16 +80,33 @@ __device__ __forceinline__ void fetch_centroids(const uint16_t* kh, const float*
   *ln = j < ck ? v : -INFINITY;
 }
 
-template <int D>
+// B operand fragments of key tile ct in cluster order (key k_perm[ct * 16 + l % 16], dims kk * 32 +
+// g * 8 .. +7): log-weight 0, -inf past the last key (row clamped).
+template <int KS>
+__device__ __forceinline__ void fetch_keys(const uint16_t* Kh, const int32_t* kp, int64_t nk, int ct, int l, int g,
+                                          u32x4_t* bv, float* ln) {
+  const int64_t p = (int64_t)ct * 16 + l % 16;
+  const int64_t row = kp[p < nk ? p : nk - 1];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    bv[kk] = *reinterpret_cast<const u32x4_t*>(Kh + row * (KS * 32) + kk * 32 + g * 8);
+  *ln = p < nk ? 0.f : -INFINITY;
+}
+
+template <int D, bool FULL>
 __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q, int64_t N,
                                                  const int32_t* __restrict__ q_perm,
                                                  const int32_t* __restrict__ q_off, int cq,
                                                  const uint16_t* __restrict__ khat, const float* __restrict__ logn,
                                                  int ck, float scale, const int32_t* __restrict__ chunk_base,
-                                                 int max_chunks, float* __restrict__ partial) {
+                                                 int max_chunks, float* __restrict__ partial,
+                                                 const uint16_t* __restrict__ K, int64_t Nk,
+                                                 const int32_t* __restrict__ k_perm,
+                                                 const int32_t* __restrict__ k_off) {
   constexpr int KS = D / 32;
   constexpr int TW = 4;  // 16-query tiles per wave: each centroid fragment feeds TW MFMAs
   __shared__ float colsum[4][kMaxClusters];
+  __shared__ int koff[FULL ? kMaxClusters + 1 : 1];
   const int h = blockIdx.y;
   const int c = blockIdx.x;
   const int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
@@ -104,9 +121,21 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
   const uint16_t* Qh = Q + (int64_t)h * N * D;
   const int32_t* ph = q_perm + (int64_t)h * N;
   const uint16_t* kh = khat + (int64_t)h * ck * D;
-  const float* lnh = logn + (int64_t)h * ck;
-  const int nct = (ck + 15) / 16;
+  const float* lnh = FULL ? nullptr : logn + (int64_t)h * ck;
+  const uint16_t* Kh = FULL ? K + (int64_t)h * Nk * D : nullptr;
+  const int32_t* kph = FULL ? k_perm + (int64_t)h * Nk : nullptr;
+  // columns: the key centroids, or (FULL) every key in cluster order, whose weights are summed per
+  // key cluster
+  const int nct = FULL ? (int)((Nk + 15) / 16) : (ck + 15) / 16;
+  auto fetch = [&](int ct, u32x4_t* bv, float* ln) __attribute__((always_inline)) {
+    if constexpr (FULL)
+      fetch_keys<KS>(Kh, kph, Nk, ct, l, g, bv, ln);
+    else
+      fetch_centroids<KS>(kh, lnh, ck, ct, l, g, bv, ln);
+  };
   for (int j = threadIdx.x; j < 4 * kMaxClusters; j += 256) (&colsum[0][0])[j] = 0.f;
+  if constexpr (FULL)
+    for (int j = threadIdx.x; j <= ck; j += 256) koff[j] = k_off[(int64_t)h * (ck + 1) + j];
   __syncthreads();
 
   const int w0 = row0 + w * 16 * TW;  // this wave's first row
@@ -141,11 +170,11 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       }
     u32x4_t bv[KS];
     float ln;
-    fetch_centroids<KS>(kh, lnh, ck, 0, l, g, bv, &ln);
+    fetch(0, bv, &ln);
     for (int ct = 0; ct < nct; ++ct) {
       u32x4_t bn[KS];
       float lnn;
-      fetch_centroids<KS>(kh, lnh, ck, min(ct + 1, nct - 1), l, g, bn, &lnn);
+      fetch(min(ct + 1, nct - 1), bn, &lnn);
       float lg[TW][4], dmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
@@ -197,12 +226,13 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       }
     }
     // pass 2: accumulate normalised weights 2^(lg2 - off) into the wave's column sums
-    fetch_centroids<KS>(kh, lnh, ck, 0, l, g, bv, &ln);
+    fetch(0, bv, &ln);
+    int cl = 0;  // FULL: the key cluster of this lane's column (advances with the tiles)
     for (int ct = 0; ct < nct; ++ct) {
       const int j = ct * 16 + l % 16;
       u32x4_t bn[KS];
       float lnn;
-      fetch_centroids<KS>(kh, lnh, ck, min(ct + 1, nct - 1), l, g, bn, &lnn);
+      fetch(min(ct + 1, nct - 1), bn, &lnn);
       float cs = 0.f;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
@@ -214,7 +244,12 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       }
       cs += __shfl_xor(cs, 16, kWave);
       cs += __shfl_xor(cs, 32, kWave);
-      if (g == 0 && j < ck) colsum[w][j] = cs;
+      if constexpr (FULL) {
+        while (cl < ck && koff[cl + 1] <= j) ++cl;
+        if (g == 0 && j < Nk) atomicAdd(&colsum[w][cl], cs);
+      } else {
+        if (g == 0 && j < ck) colsum[w][j] = cs;
+      }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) bv[kk] = bn[kk];
       ln = lnn;
@@ -305,13 +340,13 @@ hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, cons
     const dim3 pg((unsigned)ceil_div((int64_t)ck * s.D, 256), (unsigned)s.H);
     pama_prep<<<pg, 256, 0, st>>>(k_cent, k_offsets, ck, (int)s.D, static_cast<uint16_t*>(khat), logn);
     if (s.D == 128)
-      pama_bf16<128><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
-                                           static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base, maxc,
-                                           partial);
+      pama_bf16<128, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+                                                  static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base,
+                                                  maxc, partial, nullptr, 0, nullptr, nullptr);
     else
-      pama_bf16<64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
-                                          static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base, maxc,
-                                          partial);
+      pama_bf16<64, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+                                                 static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base,
+                                                 maxc, partial, nullptr, 0, nullptr, nullptr);
   } else {
     if (s.D == 128)
       pama_f32<128><<<grid, 256, 0, st>>>(static_cast<const float*>(q), s.N, q_perm, q_offsets, cq, k_cent,
@@ -320,6 +355,61 @@ hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, cons
       pama_f32<64><<<grid, 256, 0, st>>>(static_cast<const float*>(q), s.N, q_perm, q_offsets, cq, k_cent,
                                          k_offsets, ck, scale, chunk_base, maxc, partial);
   }
+  pama_reduce<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(partial, q_offsets, chunk_base, cq, ck, maxc, map);
+  return hipGetLastError();
+}
+
+namespace {
+// Centroid queries for the centroid-query estimators: rows[h][i] = bf16(cent[h][i]) (as consumed by
+// the MFMA); each non-empty query cluster owns one row (perm lists them in order, offsets count
+// them), an empty one owns none, so its map row stays zero.
+__global__ __launch_bounds__(1024) void centroid_queries(const float* __restrict__ cent, int C, int D,
+                                                         const int32_t* __restrict__ q_offsets,
+                                                         uint16_t* __restrict__ rows, int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int scratch[17];
+  const int h = blockIdx.x;
+  const int32_t* qo = q_offsets + (int64_t)h * (C + 1);
+  for (int64_t e = threadIdx.x; e < (int64_t)C * D; e += 1024)
+    rows[(int64_t)h * C * D + e] = (uint16_t)f32_to_bf16_bits(cent[(int64_t)h * C * D + e]);
+  const int per = (C + 1023) / 1024;
+  const int i0 = threadIdx.x * per;
+  int local = 0;
+  for (int k = 0; k < per; ++k)
+    if (i0 + k < C) local += qo[i0 + k + 1] > qo[i0 + k];
+  int total;
+  int run = block_exclusive_scan(local, scratch, &total);
+  for (int k = 0; k < per; ++k) {
+    const int i = i0 + k;
+    if (i < C) {
+      offsets[(int64_t)h * (C + 1) + i] = run;
+      if (qo[i + 1] > qo[i]) perm[(int64_t)h * C + run++] = i;
+    }
+  }
+  if (threadIdx.x == 0) offsets[(int64_t)h * (C + 1) + C] = total;
+}
+}  // namespace
+
+hipError_t launch_centroid_queries(int64_t H, int C, int D, const float* cent, const int32_t* q_offsets, void* rows,
+                                   int32_t* perm, int32_t* offsets, hipStream_t st) {
+  centroid_queries<<<(unsigned)H, 1024, 0, st>>>(cent, C, D, q_offsets, static_cast<uint16_t*>(rows), perm, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass(const Dims& s, const void* q, const int32_t* q_perm, const int32_t* q_offsets, int cq,
+                             const void* k, int64_t nk, const int32_t* k_perm, const int32_t* k_offsets, int ck,
+                             float scale, float* map, int32_t* chunk_base, float* partial, hipStream_t st) {
+  const int maxc = (int)pama_max_chunks(s, cq);
+  pama_chunks<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, chunk_base);
+  const dim3 grid((unsigned)maxc, (unsigned)s.H);
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
+  const uint16_t* kh = static_cast<const uint16_t*>(k);
+  if (s.D == 128)
+    pama_bf16<128, true><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
+                                               maxc, partial, kh, nk, k_perm, k_offsets);
+  else
+    pama_bf16<64, true><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
+                                              maxc, partial, kh, nk, k_perm, k_offsets);
   pama_reduce<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(partial, q_offsets, chunk_base, cq, ck, maxc, map);
   return hipGetLastError();
 }

@@ -132,6 +132,34 @@ MapWs plan_map(Carver& cv, const park::Dims& s, int cq, int ck) {
   return w;
 }
 
+// Estimator maps: centroid-query rows (CC, CF) and the map workspace sized for the query rows used.
+struct EstWs {
+  uint16_t* qrows = nullptr;
+  int32_t* qperm = nullptr;
+  int32_t* qoff = nullptr;
+  MapWs map;
+};
+EstWs plan_estimator(Carver& cv, const park::Dims& s, int cq, int ck, bool centroid_queries) {
+  EstWs w;
+  if (centroid_queries) {
+    w.qrows = cv.take<uint16_t>((size_t)(s.H * cq * s.D));
+    w.qperm = cv.take<int32_t>((size_t)(s.H * cq));
+    w.qoff = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
+    park::Dims sq = s;
+    sq.N = cq;
+    w.map = plan_map(cv, sq, cq, ck);
+  } else {
+    w.map = plan_map(cv, s, cq, ck);
+  }
+  return w;
+}
+size_t estimator_ws_bytes(const park::Dims& s, int cq, int ck) {
+  Carver a(nullptr), b(nullptr);
+  plan_estimator(a, s, cq, ck, false);
+  plan_estimator(b, s, cq, ck, true);
+  return a.off > b.off ? a.off : b.off;
+}
+
 struct AttnWs {
   int32_t* tile_base;
   int32_t* gather;
@@ -298,6 +326,9 @@ size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_p
         if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
         plan_attn(cv, s, params->cq, params->ck);
         return cv.off;
+      case PARK_ENTRY_ESTIMATOR:
+        if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
+        return estimator_ws_bytes(s, params->cq, params->ck);
       case PARK_ENTRY_FORWARD:
         if (check_params(s, params, true) != PARK_OK) return 0;
         return forward_ws_bytes(s, *params);
@@ -394,6 +425,66 @@ park_status park_retrieve_map(const park_shape* shape, const void* q, const int3
   }
 }
 
+park_status park_estimator_map(const park_shape* shape, const void* q, const void* k, const int32_t* q_perm,
+                               const int32_t* q_offsets, int32_t cq, const float* q_centroids, const int32_t* k_perm,
+                               const int32_t* k_offsets, int32_t ck, const float* k_centroids, int32_t mode,
+                               float scale, float* map, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    if (mode < PARK_EST_FC || mode > PARK_EST_FF) return fail(PARK_EINVAL, "mode must be a park_estimator, got %d", mode);
+    if (mode != PARK_EST_FC && !s.bf16) return fail(PARK_EUNSUPPORTED, "estimator modes CC, CF and FF need bf16 data");
+    PARK_TRY(check_clusters(s, cq, "cq"));
+    PARK_TRY(check_clusters(s, ck, "ck"));
+    if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
+    const bool full_q = mode == PARK_EST_FC || mode == PARK_EST_FF;
+    const bool full_k = mode == PARK_EST_CF || mode == PARK_EST_FF;
+    PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
+    if (full_q) {
+      PARK_TRY(check_ptr(q, "q", 16));
+      PARK_TRY(check_ptr(q_perm, "q_perm", 4));
+    } else {
+      PARK_TRY(check_ptr(q_centroids, "q_centroids", 4));
+    }
+    if (full_k) {
+      PARK_TRY(check_ptr(k, "k", 16));
+      PARK_TRY(check_ptr(k_perm, "k_perm", 4));
+    } else {
+      PARK_TRY(check_ptr(k_centroids, "k_centroids", 4));
+    }
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(map, "map", 4));
+    PARK_TRY(check_ws(ws, ws_bytes, estimator_ws_bytes(s, cq, ck)));
+    Carver cv(ws);
+    EstWs w = plan_estimator(cv, s, cq, ck, !full_q);
+    hipStream_t st = (hipStream_t)stream;
+    const float sc = resolve_scale(scale, s.D);
+    hipError_t e = hipSuccess;
+    park::Dims sq = s;
+    const void* qr = q;
+    const int32_t* qp = q_perm;
+    const int32_t* qo = q_offsets;
+    if (!full_q) {  // one bf16 centroid row per query cluster
+      sq.N = cq;
+      e = park::launch_centroid_queries(s.H, cq, (int)s.D, q_centroids, q_offsets, w.qrows, w.qperm, w.qoff, st);
+      qr = w.qrows;
+      qp = w.qperm;
+      qo = w.qoff;
+    }
+    if (e == hipSuccess) {
+      if (full_k)
+        e = park::launch_block_mass(sq, qr, qp, qo, cq, k, s.N, k_perm, k_offsets, ck, sc, map, w.map.chunk_base,
+                                    w.map.partial, st);
+      else
+        e = park::launch_pama(sq, qr, qp, qo, cq, k_centroids, k_offsets, ck, sc, map, w.map.khat, w.map.logn,
+                              w.map.chunk_base, w.map.partial, st);
+    }
+    return hip_check(e, "park_estimator_map");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_estimator_map: internal error");
+  }
+}
+
 park_status park_select_topp(const float* map, int64_t heads, int32_t cq, int32_t ck, const int32_t* k_offsets,
                              double p, uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys,
                              void* stream) {
@@ -412,6 +503,27 @@ park_status park_select_topp(const float* map, int64_t heads, int32_t cq, int32_
                      "park_select_topp");
   } catch (...) {
     return fail(PARK_EHIP, "park_select_topp: internal error");
+  }
+}
+
+park_status park_select_topk(const float* map, int64_t heads, int32_t cq, int32_t ck, const int32_t* k_offsets,
+                             double rho, uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys,
+                             void* stream) {
+  try {
+    if (heads < 1 || heads > 65535) return fail(PARK_EINVAL, "heads must be in [1, 65535]");
+    if (cq < 1 || cq > park::kMaxClusters) return fail(PARK_EINVAL, "cq must be in [1, %d]", park::kMaxClusters);
+    if (ck < 1 || ck > park::kMaxClusters) return fail(PARK_EINVAL, "ck must be in [1, %d]", park::kMaxClusters);
+    if (!(rho >= 0.0 && rho <= 1.0)) return fail(PARK_EINVAL, "rho must be in [0, 1], got %g", rho);
+    PARK_TRY(check_ptr(map, "map", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(counts, "counts", 4));
+    PARK_TRY(check_ptr(cols, "cols", 4));
+    if (sel_keys) PARK_TRY(check_ptr(sel_keys, "sel_keys", 8));
+    return hip_check(park::launch_select_topk(map, heads, cq, ck, k_offsets, rho, mask, counts, cols, sel_keys,
+                                              (hipStream_t)stream),
+                     "park_select_topk");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_select_topk: internal error");
   }
 }
 

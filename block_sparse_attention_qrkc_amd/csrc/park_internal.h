@@ -58,9 +58,19 @@ hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, cons
                        const float* k_cent, const int32_t* k_offsets, int ck, float scale, float* map,
                        void* khat, float* logn, int32_t* chunk_base, float* partial, hipStream_t st);
 int64_t pama_max_chunks(const Dims& s, int cq);
+// Block masses over every key (bf16 data): map[h, i, j] = mean over the rows of query cluster i of
+// the softmax mass (over all nk keys) that falls on key cluster j. Workspace as launch_pama.
+hipError_t launch_block_mass(const Dims& s, const void* q, const int32_t* q_perm, const int32_t* q_offsets, int cq,
+                             const void* k, int64_t nk, const int32_t* k_perm, const int32_t* k_offsets, int ck,
+                             float scale, float* map, int32_t* chunk_base, float* partial, hipStream_t st);
+// bf16 centroid rows [H, C, D]; one row per non-empty cluster of q_offsets (perm, offsets).
+hipError_t launch_centroid_queries(int64_t H, int C, int D, const float* cent, const int32_t* q_offsets, void* rows,
+                                   int32_t* perm, int32_t* offsets, hipStream_t st);
 
 // select.hip
 hipError_t launch_select_topp(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double p,
+                              uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st);
+hipError_t launch_select_topk(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double rho,
                               uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st);
 
 // attn.hip

@@ -1,7 +1,10 @@
-// Row-wise top-p cut of the block map (PARK page, Table 1 caption: top-p retrieval at p = 0.9).
-// One workgroup per (row, head): bitonic sort of 64-bit keys (importance bits, complemented index)
-// in LDS, fp64 prefix sums in sorted order, the shortest prefix reaching p, then an ordered
-// compaction of the kept cluster ids.
+// Row-wise cuts of the block map: top-p (PARK page, Table 1 caption: top-p retrieval at p = 0.9)
+// and top-k at a fixed retrieval ratio (Table 10 caption: rho = 0.1; k = ceil(rho * C_ne) of the
+// head's C_ne non-empty key blocks, at least 1).
+// One workgroup per (row, head): bitonic sort of 64-bit keys (importance bits, complemented index;
+// empty key blocks get key 0 and sort last) in LDS; top-p takes fp64 prefix sums in sorted order
+// and the shortest prefix reaching p, top-k the first k; then an ordered compaction of the kept
+// cluster ids.
 #include "park_common.h"
 #include "park_internal.h"
 
@@ -11,8 +14,10 @@ namespace {
 
 constexpr int kSelThreads = 256;
 
+// rho < 0: top-p with p; rho >= 0: top-k at ratio rho
 __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* __restrict__ map, int cq, int ck,
                                                                   const int32_t* __restrict__ k_off, double p,
+                                                                  double rho,
                                                                   uint8_t* __restrict__ mask,
                                                                   int32_t* __restrict__ counts,
                                                                   int32_t* __restrict__ cols,
@@ -31,13 +36,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* _
   int P2 = 1;
   while (P2 < ck) P2 <<= 1;
 
-  int any_pos = 0;
+  const bool topk = rho >= 0.0;
+  int any_pos = 0, live = 0;
   for (int j = tid; j < P2; j += kSelThreads) {
     uint64_t key = 0;
-    if (j < ck) {
+    if (j < ck && ko[j + 1] > ko[j]) {
       uint32_t bits = __float_as_uint(row[j]);
       if (bits & 0x80000000u) bits = 0;  // -0 (or a negative) counts as zero importance
       if (bits) any_pos = 1;
+      ++live;
       key = ((uint64_t)bits << 32) | (uint64_t)(~(uint32_t)j);
     }
     keys[j] = key;
@@ -45,8 +52,14 @@ __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* _
   }
   if (tid == 0) kstar = 0x7FFFFFFF;
   any_pos = __syncthreads_or(any_pos);
+  int n_live = 0;
+  if (topk) {
+    int tot;
+    (void)block_exclusive_scan(live, iscratch, &tot);
+    n_live = tot;
+  }
 
-  if (any_pos && p < 1.0) {
+  if (any_pos && (topk || p < 1.0)) {
     // descending sort: larger importance first, equal importance -> lower index first
     for (int k = 2; k <= P2; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
@@ -64,6 +77,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* _
         __syncthreads();
       }
     }
+    if (topk) {
+      // the first k sorted entries (all of them non-empty key blocks)
+      int k = (int)ceil(rho * (double)n_live - 1e-9);
+      k = k < 1 ? 1 : (k > n_live ? n_live : k);
+      for (int e = tid; e < k; e += kSelThreads) keep[~(uint32_t)(keys[e] & 0xFFFFFFFFu)] = 1;
+    } else {
     // fp64 prefix sums in sorted order: thread t owns sorted positions [t*per, t*per + per)
     const int per = (P2 + kSelThreads - 1) / kSelThreads;
     const int b0 = tid * per;
@@ -87,6 +106,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* _
       for (int e = tid; e <= ks; e += kSelThreads) keep[~(uint32_t)(keys[e] & 0xFFFFFFFFu)] = 1;
     } else {
       for (int j = tid; j < ck; j += kSelThreads) keep[j] = row[j] > 0.f;
+    }
     }
   } else if (any_pos) {
     // p >= 1: every non-empty key cluster
@@ -132,8 +152,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topp_kernel(const float* _
 
 hipError_t launch_select_topp(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double p,
                               uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st) {
-  select_topp_kernel<<<dim3((unsigned)cq, (unsigned)H), kSelThreads, 0, st>>>(map, cq, ck, k_offsets, p, mask, counts,
-                                                                               cols, sel_keys);
+  select_topp_kernel<<<dim3((unsigned)cq, (unsigned)H), kSelThreads, 0, st>>>(map, cq, ck, k_offsets, p, -1.0, mask,
+                                                                               counts, cols, sel_keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double rho,
+                              uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st) {
+  select_topp_kernel<<<dim3((unsigned)cq, (unsigned)H), kSelThreads, 0, st>>>(map, cq, ck, k_offsets, 1.0, rho, mask,
+                                                                               counts, cols, sel_keys);
   return hipGetLastError();
 }
 

@@ -42,6 +42,9 @@ typedef enum { PARK_F32 = 0, PARK_BF16 = 1 } park_dtype;
 typedef enum { PARK_EUCLID = 0, PARK_QRKC = 1 } park_metric;
 typedef enum { PARK_INIT_KMEANSPP = 0, PARK_INIT_WARM = 1 } park_init;
 typedef enum { PARK_SIDE_Q = 0, PARK_SIDE_K = 1 } park_side;
+/* Query/key representations of a block map (PARK, thelatestinai.com page, Table 1): F = full
+ * (every original query or key), C = centroid. FC is the PAMA map. */
+typedef enum { PARK_EST_FC = 0, PARK_EST_CC = 1, PARK_EST_CF = 2, PARK_EST_FF = 3 } park_estimator;
 
 typedef struct {
   int64_t heads; /* independent attention heads */
@@ -70,7 +73,8 @@ enum {
   PARK_ENTRY_RETRIEVE_MAP = 3,
   PARK_ENTRY_SELECT_TOPP = 4,
   PARK_ENTRY_SPARSE_ATTN = 5,
-  PARK_ENTRY_FORWARD = 6
+  PARK_ENTRY_FORWARD = 6,
+  PARK_ENTRY_ESTIMATOR = 7  /* park_estimator_map, any mode */
 };
 
 /* Workspace bytes an entry needs for this shape and these parameters (0 on invalid input). */
@@ -157,6 +161,41 @@ park_status park_retrieve_map(const park_shape* shape, const void* q, const int3
  */
 park_status park_select_topp(const float* map, int64_t heads, int32_t cq, int32_t ck,
                              const int32_t* k_offsets, double p, uint8_t* mask, int32_t* counts,
+                             int32_t* cols, int64_t* sel_keys, void* stream);
+
+/*
+ * Block map under one of the four query/key representations of PARK Table 1 (thelatestinai.com
+ * page; Table 4 compares the same four): row i is the mean over the queries of query cluster i of a
+ * distribution over key clusters j:
+ *   PARK_EST_FC  softmax_j(s q.c_j + ln n_j) of each original query (the PAMA map, as
+ *                park_retrieve_map);
+ *   PARK_EST_CC  the same for the query cluster's centroid instead of its queries;
+ *   PARK_EST_CF  the softmax mass of the query centroid over all keys that falls on cluster j;
+ *   PARK_EST_FF  the dense softmax mass of each original query that falls on cluster j (the exact
+ *                block importance; N^2 d work per head).
+ * Centroids enter as consumed by the matrix cores (bf16-rounded); CC, CF and FF need bf16 data
+ * (PARK_EUNSUPPORTED otherwise). Arguments a mode does not read may be NULL:
+ *   q, q_perm                  FC, FF        k, k_perm       CF, FF
+ *   q_centroids [heads, cq, d] float32: CC, CF    k_centroids [heads, ck, d] float32: FC, CC
+ *   q_offsets, k_offsets       every mode
+ *   map        [heads, cq, ck] float32 output; an empty query cluster gets a zero row
+ * Workspace: park_workspace_bytes(PARK_ENTRY_ESTIMATOR, shape, params with cq, ck).
+ */
+park_status park_estimator_map(const park_shape* shape, const void* q, const void* k, const int32_t* q_perm,
+                               const int32_t* q_offsets, int32_t cq, const float* q_centroids,
+                               const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
+                               const float* k_centroids, int32_t mode, float scale, float* map, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * Row-wise top-k cut at a fixed retrieval ratio (PARK, thelatestinai.com page, Table 10 caption:
+ * top-k block retrieval at rho = 0.1). Per head, k = ceil(rho * C_ne) of the C_ne non-empty key
+ * clusters, clamped to [1, C_ne]; every row with positive importance keeps the k non-empty key
+ * clusters of highest importance (ties to the lower index); a row without positive importance
+ * (empty query cluster) keeps nothing. Arguments and outputs as park_select_topp; rho in [0, 1].
+ */
+park_status park_select_topk(const float* map, int64_t heads, int32_t cq, int32_t ck,
+                             const int32_t* k_offsets, double rho, uint8_t* mask, int32_t* counts,
                              int32_t* cols, int64_t* sel_keys, void* stream);
 
 /*

@@ -115,6 +115,25 @@ def test_validation_errors(L):
         assert st == L.PARK_EINVAL, p
     st, _ = _status(L, "park_select_topp", FAKE, 2, 10, 4000, FAKE, 0.9, FAKE, FAKE, FAKE, FAKE, None)
     assert st == L.PARK_EINVAL
+    # top-k ratio outside [0, 1]
+    for rho in (-0.1, 1.5, float("nan")):
+        st, _ = _status(L, "park_select_topk", FAKE, 2, 10, 20, FAKE, rho, FAKE, FAKE, FAKE, FAKE, None)
+        assert st == L.PARK_EINVAL, rho
+    # estimator maps: unknown mode; centroid and full-key modes need bf16 data; missing inputs
+    st, msg = _status(L, "park_estimator_map", bp(sh), FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, FAKE, 20, FAKE, 9,
+                      0.0, FAKE, FAKE, 1 << 40, None)
+    assert st == L.PARK_EINVAL and "mode" in msg
+    sh32 = L.park_shape(2, 100, 64, L.PARK_F32)
+    st, _ = _status(L, "park_estimator_map", bp(sh32), FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, FAKE, 20, FAKE,
+                    L.PARK_EST_FF, 0.0, FAKE, FAKE, 1 << 40, None)
+    assert st == L.PARK_EUNSUPPORTED
+    shb = L.park_shape(2, 100, 64, L.PARK_BF16)
+    st, msg = _status(L, "park_estimator_map", bp(shb), FAKE, None, FAKE, FAKE, 10, FAKE, FAKE, FAKE, 20, FAKE,
+                      L.PARK_EST_FF, 0.0, FAKE, FAKE, 1 << 40, None)
+    assert st == L.PARK_EINVAL and msg.startswith("k")
+    st, msg = _status(L, "park_estimator_map", bp(shb), None, None, None, FAKE, 10, None, None, FAKE, 20, FAKE,
+                      L.PARK_EST_CC, 0.0, FAKE, FAKE, 1 << 40, None)
+    assert st == L.PARK_EINVAL and "q_centroids" in msg
     # sparse attention: null selection, small workspace
     st, msg = _status(L, "park_sparse_attn", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, None, FAKE,
                       0.0, FAKE, None, FAKE, 1 << 40, None)
