@@ -262,6 +262,52 @@ def run_schedule(args, bsa, w, dev, log):
                       "ms_per_step": {k: round(v / len(steps), 3) for k, v in tot.items()}}), flush=True)
 
 
+def run_estimators(args, bsa, w, dev, log):
+    """Retrieval quality under the four query/key representations of PARK-p2 Table 1 (FC = PAMA, CC,
+    CF, FF) on one synthetic layer: top-p (p of the workload) and top-k at rho = 0.1 (Table 10)
+    selections from each block map, attention over them, and the recall of every head
+    (exp(LSE_selected - LSE_dense) averaged over its queries); mean, P05 and worst over heads, block
+    and token density, the block-map total variation to FF, and the time of each map."""
+    Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
+    ws = bsa.Workspace()
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed,
+                         outputs=("q_perm", "q_offsets", "k_perm", "k_offsets", "map"), ws=ws)
+    cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+    cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+    _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
+                                 cols_all, ws=ws)
+    modes = {"FC": bsa.PARK_EST_FC, "CC": bsa.PARK_EST_CC, "CF": bsa.PARK_EST_CF, "FF": bsa.PARK_EST_FF}
+    kw = dict(q=Q, k=K, q_perm=r["q_perm"], q_offsets=r["q_offsets"], q_centroids=r["q_centroids"],
+              k_perm=r["k_perm"], k_centroids=r["k_centroids"], ws=ws)
+    maps, out = {}, {"estimators": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "p": w.p,
+                     "rho": 0.1, "modes": {}}
+    for name, m in modes.items():
+        E = bsa.park_estimator_map(m, r["k_offsets"], **kw)
+        maps[name] = E
+        ms = time_call(lambda: bsa.park_estimator_map(m, r["k_offsets"], out=E, **kw), 1)
+        out["modes"][name] = {"map_ms": round(ms, 3)}
+    live = torch.diff(r["q_offsets"].long(), dim=1) > 0
+    for name, E in maps.items():
+        entry = out["modes"][name]
+        tv = 0.5 * (E - maps["FF"]).abs().sum(-1)
+        entry["tv_to_ff"] = round(float(tv[live].mean()), 5)
+        for label, sel in (("top_p", bsa.park_select_topp(E, r["k_offsets"], w.p)),
+                           ("top_k", bsa.park_select_topk(E, r["k_offsets"], 0.1))):
+            _, lse = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"],
+                                          sel["counts"], sel["cols"], ws=ws)
+            head = torch.exp(lse - ld).mean(dim=1).double().cpu()
+            q = torch.diff(r["q_offsets"], dim=1).double()
+            pairs = (live.sum(1) * (torch.diff(r["k_offsets"], dim=1) > 0).sum(1)).double().sum()
+            blocks = float(sel["counts"].double().sum() / pairs)
+            tokens = float((q * sel["sel_keys"].double()).sum()) / (w.n * w.n * w.heads)
+            entry[label] = {"recall_mean": round(float(head.mean()), 4),
+                            "recall_p05": round(float(torch.quantile(head, 0.05)), 4),
+                            "recall_worst": round(float(head.min()), 4),
+                            "block_density": round(blocks, 4), "token_density": round(tokens, 4)}
+        log(f"estimator {name} {entry}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +319,8 @@ def main():
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured GEMM / copy ceilings")
     ap.add_argument("--sweep", action="store_true", help="p x Ck grid on the Wan-shaped layer (own JSON document)")
+    ap.add_argument("--estimators", action="store_true",
+                    help="FC / CC / CF / FF block maps: recall and density of their top-p and top-k selections")
     ap.add_argument("--schedule", action="store_true",
                     help="the long clip's multi-step schedule with warm starts (own JSON document)")
     ap.add_argument("--kernel-only", choices=["sparse_attn", "assign", "pama"], default=None,
@@ -293,6 +341,9 @@ def main():
     log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
     if args.sweep:
         run_sweep(args, bsa, synth.WORKLOADS["wan"], dev, log)
+        return
+    if args.estimators:
+        run_estimators(args, bsa, w, dev, log)
         return
     if args.schedule:
         run_schedule(args, bsa, synth.WORKLOADS["long"], dev, log)
