@@ -82,11 +82,35 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
     c_len[tid] = len;
     c_dst[tid] = (int)min<int64_t>(base + pre, N);
     __syncthreads();
+    // each wave copies two clusters at a time, four 64-key rows of each in flight
     const int nloc = min(256, cnt - m0);
-    for (int e = w; e < nloc; e += 4) {
-      const int s0 = c_start[e], d0 = c_dst[e];
-      const int ln = (int)min<int64_t>(c_len[e], N - d0);
-      for (int u = l; u < ln; u += kWave) dst[d0 + u] = kp[s0 + u];
+    for (int e0 = w; e0 < nloc; e0 += 8) {
+      int s0[2], d0[2], ln[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int e = e0 + 4 * x;
+        s0[x] = e < nloc ? c_start[e] : 0;
+        d0[x] = e < nloc ? c_dst[e] : 0;
+        ln[x] = e < nloc ? (int)min<int64_t>(c_len[e], N - d0[x]) : 0;
+      }
+      const int lmax = max(ln[0], ln[1]);
+      for (int u0 = 0; u0 < lmax; u0 += 4 * kWave) {
+        int v[2][4];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int u = u0 + k * kWave + l;
+            v[x][k] = kp[s0[x] + min(u, max(ln[x] - 1, 0))];  // clamped: every load is issued
+          }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int u = u0 + k * kWave + l;
+            if (u < ln[x]) dst[d0[x] + u] = v[x][k];
+          }
+      }
     }
     base += tot;
     __syncthreads();

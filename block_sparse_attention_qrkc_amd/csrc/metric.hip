@@ -39,21 +39,36 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(const uint16_t* __res
     }
   }
   int since_flush = 0;
+  // 16-byte loads per sub-block and thread; the next sub-block is loaded while this one is used
+  // (rows past the block end are clamped to its last row and stored as zeros)
+  constexpr int kLoads = kSub * D / 8 / 256;
+  u32x4_t nxt[kLoads];
+  auto fetch = [&](int64_t tn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int64_t row = tn + e % kSub < t_end ? tn + e % kSub : t_end - 1;
+      nxt[q] = *reinterpret_cast<const u32x4_t*>(Qh + row * D + (e / kSub) * 8);
+    }
+  };
+  fetch(t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kSub) {
     // stage 64 tokens transposed: qt[dim][token]
-    constexpr int kLoads = kSub * D / 8;  // 16-byte loads per sub-block
-    for (int e = threadIdx.x; e < kLoads; e += 256) {
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int e = threadIdx.x + q * 256;
       const int r = e % kSub;
       const int c8 = e / kSub;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (t0 + r < t_end) val = *reinterpret_cast<const u32x4_t*>(Qh + (t0 + r) * D + c8 * 8);
+      u32x4_t val = nxt[q];
+      if (t0 + r >= t_end) val = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        qt[(c8 * 8 + 2 * q) * kLdsStride + r] = (uint16_t)(val[q] & 0xFFFFu);
-        qt[(c8 * 8 + 2 * q + 1) * kLdsStride + r] = (uint16_t)(val[q] >> 16);
+      for (int k2 = 0; k2 < 4; ++k2) {
+        qt[(c8 * 8 + 2 * k2) * kLdsStride + r] = (uint16_t)(val[k2] & 0xFFFFu);
+        qt[(c8 * 8 + 2 * k2 + 1) * kLdsStride + r] = (uint16_t)(val[k2] >> 16);
       }
     }
     __syncthreads();
+    if (t0 + kSub < t_end) fetch(t0 + kSub);
 #pragma unroll
     for (int ks = 0; ks < kSub / 16; ++ks) {
       const int tok = ks * 16 + (l / 32) * 8;
