@@ -5,7 +5,8 @@ of ``bench.py`` may import it. It shares no code with the HIP library and import
 
 Source: "PARK: Accurate Block Retrieval for Sparse Attention in Video Diffusion Transformers"
 (abstract on both PARK pages; Figure 1, Figure 2 caption and Tables 1, 4, 5 on the
-thelatestinai.com page). Each function names the passage it follows. Where the pages leave a step
+thelatestinai.com page); the block sampling with inclusion-probability weighting follows the SIP
+paragraph of the AB-Attention page. Each function names the passage it follows. Where the pages leave a step
 open, the function states the reading it takes.
 
 Parity status:

@@ -20,6 +20,7 @@ __all__ = [
     "qrkc_metric", "metric_distance", "candidate_rows", "kmeanspp", "consumed_centroids",
     "assign", "assign_near_tie", "cluster_order", "update", "lloyd", "cluster",
     "pama", "select_topp", "topk_count", "select_topk", "key_runs", "sparse_attention", "dense_attention",
+    "SIDE_SIP", "sip_uniform", "sip_probabilities", "select_sip", "weighted_sparse_attention",
     "recall", "density", "estimator_maps", "estimator_block_maps", "tv_to_full", "raw_key_mse", "qk_score_sq_error",
     "centered_log_mass_error", "retrieve", "forward",
 ]
@@ -28,6 +29,7 @@ EUCLID = 0
 QRKC = 1
 SIDE_Q = 0
 SIDE_K = 1
+SIDE_SIP = 2  # random stream of the block sampling (select_sip)
 
 _M64 = (1 << 64) - 1
 _GAMMA = 0x9E3779B97F4A7C15
@@ -408,6 +410,78 @@ def select_topk(A, k_sizes, rho):
     return mask, counts, cols, keys
 
 
+def sip_uniform(seed: int, head: int, i: int, j: int, ck: int) -> float:
+    """Uniform draw in [0, 1) that decides whether row i samples key block j (select_sip).
+
+    Reading (the page fixes no generator): the k-means++ counter stream of stream id 2, counter
+    i * ck + j: 53 high bits of the first SplitMix64 output seeded with
+    seed ^ (head << 32) ^ (2 << 24) ^ (i * ck + j), times 2^-53."""
+    key = (seed ^ (head << 32) ^ (SIDE_SIP << 24) ^ (i * ck + j)) & _M64
+    return (splitmix64_first(key) >> 11) * (2.0 ** -53)
+
+
+def sip_probabilities(a, m):
+    """Inclusion probabilities of one map row for sampling m blocks in expectation.
+
+    AB-Attention page (SIP paragraph): blocks are sampled according to their estimated
+    importance. Reading: probability proportional to importance, capped at 1,
+    pi_j = min(1, kappa * a_j) over the blocks with a_j > 0 (others 0), with kappa chosen so that
+    sum_j pi_j = m; when m reaches the number of positive blocks every one of them has pi = 1.
+    Water filling: order the positive a descending (ties to the lower index); with the t largest
+    capped at 1 the rest share m - t, kappa_t = (m - t) / (sum of the rest); the answer is the
+    smallest t whose largest uncapped entry satisfies kappa_t * a <= 1.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    pi = np.zeros_like(a)
+    pos = np.flatnonzero(a > 0)
+    if pos.size == 0 or m <= 0:
+        return pi
+    if m >= pos.size:
+        pi[pos] = 1.0
+        return pi
+    order = pos[np.lexsort((pos, -a[pos]))]
+    vals = a[order]
+    rest = np.cumsum(vals[::-1])[::-1]  # rest[t] = sum of vals[t:]
+    for t in range(pos.size):
+        kappa = (m - t) / rest[t]
+        if kappa * vals[t] <= 1.0:
+            break
+    pi[order[:t]] = 1.0
+    pi[order[t:]] = np.minimum(kappa * vals[t:], 1.0)
+    return pi
+
+
+def select_sip(A, k_sizes, rho, seed=0, head=0):
+    """Sampling with inclusion-probability weighting of every map row (AB-Attention page, SIP
+    paragraph: sample blocks by estimated importance instead of truncating, reweight each sampled
+    block by the inverse of its inclusion probability).
+
+    Readings: the expected number of sampled blocks per row is the top-k budget at ratio rho,
+    m = topk_count(k_sizes, rho); empty key clusters have importance 0 (never sampled); block j of
+    row i is kept iff sip_uniform(seed, head, i, j) < pi_ij; a kept block carries the log weight
+    ln(1 / pi_ij). Returns (mask, counts, cols, keys, log_w, pi): the first four as select_topp,
+    log_w [Cq, Ck] (0 where not kept) and the probabilities pi [Cq, Ck].
+    """
+    A = np.asarray(A, dtype=np.float64)
+    k_sizes = np.asarray(k_sizes, dtype=np.int64)
+    cq, ck = A.shape
+    m = topk_count(k_sizes, rho)
+    mask = np.zeros((cq, ck), dtype=bool)
+    log_w = np.zeros((cq, ck))
+    pi = np.zeros((cq, ck))
+    for i in range(cq):
+        a = np.where(k_sizes > 0, np.maximum(A[i], 0.0), 0.0)
+        pi[i] = sip_probabilities(a, m)
+        for j in np.flatnonzero(pi[i] > 0):
+            if sip_uniform(seed, head, i, int(j), ck) < pi[i, j]:
+                mask[i, j] = True
+                log_w[i, j] = -math.log(pi[i, j])
+    counts = mask.sum(axis=1).astype(np.int32)
+    cols = [np.flatnonzero(mask[i]).astype(np.int32) for i in range(cq)]
+    keys = (mask * k_sizes[None, :]).sum(axis=1).astype(np.int64)
+    return mask, counts, cols, keys, log_w, pi
+
+
 def key_runs(cols, k_offsets):
     """Key ranges in sorted-key positions that one query block attends to: selected clusters in
     ascending order, adjacent clusters merged into one run. Returns a list of (start, end)."""
@@ -461,6 +535,47 @@ def sparse_attention(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, cols, scale,
             lse[t] = -np.inf
             continue
         O[t], lse[t] = _attend(Q[t], K[u], V[u], scale)
+    return O, lse
+
+
+def weighted_sparse_attention(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, cols, log_w, scale, rows=None):
+    """Attention over the selected blocks with block weights (AB-Attention page, SIP paragraph:
+    sampled blocks are reweighted by the inverse of their inclusion probability, so that one sparse
+    pass estimates dense attention).
+
+    For a query t of block i with selected key blocks S and weights w_j = exp(log_w[i, j]):
+        O_t = sum_{j in S} w_j sum_{k in j} e^{s q_t.k} v_k / sum_{j in S} w_j sum_{k in j} e^{s q_t.k},
+    i.e. the logit of every key of block j gains ln w_j; LSE_t is the log of the denominator (an
+    estimate of the dense log-sum-exp). With log_w = 0 this is sparse_attention.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    log_w = np.asarray(log_w, dtype=np.float64)
+    n, d = Q.shape
+    O = np.full((n, V.shape[1]), np.nan)
+    lse = np.full(n, np.nan)
+    cq = len(q_offsets) - 1
+    for i in (range(cq) if rows is None else rows):
+        t = np.asarray(q_perm[q_offsets[i]:q_offsets[i + 1]])
+        if t.size == 0:
+            continue
+        u, b = [], []
+        for j in cols[i]:
+            keys = np.asarray(k_perm[k_offsets[j]:k_offsets[j + 1]])
+            u.append(keys)
+            b.append(np.full(keys.size, log_w[i, j]))
+        u = np.concatenate(u) if u else np.zeros(0, dtype=np.int64)
+        if u.size == 0:
+            O[t] = 0.0
+            lse[t] = -np.inf
+            continue
+        s = scale * (Q[t] @ K[u].T) + np.concatenate(b)[None, :]
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        den = e.sum(axis=1, keepdims=True)
+        O[t] = (e @ V[u]) / den
+        lse[t] = (mx + np.log(den))[:, 0]
     return O, lse
 
 

@@ -382,6 +382,122 @@ def test_topk_is_max_mass_set_bruteforce():
             assert cols[i].tolist() == sorted(best), (trial, i)
 
 
+# ------------------------------------------------------------------------------------ SIP
+def test_sip_probabilities_hand_worked():
+    for case in _golden("sip_hand.json")["probabilities"]:
+        pi = O.sip_probabilities(case["a"], case["m"])
+        np.testing.assert_allclose(pi, case["pi"], rtol=0, atol=1e-15, err_msg=case["work"])
+
+
+def test_sip_probabilities_match_bisection():
+    """An independent solver: bisection on kappa of the monotone sum_j min(1, kappa a_j) - m."""
+    rng = np.random.default_rng(21)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        a = rng.dirichlet(np.ones(n) * float(rng.choice([0.1, 0.5, 2.0])))
+        a[rng.random(n) < 0.2] = 0.0
+        npos = int((a > 0).sum())
+        m = int(rng.integers(1, n + 2))
+        pi = O.sip_probabilities(a, m)
+        assert np.all((pi >= 0) & (pi <= 1)) and np.all(pi[a == 0] == 0), trial
+        if npos == 0:
+            continue
+        if m >= npos:
+            assert np.all(pi[a > 0] == 1), trial
+            continue
+        lo, hi = 0.0, 1.0 / a[a > 0].min()  # at hi every positive block is capped: the sum is npos > m
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if np.minimum(1.0, mid * a).sum() < m:
+                lo = mid
+            else:
+                hi = mid
+        np.testing.assert_allclose(pi, np.minimum(1.0, hi * a), rtol=0, atol=1e-12, err_msg=str(trial))
+        assert abs(pi.sum() - m) < 1e-12, trial
+
+
+def test_sip_inclusion_frequencies_match_probabilities():
+    """Over many seeds block j of a row is kept with frequency pi_j (within 5 binomial sigma), kept
+    blocks carry ln(1/pi), blocks with pi = 1 are always kept and empty clusters never."""
+    A = np.array([[0.05, 0.6, 0.0, 0.25, 0.1, 0.0], [0.3, 0.3, 0.2, 0.1, 0.05, 0.05]])
+    sizes = np.array([3, 2, 4, 1, 5, 0])
+    rho = 0.5  # 5 non-empty clusters: m = ceil(2.5) = 3
+    S = 3000
+    hits = np.zeros_like(A)
+    pi = None
+    for seed in range(S):
+        mask, counts, cols, keys, log_w, pi = O.select_sip(A, sizes, rho, seed=seed, head=3)
+        hits += mask
+        assert np.all(mask[:, 5] == 0) and np.all(mask[pi == 1.0])
+        np.testing.assert_allclose(log_w[mask], -np.log(pi[mask]), rtol=0, atol=1e-15)
+        assert np.all(log_w[~mask] == 0)
+        assert keys.tolist() == [int(sizes[c].sum()) for c in cols]
+    np.testing.assert_allclose(pi.sum(axis=1), [3.0, 3.0], atol=1e-12)
+    freq = hits / S
+    sigma = np.sqrt(pi * (1 - pi) / S)
+    assert np.all(np.abs(freq - pi) <= 5 * sigma + 1e-12), (freq, pi)
+
+
+def test_weighted_attention_hand_worked():
+    g = _golden("sip_hand.json")["weighted_attention"]
+    Q, K, V = (np.array(g[x]) for x in ("q", "k", "v"))
+    out, lse = O.weighted_sparse_attention(Q, K, V, [0], [0, 1], [0, 1], [0, 1, 2], [np.array([0, 1])],
+                                           np.log([g["w"]]), 1.0)
+    np.testing.assert_allclose(out, g["out"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, g["lse"], rtol=0, atol=1e-15)
+
+
+def test_sip_weighted_attention_is_unbiased_by_enumeration():
+    """Summed over every inclusion pattern, weighted by its probability, the weighted numerator
+    sum_j w_j sum_(k in j) e^(s q.k) v_k and denominator of each query equal the dense ones."""
+    rng = np.random.default_rng(5)
+    nq, n, d, ck = 7, 30, 8, 6
+    Q, K, V = rng.normal(size=(nq, d)), rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    labels = np.concatenate([np.arange(ck), rng.integers(0, ck, n - ck)])
+    k_perm = np.argsort(labels, kind="stable")
+    k_off = np.concatenate([[0], np.cumsum(np.bincount(labels, minlength=ck))])
+    a = np.array([0.55, 0.2, 0.1, 0.08, 0.05, 0.02])  # the first block is capped at m = 3
+    pi = O.sip_probabilities(a, 3)
+    assert pi[0] == 1.0 and np.all(pi[1:] < 1.0)
+    scale = 0.4
+    num = np.zeros((nq, d))
+    den = np.zeros(nq)
+    for pattern in itertools.product([False, True], repeat=ck):
+        inc = np.array(pattern)
+        prob = np.prod(np.where(inc, pi, 1.0 - pi))
+        if prob == 0.0:
+            continue
+        log_w = np.where(inc, -np.log(pi), 0.0)[None, :]
+        out, lse = O.weighted_sparse_attention(Q, K, V, np.arange(nq), [0, nq], k_perm, k_off,
+                                               [np.flatnonzero(inc)], log_w, scale)
+        e = np.exp(lse)
+        num += prob * e[:, None] * out
+        den += prob * e
+    Od, lsed = O.dense_attention(Q, K, V, scale)
+    np.testing.assert_allclose(den, np.exp(lsed), rtol=1e-12)
+    np.testing.assert_allclose(num, np.exp(lsed)[:, None] * Od, rtol=1e-11, atol=1e-13)
+
+
+def test_sip_full_budget_is_dense():
+    """With the budget covering every block (rho = 1) every non-empty block is kept with weight 1
+    and the weighted attention is dense attention."""
+    rng = np.random.default_rng(8)
+    n, d, cq, ck = 64, 8, 4, 5
+    Q, K, V = rng.normal(size=(n, d)), rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    ql = rng.integers(0, cq, n)
+    kl = np.concatenate([np.arange(ck), rng.integers(0, ck, n - ck)])
+    qp, kp = np.argsort(ql, kind="stable"), np.argsort(kl, kind="stable")
+    qo = np.concatenate([[0], np.cumsum(np.bincount(ql, minlength=cq))])
+    ko = np.concatenate([[0], np.cumsum(np.bincount(kl, minlength=ck))])
+    A = rng.dirichlet(np.ones(ck), size=cq)
+    mask, counts, cols, keys, log_w, pi = O.select_sip(A, np.diff(ko), 1.0, seed=2)
+    assert mask.all() and np.all(log_w == 0)
+    out, lse = O.weighted_sparse_attention(Q, K, V, qp, qo, kp, ko, cols, log_w, 0.3)
+    Od, lsed = O.dense_attention(Q, K, V, 0.3)
+    np.testing.assert_allclose(out, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-13)
+
+
 def test_topp_is_minimal_max_mass_set_bruteforce():
     """P2 by enumeration: the kept set reaches p, no smaller set does, and among sets of its size it
     has the largest mass (ties broken toward lower indices)."""
