@@ -18,7 +18,7 @@ import torch
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PARK_BF16, PARK_EHIP, PARK_EINVAL, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_CLUSTER_Q,
     PARK_ENTRY_ESTIMATOR, PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP,
-    PARK_ENTRY_SPARSE_ATTN, PARK_EST_CC, PARK_EST_CF, PARK_EST_FC, PARK_EST_FF,
+    PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_SPARSE_ATTN_WEIGHTED, PARK_EST_CC, PARK_EST_CF, PARK_EST_FC, PARK_EST_FF,
     PARK_EUCLID, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_F32, PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_OK,
     PARK_QRKC, PARK_SIDE_K, PARK_SIDE_Q, ParkError, Workspace, lib, make_params, make_shape, park_forward_outputs,
     park_params, park_shape, workspace_bytes,
@@ -109,6 +109,21 @@ def park_select_topk(map, k_offsets, rho, stream=None):
     return {"mask": mask, "counts": counts, "cols": cols, "sel_keys": sel}
 
 
+def park_select_sip(map, k_offsets, rho, seed=0, stream=None):
+    """Sampling with inclusion-probability weighting of every map row, budget = the top-k count at
+    ratio rho. Returns dict(mask, counts, cols, sel_keys, log_w)."""
+    H, cq, ck = map.shape
+    dev = map.device
+    mask = torch.empty(H, cq, ck, dtype=torch.uint8, device=dev)
+    counts = torch.empty(H, cq, dtype=torch.int32, device=dev)
+    cols = torch.empty(H, cq, ck, dtype=torch.int32, device=dev)
+    sel = torch.empty(H, cq, dtype=torch.int64, device=dev)
+    log_w = torch.empty(H, cq, ck, dtype=torch.float32, device=dev)
+    _check(lib().park_select_sip(_ptr(map), H, cq, ck, _ptr(k_offsets), float(rho), int(seed) & (2**64 - 1),
+                                 _ptr(mask), _ptr(counts), _ptr(cols), _ptr(sel), _ptr(log_w), _stream(stream)))
+    return {"mask": mask, "counts": counts, "cols": cols, "sel_keys": sel, "log_w": log_w}
+
+
 def park_estimator_map(mode, k_offsets, q=None, k=None, q_perm=None, q_offsets=None, q_centroids=None, k_perm=None,
                        k_centroids=None, scale=0.0, out=None, ws=None, stream=None):
     """Block map [heads, cq, ck] float32 under a PARK_EST_* query/key representation (Table 1). The
@@ -143,6 +158,28 @@ def park_sparse_attn(q, k, v, q_perm, q_offsets, k_perm, k_offsets, counts, cols
     _check(lib().park_sparse_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(q_perm), _ptr(q_offsets), cq,
                                   _ptr(k_perm), _ptr(k_offsets), ck, _ptr(counts), _ptr(cols), float(scale), _ptr(o),
                                   _ptr(L), wp, wn, _stream(stream)))
+    return o, L
+
+
+def park_sparse_attn_weighted(q, k, v, q_perm, q_offsets, k_perm, k_offsets, counts, cols, log_w, scale=0.0,
+                              out=None, lse=True, ws=None, stream=None):
+    """Attention over the selected blocks, the logits of block j of row i raised by log_w[h, i, j].
+    Returns (out [heads, n, d], lse [heads, n] or None)."""
+    sh = make_shape(q)
+    cq = q_offsets.shape[1] - 1
+    ck = k_offsets.shape[1] - 1
+    o = out if out is not None else torch.empty_like(q)
+    L = None
+    if lse is True:
+        L = torch.empty(sh.heads, sh.n, dtype=torch.float32, device=q.device)
+    elif isinstance(lse, torch.Tensor):
+        L = lse
+    prm = make_params(cq=cq, ck=ck)
+    wp, wn = _ws(PARK_ENTRY_SPARSE_ATTN_WEIGHTED, sh, prm, q.device, ws)
+    _check(lib().park_sparse_attn_weighted(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(q_perm),
+                                           _ptr(q_offsets), cq, _ptr(k_perm), _ptr(k_offsets), ck, _ptr(counts),
+                                           _ptr(cols), _ptr(log_w), float(scale), _ptr(o), _ptr(L), wp, wn,
+                                           _stream(stream)))
     return o, L
 
 

@@ -22,12 +22,13 @@ PARK_INIT_KMEANSPP, PARK_INIT_WARM = 0, 1
 PARK_SIDE_Q, PARK_SIDE_K = 0, 1
 PARK_EST_FC, PARK_EST_CC, PARK_EST_CF, PARK_EST_FF = range(4)
 (PARK_ENTRY_METRIC, PARK_ENTRY_CLUSTER_Q, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_RETRIEVE_MAP,
- PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_FORWARD, PARK_ENTRY_ESTIMATOR) = range(8)
+ PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_FORWARD, PARK_ENTRY_ESTIMATOR,
+ PARK_ENTRY_SPARSE_ATTN_WEIGHTED) = range(9)
 
 EXPORTED = [
     "park_workspace_bytes", "park_status_string", "park_last_error", "park_version",
     "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
-    "park_select_topk", "park_sparse_attn",
+    "park_select_topk", "park_select_sip", "park_sparse_attn", "park_sparse_attn_weighted",
     "park_permute_rows", "park_unpermute_rows", "park_forward",
 ]
 
@@ -88,7 +89,10 @@ def lib() -> ctypes.CDLL:
             "park_estimator_map": (i32, [SP, _P, _P, _P, _P, i32, _P, _P, _P, i32, _P, i32, f32, _P, _P, sz, _P]),
             "park_select_topp": (i32, [_P, i64, i32, i32, _P, f64, _P, _P, _P, _P, _P]),
             "park_select_topk": (i32, [_P, i64, i32, i32, _P, f64, _P, _P, _P, _P, _P]),
+            "park_select_sip": (i32, [_P, i64, i32, i32, _P, f64, u64, _P, _P, _P, _P, _P, _P]),
             "park_sparse_attn": (i32, [SP, _P, _P, _P, _P, _P, i32, _P, _P, i32, _P, _P, f32, _P, _P, _P, sz, _P]),
+            "park_sparse_attn_weighted": (i32, [SP, _P, _P, _P, _P, _P, i32, _P, _P, i32, _P, _P, _P, f32, _P, _P, _P,
+                                                sz, _P]),
             "park_permute_rows": (i32, [SP, _P, _P, _P, _P]),
             "park_unpermute_rows": (i32, [SP, _P, _P, _P, _P]),
             "park_forward": (i32, [SP, _P, _P, _P, _P, PP, _P, _P, ctypes.POINTER(park_forward_outputs), _P, sz,

@@ -48,9 +48,12 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
                                                    const int32_t* __restrict__ cols,
                                                    const int32_t* __restrict__ k_offsets,
                                                    const int32_t* __restrict__ k_perm, int64_t N, int cq, int ck,
-                                                   int32_t* __restrict__ gather, int32_t* __restrict__ glen) {
+                                                   const float* __restrict__ log_w, float inv_scale,
+                                                   int32_t* __restrict__ gather, int32_t* __restrict__ glen,
+                                                   float* __restrict__ gbias) {
   __shared__ int scratch[17];
   __shared__ int c_start[256], c_len[256], c_dst[256];
+  __shared__ float c_bias[256];
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -62,10 +65,13 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
   const int32_t* ko = k_offsets + (int64_t)h * (ck + 1);
   const int32_t* kp = k_perm + (int64_t)h * N;
   int32_t* dst = gather + ((int64_t)h * cq + i) * N;
+  float* bdst = log_w ? gbias + ((int64_t)h * cq + i) * N : nullptr;
+  const float* lwrow = log_w ? log_w + ((int64_t)h * cq + i) * ck : nullptr;
   int64_t base = 0;
   for (int m0 = 0; m0 < cnt; m0 += 256) {
     const int m = m0 + tid;
     int a = 0, len = 0;
+    float bias = 0.f;
     if (m < cnt) {
       const int j = crow[m];
       if (j >= 0 && j < ck) {
@@ -74,6 +80,7 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
           a = (int)lo;
           len = (int)(hi - lo);
         }
+        if (lwrow) bias = lwrow[j] * inv_scale;
       }
     }
     int tot;
@@ -81,17 +88,20 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
     c_start[tid] = a;
     c_len[tid] = len;
     c_dst[tid] = (int)min<int64_t>(base + pre, N);
+    c_bias[tid] = bias;
     __syncthreads();
     // each wave copies two clusters at a time, four 64-key rows of each in flight
     const int nloc = min(256, cnt - m0);
     for (int e0 = w; e0 < nloc; e0 += 8) {
       int s0[2], d0[2], ln[2];
+      float cb[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int e = e0 + 4 * x;
         s0[x] = e < nloc ? c_start[e] : 0;
         d0[x] = e < nloc ? c_dst[e] : 0;
         ln[x] = e < nloc ? (int)min<int64_t>(c_len[e], N - d0[x]) : 0;
+        cb[x] = e < nloc ? c_bias[e] : 0.f;
       }
       const int lmax = max(ln[0], ln[1]);
       for (int u0 = 0; u0 < lmax; u0 += 4 * kWave) {
@@ -108,7 +118,10 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int u = u0 + k * kWave + l;
-            if (u < ln[x]) dst[d0[x] + u] = v[x][k];
+            if (u < ln[x]) {
+              dst[d0[x] + u] = v[x][k];
+              if (bdst) bdst[d0[x] + u] = cb[x];
+            }
           }
       }
     }
@@ -154,7 +167,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ q_off, int cq,
                                                           const int32_t* __restrict__ tile_base,
                                                           const int32_t* __restrict__ gather,
-                                                          const int32_t* __restrict__ glen, float scale,
+                                                          const int32_t* __restrict__ glen,
+                                                          const float* __restrict__ gbias, float scale,
                                                           T* __restrict__ out, float* __restrict__ lse) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
@@ -163,6 +177,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint16_t ks[kBN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VSTR];
   __shared__ int32_t krow[kBN];
+  __shared__ float kbias[kBN];  // per-key logit offsets (block weights) in raw-score units
 
   const int h = blockIdx.y;
   const int c = blockIdx.x;
@@ -177,6 +192,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
   const int qend = min(qbeg + kAttnBM, qo[i + 1]);
   const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
+  const float* brow = gbias ? gbias + ((int64_t)h * cq + i) * N : nullptr;
   const int L = glen[(int64_t)h * cq + i];
   const T* Qh = Q + (int64_t)h * N * D;
   const T* Kh = K + (int64_t)h * N * D;
@@ -209,6 +225,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
     if (tid < kBN) {
       const int v = v0 + tid;
       krow[tid] = v < L ? rows[v] : -1;
+      kbias[tid] = (brow && v < L) ? brow[v] : 0.f;
     }
     __syncthreads();
     // K tile, row-major
@@ -249,6 +266,12 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&ks[(st * 32 + prow) * KSTR + kk * 16 + hl * 8]);
         sacc[st] = mfma32(a, qb[kk], sacc[st]);
       }
+    }
+    if (brow) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[st][e] += kbias[st * 32 + hl * 16 + e];
     }
     const int nvalid = L - v0;  // keys with index < nvalid in this tile are real
     float mx = -INFINITY;
@@ -391,7 +414,9 @@ __device__ __forceinline__ bool w8_unroll(F&& f) {
   }
 }
 
-template <int D>
+// W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
+// units), copied into LDS with the tile and added to the scores
+template <int D, bool W>
 __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restrict__ Q,
                                                          const uint16_t* __restrict__ K,
                                                          const uint16_t* __restrict__ V, int64_t N,
@@ -399,7 +424,8 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
                                                          const int32_t* __restrict__ q_off, int cq,
                                                          const int32_t* __restrict__ tile_base,
                                                          const int32_t* __restrict__ gather,
-                                                         const int32_t* __restrict__ glen, float scale,
+                                                         const int32_t* __restrict__ glen,
+                                                         const float* __restrict__ gbias, float scale,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 8;
@@ -412,10 +438,12 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   constexpr int BN = D == 64 ? 64 : kW8BN;
   constexpr int NSUB = BN / 32;                 // 32-key sub-tiles
   constexpr int TILEB = BN * ROWB;              // one K (or V) tile
-  constexpr int STAGEB = 2 * TILEB;             // K then V
+  constexpr int BIASB = W ? 256 : 0;            // per wave: the tile's key offsets (lanes l % BN)
+  constexpr int STAGEB = 2 * TILEB + NW * BIASB;  // K, V, then the key offsets
   constexpr int RPB = 1024 / ROWB;              // rows per 1 KB wave load
   constexpr int LOADS = TILEB / (1024 * NW);    // 1 KB loads per wave per tile, for K and for V
   static_assert(LOADS >= 1, "tile smaller than one load per wave");
+  constexpr int CP = 2 * LOADS + (W ? 1 : 0);   // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) uint8_t stages[NST * STAGEB];
 
   int h, c;
@@ -437,6 +465,10 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
+  // key offsets past the list end read as 0 (the range check of the buffer resource)
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W ? gbias + ((int64_t)h * cq + i) * N : nullptr), (short)0, (int)(uint32_t)(W ? L * 4 : 0),
+      kBufferFlags);
 
   const int qpos = qbeg + w * 32 + l % 32;
   const bool qok = qpos < qend;
@@ -468,13 +500,18 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) nrow[set][q] = gp[min(tile * BN + trow[q], L - 1)];
   };
-  auto issue = [&](int set, int slot) __attribute__((always_inline)) {
+  auto issue = [&](int set, int slot, int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       const int boff = slot * STAGEB + (w * LOADS + q) * 1024;
       const int voff = (int)((uint32_t)nrow[set][q] * ROWB + lbyte[q]);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
+    }
+    if constexpr (W) {
+      const int boff = slot * STAGEB + 2 * TILEB + w * BIASB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (PARK_LDS void*)(stages + boff), 4, (tile * BN + l % BN) * 4, 0,
+                                               0, 0);
     }
   };
 
@@ -531,6 +568,18 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       for (int kk = 0; kk < KS; ++kk) ka[kk] = *reinterpret_cast<const u32x4_t*>(kt + kofs[st][kk]);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) sacc[st] = mfma32(ka[kk], qb[kk], sacc[st]);
+    }
+    if constexpr (W) {
+      // accumulator e of sub-tile st holds key st * 32 + hl * 16 + e
+      const float* bt = reinterpret_cast<const float*>(kt + 2 * TILEB + w * BIASB);
+#pragma unroll
+      for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(bt + st * 32 + hl * 16 + q * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[st][q * 4 + e] += b4[e];
+        }
     }
     const int nvalid = L - v0;
     if (__builtin_expect(nvalid < BN, 0)) {
@@ -612,14 +661,15 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
 #pragma unroll
     for (int x = 0; x < NST - 1; ++x) load_idx(x, x);
 #pragma unroll
-    for (int x = 0; x < NST - 1; ++x) issue(x, x);
+    for (int x = 0; x < NST - 1; ++x) issue(x, x, x);
 #pragma unroll
     for (int x = NST - 1; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
   }
   // iteration t (stage SL = t % NST): tile t landed, tile t + NST - 1 goes into the stage tile t - 1
   // used, then tile t is computed. Tile t was copied in iteration t - NST + 1 (or the prologue); each
-  // of the NST - 2 iterations since issued 3 LOADS operations (copies and index loads stay within
-  // their iteration; the index loads of iteration t - NST + 1 may precede its copies, so they are not
+  // of the NST - 2 iterations since issued CP + LOADS operations (CP copies: LOADS of K and of V,
+  // plus the key offsets when weighted; LOADS index loads. Copies and index loads stay within their
+  // iteration; the index loads of iteration t - NST + 1 may precede its copies, so they are not
   // counted). In the prologue only the copies of later tiles are counted.
   for (int t = 0; t < nt; t += NST) {
     const bool go_on = w8_unroll<0, NST>([&](auto SLc) __attribute__((always_inline)) {
@@ -628,10 +678,10 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       const int tt = t + SL;
       if (tt >= nt) return false;
       if (tt < NST - 1)
-        w8_wait_barrier<(NST - 2) * 2 * LOADS>();
+        w8_wait_barrier<(NST - 2) * CP>();
       else
-        w8_wait_barrier<3 * LOADS * (NST - 2)>();
-      issue(XS, XS);
+        w8_wait_barrier<(CP + LOADS) * (NST - 2)>();
+      issue(XS, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
       if (active) compute(stages + SL * STAGEB, stages + SL * STAGEB + TILEB, tt * BN);
       return true;
@@ -667,28 +717,40 @@ size_t attn_gather_ints(const Dims& s, int cq) { return (size_t)(s.H * cq) * (si
 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
                               const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
-                              int ck, const int32_t* counts, const int32_t* cols, float scale, void* out, float* lse,
-                              int32_t* tile_base, int32_t* gather, hipStream_t st) {
+                              int ck, const int32_t* counts, const int32_t* cols, const float* log_w, float scale,
+                              void* out, float* lse, int32_t* tile_base, int32_t* gather, float* gbias,
+                              hipStream_t st) {
   int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
+  float* gb = log_w ? gbias : nullptr;
   attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, s.bf16 ? kW8BM : kAttnBM, tile_base);
-  attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, gather,
-                                                                glen);
+  attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, log_w,
+                                                                1.f / scale, gather, glen, gb);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
 #define PARK_ATTN(T, D)                                                                                          \
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
                                                  static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, tile_base, \
-                                                 gather, glen, scale, static_cast<T*>(out), lse);
+                                                 gather, glen, gb, scale, static_cast<T*>(out), lse);
+#define PARK_W8(D, W)                                                                                            \
+  sparse_attn_w8<D, W><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen, gb, \
+                                             scale, oh, lse);
   if (s.bf16) {
     const uint16_t* qh = static_cast<const uint16_t*>(q);
     const uint16_t* kh = static_cast<const uint16_t*>(k);
     const uint16_t* vh = static_cast<const uint16_t*>(v);
     uint16_t* oh = static_cast<uint16_t*>(out);
-    if (s.D == 128)
-      sparse_attn_w8<128><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
-                                                 scale, oh, lse);
-    else
-      sparse_attn_w8<64><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen,
-                                                scale, oh, lse);
+    if (s.D == 128) {
+      if (gb) {
+        PARK_W8(128, true)
+      } else {
+        PARK_W8(128, false)
+      }
+    } else {
+      if (gb) {
+        PARK_W8(64, true)
+      } else {
+        PARK_W8(64, false)
+      }
+    }
   } else {
     if (s.D == 128) {
       PARK_ATTN(float, 128)
@@ -696,6 +758,7 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
       PARK_ATTN(float, 64)
     }
   }
+#undef PARK_W8
 #undef PARK_ATTN
   return hipGetLastError();
 }

@@ -20,13 +20,6 @@ namespace {
 // k-means++ seeding
 // ------------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ uint64_t splitmix_first(uint64_t seed) {
-  uint64_t z = seed + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
 __device__ __forceinline__ double kpp_uniform(uint64_t seed, int head, int side, int m) {
   const uint64_t key = seed ^ ((uint64_t)head << 32) ^ ((uint64_t)side << 24) ^ (uint64_t)m;
   return (double)(splitmix_first(key) >> 11) * 0x1.0p-53;

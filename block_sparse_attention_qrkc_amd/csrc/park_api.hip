@@ -163,11 +163,13 @@ size_t estimator_ws_bytes(const park::Dims& s, int cq, int ck) {
 struct AttnWs {
   int32_t* tile_base;
   int32_t* gather;
+  float* gbias;  // per-key logit offsets of the gather lists (weighted attention only)
 };
-AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck) {
+AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck, bool weighted = false) {
   AttnWs w;
   w.tile_base = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
   w.gather = cv.take<int32_t>(park::attn_gather_ints(s, cq));
+  w.gbias = weighted ? cv.take<float>((size_t)(s.H * cq) * (size_t)s.N) : nullptr;
   return w;
 }
 
@@ -325,6 +327,10 @@ size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_p
       case PARK_ENTRY_SPARSE_ATTN:
         if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
         plan_attn(cv, s, params->cq, params->ck);
+        return cv.off;
+      case PARK_ENTRY_SPARSE_ATTN_WEIGHTED:
+        if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
+        plan_attn(cv, s, params->cq, params->ck, true);
         return cv.off;
       case PARK_ENTRY_ESTIMATOR:
         if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
@@ -527,38 +533,87 @@ park_status park_select_topk(const float* map, int64_t heads, int32_t cq, int32_
   }
 }
 
+park_status park_select_sip(const float* map, int64_t heads, int32_t cq, int32_t ck, const int32_t* k_offsets,
+                            double rho, uint64_t seed, uint8_t* mask, int32_t* counts, int32_t* cols,
+                            int64_t* sel_keys, float* log_w, void* stream) {
+  try {
+    if (heads < 1 || heads > 65535) return fail(PARK_EINVAL, "heads must be in [1, 65535]");
+    if (cq < 1 || cq > park::kMaxClusters) return fail(PARK_EINVAL, "cq must be in [1, %d]", park::kMaxClusters);
+    if (ck < 1 || ck > park::kMaxClusters) return fail(PARK_EINVAL, "ck must be in [1, %d]", park::kMaxClusters);
+    if (!(rho >= 0.0 && rho <= 1.0)) return fail(PARK_EINVAL, "rho must be in [0, 1], got %g", rho);
+    PARK_TRY(check_ptr(map, "map", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(counts, "counts", 4));
+    PARK_TRY(check_ptr(cols, "cols", 4));
+    PARK_TRY(check_ptr(log_w, "log_w", 4));
+    if (sel_keys) PARK_TRY(check_ptr(sel_keys, "sel_keys", 8));
+    return hip_check(park::launch_select_sip(map, heads, cq, ck, k_offsets, rho, seed, mask, counts, cols, sel_keys,
+                                             log_w, (hipStream_t)stream),
+                     "park_select_sip");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_select_sip: internal error");
+  }
+}
+
+namespace {
+park_status sparse_attn_impl(const char* name, const park_shape* shape, const void* q, const void* k, const void* v,
+                             const int32_t* q_perm, const int32_t* q_offsets, int32_t cq, const int32_t* k_perm,
+                             const int32_t* k_offsets, int32_t ck, const int32_t* counts, const int32_t* cols,
+                             const float* log_w, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  park::Dims s;
+  PARK_TRY(check_shape(shape, &s));
+  PARK_TRY(check_ptr(q, "q", 16));
+  PARK_TRY(check_ptr(k, "k", 16));
+  PARK_TRY(check_ptr(v, "v", 16));
+  PARK_TRY(check_ptr(out, "out", 16));
+  PARK_TRY(check_ptr(q_perm, "q_perm", 4));
+  PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
+  PARK_TRY(check_ptr(k_perm, "k_perm", 4));
+  PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+  PARK_TRY(check_ptr(counts, "counts", 4));
+  PARK_TRY(check_ptr(cols, "cols", 4));
+  if (log_w) PARK_TRY(check_ptr(log_w, "log_w", 4));
+  if (lse) PARK_TRY(check_ptr(lse, "lse", 4));
+  PARK_TRY(check_clusters(s, cq, "cq"));
+  PARK_TRY(check_clusters(s, ck, "ck"));
+  if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
+  const bool weighted = log_w != nullptr;
+  Carver meas(nullptr);
+  plan_attn(meas, s, cq, ck, weighted);
+  PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+  Carver cv(ws);
+  AttnWs w = plan_attn(cv, s, cq, ck, weighted);
+  return hip_check(park::launch_sparse_attn(s, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts, cols,
+                                            log_w, resolve_scale(scale, s.D), out, lse, w.tile_base, w.gather,
+                                            w.gbias, (hipStream_t)stream),
+                   name);
+}
+}  // namespace
+
 park_status park_sparse_attn(const park_shape* shape, const void* q, const void* k, const void* v, const int32_t* q_perm,
                              const int32_t* q_offsets, int32_t cq, const int32_t* k_perm, const int32_t* k_offsets,
                              int32_t ck, const int32_t* counts, const int32_t* cols, float scale, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream) {
   try {
-    park::Dims s;
-    PARK_TRY(check_shape(shape, &s));
-    PARK_TRY(check_ptr(q, "q", 16));
-    PARK_TRY(check_ptr(k, "k", 16));
-    PARK_TRY(check_ptr(v, "v", 16));
-    PARK_TRY(check_ptr(out, "out", 16));
-    PARK_TRY(check_ptr(q_perm, "q_perm", 4));
-    PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
-    PARK_TRY(check_ptr(k_perm, "k_perm", 4));
-    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
-    PARK_TRY(check_ptr(counts, "counts", 4));
-    PARK_TRY(check_ptr(cols, "cols", 4));
-    if (lse) PARK_TRY(check_ptr(lse, "lse", 4));
-    PARK_TRY(check_clusters(s, cq, "cq"));
-    PARK_TRY(check_clusters(s, ck, "ck"));
-    if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
-    Carver meas(nullptr);
-    plan_attn(meas, s, cq, ck);
-    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
-    Carver cv(ws);
-    AttnWs w = plan_attn(cv, s, cq, ck);
-    return hip_check(park::launch_sparse_attn(s, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts, cols,
-                                              resolve_scale(scale, s.D), out, lse, w.tile_base, w.gather,
-                                              (hipStream_t)stream),
-                     "park_sparse_attn");
+    return sparse_attn_impl("park_sparse_attn", shape, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts,
+                            cols, nullptr, scale, out, lse, ws, ws_bytes, stream);
   } catch (...) {
     return fail(PARK_EHIP, "park_sparse_attn: internal error");
+  }
+}
+
+park_status park_sparse_attn_weighted(const park_shape* shape, const void* q, const void* k, const void* v,
+                                      const int32_t* q_perm, const int32_t* q_offsets, int32_t cq,
+                                      const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
+                                      const int32_t* counts, const int32_t* cols, const float* log_w, float scale,
+                                      void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!log_w) return fail(PARK_EINVAL, "log_w is NULL");
+    return sparse_attn_impl("park_sparse_attn_weighted", shape, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets,
+                            ck, counts, cols, log_w, scale, out, lse, ws, ws_bytes, stream);
+  } catch (...) {
+    return fail(PARK_EHIP, "park_sparse_attn_weighted: internal error");
   }
 }
 
@@ -657,8 +712,8 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
     if (e == hipSuccess)
       e = park::launch_select_topp(map, s.H, p.cq, p.ck, ko, p.p, o.mask, counts, cols, sk, st);
     if (e == hipSuccess)
-      e = park::launch_sparse_attn(s, q, k, v, qp, qo, p.cq, kp, ko, p.ck, counts, cols, scale, out, o.lse,
-                                   w.aw.tile_base, w.aw.gather, st);
+      e = park::launch_sparse_attn(s, q, k, v, qp, qo, p.cq, kp, ko, p.ck, counts, cols, nullptr, scale, out, o.lse,
+                                   w.aw.tile_base, w.aw.gather, nullptr, st);
     return hip_check(e, "park_forward");
   } catch (...) {
     return fail(PARK_EHIP, "park_forward: internal error");

@@ -155,4 +155,14 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T* total) {
   return res;
 }
 
+// First output of a SplitMix64 generator seeded with `seed` (Steele, Lea & Flood, OOPSLA 2014: the
+// state advances by the golden-ratio increment and passes through a 64-bit finaliser). The counter
+// streams of the seeding and of the block sampling both draw from it.
+__device__ __forceinline__ uint64_t splitmix_first(uint64_t seed) {
+  uint64_t z = seed + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 }  // namespace park

@@ -72,12 +72,16 @@ hipError_t launch_select_topp(const float* map, int64_t H, int cq, int ck, const
                               uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st);
 hipError_t launch_select_topk(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double rho,
                               uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys, hipStream_t st);
+hipError_t launch_select_sip(const float* map, int64_t H, int cq, int ck, const int32_t* k_offsets, double rho,
+                             uint64_t seed, uint8_t* mask, int32_t* counts, int32_t* cols, int64_t* sel_keys,
+                             float* log_w, hipStream_t st);
 
 // attn.hip
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
                               const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
-                              int ck, const int32_t* counts, const int32_t* cols, float scale, void* out,
-                              float* lse, int32_t* tile_base, int32_t* gather, hipStream_t st);
+                              int ck, const int32_t* counts, const int32_t* cols, const float* log_w, float scale,
+                              void* out, float* lse, int32_t* tile_base, int32_t* gather, float* gbias,
+                              hipStream_t st);
 int64_t attn_max_tiles(const Dims& s, int cq);
 // ints of the gather workspace: [H, cq, N] key rows + [H, cq] lengths
 size_t attn_gather_ints(const Dims& s, int cq);

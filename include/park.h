@@ -74,7 +74,8 @@ enum {
   PARK_ENTRY_SELECT_TOPP = 4,
   PARK_ENTRY_SPARSE_ATTN = 5,
   PARK_ENTRY_FORWARD = 6,
-  PARK_ENTRY_ESTIMATOR = 7  /* park_estimator_map, any mode */
+  PARK_ENTRY_ESTIMATOR = 7,  /* park_estimator_map, any mode */
+  PARK_ENTRY_SPARSE_ATTN_WEIGHTED = 8
 };
 
 /* Workspace bytes an entry needs for this shape and these parameters (0 on invalid input). */
@@ -199,6 +200,28 @@ park_status park_select_topk(const float* map, int64_t heads, int32_t cq, int32_
                              int32_t* cols, int64_t* sel_keys, void* stream);
 
 /*
+ * Sampling with inclusion-probability weighting (AB-Attention page, SIP paragraph: blocks are
+ * sampled according to their estimated importance instead of being truncated, and each sampled
+ * block is reweighted by the inverse of its inclusion probability, so that one sparse pass
+ * estimates dense attention). Per row i of head h, with m = the top-k budget of park_select_topk
+ * at ratio rho (the expected number of sampled blocks) and a_j the map row with empty key clusters
+ * and non-positive entries at 0:
+ *   pi_j = min(1, kappa a_j), kappa such that sum_j pi_j = m (every positive block has pi = 1 when
+ *   m reaches their number; computed in fp64 from the fp32 map);
+ *   u_j  = 53 high bits of the first SplitMix64 output seeded with
+ *          seed ^ (h << 32) ^ (2 << 24) ^ (i * ck + j), times 2^-53;
+ *   block j is kept iff u_j < pi_j, with log weight ln(1 / pi_j).
+ * Arguments and outputs as park_select_topk, plus
+ *   seed   the draws' seed (h is the head index within this call)
+ *   log_w  [heads, cq, ck] float32 output: ln(1 / pi_j) for kept blocks, 0 elsewhere; pass it to
+ *          park_sparse_attn_weighted together with counts and cols.
+ */
+park_status park_select_sip(const float* map, int64_t heads, int32_t cq, int32_t ck,
+                            const int32_t* k_offsets, double rho, uint64_t seed, uint8_t* mask,
+                            int32_t* counts, int32_t* cols, int64_t* sel_keys, float* log_w,
+                            void* stream);
+
+/*
  * Attention over the selected blocks only (PARK abstract: attention computed only within the
  * retrieved blocks). Every query of cluster i attends to the keys of the clusters in
  * cols[h, i, 0 .. counts[h, i]-1]; the softmax is renormalised over those keys.
@@ -213,6 +236,24 @@ park_status park_sparse_attn(const park_shape* shape, const void* q, const void*
                              const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
                              const int32_t* counts, const int32_t* cols, float scale, void* out,
                              float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-weighted attention over the selected blocks (AB-Attention page, SIP paragraph: sampled blocks
+ * reweighted by the inverse of their inclusion probability). As park_sparse_attn, except that every
+ * key of selected block j of row i enters the softmax with weight w = exp(log_w[h, i, j]):
+ *   O_t = sum_{j in S} w_j sum_{k in j} e^{s q_t.k} v_k / sum_{j in S} w_j sum_{k in j} e^{s q_t.k},
+ * i.e. each of those logits gains log_w[h, i, j]; lse is the log of the denominator.
+ *   log_w  [heads, cq, ck] float32, read at the selected (i, j) only (from park_select_sip, or any
+ *          finite log weights)
+ * Workspace: park_workspace_bytes(PARK_ENTRY_SPARSE_ATTN_WEIGHTED, ...): the gather lists plus one
+ * float32 logit offset per listed key, [heads, cq, n].
+ */
+park_status park_sparse_attn_weighted(const park_shape* shape, const void* q, const void* k, const void* v,
+                                      const int32_t* q_perm, const int32_t* q_offsets, int32_t cq,
+                                      const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
+                                      const int32_t* counts, const int32_t* cols, const float* log_w,
+                                      float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /*
  * Cluster-contiguous gather and its inverse (the "Clustered" token ordering of PARK Tables 1/10).

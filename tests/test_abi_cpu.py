@@ -119,6 +119,12 @@ def test_validation_errors(L):
     for rho in (-0.1, 1.5, float("nan")):
         st, _ = _status(L, "park_select_topk", FAKE, 2, 10, 20, FAKE, rho, FAKE, FAKE, FAKE, FAKE, None)
         assert st == L.PARK_EINVAL, rho
+    # SIP: ratio outside [0, 1], log weights required
+    for rho in (-0.1, 1.5, float("nan")):
+        st, _ = _status(L, "park_select_sip", FAKE, 2, 10, 20, FAKE, rho, 7, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+        assert st == L.PARK_EINVAL, rho
+    st, msg = _status(L, "park_select_sip", FAKE, 2, 10, 20, FAKE, 0.1, 7, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == L.PARK_EINVAL and "log_w" in msg
     # estimator maps: unknown mode; centroid and full-key modes need bf16 data; missing inputs
     st, msg = _status(L, "park_estimator_map", bp(sh), FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, FAKE, 20, FAKE, 9,
                       0.0, FAKE, FAKE, 1 << 40, None)
@@ -140,6 +146,15 @@ def test_validation_errors(L):
     assert st == L.PARK_EINVAL and "counts" in msg
     st, msg = _status(L, "park_sparse_attn", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE,
                       0.0, FAKE, None, FAKE, 8, None)
+    assert st == L.PARK_EWORKSPACE
+    # weighted attention: log weights required; its workspace also holds the per-key offsets
+    st, msg = _status(L, "park_sparse_attn_weighted", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE,
+                      FAKE, None, 0.0, FAKE, None, FAKE, 1 << 40, None)
+    assert st == L.PARK_EINVAL and "log_w" in msg
+    prm = L.make_params(10, 20, 1, 0.9)
+    plain = L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, sh, prm)
+    st, _ = _status(L, "park_sparse_attn_weighted", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE,
+                    FAKE, FAKE, 0.0, FAKE, None, FAKE, plain, None)
     assert st == L.PARK_EWORKSPACE
     # forward: iters must be >= 1, p in range
     prm = L.make_params(10, 20, 0, 0.9)
@@ -164,3 +179,7 @@ def test_workspace_bytes(L):
     assert L.workspace_bytes(L.PARK_ENTRY_FORWARD, L.park_shape(40, 75600, 96, 1), prm) == 0
     assert L.workspace_bytes(L.PARK_ENTRY_FORWARD, wan, L.make_params(100, 500, 0, 0.9)) == 0
     assert L.workspace_bytes(L.PARK_ENTRY_CLUSTER_K, wan, prm) > L.workspace_bytes(L.PARK_ENTRY_CLUSTER_Q, wan, prm)
+    # the weighted attention adds one float32 offset per gather-list slot, [heads, cq, n]
+    extra = (L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN_WEIGHTED, wan, prm)
+             - L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, wan, prm))
+    assert 40 * 100 * 75600 * 4 <= extra <= 40 * 100 * 75600 * 4 + 1024
