@@ -3,6 +3,8 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan] [--no-cpu] [--no-stages]
 python bench.py --sweep        # p x Ck grid on the Wan-shaped layer (one JSON document)
 python bench.py --schedule     # the long clip's 10-step schedule: full K-means at anchors, warm starts
+python bench.py --estimators   # FC / CC / CF / FF block maps: recall and density of top-p / top-k
+python bench.py --sip          # top-k truncation vs SIP sampling with inverse-probability weights
 
 A step is one park_forward call (QRKC metric, seeded K-means on queries and keys, PAMA map, top-p,
 block-sparse attention) over one synthetic layer already resident in HBM. Prints one JSON line.
@@ -308,6 +310,58 @@ def run_estimators(args, bsa, w, dev, log):
     print(json.dumps(out), flush=True)
 
 
+def run_sip(args, bsa, w, dev, log):
+    """Top-k truncation against sampling with inclusion-probability weighting (AB-Attention page, SIP
+    paragraph) at the same budget on one synthetic layer: for each ratio rho, top-k keeps the k
+    most important blocks of every PAMA row; SIP samples k blocks in expectation with
+    probabilities proportional to importance (capped at 1) and reweights them by 1/pi. Reported per
+    selection: the mean over queries of the relative L2 error of the attention output against dense
+    attention, the mean |LSE - LSE_dense| (top-k's LSE is the log of the kept mass, SIP's estimates
+    the dense one), the recall of the selected keys (dense softmax mass they hold), token density
+    and the attention time; SIP figures are averaged over three seeds."""
+    Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
+    ws = bsa.Workspace()
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed,
+                         outputs=("q_perm", "q_offsets", "k_perm", "k_offsets", "map"), ws=ws)
+    geo = (r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"])
+    cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+    cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+    od, ld = bsa.park_sparse_attn(Q, K, V, *geo, cnt_all, cols_all, ws=ws)
+    odn = od.float().norm(dim=-1)
+    qsz = torch.diff(r["q_offsets"], dim=1).double()
+    out = {"sip": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "points": []}
+
+    def stats(o, lse, sel, ms):
+        err = ((o.float() - od.float()).norm(dim=-1) / odn.clamp_min(1e-30)).mean()
+        fin = torch.isfinite(lse)
+        lerr = torch.where(fin, (lse - ld).abs(), torch.zeros_like(lse)).sum() / fin.sum()
+        _, lsel = bsa.park_sparse_attn(Q, K, V, *geo, sel["counts"], sel["cols"], ws=ws)
+        rec = torch.exp(lsel - ld).mean()
+        tokens = float((qsz * sel["sel_keys"].double()).sum()) / (w.n * w.n * w.heads)
+        return {"out_rel_err": float(err), "lse_abs_err": float(lerr), "recall": float(rec),
+                "token_density": tokens, "attn_ms": ms, "unselected_queries": int((~fin).sum())}
+
+    for rho in (0.05, 0.1, 0.2):
+        sel = bsa.park_select_topk(r["map"], r["k_offsets"], rho)
+        o, lse = bsa.park_sparse_attn(Q, K, V, *geo, sel["counts"], sel["cols"], ws=ws)
+        ms = time_call(lambda: bsa.park_sparse_attn(Q, K, V, *geo, sel["counts"], sel["cols"], out=o, lse=lse, ws=ws), 3)
+        top = stats(o, lse, sel, ms)
+        runs = []
+        for seed in range(3):
+            ss = bsa.park_select_sip(r["map"], r["k_offsets"], rho, seed=seed)
+            o, lse = bsa.park_sparse_attn_weighted(Q, K, V, *geo, ss["counts"], ss["cols"], ss["log_w"], ws=ws)
+            ms = time_call(lambda: bsa.park_sparse_attn_weighted(Q, K, V, *geo, ss["counts"], ss["cols"], ss["log_w"],
+                                                                 out=o, lse=lse, ws=ws), 3)
+            runs.append(stats(o, lse, ss, ms))
+        sip = {k: sum(x[k] for x in runs) / len(runs) for k in runs[0]}
+        sel_ms = time_call(lambda: bsa.park_select_sip(r["map"], r["k_offsets"], rho, seed=0), 3)
+        pt = {"rho": rho, "top_k": {k: round(v, 5) for k, v in top.items()},
+              "sip": {k: round(v, 5) for k, v in sip.items()}, "sip_select_ms": round(sel_ms, 3)}
+        out["points"].append(pt)
+        log(f"sip {pt}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +375,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="p x Ck grid on the Wan-shaped layer (own JSON document)")
     ap.add_argument("--estimators", action="store_true",
                     help="FC / CC / CF / FF block maps: recall and density of their top-p and top-k selections")
+    ap.add_argument("--sip", action="store_true",
+                    help="top-k truncation vs SIP sampling with inverse-probability weights at equal budgets")
     ap.add_argument("--schedule", action="store_true",
                     help="the long clip's multi-step schedule with warm starts (own JSON document)")
     ap.add_argument("--kernel-only", choices=["sparse_attn", "assign", "pama"], default=None,
@@ -347,6 +403,9 @@ def main():
         return
     if args.schedule:
         run_schedule(args, bsa, synth.WORKLOADS["long"], dev, log)
+        return
+    if args.sip:
+        run_sip(args, bsa, w, dev, log)
         return
     Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
     torch.cuda.synchronize()
