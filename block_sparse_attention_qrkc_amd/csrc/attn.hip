@@ -387,8 +387,10 @@ __device__ __forceinline__ int chunk_swz(int r) {
 // 256-query tiles: eight waves x 32 queries share one work-group per CU (two waves per SIMD), so
 // each key/value tile copied to LDS serves 256 queries. Tiles of 32 keys (d = 128; 64 for d = 64,
 // so each wave copies 1 KB of K and of V per tile) stream through a ring of four stages, copied
-// three tiles ahead; a wave waits only for the copies of the tile it is about to read (a counted
-// vmcnt, then a plain barrier: a fenced barrier would also wait for the copies still in flight).
+// two tiles ahead of the tile being scored; a wave waits only for the copies of the tile it is about
+// to read (a counted vmcnt, then a plain barrier: a fenced barrier would also wait for the copies
+// still in flight). The loop is software-pipelined: the score MFMAs of tile t + 1 are interleaved
+// with the softmax of tile t.
 constexpr int kW8BM = 256;  // queries per work item
 [[maybe_unused]] constexpr int kW8BN = 32;   // keys per tile for d = 128
 [[maybe_unused]] constexpr int kW8NST = 4;   // LDS stages of one tile (K and V)
@@ -556,21 +558,25 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       }
   }
 
-  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int v0) __attribute__((always_inline)) {
-    f32x16_t sacc[NSUB];
+  // Software-pipelined loop: iteration t issues the score MFMAs of tile t + 1 and then runs the
+  // softmax of tile t, whose scores came from iteration t - 1, so the matrix cores work on the next
+  // tile while the vector ALUs exponentiate this one; then the P V MFMAs of tile t.
+  f32x16_t sbuf[2][NSUB];
+  auto s_tile = [&](const uint8_t* kt, f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < NSUB; ++st) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
-      // all K operands of the sub-tile are read before its MFMAs, so LDS latency is paid once
+      for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
       u32x4_t ka[KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) ka[kk] = *reinterpret_cast<const u32x4_t*>(kt + kofs[st][kk]);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) sacc[st] = mfma32(ka[kk], qb[kk], sacc[st]);
+      for (int kk = 0; kk < KS; ++kk) sa[st] = mfma32(ka[kk], qb[kk], sa[st]);
     }
+  };
+  // key offsets (weighted form) and the mask of keys past the list end
+  auto adjust = [&](const uint8_t* kt, f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
     if constexpr (W) {
-      // accumulator e of sub-tile st holds key st * 32 + hl * 16 + e
       const float* bt = reinterpret_cast<const float*>(kt + 2 * TILEB + w * BIASB);
 #pragma unroll
       for (int st = 0; st < NSUB; ++st)
@@ -578,7 +584,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
         for (int q = 0; q < 4; ++q) {
           const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(bt + st * 32 + hl * 16 + q * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[st][q * 4 + e] += b4[e];
+          for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += b4[e];
         }
     }
     const int nvalid = L - v0;
@@ -587,53 +593,37 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       for (int st = 0; st < NSUB; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (st * 32 + hl * 16 + e >= nvalid) sacc[st][e] = -INFINITY;
+          if (st * 32 + hl * 16 + e >= nvalid) sa[st][e] = -INFINITY;
     }
-    auto tile_max = [&]() __attribute__((always_inline)) {
-      float mx = sacc[0][0];
+  };
+  auto tile_max = [&](const f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
+    float mx = sa[0][0];
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st)
+    for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
-      return fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    };
-    if (v0 == 0) m_ref = tile_max();
-    u32x4_t pb[NSUB][2];
-    float ps;
-    auto weights = [&]() __attribute__((always_inline)) {
-      const float mb = m_ref * sl2;
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[st][e]);
+    return fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  };
+  auto weights = [&](const f32x16_t(&sa)[NSUB], u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
+    const float mb = m_ref * sl2;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st) {
-        float pv[16];
+    for (int st = 0; st < NSUB; ++st) {
+      float pv[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][e], sl2, -mb));
+      for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[st][e], sl2, -mb));
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t pk = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
-            pb[st][kh][q] = pk;
-            s4[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, s4[q], false);
-          }
-      }
-      ps = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    };
-    weights();
-    if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
-      const float mx = tile_max();
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-      m_ref = m_new;
-      weights();
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t pk = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
+          pb[st][kh][q] = pk;
+          s4[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, s4[q], false);
+        }
     }
-    l_run += ps;
-    // V^T operands of all head-dim blocks are read before the PV MFMAs
+    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  };
+  auto pv_tile = [&](const uint8_t* vt, const u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
     u32x4_t va[DT][NSUB][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -657,33 +647,70 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   };
 
   if (nt > 0) {
-    // prologue: tiles 0 .. NST-2 into stages 0 .. NST-2, rows of tiles NST-1 .. 2 NST-2 into their sets
+    // prologue: tiles 0 .. NST-2 into stages 0 .. NST-2, rows of tiles NST-1 .. 2 NST-2 into their
+    // sets; then the scores of tile 0 (its copies are followed by NST - 2 tiles' copies)
 #pragma unroll
     for (int x = 0; x < NST - 1; ++x) load_idx(x, x);
 #pragma unroll
     for (int x = 0; x < NST - 1; ++x) issue(x, x, x);
 #pragma unroll
     for (int x = NST - 1; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
+    w8_wait_barrier<(NST - 2) * CP>();
+    if (active) {
+      s_tile(stages, sbuf[0]);
+      adjust(stages, sbuf[0], 0);
+      m_ref = tile_max(sbuf[0]);
+    }
   }
-  // iteration t (stage SL = t % NST): tile t landed, tile t + NST - 1 goes into the stage tile t - 1
-  // used, then tile t is computed. Tile t was copied in iteration t - NST + 1 (or the prologue); each
-  // of the NST - 2 iterations since issued CP + LOADS operations (CP copies: LOADS of K and of V,
-  // plus the key offsets when weighted; LOADS index loads. Copies and index loads stay within their
-  // iteration; the index loads of iteration t - NST + 1 may precede its copies, so they are not
-  // counted). In the prologue only the copies of later tiles are counted.
+  // iteration t (stage SL = t % NST): tile t + 1 landed, tile t + NST - 1 goes into the stage tile
+  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2 (or the prologue); each of the NST - 3
+  // iterations since issued CP + LOADS operations. Early iterations wait for all but (NST - 3) CP
+  // operations, which covers the prologue's copies of tile t + 1. Scores of tile t live in
+  // sbuf[t % 2] (NST is even, so the parity of the stage is the parity of the tile).
+  static_assert(NST % 2 == 0 && NST >= 4, "pipelined ring: an even number of stages, at least four");
   for (int t = 0; t < nt; t += NST) {
     const bool go_on = w8_unroll<0, NST>([&](auto SLc) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLc)::value;
+      constexpr int SN = (SL + 1) % NST;
       constexpr int XS = (SL + NST - 1) % NST;
+      constexpr int PC = SL % 2, PN = (SL + 1) % 2;
       const int tt = t + SL;
       if (tt >= nt) return false;
-      if (tt < NST - 1)
-        w8_wait_barrier<(NST - 2) * CP>();
+      if (tt < NST - 2)
+        w8_wait_barrier<(NST - 3) * CP>();
       else
-        w8_wait_barrier<(CP + LOADS) * (NST - 2)>();
+        w8_wait_barrier<(CP + LOADS) * (NST - 3)>();
       issue(XS, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
-      if (active) compute(stages + SL * STAGEB, stages + SL * STAGEB + TILEB, tt * BN);
+      if (active) {
+        // scores of tile tt + 1 (a tile past the list end holds clamped, valid rows)
+        s_tile(stages + SN * STAGEB, sbuf[PN]);
+        u32x4_t pb[NSUB][2];
+        float ps = weights(sbuf[PC], pb);
+        // instruction order of the block above: the first K reads, then each score MFMA followed by
+        // a share of the softmax (ALU, then exponentials) that runs while the matrix core works
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int g = 0; g < KS * NSUB; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4 * NSUB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x400, 2 * NSUB, 0);
+        }
+        if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
+          const float m_new = fmaxf(m_ref, tile_max(sbuf[PC]));
+          const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+          m_ref = m_new;
+          ps = weights(sbuf[PC], pb);
+        }
+        l_run += ps;
+        pv_tile(stages + SL * STAGEB + TILEB, pb);
+        adjust(stages + SN * STAGEB, sbuf[PN], (tt + 1) * BN);
+      }
       return true;
     });
     if (!go_on) break;
@@ -708,6 +735,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   }
 #endif
 }
+
 
 }  // namespace
 
