@@ -425,8 +425,9 @@ __device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
   return v;
 }
 
+// H heads from head h0 on: the side pointers start at head h0, the draws use the head's own index.
 template <int D, int NT>
-__global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, int64_t N, uint64_t seed) {
+__global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, int h0, int64_t N, uint64_t seed) {
   constexpr int kCoopWaves = NT / kWave;
   constexpr int ROW_U32 = D / 2;
   extern __shared__ uint32_t lrows[];  // [SP - threads][D / 2] bf16 pairs of the LDS-resident rows
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
   for (int m = 0; m < C; ++m) {
     int t;
     if (m == 0) {
-      const int t0 = (int)(kpp_uniform(seed, h, sd.side, 0) * (double)S);
+      const int t0 = (int)(kpp_uniform(seed, h0 + h, sd.side, 0) * (double)S);
       t = t0 < S ? t0 : S - 1;
     } else {
       // ---- running D^2 sums inside each wave (candidate order: register rows of waves 0..7, then
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
         int owner = -1;
         double v = 0.0;
         if (total > 0.0) {
-          v = kpp_uniform(seed, h, sd.side, m) * total;
+          v = kpp_uniform(seed, h0 + h, sd.side, m) * total;
           const uint64_t over = __ballot(l < G && run > v);
           if (over) {
             owner = __ffsll((unsigned long long)over) - 1;
@@ -1236,8 +1237,12 @@ static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budg
   return true;
 }
 
+// One cooperative launch over heads h0 .. h0 + Hb - 1. The failure flag of a launch sits after its
+// heads' step flags (for a leading batch: on the first flag of the next batch, which that batch's
+// own launch clears before it runs).
 static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nsides, const int* G, int nt,
-                                  uint64_t seed, hipStream_t st) {
+                                  uint64_t seed, hipStream_t st, int h0 = 0, int Hb = -1) {
+  if (Hb < 0) Hb = (int)s.H;
   CoopSide cs[2];
   size_t lds = 0;
   int64_t total = 0;
@@ -1245,15 +1250,18 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
     const KppArgs& a = sides[q];
     const int S = kpp_candidates(s.N, a.C);
     const int SP = (int)ceil_div(S, G[q]);
-    cs[q] = CoopSide{static_cast<const uint16_t*>(a.x), a.xx, a.metric ? a.y : nullptr, a.cent,
-                     reinterpret_cast<uint64_t*>(a.psum), a.sync, a.C, S, a.side, G[q], SP};
+    uint64_t* psum = reinterpret_cast<uint64_t*>(a.psum) + (int64_t)h0 * a.C * kCoopMaxParts * 2;
+    int* sync = a.sync + (int64_t)h0 * a.C * 3;
+    cs[q] = CoopSide{static_cast<const uint16_t*>(a.x) + (int64_t)h0 * s.N * s.D, a.xx + (int64_t)h0 * S,
+                     a.metric ? a.y + (int64_t)h0 * S * s.D : nullptr, a.cent + (int64_t)h0 * a.C * s.D, psum,
+                     sync, a.C, S, a.side, G[q], SP};
     const size_t l = (size_t)(SP > nt ? SP - nt : 0) * (size_t)s.D * 2;
     lds = l > lds ? l : lds;
-    total += s.H * G[q];
-    const int64_t nsync = s.H * (int64_t)a.C * 3 + 1;
-    fill_i32<<<(unsigned)ceil_div(nsync, 256), 256, 0, st>>>(a.sync, nsync, 0);
-    const int64_t nslot = s.H * (int64_t)a.C * kCoopMaxParts * 2 * 2;  // as int32 words
-    fill_i32<<<(unsigned)ceil_div(nslot, 256), 256, 0, st>>>(reinterpret_cast<int*>(a.psum), nslot, 0);
+    total += (int64_t)Hb * G[q];
+    const int64_t nsync = (int64_t)Hb * a.C * 3 + 1;
+    fill_i32<<<(unsigned)ceil_div(nsync, 256), 256, 0, st>>>(sync, nsync, 0);
+    const int64_t nslot = (int64_t)Hb * a.C * kCoopMaxParts * 2 * 2;  // as int32 words
+    fill_i32<<<(unsigned)ceil_div(nslot, 256), 256, 0, st>>>(reinterpret_cast<int*>(psum), nslot, 0);
   }
   if (nsides == 1) {
     cs[1] = cs[0];
@@ -1261,15 +1269,40 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int H = (int)s.H;
+  int H = Hb;
   int64_t N = s.N;
-  void* args[] = {&cs[0], &cs[1], &H, &N, &seed};
+  void* args[] = {&cs[0], &cs[1], &H, &h0, &N, &seed};
   const void* fn = nt == kCoopThreads
                        ? (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreads> : (const void*)kpp_coop<64, kCoopThreads>)
                        : (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreadsWide>
                                      : (const void*)kpp_coop<64, kCoopThreadsWide>);
   (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   return hipLaunchCooperativeKernel(fn, dim3((unsigned)total), dim3((unsigned)nt), args, (unsigned)lds, st);
+}
+
+// Sides whose candidates need more 512-thread parts per head than one launch over all heads can
+// hold run in batches of heads, 2 to 4 launches per side, each with the whole chip for its heads
+// (the 1024-thread parts are kept for what still does not fit). True when every side launched.
+static bool batched_kpp(const Dims& s, const KppArgs* sides, int nsides, int cus, uint64_t seed, hipStream_t st) {
+  int nb[2] = {0, 0}, G[2][1];
+  for (int q = 0; q < nsides; ++q) {
+    for (int B = 1; B <= 4 && !nb[q]; ++B) {
+      const int hb = (int)ceil_div(s.H, B);
+      if (cus / hb > 0 && plan_parts(s, sides + q, 1, cus / hb, kCoopThreads, G[q])) nb[q] = B;
+    }
+    if (!nb[q]) return false;
+  }
+  for (int q = 0; q < nsides; ++q) {
+    const int hb = (int)ceil_div(s.H, nb[q]);
+    for (int h0 = 0; h0 < (int)s.H; h0 += hb) {
+      if (launch_kpp_coop(s, sides + q, 1, G[q], kCoopThreads, seed, st, h0, (int)std::min<int64_t>(hb, s.H - h0)) !=
+          hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+      }
+    }
+  }
+  return true;
 }
 
 hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
@@ -1308,7 +1341,8 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
       const int budget = cus / (int)s.H;
       int G[2];
       // in order: both sides in one launch with 512-thread parts; one launch per side with
-      // 512-thread parts; both sides with 1024-thread parts; per side the narrowest parts that fit
+      // 512-thread parts; per side, 512-thread parts over batches of heads; both sides with
+      // 1024-thread parts; per side the narrowest parts that fit
       if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreads, G)) {
         if (launch_kpp_coop(s, sides, nsides, G, kCoopThreads, seed, st) == hipSuccess) return hipSuccess;
         (void)hipGetLastError();
@@ -1318,6 +1352,8 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
             launch_kpp_coop(s, sides + 1, 1, G + 1, kCoopThreads, seed, st) == hipSuccess)
           return hipSuccess;
         (void)hipGetLastError();
+      } else if (batched_kpp(s, sides, nsides, cus, seed, st)) {
+        return hipSuccess;
       } else if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreadsWide, G)) {
         if (launch_kpp_coop(s, sides, nsides, G, kCoopThreadsWide, seed, st) == hipSuccess) return hipSuccess;
         (void)hipGetLastError();
