@@ -418,6 +418,76 @@ __device__ __forceinline__ bool w8_unroll(F&& f) {
 
 // W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
 // units), copied into LDS with the tile and added to the scores
+// LDS reads the kernel writes out itself, each block ending by waiting for its reads. The compiler
+// cannot tell which LDS the transposing read builtin reads, nor order a read of the index lists
+// against the direct HBM -> LDS copies of later tiles, and would wait for every copy in flight
+// before such a read; the explicit counted waits and barriers already order them.
+// Sixteen transposing reads (ds_read_b64_tr_b16, 4 x 16-bit per lane) at a common offset.
+template <int OFF>
+__device__ __forceinline__ void tr_read16(u32x2_t (&r)[16], const uint32_t (&a)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %3, %19 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %4, %20 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %5, %21 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %6, %22 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %7, %23 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %8, %24 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %9, %25 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %10, %26 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %11, %27 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %12, %28 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %13, %29 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %14, %30 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %15, %31 offset:%32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]),
+        "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15]), "i"(OFF)
+      : "memory");
+}
+// Eight 16-byte reads at a common offset.
+template <int OFF>
+__device__ __forceinline__ void lds_read8_b128(u32x4_t (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%16\n\t"
+      "ds_read_b128 %1, %9 offset:%16\n\t"
+      "ds_read_b128 %2, %10 offset:%16\n\t"
+      "ds_read_b128 %3, %11 offset:%16\n\t"
+      "ds_read_b128 %4, %12 offset:%16\n\t"
+      "ds_read_b128 %5, %13 offset:%16\n\t"
+      "ds_read_b128 %6, %14 offset:%16\n\t"
+      "ds_read_b128 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+      : "memory");
+}
+// Four 16-byte reads at consecutive 16-byte offsets.
+template <int OFF>
+__device__ __forceinline__ void lds_read4_b128(u32x4_t (&r)[4], uint32_t a) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a), "i"(OFF), "i"(OFF + 16), "i"(OFF + 32), "i"(OFF + 48)
+      : "memory");
+}
+// One dword.
+__device__ __forceinline__ int lds_read_b32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
+// units), copied into LDS with the tile and added to the scores
 template <int D, bool W>
 __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restrict__ Q,
                                                          const uint16_t* __restrict__ K,
@@ -492,21 +562,31 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
   }
   const int nt = (L + BN - 1) / BN;
-  int nrow[NST][LOADS];  // gather-list rows of tile x live in set x % NST from iteration x - 2 NST + 1 on
+  // Gather-list entries of tile x reach LDS (set x % NST, one 256-byte region per wave, lane l
+  // holding entry x * BN + l % BN) by a direct load in iteration x - 2 NST + 1; the lane's entry is
+  // read into a register at the end of iteration x - NST, ready for the copies of iteration
+  // x - NST + 1.
+  static_assert(LOADS == 1, "one 1 KB copy per wave and tile");
+  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][NW][kWave];
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, (int)(uint32_t)(L * 4),
+                                                                       kBufferFlags);
+  constexpr int IL = 1;  // index loads per wave and tile
   auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
-    // read through a pointer the compiler cannot see through, so the loads stay between the barriers
-    // of their iteration (the wait counts below count every vector-memory operation of one)
-    const int32_t* rp = rows;
-    asm volatile("" : "+s"(rp));
-    const __attribute__((address_space(1))) int32_t* gp = (const __attribute__((address_space(1))) int32_t*)rp;
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) nrow[set][q] = gp[min(tile * BN + trow[q], L - 1)];
+    // entries past the list end read as 0 (a valid row; its scores are masked)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][w][0], 4, (tile * BN + l % BN) * 4, 0, 0,
+                                             0);
   };
-  auto issue = [&](int set, int slot, int tile) __attribute__((always_inline)) {
+  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][w][trow[0]]);
+  auto read_idx = [&](int set) __attribute__((always_inline)) {
+    return lds_read_b32(ibase + (uint32_t)(set * NW * kWave * 4));
+  };
+  int nnext = 0;  // gather-list row of this lane's copy in the next issue
+  auto issue = [&](int nrow0, int slot, int tile) __attribute__((always_inline)) {
+    const int nrow[1] = {nrow0};
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       const int boff = slot * STAGEB + (w * LOADS + q) * 1024;
-      const int voff = (int)((uint32_t)nrow[set][q] * ROWB + lbyte[q]);
+      const int voff = (int)((uint32_t)nrow[q] * ROWB + lbyte[q]);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
     }
@@ -562,30 +642,50 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   // softmax of tile t, whose scores came from iteration t - 1, so the matrix cores work on the next
   // tile while the vector ALUs exponentiate this one; then the P V MFMAs of tile t.
   f32x16_t sbuf[2][NSUB];
-  auto s_tile = [&](const uint8_t* kt, f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
+  // scores of one tile: its eight K operand reads in one block, then the MFMAs
+  const uint32_t sbase = (uint32_t)(size_t)((PARK_LDS uint8_t*)stages);
+  static_assert(KS * NSUB == 8, "eight K reads per tile");
+  auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(OFFc)::value;
+    uint32_t a[8];
+    u32x4_t ka[8];
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) a[st * KS + kk] = sbase + kofs[st][kk];
+    if constexpr (OFF <= 65535) {
+      lds_read8_b128<OFF>(ka, a);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] += OFF;
+      lds_read8_b128<0>(ka, a);
+    }
 #pragma unroll
     for (int st = 0; st < NSUB; ++st) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
-      u32x4_t ka[KS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) ka[kk] = *reinterpret_cast<const u32x4_t*>(kt + kofs[st][kk]);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) sa[st] = mfma32(ka[kk], qb[kk], sa[st]);
+      for (int kk = 0; kk < KS; ++kk) sa[st] = mfma32(ka[st * KS + kk], qb[kk], sa[st]);
     }
   };
   // key offsets (weighted form) and the mask of keys past the list end
-  auto adjust = [&](const uint8_t* kt, f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
+  auto adjust = [&](auto OFFc, f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
     if constexpr (W) {
-      const float* bt = reinterpret_cast<const float*>(kt + 2 * TILEB + w * BIASB);
+      constexpr int OFF = decltype(OFFc)::value;  // the stage
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(bt + st * 32 + hl * 16 + q * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += b4[e];
+      for (int st = 0; st < NSUB; ++st) {
+        u32x4_t b[4];
+        const uint32_t ba = sbase + 2 * TILEB + w * BIASB + (st * 32 + hl * 16) * 4;
+        if constexpr (OFF + 48 <= 65535) {
+          lds_read4_b128<OFF>(b, ba);
+        } else {
+          lds_read4_b128<0>(b, ba + OFF);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += __uint_as_float(b[q][e]);
+      }
     }
     const int nvalid = L - v0;
     if (__builtin_expect(nvalid < BN, 0)) {
@@ -623,27 +723,37 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     }
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
   };
-  auto pv_tile = [&](const uint8_t* vt, const u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
-    u32x4_t va[DT][NSUB][2];
+  // V^T operands of a tile: all sixteen reads in one block, then the P V MFMAs
+  static_assert(DT * NSUB * 4 == 16, "sixteen V^T reads per tile");
+  auto pv_tile = [&](auto OFFc, const u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(OFFc)::value;
+    uint32_t a[16];
+    u32x2_t r[16];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(vt + vofs[dt][st][kh][0]));
-          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(vt + vofs[dt][st][kh][1]));
-          const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
-          const u32x2_t a2 = __builtin_bit_cast(u32x2_t, t2);
-          va[dt][st][kh] = u32x4_t{a1[0], a1[1], a2[0], a2[1]};
-        }
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int z = 0; z < 2; ++z) a[((dt * NSUB + st) * 2 + kh) * 2 + z] = sbase + vofs[dt][st][kh][z];
+    if constexpr (OFF <= 65535) {  // the instruction's offset field holds 16 bits
+      tr_read16<OFF>(r, a);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a[j] += OFF;
+      tr_read16<0>(r, a);
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) o[dt] = mfma32(va[dt][st][kh], pb[st][kh], o[dt]);
+        for (int kh = 0; kh < 2; ++kh) {
+          const int j = ((dt * NSUB + st) * 2 + kh) * 2;
+          const u32x4_t va = u32x4_t{r[j][0], r[j][1], r[j + 1][0], r[j + 1][1]};
+          o[dt] = mfma32(va, pb[st][kh], o[dt]);
+        }
   };
 
   if (nt > 0) {
@@ -651,21 +761,23 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     // sets; then the scores of tile 0 (its copies are followed by NST - 2 tiles' copies)
 #pragma unroll
     for (int x = 0; x < NST - 1; ++x) load_idx(x, x);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
-    for (int x = 0; x < NST - 1; ++x) issue(x, x, x);
+    for (int x = 0; x < NST - 1; ++x) issue(read_idx(x), x, x);
 #pragma unroll
     for (int x = NST - 1; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
-    w8_wait_barrier<(NST - 2) * CP>();
+    w8_wait_barrier<0>();  // once per work item: every copy and entry of the prologue landed
+    nnext = read_idx(NST - 1);
     if (active) {
-      s_tile(stages, sbuf[0]);
-      adjust(stages, sbuf[0], 0);
+      s_tile(std::integral_constant<int, 0>{}, sbuf[0]);
+      adjust(std::integral_constant<int, 0>{}, sbuf[0], 0);
       m_ref = tile_max(sbuf[0]);
     }
   }
   // iteration t (stage SL = t % NST): tile t + 1 landed, tile t + NST - 1 goes into the stage tile
-  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2 (or the prologue); each of the NST - 3
-  // iterations since issued CP + LOADS operations. Early iterations wait for all but (NST - 3) CP
-  // operations, which covers the prologue's copies of tile t + 1. Scores of tile t live in
+  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2 (or the prologue, which waited for all
+  // of its copies); each of the NST - 3 iterations since issued CP + IL vector-memory operations
+  // (copies, then the index load). Scores of tile t live in
   // sbuf[t % 2] (NST is even, so the parity of the stage is the parity of the tile).
   static_assert(NST % 2 == 0 && NST >= 4, "pipelined ring: an even number of stages, at least four");
   for (int t = 0; t < nt; t += NST) {
@@ -676,20 +788,16 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       constexpr int PC = SL % 2, PN = (SL + 1) % 2;
       const int tt = t + SL;
       if (tt >= nt) return false;
-      if (tt < NST - 2)
-        w8_wait_barrier<(NST - 3) * CP>();
-      else
-        w8_wait_barrier<(CP + LOADS) * (NST - 3)>();
-      issue(XS, XS, tt + NST - 1);
+      w8_wait_barrier<(NST - 3) * (CP + IL)>();
+      issue(nnext, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
       if (active) {
         // scores of tile tt + 1 (a tile past the list end holds clamped, valid rows)
-        s_tile(stages + SN * STAGEB, sbuf[PN]);
+        s_tile(std::integral_constant<int, SN * STAGEB>{}, sbuf[PN]);
         u32x4_t pb[NSUB][2];
         float ps = weights(sbuf[PC], pb);
-        // instruction order of the block above: the first K reads, then each score MFMA followed by
-        // a share of the softmax (ALU, then exponentials) that runs while the matrix core works
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // instruction order of the block above: each score MFMA followed by a share of the softmax
+        // (ALU, then exponentials) that runs while the matrix core works
 #pragma unroll
         for (int g = 0; g < KS * NSUB; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -708,9 +816,12 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
           ps = weights(sbuf[PC], pb);
         }
         l_run += ps;
-        pv_tile(stages + SL * STAGEB + TILEB, pb);
-        adjust(stages + SN * STAGEB, sbuf[PN], (tt + 1) * BN);
+        pv_tile(std::integral_constant<int, SL * STAGEB + TILEB>{}, pb);
+        adjust(std::integral_constant<int, SN * STAGEB>{}, sbuf[PN], (tt + 1) * BN);
       }
+      // entries of tile tt + NST (set SL, loaded in iteration tt - NST + 1: landed before this
+      // iteration's wait) for the next iteration's copies
+      nnext = read_idx(SL);
       return true;
     });
     if (!go_on) break;
