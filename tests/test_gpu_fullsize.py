@@ -200,6 +200,66 @@ def test_full_attention_sampled(full):
     print(f"[full attention] max-abs {worst:.2e} mean-abs {tot / n:.2e}; recall mean-abs error {rec_err:.2e}")
 
 
+def test_full_topk_and_sip(full):
+    """Top-k at rho = 0.1 on every row of every head, and SIP sampling at the same budget on the
+    sampled heads, against the oracle fed the kernel's map (differing SIP decisions must be draws
+    within 1e-9 of their probability)."""
+    w, Q, K, V, r, ws = full
+    A = to64(r["map"])
+    tk = bsa.park_select_topk(r["map"], r["k_offsets"], 0.1)
+    si = bsa.park_select_sip(r["map"], r["k_offsets"], 0.1, seed=3)
+    cnt, cols = np_i(tk["counts"]), np_i(tk["cols"])
+    near = 0
+    for h in range(w.heads):
+        sizes = np.diff(np_i(r["k_offsets"][h]))
+        _, co, colo, _ = O.select_topk(A[h], sizes, 0.1)
+        assert np.array_equal(cnt[h], co)
+        for i in range(w.cq):
+            cg = cols[h, i, :cnt[h, i]]
+            if not np.array_equal(cg, colo[i]):
+                kept = A[h, i, colo[i]]
+                assert np.all(np.abs(A[h, i, np.setxor1d(cg, colo[i])] - kept.min()) <= TAU), (h, i)
+                near += 1
+    sc, scol, slw = np_i(si["counts"]), np_i(si["cols"]), to64(si["log_w"])
+    for h in _heads(w):
+        sizes = np.diff(np_i(r["k_offsets"][h]))
+        _, _, colo, _, lwo, pi = O.select_sip(A[h], sizes, 0.1, seed=3, head=h)
+        for i in range(w.cq):
+            cg = scol[h, i, :sc[h, i]]
+            for j in np.setxor1d(cg, colo[i]):
+                assert abs(O.sip_uniform(3, h, i, int(j), w.ck) - pi[i, j]) <= 1e-9, (h, i, j)
+            both = np.intersect1d(cg, colo[i])
+            assert np.abs(slw[h, i, both] - lwo[i, both]).max(initial=0.0) <= 1e-6
+    print(f"[full top-k] near-ties: {near}")
+
+
+def test_full_weighted_attention_sampled(full):
+    """Block-weighted attention over a SIP selection (rho = 0.1): sampled query blocks of the sampled
+    heads against the fp64 weighted softmax."""
+    w, Q, K, V, r, ws = full
+    si = bsa.park_select_sip(r["map"], r["k_offsets"], 0.1, seed=4)
+    out, lse = bsa.park_sparse_attn_weighted(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"],
+                                             si["counts"], si["cols"], si["log_w"], ws=ws)
+    rng = np.random.default_rng(17)
+    worst, tot, n = 0.0, 0.0, 0
+    for h in _heads(w):
+        qp, qo = np_i(r["q_perm"][h]), np_i(r["q_offsets"][h])
+        kp, ko = np_i(r["k_perm"][h]), np_i(r["k_offsets"][h])
+        rows = _sample_blocks(qo, rng)
+        Oo, Lo = O.weighted_sparse_attention(to64(Q[h]), to64(K[h]), to64(V[h]), qp, qo, kp, ko,
+                                             cols_list(np_i(si["counts"][h]), np_i(si["cols"][h])),
+                                             to64(si["log_w"][h]), w.scale, rows=rows)
+        t = np.concatenate([qp[qo[i]:qo[i + 1]] for i in rows])
+        e = np.abs(to64(out[h])[t] - Oo[t])
+        worst = max(worst, e.max())
+        tot += e.sum()
+        n += e.size
+        assert np.abs(to64(lse[h])[t] - Lo[t]).max() <= LSE_ABS
+    assert worst <= ATTN_MAX_ABS, worst
+    assert tot / n <= ATTN_MEAN_ABS, tot / n
+    print(f"[full weighted attention] max-abs {worst:.2e} mean-abs {tot / n:.2e}")
+
+
 def test_full_output_everywhere(full):
     """Every token of every head gets a finite output (every live query block selects at least one
     non-empty key block at p < 1), and a second call is bitwise identical."""
