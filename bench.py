@@ -47,20 +47,36 @@ def time_call(fn, reps, warmup=1):
 
 
 def cpu_baseline(w, Q, K, V, seed):
-    """The oracle as it stands on a bounded sample of the workload, scaled to ms per layer.
+    """The oracle as it stands on a bounded sample of the workload, scaled to ms per layer, with the
+    per-stage split.
 
-    Sample: the whole retrieval of head 0 (metric, both seedings and clusterings, PAMA, top-p) and
-    the sparse attention of the first `na` query clusters of head 0; scaled by heads and by
-    query clusters respectively."""
+    Sample: the whole retrieval of heads 0-3 (metric, both seedings and clusterings, PAMA, top-p,
+    each stage timed; the oracle's own retrieval steps called one by one) and the sparse attention
+    of the first `na` query clusters of head 0; scaled by heads and by query clusters respectively."""
     import oracle as O
     nh = min(4, w.heads)
-    t0 = time.perf_counter()
+    st = {"metric": 0.0, "cluster_q": 0.0, "cluster_k": 0.0, "pama": 0.0, "select": 0.0}
+    bf = w.dtype == "bf16"
+
+    def timed(key, fn):
+        t0 = time.perf_counter()
+        out = fn()
+        st[key] += time.perf_counter() - t0
+        return out
+
+    r = None
     for hh in range(nh):
         qh, kh = (x[hh].to(torch.float64).cpu().numpy() for x in (Q, K))
-        rh = O.retrieve(qh, kh, w.cq, w.ck, w.iters, w.p, w.scale, seed=seed, head=hh, bf16=(w.dtype == "bf16"))
+        Mr = timed("metric", lambda: O.round_f32(O.qrkc_metric(qh)))
+        qc = timed("cluster_q", lambda: O.cluster(qh, w.cq, w.iters, O.EUCLID, None, seed, hh, O.SIDE_Q, bf))
+        kc = timed("cluster_k", lambda: O.cluster(kh, w.ck, w.iters, O.QRKC, Mr, seed, hh, O.SIDE_K, bf))
+        ks = np.diff(kc["offsets"])
+        khat = O.round_bf16(kc["centroids"]) if bf else kc["centroids"]
+        A = timed("pama", lambda: O.pama(qh, qc["perm"], qc["offsets"], khat, ks, w.scale))
+        sel = timed("select", lambda: O.select_topp(A, ks, w.p))
         if hh == 0:
-            r = rh
-    t_ret = (time.perf_counter() - t0) / nh
+            r = {"q": qc, "k": kc, "cols": sel[2]}
+    t_ret = sum(st.values()) / nh
     q, k, v = (x[0].to(torch.float64).cpu().numpy() for x in (Q, K, V))
     na = 50
     qp, qo = r["q"]["perm"], r["q"]["offsets"]
@@ -69,12 +85,22 @@ def cpu_baseline(w, Q, K, V, seed):
     O.sparse_attention(q, k, v, qp, qo, r["k"]["perm"], r["k"]["offsets"], r["cols"], w.scale, rows=rows)
     t_att = time.perf_counter() - t0
     n_live = sum(1 for i in range(w.cq) if qo[i + 1] > qo[i])
-    ms = 1e3 * (t_ret * w.heads + t_att * (n_live / max(len(rows), 1)) * w.heads)
+    att_ms = 1e3 * t_att * (n_live / max(len(rows), 1)) * w.heads
+    stages = {key: round(1e3 * val / nh * w.heads, 1) for key, val in st.items()}
+    stages["sparse_attn"] = round(att_ms, 1)
+    ms = 1e3 * t_ret * w.heads + att_ms
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": ms, "unit": "ms/layer", "cores": cores, "kind": "oracle",
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    return {"value": ms, "unit": "ms/layer", "cores": cores, "kind": "oracle", "stages_ms": stages,
+            "cpu_count": os.cpu_count(), "blas_threads": blas,
             "sample": f"retrieval of heads 0-{nh - 1} ({t_ret:.1f} s per head) x {w.heads} heads + sparse attention "
                       f"of {len(rows)} of {n_live} query clusters of head 0 ({t_att:.1f} s) scaled to all clusters "
                       f"and heads"}
@@ -365,7 +391,7 @@ def run_sip(args, bsa, w, dev, log):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
