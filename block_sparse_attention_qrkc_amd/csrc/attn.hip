@@ -759,15 +759,20 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   if (nt > 0) {
     // prologue: tiles 0 .. NST-2 into stages 0 .. NST-2, rows of tiles NST-1 .. 2 NST-2 into their
     // sets; then the scores of tile 0 (its copies are followed by NST - 2 tiles' copies)
+    // entries of tiles 0 .. NST-1 (one wait), then those of tiles NST .. 2 NST-2 into the sets just
+    // read, then the copies of tiles 0 .. NST-2: waiting for tile 0 also covers the entries
 #pragma unroll
-    for (int x = 0; x < NST - 1; ++x) load_idx(x, x);
+    for (int x = 0; x < NST; ++x) load_idx(x, x);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    int n0[NST];
 #pragma unroll
-    for (int x = 0; x < NST - 1; ++x) issue(read_idx(x), x, x);
+    for (int x = 0; x < NST; ++x) n0[x] = read_idx(x);
 #pragma unroll
-    for (int x = NST - 1; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
-    w8_wait_barrier<0>();  // once per work item: every copy and entry of the prologue landed
-    nnext = read_idx(NST - 1);
+    for (int x = NST; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
+#pragma unroll
+    for (int x = 0; x < NST - 1; ++x) issue(n0[x], x, x);
+    nnext = n0[NST - 1];
+    w8_wait_barrier<(NST - 2) * CP>();
     if (active) {
       s_tile(std::integral_constant<int, 0>{}, sbuf[0]);
       adjust(std::integral_constant<int, 0>{}, sbuf[0], 0);
@@ -775,9 +780,10 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     }
   }
   // iteration t (stage SL = t % NST): tile t + 1 landed, tile t + NST - 1 goes into the stage tile
-  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2 (or the prologue, which waited for all
-  // of its copies); each of the NST - 3 iterations since issued CP + IL vector-memory operations
-  // (copies, then the index load). Scores of tile t live in
+  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2, after which each of the NST - 3
+  // iterations since issued CP + IL vector-memory operations (copies, then the index load); or in
+  // the prologue, after which at least NST - 3 tiles' CP copies were issued. The entries read at the
+  // end of iteration t (tile t + NST) were loaded before both. Scores of tile t live in
   // sbuf[t % 2] (NST is even, so the parity of the stage is the parity of the tile).
   static_assert(NST % 2 == 0 && NST >= 4, "pipelined ring: an even number of stages, at least four");
   for (int t = 0; t < nt; t += NST) {
@@ -788,7 +794,10 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       constexpr int PC = SL % 2, PN = (SL + 1) % 2;
       const int tt = t + SL;
       if (tt >= nt) return false;
-      w8_wait_barrier<(NST - 3) * (CP + IL)>();
+      if (tt < NST - 2)
+        w8_wait_barrier<(NST - 3) * CP>();
+      else
+        w8_wait_barrier<(NST - 3) * (CP + IL)>();
       issue(nnext, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
       if (active) {
