@@ -416,8 +416,6 @@ __device__ __forceinline__ bool w8_unroll(F&& f) {
   }
 }
 
-// W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
-// units), copied into LDS with the tile and added to the scores
 // LDS reads the kernel writes out itself, each block ending by waiting for its reads. The compiler
 // cannot tell which LDS the transposing read builtin reads, nor order a read of the index lists
 // against the direct HBM -> LDS copies of later tiles, and would wait for every copy in flight
