@@ -520,6 +520,11 @@ def main():
         res["sparse_attn_ms"] = round(st["sparse_attn"], 3)
         res["dense_attn_ms"] = round(st["dense_attn"], 3)
         res["retrieval_over_dense"] = round(retrieval / st["dense_attn"], 4)
+        # the same ratio against dense attention at the bf16 matrix-core peak (the ideal kernel)
+        res["retrieval_over_dense_at_peak"] = round(retrieval / (dense_flops / (PEAK_BF16_TFLOPS * 1e9)), 4)
+        live_q = (torch.diff(qc["offsets"], dim=1) > 0).sum(1).double()
+        live_k = (torch.diff(kc["offsets"], dim=1) > 0).sum(1).double()
+        res["block_density"] = round(float(sel["counts"].double().sum() / (live_q * live_k).sum()), 5)
         res["effective_tflops_dense_equiv"] = round(dense_flops / (ms_step * 1e9), 2)
         res["computed_tflops"] = round(computed_flops / (ms_step * 1e9), 2)
         res["mfma_frac_whole_path"] = round(computed_flops / (ms_step * 1e9) / PEAK_BF16_TFLOPS, 4)
