@@ -441,8 +441,16 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
   __shared__ double pre_s, v_s, cc_s;
   __shared__ int owner_s, pick_s;
 
-  // decode (side, head, part)
-  int b = blockIdx.x;
+  // decode (side, head, part) from an XCD-grouped order: work-groups are dealt to the 8 XCDs
+  // round-robin, so XCD x receives ids x, x + 8, ...; those are given the x-th contiguous range of
+  // (side, head, part), which keeps the parts of a head, which exchange partial sums every step, on
+  // one XCD and its L2
+  int b;
+  {
+    const int G = (int)gridDim.x;
+    const int x = (int)blockIdx.x & 7, per = G >> 3, rem = G & 7;
+    b = x * per + min(x, rem) + ((int)blockIdx.x >> 3);
+  }
   const bool second = b >= H * s0.G;
   const CoopSide sd = second ? s1 : s0;
   if (second) b -= H * s0.G;
