@@ -131,7 +131,7 @@ def kernel_only(args, w, Q, K, V, step, bsa, ws, log):
     log(f"ran {args.kernel_only} x{args.steps} and a 1 GiB copy")
 
 
-PROFILE_PMC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sparse_attn_w8_wan_pmc.md")
+PROFILE_PMC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sparse_attn_bf16_wan_pmc.md")
 ATTN_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_qrkc_amd", "csrc",
                         "attn.hip")
 
@@ -534,12 +534,12 @@ def main():
         ach = flops_sel / (st["sparse_attn"] * 1e9)
         log(f"stages: {res['stages_ms']}")
         traffic = measured_traffic() if w.name == "wan" else None
-        res["roofline"] = {"kernel": "sparse_attn_w8", "bound": "mfma", "achieved": round(ach, 2),
+        res["roofline"] = {"kernel": "sparse_attn_bf16", "bound": "mfma", "achieved": round(ach, 2),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                            "traffic": traffic,
                            "work": f"4*d*sum_i n_q(i)*L(i) = {flops_sel / 1e12:.3f} TFLOP per launch",
                            "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from "
-                                           "profiles/sparse_attn_w8_wan_pmc.md; null when the kernel source changed"}
+                                           "profiles/sparse_attn_bf16_wan_pmc.md; null when the kernel source changed"}
         if not args.no_ceilings:
             res["ceilings"] = ceilings(dev)
             res["roofline"]["frac_of_measured_gemm"] = round(ach / res["ceilings"]["gemm_bf16_tflops"], 4)

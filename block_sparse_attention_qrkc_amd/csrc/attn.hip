@@ -384,20 +384,19 @@ __device__ __forceinline__ int chunk_swz(int r) {
   c = L - h * nx;
 }
 
-// 256-query tiles: eight waves x 32 queries share one work-group per CU (two waves per SIMD), so
-// each key/value tile copied to LDS serves 256 queries. Tiles of 32 keys (d = 128; 64 for d = 64,
-// so each wave copies 1 KB of K and of V per tile) stream through a ring of four stages, copied
-// two tiles ahead of the tile being scored; a wave waits only for the copies of the tile it is about
-// to read (a counted vmcnt, then a plain barrier: a fenced barrier would also wait for the copies
-// still in flight). The loop is software-pipelined: the score MFMAs of tile t + 1 are interleaved
-// with the softmax of tile t.
-constexpr int kW8BM = 256;  // queries per work item
-[[maybe_unused]] constexpr int kW8BN = 32;   // keys per tile for d = 128
-[[maybe_unused]] constexpr int kW8NST = 4;   // LDS stages of one tile (K and V)
+// 384-query tiles: twelve waves x 32 queries share one work-group per CU (three waves per SIMD,
+// 168 registers each), so each key/value tile copied to LDS serves 384 queries and each SIMD has
+// three waves to interleave matrix-core, vector and LDS work. Tiles of 32 keys (d = 128; 64 for
+// d = 64) are copied by eight of the waves, 1 KB of K and of V each, through a ring of four stages
+// three tiles ahead; a wave waits only for the copies of the tile it is about to read (a counted
+// vmcnt, then a plain barrier: a fenced barrier would also wait for the copies still in flight).
+constexpr int kBf16BM = 384;  // queries per work item
+[[maybe_unused]] constexpr int kBf16BN = 32;   // keys per tile for d = 128
+[[maybe_unused]] constexpr int kBf16NST = 4;   // LDS stages of one tile (K and V)
 
 // vmcnt(n) & lgkmcnt(0), then a plain workgroup barrier
 template <int VM>
-__device__ __forceinline__ void w8_wait_barrier() {
+__device__ __forceinline__ void wait_barrier() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 15) | (0x7 << 4) | ((VM >> 4) << 14));
   asm volatile("" ::: "memory");
@@ -407,10 +406,10 @@ __device__ __forceinline__ void w8_wait_barrier() {
 
 // f(integral_constant<I>) for I = B .. E-1 in order while it returns true
 template <int B, int E, typename F>
-__device__ __forceinline__ bool w8_unroll(F&& f) {
+__device__ __forceinline__ bool unroll_while(F&& f) {
   if constexpr (B < E) {
     if (!f(std::integral_constant<int, B>{})) return false;
-    return w8_unroll<B + 1, E>(f);
+    return unroll_while<B + 1, E>(f);
   } else {
     return true;
   }
@@ -420,50 +419,6 @@ __device__ __forceinline__ bool w8_unroll(F&& f) {
 // cannot tell which LDS the transposing read builtin reads, nor order a read of the index lists
 // against the direct HBM -> LDS copies of later tiles, and would wait for every copy in flight
 // before such a read; the explicit counted waits and barriers already order them.
-// Sixteen transposing reads (ds_read_b64_tr_b16, 4 x 16-bit per lane) at a common offset.
-template <int OFF>
-__device__ __forceinline__ void tr_read16(u32x2_t (&r)[16], const uint32_t (&a)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %1, %17 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %2, %18 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %3, %19 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %4, %20 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %5, %21 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %6, %22 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %7, %23 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %8, %24 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %9, %25 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %10, %26 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %11, %27 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %12, %28 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %13, %29 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %14, %30 offset:%32\n\t"
-      "ds_read_b64_tr_b16 %15, %31 offset:%32\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]),
-        "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15]), "i"(OFF)
-      : "memory");
-}
-// Eight 16-byte reads at a common offset.
-template <int OFF>
-__device__ __forceinline__ void lds_read8_b128(u32x4_t (&r)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%16\n\t"
-      "ds_read_b128 %1, %9 offset:%16\n\t"
-      "ds_read_b128 %2, %10 offset:%16\n\t"
-      "ds_read_b128 %3, %11 offset:%16\n\t"
-      "ds_read_b128 %4, %12 offset:%16\n\t"
-      "ds_read_b128 %5, %13 offset:%16\n\t"
-      "ds_read_b128 %6, %14 offset:%16\n\t"
-      "ds_read_b128 %7, %15 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
-      : "memory");
-}
 // Four 16-byte reads at consecutive 16-byte offsets.
 template <int OFF>
 __device__ __forceinline__ void lds_read4_b128(u32x4_t (&r)[4], uint32_t a) {
@@ -477,6 +432,34 @@ __device__ __forceinline__ void lds_read4_b128(u32x4_t (&r)[4], uint32_t a) {
       : "v"(a), "i"(OFF), "i"(OFF + 16), "i"(OFF + 32), "i"(OFF + 48)
       : "memory");
 }
+template <int OFF>
+__device__ __forceinline__ void lds_read4x_b128(u32x4_t (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void tr_read8(u32x2_t (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+      : "memory");
+}
 // One dword.
 __device__ __forceinline__ int lds_read_b32(uint32_t addr) {
   int v;
@@ -487,7 +470,7 @@ __device__ __forceinline__ int lds_read_b32(uint32_t addr) {
 // W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
 // units), copied into LDS with the tile and added to the scores
 template <int D, bool W>
-__global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __restrict__ Q,
                                                          const uint16_t* __restrict__ K,
                                                          const uint16_t* __restrict__ V, int64_t N,
                                                          const int32_t* __restrict__ q_perm,
@@ -498,20 +481,21 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
                                                          const float* __restrict__ gbias, float scale,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 8;
-  constexpr int NST = kW8NST;
+  constexpr int NW = 12;
+  constexpr int NWC = 8;  // copier waves
+  constexpr int NST = kBf16NST;
   constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw (untyped) access
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CPR = D / 8;
   constexpr int ROWB = D * 2;
-  constexpr int BN = D == 64 ? 64 : kW8BN;
+  constexpr int BN = D == 64 ? 64 : kBf16BN;
   constexpr int NSUB = BN / 32;                 // 32-key sub-tiles
   constexpr int TILEB = BN * ROWB;              // one K (or V) tile
   constexpr int BIASB = W ? 256 : 0;            // per wave: the tile's key offsets (lanes l % BN)
-  constexpr int STAGEB = 2 * TILEB + NW * BIASB;  // K, V, then the key offsets
+  constexpr int STAGEB = 2 * TILEB + NWC * BIASB;  // K, V, then the key offsets
   constexpr int RPB = 1024 / ROWB;              // rows per 1 KB wave load
-  constexpr int LOADS = TILEB / (1024 * NW);    // 1 KB loads per wave per tile, for K and for V
+  constexpr int LOADS = TILEB / (1024 * NWC);    // 1 KB loads per wave per tile, for K and for V
   static_assert(LOADS >= 1, "tile smaller than one load per wave");
   constexpr int CP = 2 * LOADS + (W ? 1 : 0);   // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) uint8_t stages[NST * STAGEB];
@@ -523,10 +507,12 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   const int i = find_tile(tb, cq, c);
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool copier = w < NWC;
+  const int wc = copier ? w : NWC - 1;
   const int hl = l / 32;
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
-  const int qbeg = qo[i] + (c - tb[i]) * kW8BM;
-  const int qend = min(qbeg + kW8BM, qo[i + 1]);
+  const int qbeg = qo[i] + (c - tb[i]) * kBf16BM;
+  const int qend = min(qbeg + kBf16BM, qo[i + 1]);
   const bool active = qbeg + w * 32 < qend;  // this wave has at least one query
   const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
   const int L = glen[(int64_t)h * cq + i];
@@ -556,7 +542,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   int trow[LOADS], lbyte[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
-    trow[q] = (w * LOADS + q) * RPB + l / CPR;
+    trow[q] = (wc * LOADS + q) * RPB + l / CPR;
     lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
   }
   const int nt = (L + BN - 1) / BN;
@@ -565,21 +551,23 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
   // read into a register at the end of iteration x - NST, ready for the copies of iteration
   // x - NST + 1.
   static_assert(LOADS == 1, "one 1 KB copy per wave and tile");
-  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][NW][kWave];
+  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][NWC][kWave];
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, (int)(uint32_t)(L * 4),
                                                                        kBufferFlags);
   constexpr int IL = 1;  // index loads per wave and tile
   auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
+    if (!copier) return;
     // entries past the list end read as 0 (a valid row; its scores are masked)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][w][0], 4, (tile * BN + l % BN) * 4, 0, 0,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][wc][0], 4, (tile * BN + l % BN) * 4, 0, 0,
                                              0);
   };
-  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][w][trow[0]]);
+  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][wc][trow[0]]);
   auto read_idx = [&](int set) __attribute__((always_inline)) {
-    return lds_read_b32(ibase + (uint32_t)(set * NW * kWave * 4));
+    return lds_read_b32(ibase + (uint32_t)(set * NWC * kWave * 4));
   };
   int nnext = 0;  // gather-list row of this lane's copy in the next issue
   auto issue = [&](int nrow0, int slot, int tile) __attribute__((always_inline)) {
+    if (!copier) return;
     const int nrow[1] = {nrow0};
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
@@ -589,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
     }
     if constexpr (W) {
-      const int boff = slot * STAGEB + 2 * TILEB + w * BIASB;
+      const int boff = slot * STAGEB + 2 * TILEB + wc * BIASB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (PARK_LDS void*)(stages + boff), 4, (tile * BN + l % BN) * 4, 0,
                                                0, 0);
     }
@@ -636,34 +624,31 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
       }
   }
 
-  // Software-pipelined loop: iteration t issues the score MFMAs of tile t + 1 and then runs the
-  // softmax of tile t, whose scores came from iteration t - 1, so the matrix cores work on the next
-  // tile while the vector ALUs exponentiate this one; then the P V MFMAs of tile t.
-  f32x16_t sbuf[2][NSUB];
-  // scores of one tile: its eight K operand reads in one block, then the MFMAs
+  static_assert((NST - 1) * STAGEB + TILEB + 64 <= 65535, "stage offsets fit the LDS reads' 16-bit offset field");
+  // scores of one tile: its eight K operand reads in two blocks of four, each followed by its MFMAs
   const uint32_t sbase = (uint32_t)(size_t)((PARK_LDS uint8_t*)stages);
   static_assert(KS * NSUB == 8, "eight K reads per tile");
   auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
     constexpr int OFF = decltype(OFFc)::value;
-    uint32_t a[8];
-    u32x4_t ka[8];
 #pragma unroll
     for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) a[st * KS + kk] = sbase + kofs[st][kk];
-    if constexpr (OFF <= 65535) {
-      lds_read8_b128<OFF>(ka, a);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] += OFF;
-      lds_read8_b128<0>(ka, a);
-    }
-#pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-#pragma unroll
       for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) sa[st] = mfma32(ka[st * KS + kk], qb[kk], sa[st]);
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t a[4];
+      u32x4_t ka[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = hh * 4 + j;
+        a[j] = sbase + kofs[idx / KS][idx % KS];
+      }
+      lds_read4x_b128<OFF>(ka, a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = hh * 4 + j;
+        sa[idx / KS] = mfma32(ka[j], qb[idx % KS], sa[idx / KS]);
+      }
     }
   };
   // key offsets (weighted form) and the mask of keys past the list end
@@ -673,7 +658,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
 #pragma unroll
       for (int st = 0; st < NSUB; ++st) {
         u32x4_t b[4];
-        const uint32_t ba = sbase + 2 * TILEB + w * BIASB + (st * 32 + hl * 16) * 4;
+        const uint32_t ba = sbase + 2 * TILEB + (w % NWC) * BIASB + (st * 32 + hl * 16) * 4;
         if constexpr (OFF + 48 <= 65535) {
           lds_read4_b128<OFF>(b, ba);
         } else {
@@ -687,11 +672,12 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     }
     const int nvalid = L - v0;
     if (__builtin_expect(nvalid < BN, 0)) {
+      const int lim = nvalid - hl * 16;  // accumulator e of sub-tile st is key st * 32 + hl * 16 + e
 #pragma unroll
       for (int st = 0; st < NSUB; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (st * 32 + hl * 16 + e >= nvalid) sa[st][e] = -INFINITY;
+          if (st * 32 + e >= lim) sa[st][e] = -INFINITY;
     }
   };
   auto tile_max = [&](const f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
@@ -721,44 +707,39 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
     }
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
   };
-  // V^T operands of a tile: all sixteen reads in one block, then the P V MFMAs
-  static_assert(DT * NSUB * 4 == 16, "sixteen V^T reads per tile");
+  // V^T operands of a tile: two blocks of eight reads, each followed by its P V MFMAs
   auto pv_tile = [&](auto OFFc, const u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
     constexpr int OFF = decltype(OFFc)::value;
-    uint32_t a[16];
-    u32x2_t r[16];
+    constexpr int DG = 2 / NSUB;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int d0 = 0; d0 < DT; d0 += DG) {
+      uint32_t a[8];
+      u32x2_t r[8];
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st)
+      for (int x = 0; x < DG; ++x)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-          for (int z = 0; z < 2; ++z) a[((dt * NSUB + st) * 2 + kh) * 2 + z] = sbase + vofs[dt][st][kh][z];
-    if constexpr (OFF <= 65535) {  // the instruction's offset field holds 16 bits
-      tr_read16<OFF>(r, a);
-    } else {
+          for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) a[j] += OFF;
-      tr_read16<0>(r, a);
+            for (int z = 0; z < 2; ++z) a[((x * NSUB + st) * 2 + kh) * 2 + z] = sbase + vofs[d0 + x][st][kh][z];
+      tr_read8<OFF>(r, a);
+#pragma unroll
+      for (int x = 0; x < DG; ++x)
+#pragma unroll
+        for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int j = ((x * NSUB + st) * 2 + kh) * 2;
+            const u32x4_t va = u32x4_t{r[j][0], r[j][1], r[j + 1][0], r[j + 1][1]};
+            o[d0 + x] = mfma32(va, pb[st][kh], o[d0 + x]);
+          }
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const int j = ((dt * NSUB + st) * 2 + kh) * 2;
-          const u32x4_t va = u32x4_t{r[j][0], r[j][1], r[j + 1][0], r[j + 1][1]};
-          o[dt] = mfma32(va, pb[st][kh], o[dt]);
-        }
   };
 
   if (nt > 0) {
-    // prologue: tiles 0 .. NST-2 into stages 0 .. NST-2, rows of tiles NST-1 .. 2 NST-2 into their
-    // sets; then the scores of tile 0 (its copies are followed by NST - 2 tiles' copies)
-    // entries of tiles 0 .. NST-1 (one wait), then those of tiles NST .. 2 NST-2 into the sets just
-    // read, then the copies of tiles 0 .. NST-2: waiting for tile 0 also covers the entries
+    // prologue: entries of tiles 0 .. NST-1 (one wait), then those of tiles NST .. 2 NST-2 into the
+    // sets just read, then the copies of tiles 0 .. NST-2 into stages 0 .. NST-2
 #pragma unroll
     for (int x = 0; x < NST; ++x) load_idx(x, x);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -770,49 +751,40 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
 #pragma unroll
     for (int x = 0; x < NST - 1; ++x) issue(n0[x], x, x);
     nnext = n0[NST - 1];
-    w8_wait_barrier<(NST - 2) * CP>();
-    if (active) {
-      s_tile(std::integral_constant<int, 0>{}, sbuf[0]);
-      adjust(std::integral_constant<int, 0>{}, sbuf[0], 0);
-      m_ref = tile_max(sbuf[0]);
-    }
   }
-  // iteration t (stage SL = t % NST): tile t + 1 landed, tile t + NST - 1 goes into the stage tile
-  // t - 1 used. Tile t + 1 was copied in iteration t - NST + 2, after which each of the NST - 3
-  // iterations since issued CP + IL vector-memory operations (copies, then the index load); or in
-  // the prologue, after which at least NST - 3 tiles' CP copies were issued. The entries read at the
-  // end of iteration t (tile t + NST) were loaded before both. Scores of tile t live in
-  // sbuf[t % 2] (NST is even, so the parity of the stage is the parity of the tile).
-  static_assert(NST % 2 == 0 && NST >= 4, "pipelined ring: an even number of stages, at least four");
+  // Iteration t (stage SL = t % NST): wait until tile t landed, copy tile t + NST - 1 into the stage
+  // tile t - 1 used, load the entries of tile t + 2 NST - 1, compute tile t, read the entries of
+  // tile t + NST. Tile t was copied in iteration t - NST + 1, after which each of the NST - 2
+  // iterations since issued CP + IL vector-memory operations (copies, then the index load), or in
+  // the prologue, after which at least NST - 2 tiles' CP copies were issued; the entries read at the
+  // end of iteration t were loaded before those copies. Copier waves only issue copies; the waits
+  // hold trivially for the others.
   for (int t = 0; t < nt; t += NST) {
-    const bool go_on = w8_unroll<0, NST>([&](auto SLc) __attribute__((always_inline)) {
+    const bool go_on = unroll_while<0, NST>([&](auto SLc) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLc)::value;
-      constexpr int SN = (SL + 1) % NST;
       constexpr int XS = (SL + NST - 1) % NST;
-      constexpr int PC = SL % 2, PN = (SL + 1) % 2;
       const int tt = t + SL;
       if (tt >= nt) return false;
-      if (tt < NST - 2)
-        w8_wait_barrier<(NST - 3) * CP>();
+      if (tt < NST - 1)
+        wait_barrier<(NST - 2) * CP>();
       else
-        w8_wait_barrier<(NST - 3) * (CP + IL)>();
+        wait_barrier<(NST - 2) * (CP + IL)>();
       issue(nnext, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
       if (active) {
-        // scores of tile tt + 1 (a tile past the list end holds clamped, valid rows)
-        s_tile(std::integral_constant<int, SN * STAGEB>{}, sbuf[PN]);
+        f32x16_t sc[NSUB];
+        s_tile(std::integral_constant<int, SL * STAGEB>{}, sc);
+        adjust(std::integral_constant<int, SL * STAGEB>{}, sc, tt * BN);
+        if (tt == 0) m_ref = tile_max(sc);
         u32x4_t pb[NSUB][2];
-        float ps = weights(sbuf[PC], pb);
-        // instruction order of the block above: each score MFMA followed by a share of the softmax
-        // (ALU, then exponentials) that runs while the matrix core works
-#pragma unroll
-        for (int g = 0; g < KS * NSUB; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4 * NSUB, 0);
-          __builtin_amdgcn_sched_group_barrier(0x400, 2 * NSUB, 0);
-        }
+        float ps = weights(sc, pb);
         if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
-          const float m_new = fmaxf(m_ref, tile_max(sbuf[PC]));
+          // rare: the scores are computed again (the tile is still in LDS), so they need not stay
+          // live through the softmax
+          f32x16_t s2[NSUB];
+          s_tile(std::integral_constant<int, SL * STAGEB>{}, s2);
+          adjust(std::integral_constant<int, SL * STAGEB>{}, s2, tt * BN);
+          const float m_new = fmaxf(m_ref, tile_max(s2));
           const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
           l_run *= alpha;
 #pragma unroll
@@ -820,14 +792,11 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_w8(const uint16_t* __restr
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
           m_ref = m_new;
-          ps = weights(sbuf[PC], pb);
+          ps = weights(s2, pb);
         }
         l_run += ps;
         pv_tile(std::integral_constant<int, SL * STAGEB + TILEB>{}, pb);
-        adjust(std::integral_constant<int, SN * STAGEB>{}, sbuf[PN], (tt + 1) * BN);
       }
-      // entries of tile tt + NST (set SL, loaded in iteration tt - NST + 1: landed before this
-      // iteration's wait) for the next iteration's copies
       nnext = read_idx(SL);
       return true;
     });
@@ -868,7 +837,7 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
                               hipStream_t st) {
   int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
   float* gb = log_w ? gbias : nullptr;
-  attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, s.bf16 ? kW8BM : kAttnBM, tile_base);
+  attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
   attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, log_w,
                                                                 1.f / scale, gather, glen, gb);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
@@ -876,8 +845,8 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
                                                  static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, tile_base, \
                                                  gather, glen, gb, scale, static_cast<T*>(out), lse);
-#define PARK_W8(D, W)                                                                                            \
-  sparse_attn_w8<D, W><<<grid, 512, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen, gb, \
+#define PARK_BF16ATTN(D, W)                                                                                            \
+  sparse_attn_bf16<D, W><<<grid, 768, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen, gb, \
                                              scale, oh, lse);
   if (s.bf16) {
     const uint16_t* qh = static_cast<const uint16_t*>(q);
@@ -886,15 +855,15 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
     uint16_t* oh = static_cast<uint16_t*>(out);
     if (s.D == 128) {
       if (gb) {
-        PARK_W8(128, true)
+        PARK_BF16ATTN(128, true)
       } else {
-        PARK_W8(128, false)
+        PARK_BF16ATTN(128, false)
       }
     } else {
       if (gb) {
-        PARK_W8(64, true)
+        PARK_BF16ATTN(64, true)
       } else {
-        PARK_W8(64, false)
+        PARK_BF16ATTN(64, false)
       }
     }
   } else {
@@ -904,7 +873,7 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
       PARK_ATTN(float, 64)
     }
   }
-#undef PARK_W8
+#undef PARK_BF16ATTN
 #undef PARK_ATTN
   return hipGetLastError();
 }
