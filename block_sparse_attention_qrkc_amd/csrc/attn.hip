@@ -18,27 +18,60 @@ namespace park {
 
 namespace {
 
-// Per head: tile_base[i] = bm-query tiles of query clusters before i; tile_base[cq] = total.
-__global__ __launch_bounds__(1024) void attn_tiles(const int32_t* __restrict__ q_offsets, int cq, int bm,
+// Per head, the work list in longest-first order (the schedule step of the PARK page: per query
+// cluster a list of bm-query work items; clusters with more selected keys first, so that the last
+// work items dealt to a CU are the short ones). Clusters are sorted by their gathered key count,
+// descending, ties by lower index; ord[k] is the k-th cluster in that order and tb[k] the number of
+// work items before it, tb[cq] the total. Per head the layout is tb[0 .. cq], then ord[0 .. cq-1].
+__global__ __launch_bounds__(1024) void attn_order(const int32_t* __restrict__ q_offsets,
+                                                   const int32_t* __restrict__ glen, int cq, int bm,
                                                    int32_t* __restrict__ tile_base) {
+  __shared__ uint64_t keys[kMaxClusters];
   __shared__ int scratch[17];
   const int h = blockIdx.x;
+  const int tid = threadIdx.x;
   const int32_t* off = q_offsets + (int64_t)h * (cq + 1);
-  int32_t* tb = tile_base + (int64_t)h * (cq + 1);
-  const int per = (cq + 1023) / 1024;
-  const int i0 = threadIdx.x * per;
-  int local = 0;
-  for (int k = 0; k < per; ++k)
-    if (i0 + k < cq) local += (off[i0 + k + 1] - off[i0 + k] + bm - 1) / bm;
-  int total;
-  int run = block_exclusive_scan(local, scratch, &total);
-  for (int k = 0; k < per; ++k) {
-    if (i0 + k < cq) {
-      tb[i0 + k] = run;
-      run += (off[i0 + k + 1] - off[i0 + k] + bm - 1) / bm;
+  const int32_t* gl = glen + (int64_t)h * cq;
+  int32_t* tb = tile_base + (int64_t)h * (2 * cq + 1);
+  int32_t* ord = tb + cq + 1;
+  int P2 = 1;
+  while (P2 < cq) P2 <<= 1;
+  // key: gathered key count, then the complemented cluster index; padding (key 0) sorts last
+  for (int j = tid; j < P2; j += 1024)
+    keys[j] = j < cq ? ((uint64_t)(uint32_t)max(gl[j], 0) << 32) | (uint64_t)(~(uint32_t)j) : 0;
+  __syncthreads();
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int idx = tid; idx < P2; idx += 1024) {
+        const int ixj = idx ^ jj;
+        if (ixj > idx) {
+          const uint64_t a = keys[idx], b = keys[ixj];
+          if ((a < b) == ((idx & k) == 0)) {
+            keys[idx] = b;
+            keys[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
     }
   }
-  if (threadIdx.x == 0) tb[cq] = total;
+  // thread t owns sorted positions [t * per, t * per + per)
+  const int per = (cq + 1023) / 1024;
+  const int k0 = tid * per;
+  int local = 0;
+  for (int k = k0; k < min(k0 + per, cq); ++k) {
+    const int i = (int)~(uint32_t)(keys[k] & 0xFFFFFFFFu);
+    local += (max(off[i + 1] - off[i], 0) + bm - 1) / bm;
+  }
+  int total;
+  int run = block_exclusive_scan(local, scratch, &total);
+  for (int k = k0; k < min(k0 + per, cq); ++k) {
+    const int i = (int)~(uint32_t)(keys[k] & 0xFFFFFFFFu);
+    tb[k] = run;
+    ord[k] = i;
+    run += (max(off[i + 1] - off[i], 0) + bm - 1) / bm;
+  }
+  if (tid == 0) tb[cq] = total;
 }
 
 // Per (query cluster, head): the original key rows of the selected key clusters, concatenated in
@@ -181,15 +214,16 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
 
   const int h = blockIdx.y;
   const int c = blockIdx.x;
-  const int32_t* tb = tile_base + (int64_t)h * (cq + 1);
+  const int32_t* tb = tile_base + (int64_t)h * (2 * cq + 1);
   if (c >= tb[cq]) return;
-  const int i = find_tile(tb, cq, c);
+  const int ti = find_tile(tb, cq, c);
+  const int i = tb[cq + 1 + ti];
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int w = tid / kWave;
   const int hl = l / 32;
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
-  const int qbeg = qo[i] + (c - tb[i]) * kAttnBM;
+  const int qbeg = qo[i] + (c - tb[ti]) * kAttnBM;
   const int qend = min(qbeg + kAttnBM, qo[i + 1]);
   const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
   const float* brow = gbias ? gbias + ((int64_t)h * cq + i) * N : nullptr;
@@ -502,16 +536,17 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
 
   int h, c;
   xcd_tile(h, c);
-  const int32_t* tb = tile_base + (int64_t)h * (cq + 1);
+  const int32_t* tb = tile_base + (int64_t)h * (2 * cq + 1);
   if (c >= tb[cq]) return;
-  const int i = find_tile(tb, cq, c);
+  const int ti = find_tile(tb, cq, c);
+  const int i = tb[cq + 1 + ti];
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const bool copier = w < NWC;
   const int wc = copier ? w : NWC - 1;
   const int hl = l / 32;
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
-  const int qbeg = qo[i] + (c - tb[i]) * kBf16BM;
+  const int qbeg = qo[i] + (c - tb[ti]) * kBf16BM;
   const int qend = min(qbeg + kBf16BM, qo[i + 1]);
   const bool active = qbeg + w * 32 < qend;  // this wave has at least one query
   const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
@@ -826,7 +861,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
 
 }  // namespace
 
-int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, kAttnBM) + cq; }
+int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, s.bf16 ? kBf16BM : kAttnBM) + cq; }
 
 size_t attn_gather_ints(const Dims& s, int cq) { return (size_t)(s.H * cq) * (size_t)(s.N + 1); }
 
@@ -837,9 +872,9 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
                               hipStream_t st) {
   int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
   float* gb = log_w ? gbias : nullptr;
-  attn_tiles<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
   attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, log_w,
                                                                 1.f / scale, gather, glen, gb);
+  attn_order<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, glen, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
 #define PARK_ATTN(T, D)                                                                                          \
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \

@@ -167,7 +167,7 @@ struct AttnWs {
 };
 AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck, bool weighted = false) {
   AttnWs w;
-  w.tile_base = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
+  w.tile_base = cv.take<int32_t>((size_t)(s.H * (2 * cq + 1)));
   w.gather = cv.take<int32_t>(park::attn_gather_ints(s, cq));
   w.gbias = weighted ? cv.take<float>((size_t)(s.H * cq) * (size_t)s.N) : nullptr;
   return w;
