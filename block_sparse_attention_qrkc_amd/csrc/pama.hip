@@ -414,4 +414,220 @@ hipError_t launch_block_mass(const Dims& s, const void* q, const int32_t* q_perm
   return hipGetLastError();
 }
 
+
+// Centroid-query / full-key map (the CF estimator: the query centroid's softmax over every key,
+// summed per key cluster). Rows are the Cq bf16 centroid rows of a head, few against N keys, so the
+// work is split over the keys: a first pass keeps per (row, 1024-key chunk) a running (reference,
+// sum) in base 2, a merge folds the chunks in order into each row's offset r + log2(sum), and a
+// second pass gives each work-group eight key clusters, walks their keys in cluster order and
+// writes each (row, cluster) mass directly (lane sums reduced in a fixed order, no atomics).
+namespace {
+constexpr int kCfChunk = 1024;   // key positions per first-pass work-group
+constexpr int kCfClusters = 8;   // key clusters per second-pass work-group
+constexpr int kCfTW = 2;         // 16-row tiles per wave
+
+// A operands of row tile rt: centroid row rt * 16 + l % 16 (clamped), dims kk * 32 + g * 8 .. +7
+template <int KS>
+__device__ __forceinline__ void cf_rows(const uint16_t* R, int cq, int rt, int l, int g, u32x4_t* qa) {
+  const int r = min(rt * 16 + l % 16, cq - 1);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qa[kk] = *reinterpret_cast<const u32x4_t*>(R + (int64_t)r * (KS * 32) + kk * 32 + g * 8);
+}
+
+// B operands of the key at cluster-order position pos (clamped to the last key)
+template <int KS>
+__device__ __forceinline__ void cf_key(const uint16_t* Kh, const int32_t* kp, int64_t nk, int64_t pos, int g,
+                                       u32x4_t* bv) {
+  const int64_t row = kp[pos < nk ? pos : nk - 1];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) bv[kk] = *reinterpret_cast<const u32x4_t*>(Kh + row * (KS * 32) + kk * 32 + g * 8);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void cf_lse(const uint16_t* __restrict__ rows, int cq,
+                                              const uint16_t* __restrict__ K, int64_t N,
+                                              const int32_t* __restrict__ k_perm, float c1, int nchunk,
+                                              float* __restrict__ part) {
+  constexpr int KS = D / 32;
+  constexpr float kRaise = 16.f;
+  const int h = blockIdx.y, ch = blockIdx.x;
+  const int l = lane_id(), w = threadIdx.x / kWave, g = l / 16;
+  const uint16_t* Rh = rows + (int64_t)h * cq * D;
+  const uint16_t* Kh = K + (int64_t)h * N * D;
+  const int32_t* kp = k_perm + (int64_t)h * N;
+  const int64_t p0 = (int64_t)ch * kCfChunk;
+  const int nkt = (int)((min<int64_t>(p0 + kCfChunk, N) - p0 + 15) / 16);
+  const int nrt = (cq + 15) / 16;
+  for (int rt0 = w * kCfTW; rt0 < nrt; rt0 += 4 * kCfTW) {
+    u32x4_t qa[kCfTW][KS];
+#pragma unroll
+    for (int t = 0; t < kCfTW; ++t) cf_rows<KS>(Rh, cq, rt0 + t, l, g, qa[t]);
+    float r[kCfTW][4], s[kCfTW][4];
+#pragma unroll
+    for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[t][e] = -1e30f;
+        s[t][e] = 0.f;
+      }
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int64_t pos = p0 + kt * 16 + l % 16;
+      u32x4_t bv[KS];
+      cf_key<KS>(Kh, kp, N, pos, g, bv);
+      const float ln = pos < N ? 0.f : -INFINITY;
+      float lg[kCfTW][4], dmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < kCfTW; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lg[t][e] = __builtin_fmaf(acc[e], c1, ln);
+          dmax = fmaxf(dmax, lg[t][e] - r[t][e]);
+        }
+      }
+      if (__builtin_expect(__ballot(dmax > kRaise) != 0, 0)) {
+#pragma unroll
+        for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (lg[t][e] - r[t][e] > kRaise) {
+              s[t][e] *= __builtin_amdgcn_exp2f(r[t][e] - lg[t][e]);
+              r[t][e] = lg[t][e];
+            }
+      }
+#pragma unroll
+      for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[t][e] += __builtin_amdgcn_exp2f(lg[t][e] - r[t][e]);
+    }
+#pragma unroll
+    for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float ro = __shfl_xor(r[t][e], o, kWave);
+          const float so = __shfl_xor(s[t][e], o, kWave);
+          const float rn = fmaxf(r[t][e], ro);
+          s[t][e] = s[t][e] * __builtin_amdgcn_exp2f(r[t][e] - rn) + so * __builtin_amdgcn_exp2f(ro - rn);
+          r[t][e] = rn;
+        }
+        const int row = (rt0 + t) * 16 + g * 4 + e;
+        if (l % 16 == 0 && row < cq) {
+          float* dst = part + (((int64_t)h * nchunk + ch) * cq + row) * 2;
+          dst[0] = r[t][e];
+          dst[1] = s[t][e];
+        }
+      }
+  }
+}
+
+// Per row: fold the chunks' (reference, sum) pairs in chunk order into off = r + log2(sum).
+__global__ __launch_bounds__(256) void cf_merge(const float* __restrict__ part, int nchunk, int cq,
+                                                float* __restrict__ off) {
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= cq) return;
+  float r = -1e30f, s = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const float* p = part + (((int64_t)h * nchunk + c) * cq + row) * 2;
+    const float rc = p[0], sc = p[1];
+    const float rn = fmaxf(r, rc);
+    s = s * __builtin_amdgcn_exp2f(r - rn) + sc * __builtin_amdgcn_exp2f(rc - rn);
+    r = rn;
+  }
+  off[(int64_t)h * cq + row] = s > 0.f ? r + log2f(s) : INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void cf_mass(const uint16_t* __restrict__ rows, const int32_t* __restrict__ q_off,
+                                               int cq, const uint16_t* __restrict__ K, int64_t N,
+                                               const int32_t* __restrict__ k_perm,
+                                               const int32_t* __restrict__ k_off, int ck, float c1,
+                                               const float* __restrict__ off, float* __restrict__ map) {
+  constexpr int KS = D / 32;
+  const int h = blockIdx.y;
+  const int j0 = blockIdx.x * kCfClusters, j1 = min(j0 + kCfClusters, ck);
+  const int l = lane_id(), w = threadIdx.x / kWave, g = l / 16;
+  const uint16_t* Rh = rows + (int64_t)h * cq * D;
+  const uint16_t* Kh = K + (int64_t)h * N * D;
+  const int32_t* kp = k_perm + (int64_t)h * N;
+  const int32_t* ko = k_off + (int64_t)h * (ck + 1);
+  const int32_t* qo = q_off + (int64_t)h * (cq + 1);
+  const int nrt = (cq + 15) / 16;
+  for (int rt0 = w * kCfTW; rt0 < nrt; rt0 += 4 * kCfTW) {
+    u32x4_t qa[kCfTW][KS];
+    float ro[kCfTW][4];
+#pragma unroll
+    for (int t = 0; t < kCfTW; ++t) {
+      cf_rows<KS>(Rh, cq, rt0 + t, l, g, qa[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = (rt0 + t) * 16 + g * 4 + e;
+        ro[t][e] = row < cq ? off[(int64_t)h * cq + row] : INFINITY;
+      }
+    }
+    for (int j = j0; j < j1; ++j) {
+      const int a = max(ko[j], 0), b = (int)min<int64_t>(ko[j + 1], N);  // malformed offsets stay in range
+      float cs[kCfTW][4];
+#pragma unroll
+      for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[t][e] = 0.f;
+      for (int p = a; p < b; p += 16) {
+        const int pos = p + l % 16;
+        u32x4_t bv[KS];
+        cf_key<KS>(Kh, kp, N, pos, g, bv);
+        const bool ok = pos < b;
+#pragma unroll
+        for (int t = 0; t < kCfTW; ++t) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = __builtin_amdgcn_exp2f(acc[e] * c1 - ro[t][e]);
+            cs[t][e] += ok ? v : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kCfTW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) cs[t][e] += __shfl_xor(cs[t][e], o, kWave);
+          const int row = (rt0 + t) * 16 + g * 4 + e;
+          if (l % 16 == 0 && row < cq) map[((int64_t)h * cq + row) * ck + j] = qo[row + 1] > qo[row] ? cs[t][e] : 0.f;
+        }
+    }
+  }
+}
+}  // namespace
+
+int64_t cf_chunks(const Dims& s) { return ceil_div(s.N, kCfChunk); }
+
+hipError_t launch_cf_map(const Dims& s, const void* rows, const int32_t* q_offsets, int cq, const void* k,
+                         const int32_t* k_perm, const int32_t* k_offsets, int ck, float scale, float* map, float* part,
+                         float* off, hipStream_t st) {
+  const int nchunk = (int)cf_chunks(s);
+  const float c1 = scale * 1.4426950408889634f;
+  const uint16_t* rh = static_cast<const uint16_t*>(rows);
+  const uint16_t* kh = static_cast<const uint16_t*>(k);
+  const dim3 g1((unsigned)nchunk, (unsigned)s.H), g2((unsigned)ceil_div(cq, 256), (unsigned)s.H),
+      g3((unsigned)ceil_div(ck, kCfClusters), (unsigned)s.H);
+  if (s.D == 128) {
+    cf_lse<128><<<g1, 256, 0, st>>>(rh, cq, kh, s.N, k_perm, c1, nchunk, part);
+    cf_merge<<<g2, 256, 0, st>>>(part, nchunk, cq, off);
+    cf_mass<128><<<g3, 256, 0, st>>>(rh, q_offsets, cq, kh, s.N, k_perm, k_offsets, ck, c1, off, map);
+  } else {
+    cf_lse<64><<<g1, 256, 0, st>>>(rh, cq, kh, s.N, k_perm, c1, nchunk, part);
+    cf_merge<<<g2, 256, 0, st>>>(part, nchunk, cq, off);
+    cf_mass<64><<<g3, 256, 0, st>>>(rh, q_offsets, cq, kh, s.N, k_perm, k_offsets, ck, c1, off, map);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace park

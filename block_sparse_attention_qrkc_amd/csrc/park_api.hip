@@ -132,19 +132,27 @@ MapWs plan_map(Carver& cv, const park::Dims& s, int cq, int ck) {
   return w;
 }
 
-// Estimator maps: centroid-query rows (CC, CF) and the map workspace sized for the query rows used.
+// Estimator maps: centroid-query rows (CC, CF), the map workspace sized for the query rows used
+// (FC, CC, FF) and the CF passes' per-chunk pairs and row offsets.
 struct EstWs {
   uint16_t* qrows = nullptr;
   int32_t* qperm = nullptr;
   int32_t* qoff = nullptr;
+  float* cf_part = nullptr;
+  float* cf_off = nullptr;
   MapWs map;
 };
-EstWs plan_estimator(Carver& cv, const park::Dims& s, int cq, int ck, bool centroid_queries) {
+EstWs plan_estimator(Carver& cv, const park::Dims& s, int cq, int ck, int mode) {
   EstWs w;
-  if (centroid_queries) {
+  if (mode == PARK_EST_CC || mode == PARK_EST_CF) {
     w.qrows = cv.take<uint16_t>((size_t)(s.H * cq * s.D));
     w.qperm = cv.take<int32_t>((size_t)(s.H * cq));
     w.qoff = cv.take<int32_t>((size_t)(s.H * (cq + 1)));
+  }
+  if (mode == PARK_EST_CF) {
+    w.cf_part = cv.take<float>((size_t)(s.H * park::cf_chunks(s) * cq * 2));
+    w.cf_off = cv.take<float>((size_t)(s.H * cq));
+  } else if (mode == PARK_EST_CC) {
     park::Dims sq = s;
     sq.N = cq;
     w.map = plan_map(cv, sq, cq, ck);
@@ -154,10 +162,13 @@ EstWs plan_estimator(Carver& cv, const park::Dims& s, int cq, int ck, bool centr
   return w;
 }
 size_t estimator_ws_bytes(const park::Dims& s, int cq, int ck) {
-  Carver a(nullptr), b(nullptr);
-  plan_estimator(a, s, cq, ck, false);
-  plan_estimator(b, s, cq, ck, true);
-  return a.off > b.off ? a.off : b.off;
+  size_t m = 0;
+  for (int mode = PARK_EST_FC; mode <= PARK_EST_FF; ++mode) {
+    Carver c(nullptr);
+    plan_estimator(c, s, cq, ck, mode);
+    m = c.off > m ? c.off : m;
+  }
+  return m;
 }
 
 struct AttnWs {
@@ -462,7 +473,7 @@ park_status park_estimator_map(const park_shape* shape, const void* q, const voi
     PARK_TRY(check_ptr(map, "map", 4));
     PARK_TRY(check_ws(ws, ws_bytes, estimator_ws_bytes(s, cq, ck)));
     Carver cv(ws);
-    EstWs w = plan_estimator(cv, s, cq, ck, !full_q);
+    EstWs w = plan_estimator(cv, s, cq, ck, mode);
     hipStream_t st = (hipStream_t)stream;
     const float sc = resolve_scale(scale, s.D);
     hipError_t e = hipSuccess;
@@ -478,7 +489,9 @@ park_status park_estimator_map(const park_shape* shape, const void* q, const voi
       qo = w.qoff;
     }
     if (e == hipSuccess) {
-      if (full_k)
+      if (mode == PARK_EST_CF)
+        e = park::launch_cf_map(s, w.qrows, q_offsets, cq, k, k_perm, k_offsets, ck, sc, map, w.cf_part, w.cf_off, st);
+      else if (full_k)
         e = park::launch_block_mass(sq, qr, qp, qo, cq, k, s.N, k_perm, k_offsets, ck, sc, map, w.map.chunk_base,
                                     w.map.partial, st);
       else

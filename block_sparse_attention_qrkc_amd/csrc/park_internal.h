@@ -60,6 +60,12 @@ hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, cons
 int64_t pama_max_chunks(const Dims& s, int cq);
 // Block masses over every key (bf16 data): map[h, i, j] = mean over the rows of query cluster i of
 // the softmax mass (over all nk keys) that falls on key cluster j. Workspace as launch_pama.
+// CF estimator map: centroid rows [H, cq, D] bf16 against every key; part holds H * cf_chunks(s) * cq
+// (reference, sum) pairs, off H * cq floats.
+int64_t cf_chunks(const Dims& s);
+hipError_t launch_cf_map(const Dims& s, const void* rows, const int32_t* q_offsets, int cq, const void* k,
+                         const int32_t* k_perm, const int32_t* k_offsets, int ck, float scale, float* map, float* part,
+                         float* off, hipStream_t st);
 hipError_t launch_block_mass(const Dims& s, const void* q, const int32_t* q_perm, const int32_t* q_offsets, int cq,
                              const void* k, int64_t nk, const int32_t* k_perm, const int32_t* k_offsets, int ck,
                              float scale, float* map, int32_t* chunk_base, float* partial, hipStream_t st);
