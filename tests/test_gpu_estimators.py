@@ -86,3 +86,39 @@ def test_estimator_maps(clustered, mode):
         assert np.abs(Eg[h][live].sum(1) - 1).max() <= MAP_ABS
         assert np.all(Eg[h][~live] == 0) and np.all(Eg[h][:, np.diff(ko) == 0] == 0)
     print(f"[estimator {mode}] ok")
+
+
+@pytest.mark.parametrize("name", ["small", "small64"])
+def test_cf_map_many_clusters(name):
+    """The CF map's key-split passes at cluster counts beyond one merge block (300 query clusters)
+    and a key-cluster count that is not a multiple of a work-group's eight, with an empty query
+    cluster (zero row) and an empty key cluster (zero column); centroids are arbitrary rows."""
+    w = SMALL[name]
+    rng = np.random.default_rng(5)
+    Q, K, V = inputs(w)
+    H, N, d = w.heads, w.n, w.d
+    cq, ck = 300, 203
+    qps, qos, kps, kos = [], [], [], []
+    for h in range(H):
+        ql = rng.integers(0, cq, N)
+        ql[ql == 17] = 18            # empty query cluster
+        kl = rng.integers(0, ck, N)
+        kl[kl == 40] = 41            # empty key cluster
+        qp, qo = O.cluster_order(ql, cq)
+        kp, ko = O.cluster_order(kl, ck)
+        qps.append(qp); qos.append(qo); kps.append(kp); kos.append(ko)
+    T = lambda a: torch.tensor(np.stack(a), dtype=torch.int32, device="cuda").contiguous()
+    qp, qo, kp, ko = map(T, (qps, qos, kps, kos))
+    qcent = torch.tensor(rng.normal(0.0, 1.0, (H, cq, d)), dtype=torch.float32, device="cuda")
+    kcent = torch.tensor(rng.normal(0.0, 1.0, (H, ck, d)), dtype=torch.float32, device="cuda")
+    E = bsa.park_estimator_map(bsa.PARK_EST_CF, ko, q=Q, k=K, q_perm=qp, q_offsets=qo, q_centroids=qcent,
+                               k_perm=kp, k_centroids=kcent)
+    Eg = to64(E)
+    for h in range(H):
+        qcent64 = O.round_bf16(to64(qcent[h]))
+        Eo = O.estimator_block_maps(to64(Q[h]), to64(K[h]), np_i(qp[h]), np_i(qo[h]), qcent64, np_i(kp[h]),
+                                    np_i(ko[h]), O.round_bf16(to64(kcent[h])), w.scale)["CF"]
+        err = np.abs(Eg[h] - Eo).max()
+        assert err <= MAP_ABS, (h, err)
+        assert np.all(Eg[h][17] == 0) and np.all(Eg[h][:, 40] == 0)
+    print(f"[cf many clusters {name}] ok")

@@ -237,6 +237,36 @@ def test_sparse_attention_edge_selections():
         assert np.all(to64(out[h])[rows] == 0) and np.all(np.isneginf(to64(lse[h])[rows]))
 
 
+def test_sparse_attention_many_clusters():
+    """More query and key clusters than one 1024-thread block has threads (the per-head work order
+    sorts 1500 clusters, several per thread), a few large query clusters spanning several 384-query
+    work items among many tiny ones, and many clusters with equal selected key counts (ties)."""
+    w = SMALL["small"]
+    rng = np.random.default_rng(11)
+    Q, K, V = inputs(w)
+    H, N = w.heads, w.n
+    cq, ck = 1500, 1100
+    qps, qos, kps, kos, cnts, colss = [], [], [], [], [], []
+    for h in range(H):
+        ql = rng.integers(3, cq, N)
+        big = rng.random(N) < 0.45
+        ql[big] = rng.integers(0, 3, int(big.sum()))   # clusters 0..2 hold ~500 queries each
+        kl = rng.integers(0, ck, N)
+        qp, qo = O.cluster_order(ql, cq)
+        kp, ko = O.cluster_order(kl, ck)
+        cols = np.zeros((cq, ck), dtype=np.int32)
+        cnt = np.zeros(cq, dtype=np.int32)
+        for i in range(cq):
+            sel = np.sort(rng.choice(ck, size=int(rng.integers(1, 40)), replace=False))
+            cnt[i] = sel.size
+            cols[i, :sel.size] = sel
+        qps.append(qp); qos.append(qo); kps.append(kp); kos.append(ko); cnts.append(cnt); colss.append(cols)
+    T = lambda a: torch.tensor(np.stack(a), dtype=torch.int32, device="cuda").contiguous()
+    qp, qo, kp, ko, counts, cols = map(T, (qps, qos, kps, kos, cnts, colss))
+    out, lse = bsa.park_sparse_attn(Q, K, V, qp, qo, kp, ko, counts, cols)
+    _attn_check(w, Q, K, V, qp, qo, kp, ko, counts, cols, out, lse)
+
+
 def test_permute_roundtrip(case):
     """P12: gather then scatter is the identity; the gather matches the permutation."""
     w, Q, K, V, M = case
