@@ -168,6 +168,31 @@ def ceilings(dev):
     return {"gemm_bf16_tflops": round(gemm, 1), "copy_gbs": round(copy, 1)}
 
 
+def topp_near_ties(A, k_offsets, counts, p, tau=1e-5):
+    """Top-p rows whose cut lies within tau of a decision boundary: the kept prefix sums to within
+    tau of p, the prefix one shorter does, or the last kept and first dropped importances differ by
+    at most tau. Such rows may legitimately differ between two correct implementations."""
+    if p >= 1.0:
+        return {"rows": 0, "near": 0, "tau": tau}
+    A = A.double().cpu().numpy()
+    ko = k_offsets.cpu().numpy()
+    cnt = counts.cpu().numpy().astype(np.int64)
+    rows = near = 0
+    for h in range(A.shape[0]):
+        live = np.diff(ko[h]) > 0
+        v = -np.sort(-np.maximum(A[h][:, live], 0.0), axis=1)
+        cum = np.cumsum(v, axis=1)
+        for i in range(A.shape[1]):
+            k = int(cnt[h, i])
+            if k <= 0 or k > v.shape[1]:
+                continue
+            rows += 1
+            close = abs(cum[i, k - 1] - p) <= tau or (k >= 2 and abs(cum[i, k - 2] - p) <= tau)
+            close = close or (k < v.shape[1] and v[i, k - 1] - v[i, k] <= tau)
+            near += int(close)
+    return {"rows": rows, "near": near, "tau": tau}
+
+
 def selection_stats(w, r):
     """Token density, computed and padded FLOPs of one layer's selection."""
     qsz = torch.diff(r["q_offsets"], dim=1).to(torch.float64)
@@ -531,6 +556,7 @@ def main():
         res["dense_attn_tflops"] = round(dense_flops / (st["dense_attn"] * 1e9), 2)
         res["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
                          "worst": round(float(rec.min()), 4)}
+        res["near_ties"] = topp_near_ties(A, kc["offsets"], sel["counts"], w.p)
         ach = flops_sel / (st["sparse_attn"] * 1e9)
         log(f"stages: {res['stages_ms']}")
         traffic = measured_traffic() if w.name == "wan" else None
