@@ -169,15 +169,16 @@ def ceilings(dev):
 
 
 def topp_near_ties(A, k_offsets, counts, p, tau=1e-5):
-    """Top-p rows whose cut lies within tau of a decision boundary: the kept prefix sums to within
-    tau of p, the prefix one shorter does, or the last kept and first dropped importances differ by
-    at most tau. Such rows may legitimately differ between two correct implementations."""
+    """Top-p rows whose cut is close to a decision boundary: `sum` counts rows where the kept prefix,
+    or the prefix one shorter, sums to within tau of p; `order` counts rows where the last kept and
+    the first dropped importances agree to a relative tau (an order two correct implementations may
+    resolve differently). Either kind may legitimately differ between implementations."""
     if p >= 1.0:
-        return {"rows": 0, "near": 0, "tau": tau}
+        return {"rows": 0, "sum": 0, "order": 0, "tau": tau}
     A = A.double().cpu().numpy()
     ko = k_offsets.cpu().numpy()
     cnt = counts.cpu().numpy().astype(np.int64)
-    rows = near = 0
+    rows = n_sum = n_order = 0
     for h in range(A.shape[0]):
         live = np.diff(ko[h]) > 0
         v = -np.sort(-np.maximum(A[h][:, live], 0.0), axis=1)
@@ -187,10 +188,9 @@ def topp_near_ties(A, k_offsets, counts, p, tau=1e-5):
             if k <= 0 or k > v.shape[1]:
                 continue
             rows += 1
-            close = abs(cum[i, k - 1] - p) <= tau or (k >= 2 and abs(cum[i, k - 2] - p) <= tau)
-            close = close or (k < v.shape[1] and v[i, k - 1] - v[i, k] <= tau)
-            near += int(close)
-    return {"rows": rows, "near": near, "tau": tau}
+            n_sum += int(abs(cum[i, k - 1] - p) <= tau or (k >= 2 and abs(cum[i, k - 2] - p) <= tau))
+            n_order += int(k < v.shape[1] and v[i, k - 1] - v[i, k] <= tau * v[i, k - 1])
+    return {"rows": rows, "sum": n_sum, "order": n_order, "tau": tau}
 
 
 def selection_stats(w, r):
