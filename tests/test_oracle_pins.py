@@ -59,9 +59,26 @@ def test_round_bf16_matches_torch_rne():
     np.testing.assert_array_equal(O.round_bf16(x), want)
 
 
-def test_round_f32_matches_numpy_cast():
-    x = np.random.default_rng(1).normal(size=1000) * 1e3
-    np.testing.assert_array_equal(O.round_f32(x), x.astype(np.float32).astype(np.float64))
+def test_round_f32_known_neighbours_and_ties():
+    """Nearest float32, ties to even, on values worked out from the binary expansions."""
+    # 0.1 lies between the float32 values 13421772 * 2^-27 and 13421773 * 2^-27 and is nearer
+    # the second (0.1 * 2^27 = 13421772.8)
+    assert O.round_f32(0.1) == 13421773 * 2.0 ** -27 == 0.100000001490116119384765625
+    assert O.round_f32(-0.1) == -13421773 * 2.0 ** -27
+    # 1/3 * 2^25 = 11184810.67 -> 11184811 * 2^-25
+    assert O.round_f32(1.0 / 3.0) == 11184811 * 2.0 ** -25
+    # exact halfway cases: 1 + 2^-24 lies between 1 (even) and 1 + 2^-23 (odd) -> 1;
+    # 1 + 3 * 2^-24 between 1 + 2^-23 (odd) and 1 + 2^-22 (even) -> 1 + 2^-22
+    assert O.round_f32(1.0 + 2.0 ** -24) == 1.0
+    assert O.round_f32(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22
+    # just above a halfway point rounds up
+    assert O.round_f32(1.0 + 2.0 ** -24 + 2.0 ** -40) == 1.0 + 2.0 ** -23
+    # values already in float32 are unchanged, including the largest finite one
+    for v in (0.0, 1.5, -2.0 ** -149, (2.0 - 2.0 ** -23) * 2.0 ** 127):
+        assert O.round_f32(v) == v
+    # below half the smallest subnormal flushes to zero; above it rounds to 2^-149
+    assert O.round_f32(2.0 ** -151) == 0.0
+    assert O.round_f32(0.75 * 2.0 ** -149) == 2.0 ** -149
 
 
 # ------------------------------------------------------------------------------------ metric
@@ -163,6 +180,24 @@ def test_assign_matches_scipy_argmin():
     clear = (srt[:, 1] - srt[:, 0]) > 1e-6 * (1 + srt[:, 0])
     assert clear.mean() > 0.95
     np.testing.assert_array_equal(O.assign(X, g, b)[clear], np.argmin(dm, axis=1)[clear])
+
+
+def test_assign_near_tie_hand_worked():
+    """The classifier that turns a differing GPU label into a near-tie or an error."""
+    c = _golden("assign_near_tie_hand.json")
+    X, g, b = (np.array(c[k], dtype=np.float64) for k in ("X", "g", "b"))
+    np.testing.assert_array_equal(O.assign(X, g, b), c["argmin"])
+    n_near, bad = O.assign_near_tie(X, g, b, np.array(c["labels_other"]), tau=c["tau"])
+    assert n_near == c["near_ties"]
+    np.testing.assert_array_equal(bad, c["bad_rows"])
+    # identical labels: nothing to classify
+    n_near, bad = O.assign_near_tie(X, g, b, np.array(c["argmin"]), tau=c["tau"])
+    assert n_near == 0 and bad.size == 0
+    # the band scales with tau: at tau = 0 both differing rows are errors, at 1e-4 both pass
+    n_near, bad = O.assign_near_tie(X, g, b, np.array(c["labels_other"]), tau=0.0)
+    assert n_near == 0 and list(bad) == [0, 1]
+    n_near, bad = O.assign_near_tie(X, g, b, np.array(c["labels_other"]), tau=1e-4)
+    assert n_near == 2 and bad.size == 0
 
 
 def test_assign_ties_go_to_lowest_index():
@@ -708,6 +743,30 @@ def test_estimator_block_maps_collapse_in_the_limits():
     m = O.estimator_block_maps(Q, K2, qp, qo, qc, kp, ko, base, 0.5)
     np.testing.assert_allclose(m["FC"], m["FF"], atol=1e-12)
     np.testing.assert_allclose(m["CC"], m["CF"], atol=1e-12)
+
+
+def test_tv_to_full_hand_values():
+    """Mean over rows of half the L1 distance (PARK page, Table 4: mean attention-weight TV)."""
+    assert O.tv_to_full([[0.5, 0.5]], [[1.0, 0.0]]) == 0.5
+    assert O.tv_to_full([[0.0, 1.0]], [[1.0, 0.0]]) == 1.0  # disjoint supports: the maximum
+    # rows 0.5 and 0 -> mean 0.25
+    assert O.tv_to_full([[0.5, 0.5], [1.0, 0.0]], [[1.0, 0.0], [1.0, 0.0]]) == 0.25
+    # 0.5 * (0.3 + 0 + 0.3) = 0.3
+    assert abs(O.tv_to_full([[0.2, 0.3, 0.5]], [[0.5, 0.3, 0.2]]) - 0.3) < 1e-15
+    # symmetric
+    a, b = [[0.1, 0.6, 0.3]], [[0.4, 0.4, 0.2]]
+    assert O.tv_to_full(a, b) == O.tv_to_full(b, a)
+
+
+def test_raw_key_mse_hand_value():
+    """Mean over keys of the squared distance to the key's centroid (PARK page, Table 5)."""
+    K = [[1.0, 2.0], [3.0, 5.0], [0.0, 0.0]]
+    cent = [[2.0, 3.0], [1.0, -1.0]]
+    # |(-1,-1)|^2 = 2, |(1,2)|^2 = 5, |(-1,1)|^2 = 2 -> mean 3
+    assert O.raw_key_mse(K, np.array([0, 0, 1]), cent) == 3.0
+    # labels index the centroids: swapping them changes the value
+    # |(0,3)|^2 = 9, |(2,6)|^2 = 40, |(-2,-3)|^2 = 13 -> mean 62 / 3
+    assert abs(O.raw_key_mse(K, np.array([1, 1, 0]), cent) - 62.0 / 3.0) < 1e-13
 
 
 def test_tv_zero_for_full_and_estimators_are_distributions():
