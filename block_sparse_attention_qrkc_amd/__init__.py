@@ -20,7 +20,7 @@ from ._lib import (  # noqa: F401
     PARK_ENTRY_ESTIMATOR, PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP,
     PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_SPARSE_ATTN_WEIGHTED, PARK_EST_CC, PARK_EST_CF, PARK_EST_FC, PARK_EST_FF,
     PARK_EUCLID, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_F32, PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_OK,
-    PARK_QRKC, PARK_SIDE_K, PARK_SIDE_Q, ParkError, Workspace, lib, make_params, make_shape, park_forward_outputs,
+    PARK_QRKC, PARK_SIDE_K, PARK_SIDE_Q, PARK_DEVSTATUS_SEED_TIMEOUT, ParkError, Workspace, lib, make_params, make_shape, park_forward_outputs,
     park_params, park_shape, workspace_bytes,
 )
 from ._lib import _check, _ptr, _stream, _ws
@@ -46,11 +46,12 @@ def park_qrkc_metric(q, out=None, ws=None, stream=None):
 
 
 def park_cluster(x, n_clusters, iters, metric=PARK_EUCLID, qmetric=None, init=PARK_INIT_KMEANSPP, seed=0,
-                 side=PARK_SIDE_Q, centroids=None, ws=None, stream=None):
+                 side=PARK_SIDE_Q, centroids=None, status=None, ws=None, stream=None):
     """K-means of one token side. Returns dict(centroids, labels, perm, offsets).
 
     With ``init=PARK_INIT_WARM`` the given ``centroids`` [heads, C, d] float32 are the start (and are
-    updated in place)."""
+    updated in place). ``status``: optional int32 device tensor of one element; PARK_DEVSTATUS_*
+    bits are or-ed into it (never cleared)."""
     sh = make_shape(x)
     H, N, D = sh.heads, sh.n, sh.d
     dev = x.device
@@ -66,7 +67,7 @@ def park_cluster(x, n_clusters, iters, metric=PARK_EUCLID, qmetric=None, init=PA
     wp, wn = _ws(entry, sh, prm, dev, ws)
     _check(lib().park_cluster(ctypes.byref(sh), _ptr(x), int(metric), _ptr(qmetric), int(n_clusters), int(iters),
                               int(init), int(seed) & ((1 << 64) - 1), int(side), _ptr(centroids), _ptr(labels),
-                              _ptr(perm), _ptr(offsets), wp, wn, _stream(stream)))
+                              _ptr(perm), _ptr(offsets), _ptr(status), wp, wn, _stream(stream)))
     return {"centroids": centroids, "labels": labels, "perm": perm, "offsets": offsets}
 
 
@@ -213,6 +214,7 @@ _FWD_FIELDS = {
     "cols": lambda H, N, D, cq, ck: ((H, cq, ck), torch.int32),
     "sel_keys": lambda H, N, D, cq, ck: ((H, cq), torch.int64),
     "lse": lambda H, N, D, cq, ck: ((H, N), torch.float32),
+    "status": lambda H, N, D, cq, ck: ((1,), torch.int32),
 }
 
 
@@ -232,7 +234,7 @@ def park_forward(q, k, v, cq, ck, iters, p, scale=0.0, seed=0, kmetric=PARK_QRKC
     fo = park_forward_outputs()
     for name in outputs:
         shp, dt = _FWD_FIELDS[name](H, N, D, cq, ck)
-        t = torch.empty(shp, dtype=dt, device=dev)
+        t = torch.zeros(shp, dtype=dt, device=dev) if name == "status" else torch.empty(shp, dtype=dt, device=dev)
         res[name] = t
         setattr(fo, name, t.data_ptr())
     prm = make_params(cq, ck, iters, p, scale, seed, kmetric, init)

@@ -24,12 +24,13 @@ PARK_EST_FC, PARK_EST_CC, PARK_EST_CF, PARK_EST_FF = range(4)
 (PARK_ENTRY_METRIC, PARK_ENTRY_CLUSTER_Q, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_RETRIEVE_MAP,
  PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_FORWARD, PARK_ENTRY_ESTIMATOR,
  PARK_ENTRY_SPARSE_ATTN_WEIGHTED) = range(9)
+PARK_DEVSTATUS_SEED_TIMEOUT = 1
 
 EXPORTED = [
     "park_workspace_bytes", "park_status_string", "park_last_error", "park_version",
     "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
     "park_select_topk", "park_select_sip", "park_sparse_attn", "park_sparse_attn_weighted",
-    "park_permute_rows", "park_unpermute_rows", "park_forward",
+    "park_permute_rows", "park_unpermute_rows", "park_forward", "park_debug_force_seed_timeout",
 ]
 
 
@@ -58,7 +59,8 @@ _P = ctypes.c_void_p
 
 class park_forward_outputs(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("metric", "q_labels", "q_perm", "q_offsets", "k_labels", "k_perm", "k_offsets",
-                                  "map", "mask", "counts", "cols", "sel_keys", "lse")]
+                                  "map", "mask", "counts", "cols", "sel_keys", "lse",
+                                  "status")]
 
 
 _lib = None
@@ -84,7 +86,8 @@ def lib() -> ctypes.CDLL:
             "park_last_error": (ctypes.c_char_p, []),
             "park_version": (ctypes.c_char_p, []),
             "park_qrkc_metric": (i32, [SP, _P, _P, _P, sz, _P]),
-            "park_cluster": (i32, [SP, _P, i32, _P, i32, i32, i32, u64, i32, _P, _P, _P, _P, _P, sz, _P]),
+            "park_cluster": (i32, [SP, _P, i32, _P, i32, i32, i32, u64, i32, _P, _P, _P, _P, _P, _P, sz, _P]),
+            "park_debug_force_seed_timeout": (None, [i32]),
             "park_retrieve_map": (i32, [SP, _P, _P, _P, i32, _P, _P, i32, f32, _P, _P, sz, _P]),
             "park_estimator_map": (i32, [SP, _P, _P, _P, _P, i32, _P, _P, _P, i32, _P, i32, f32, _P, _P, sz, _P]),
             "park_select_topp": (i32, [_P, i64, i32, i32, _P, f64, _P, _P, _P, _P, _P]),

@@ -426,8 +426,11 @@ __device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
 }
 
 // H heads from head h0 on: the side pointers start at head h0, the draws use the head's own index.
+// status (may be NULL): bit 0 is set at the end of the launch when any bounded wait of a side gave
+// up, so a lost exchange reaches the caller instead of passing silently.
 template <int D, int NT>
-__global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, int h0, int64_t N, uint64_t seed) {
+__global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, int h0, int64_t N, uint64_t seed,
+                                               int* status) {
   constexpr int kCoopWaves = NT / kWave;
   constexpr int ROW_U32 = D / 2;
   extern __shared__ uint32_t lrows[];  // [SP - threads][D / 2] bf16 pairs of the LDS-resident rows
@@ -699,6 +702,8 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
     }
     __syncthreads();
   }
+  if (tid == 0 && status != nullptr && __hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+    __hip_atomic_fetch_or(status, kSeedTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void fill_i32(int* p, int64_t n, int v) {
@@ -1179,6 +1184,8 @@ __global__ __launch_bounds__(64) void sort_scatter(const int32_t* __restrict__ l
 // Launchers
 // ------------------------------------------------------------------------------------------------
 
+std::atomic<int> g_force_seed_timeout{0};
+
 // Single-workgroup seeding (any dtype): candidate norms, then one workgroup per (head, side).
 static hipError_t launch_kpp_single(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
   KppSide ks[2];
@@ -1249,7 +1256,7 @@ static bool plan_parts(const Dims& s, const KppArgs* sides, int nsides, int budg
 // heads' step flags (for a leading batch: on the first flag of the next batch, which that batch's
 // own launch clears before it runs).
 static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nsides, const int* G, int nt,
-                                  uint64_t seed, hipStream_t st, int h0 = 0, int Hb = -1) {
+                                  uint64_t seed, int* status, hipStream_t st, int h0 = 0, int Hb = -1) {
   if (Hb < 0) Hb = (int)s.H;
   CoopSide cs[2];
   size_t lds = 0;
@@ -1270,6 +1277,9 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
     fill_i32<<<(unsigned)ceil_div(nsync, 256), 256, 0, st>>>(sync, nsync, 0);
     const int64_t nslot = (int64_t)Hb * a.C * kCoopMaxParts * 2 * 2;  // as int32 words
     fill_i32<<<(unsigned)ceil_div(nslot, 256), 256, 0, st>>>(reinterpret_cast<int*>(psum), nslot, 0);
+    // failure-handling hook: a raised flag makes every wait of the launch give up at once
+    if (g_force_seed_timeout.load(std::memory_order_relaxed))
+      fill_i32<<<1, 256, 0, st>>>(sync + (int64_t)Hb * a.C * 3, 1, 1);
   }
   if (nsides == 1) {
     cs[1] = cs[0];
@@ -1279,7 +1289,7 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
   if (e != hipSuccess) return e;
   int H = Hb;
   int64_t N = s.N;
-  void* args[] = {&cs[0], &cs[1], &H, &h0, &N, &seed};
+  void* args[] = {&cs[0], &cs[1], &H, &h0, &N, &seed, &status};
   const void* fn = nt == kCoopThreads
                        ? (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreads> : (const void*)kpp_coop<64, kCoopThreads>)
                        : (s.D == 128 ? (const void*)kpp_coop<128, kCoopThreadsWide>
@@ -1291,7 +1301,8 @@ static hipError_t launch_kpp_coop(const Dims& s, const KppArgs* sides, int nside
 // Sides whose candidates need more 512-thread parts per head than one launch over all heads can
 // hold run in batches of heads, 2 to 4 launches per side, each with the whole chip for its heads
 // (the 1024-thread parts are kept for what still does not fit). True when every side launched.
-static bool batched_kpp(const Dims& s, const KppArgs* sides, int nsides, int cus, uint64_t seed, hipStream_t st) {
+static bool batched_kpp(const Dims& s, const KppArgs* sides, int nsides, int cus, uint64_t seed, int* status,
+                        hipStream_t st) {
   int nb[2] = {0, 0}, G[2][1];
   for (int q = 0; q < nsides; ++q) {
     for (int B = 1; B <= 4 && !nb[q]; ++B) {
@@ -1303,8 +1314,8 @@ static bool batched_kpp(const Dims& s, const KppArgs* sides, int nsides, int cus
   for (int q = 0; q < nsides; ++q) {
     const int hb = (int)ceil_div(s.H, nb[q]);
     for (int h0 = 0; h0 < (int)s.H; h0 += hb) {
-      if (launch_kpp_coop(s, sides + q, 1, G[q], kCoopThreads, seed, st, h0, (int)std::min<int64_t>(hb, s.H - h0)) !=
-          hipSuccess) {
+      if (launch_kpp_coop(s, sides + q, 1, G[q], kCoopThreads, seed, status, st, h0,
+                          (int)std::min<int64_t>(hb, s.H - h0)) != hipSuccess) {
         (void)hipGetLastError();
         return false;
       }
@@ -1313,7 +1324,7 @@ static bool batched_kpp(const Dims& s, const KppArgs* sides, int nsides, int cus
   return true;
 }
 
-hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st) {
+hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, int* status, hipStream_t st) {
   // candidate norms (and metric products) for every side
   for (int q = 0; q < nsides; ++q) {
     const KppArgs& a = sides[q];
@@ -1352,18 +1363,18 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
       // 512-thread parts; per side, 512-thread parts over batches of heads; both sides with
       // 1024-thread parts; per side the narrowest parts that fit
       if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreads, G)) {
-        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreads, seed, st) == hipSuccess) return hipSuccess;
+        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreads, seed, status, st) == hipSuccess) return hipSuccess;
         (void)hipGetLastError();
       } else if (budget > 0 && nsides == 2 && plan_parts(s, sides, 1, budget, kCoopThreads, G) &&
                  plan_parts(s, sides + 1, 1, budget, kCoopThreads, G + 1)) {
-        if (launch_kpp_coop(s, sides, 1, G, kCoopThreads, seed, st) == hipSuccess &&
-            launch_kpp_coop(s, sides + 1, 1, G + 1, kCoopThreads, seed, st) == hipSuccess)
+        if (launch_kpp_coop(s, sides, 1, G, kCoopThreads, seed, status, st) == hipSuccess &&
+            launch_kpp_coop(s, sides + 1, 1, G + 1, kCoopThreads, seed, status, st) == hipSuccess)
           return hipSuccess;
         (void)hipGetLastError();
-      } else if (batched_kpp(s, sides, nsides, cus, seed, st)) {
+      } else if (batched_kpp(s, sides, nsides, cus, seed, status, st)) {
         return hipSuccess;
       } else if (budget > 0 && plan_parts(s, sides, nsides, budget, kCoopThreadsWide, G)) {
-        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreadsWide, seed, st) == hipSuccess) return hipSuccess;
+        if (launch_kpp_coop(s, sides, nsides, G, kCoopThreadsWide, seed, status, st) == hipSuccess) return hipSuccess;
         (void)hipGetLastError();
       } else if (budget > 0) {
         int nt[2] = {0, 0};
@@ -1373,7 +1384,7 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
         if (nt[0] && (nsides == 1 || nt[1])) {
           bool ok = true;
           for (int q = 0; q < nsides && ok; ++q)
-            ok = launch_kpp_coop(s, sides + q, 1, G + q, nt[q], seed, st) == hipSuccess;
+            ok = launch_kpp_coop(s, sides + q, 1, G + q, nt[q], seed, status, st) == hipSuccess;
           if (ok) return hipSuccess;
           (void)hipGetLastError();
         }

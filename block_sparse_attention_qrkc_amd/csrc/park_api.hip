@@ -312,6 +312,8 @@ const char* park_status_string(int32_t status) {
 
 const char* park_last_error(void) { return g_last_error.c_str(); }
 
+void park_debug_force_seed_timeout(int32_t on) { park::g_force_seed_timeout.store(on != 0 ? 1 : 0); }
+
 size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_params* params) {
   try {
     park::Dims s;
@@ -377,7 +379,8 @@ park_status park_qrkc_metric(const park_shape* shape, const void* q, float* metr
 
 park_status park_cluster(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
                          int32_t n_clusters, int32_t iters, int32_t init, uint64_t seed, int32_t side, float* centroids,
-                         int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+                         int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status, void* ws, size_t ws_bytes,
+                         void* stream) {
   try {
     park::Dims s;
     PARK_TRY(check_shape(shape, &s));
@@ -389,6 +392,7 @@ park_status park_cluster(const park_shape* shape, const void* x, int32_t metric,
     if (init != PARK_INIT_KMEANSPP && init != PARK_INIT_WARM) return fail(PARK_EINVAL, "init must be PARK_INIT_KMEANSPP or PARK_INIT_WARM");
     if (side != PARK_SIDE_Q && side != PARK_SIDE_K) return fail(PARK_EINVAL, "side must be PARK_SIDE_Q or PARK_SIDE_K");
     PARK_TRY(check_ptr(centroids, "centroids", 4));
+    if (status && !aligned(status, 4)) return fail(PARK_EINVAL, "status must be 4-byte aligned");
     if (iters > 0) {
       PARK_TRY(check_ptr(labels, "labels", 4));
       PARK_TRY(check_ptr(perm, "perm", 4));
@@ -404,7 +408,7 @@ park_status park_cluster(const park_shape* shape, const void* x, int32_t metric,
     hipError_t e = hipSuccess;
     if (init == PARK_INIT_KMEANSPP) {
       const park::KppArgs a = kpp_args(x, mp, n_clusters, side, centroids, w);
-      e = park::launch_kpp(s, &a, 1, seed, st);
+      e = park::launch_kpp(s, &a, 1, seed, status, st);
     }
     if (e == hipSuccess) e = run_lloyd(s, x, mp, n_clusters, iters, centroids, labels, perm, offsets, w, st);
     return hip_check(e, "park_cluster");
@@ -675,7 +679,7 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
     std::memset(&o, 0, sizeof(o));
     if (outputs) o = *outputs;
     const void* opt[] = {o.metric, o.q_labels, o.q_perm, o.q_offsets, o.k_labels, o.k_perm, o.k_offsets,
-                         o.map, o.counts, o.cols, o.lse};
+                         o.map, o.counts, o.cols, o.lse, o.status};
     for (const void* ptr : opt)
       if (ptr && !aligned(ptr, 4)) return fail(PARK_EINVAL, "forward outputs must be 4-byte aligned");
     if (o.sel_keys && !aligned(o.sel_keys, 8)) return fail(PARK_EINVAL, "sel_keys must be 8-byte aligned");
@@ -704,7 +708,7 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
       // both sides seeded in one launch (one workgroup per head and side)
       const park::KppArgs a[2] = {kpp_args(q, nullptr, p.cq, PARK_SIDE_Q, q_centroids, w.qc),
                                   kpp_args(k, qrkc ? M : nullptr, p.ck, PARK_SIDE_K, k_centroids, w.kc)};
-      e = park::launch_kpp(s, a, 2, p.seed, st);
+      e = park::launch_kpp(s, a, 2, p.seed, o.status, st);
     }
     if (e == hipSuccess) {
       // query side on the helper stream, key side on the caller's, joined before the map

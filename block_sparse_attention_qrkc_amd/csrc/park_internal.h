@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace park {
 
 struct Dims {
@@ -31,6 +33,11 @@ hipError_t launch_metric(const Dims& s, const void* q, float* metric, double* pa
 size_t metric_partial_count(const Dims& s);
 
 // kmeans.hip
+// Bits of the optional device status word (PARK_DEVSTATUS_* of the C ABI).
+constexpr int kSeedTimeout = 1;  // a bounded wait of the cooperative k-means++ seeding gave up
+// Failure-handling hook: while non-zero, every cooperative seeding launch starts with its failure
+// flag raised, so each bounded wait gives up at once and the status bit is set.
+extern std::atomic<int> g_force_seed_timeout;
 struct KppArgs {
   const void* x;        // [H, N, D] data of the side
   const float* metric;  // [H, D, D] query metric (QRKC side) or NULL (Euclidean)
@@ -43,7 +50,8 @@ struct KppArgs {
   int* sync;            // workspace [H, C, 3] step flags of the cooperative seeding
 };
 // k-means++ seeding of one or two sides in a single launch.
-hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, hipStream_t st);
+// status (device, may be NULL): kSeedTimeout is or-ed in when a cooperative exchange timed out.
+hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, int* status, hipStream_t st);
 // Centroid means (do_update) and the consumed form (g, b) of the centroids for the next assignment.
 hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets, float* cent,
                          int do_update, const float* metric, void* g, float* b, hipStream_t st);

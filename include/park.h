@@ -90,6 +90,22 @@ const char* park_last_error(void);
 /* Library version string. */
 const char* park_version(void);
 
+/* Bits of the optional device status word (int32) that park_cluster and park_forward take. The
+ * library only sets bits (atomic or), never clears them: the caller zeroes the word before the
+ * calls it wants to check and reads it after synchronising. */
+enum {
+  /* a bounded wait of the cooperative k-means++ seeding gave up (a part of the launch did not
+   * answer within ~30 ms): every later wait of that launch returned at once, so the seeded
+   * centroids, and all that follows from them in this call, are not the seeding the draws define */
+  PARK_DEVSTATUS_SEED_TIMEOUT = 1
+};
+
+/* Failure-handling hook for tests: while `on` is non-zero, every cooperative seeding launch of this
+ * process starts with its failure flag raised, so each of its bounded waits gives up at once, the
+ * launch ends normally with wrong centroids, and PARK_DEVSTATUS_SEED_TIMEOUT is set. Not for
+ * production use. */
+void park_debug_force_seed_timeout(int32_t on);
+
 /*
  * QRKC key metric. PARK page, Figure 2 caption and abstract: keys are transformed with a metric
  * derived from the current queries so that keys with similar QK scores group together. Reading:
@@ -123,11 +139,13 @@ park_status park_qrkc_metric(const park_shape* shape, const void* q, float* metr
  * centroid: Euclidean g_j = c_j (bf16-rounded for bf16 data), b_j = |g_j|^2; QRKC g_j = M c_j
  * (fp32, then bf16 for bf16 data), b_j = c_j^T M c_j. With iters == 0 only the centroids are
  * written and labels/perm/offsets may be NULL.
+ *   status     optional device int32 (NULL: not reported): PARK_DEVSTATUS_* bits are or-ed in
+ *              when the seeding's cooperative exchange fails (see PARK_DEVSTATUS_SEED_TIMEOUT)
  */
 park_status park_cluster(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
                          int32_t n_clusters, int32_t iters, int32_t init, uint64_t seed, int32_t side,
-                         float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws,
-                         size_t ws_bytes, void* stream);
+                         float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * PAMA block-importance map (PARK page, Figure 2 caption and abstract: each original query keeps
@@ -281,6 +299,7 @@ typedef struct {
   int32_t* cols;       /* [heads, cq, ck] */
   int64_t* sel_keys;   /* [heads, cq] */
   float* lse;          /* [heads, n] */
+  int32_t* status;     /* one int32: PARK_DEVSTATUS_* bits or-ed in (see park_cluster) */
 } park_forward_outputs;
 
 /*

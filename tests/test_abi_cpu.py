@@ -22,7 +22,7 @@ def L():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:park_status|size_t|const char\*)\s+(park_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:park_status|size_t|const char\*|void)\s+(park_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -61,6 +61,7 @@ def test_status_strings(L):
 
 FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
 MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned for 16-byte data
+ODD = ctypes.c_void_p((1 << 20) + 2)  # misaligned for 4-byte words
 
 
 def _shape(L, H=2, N=1000, d=128, dt=1):
@@ -90,24 +91,28 @@ def test_validation_errors(L):
     st, msg = _status(L, "park_qrkc_metric", bp(sh), FAKE, FAKE, FAKE, 16, None)
     assert st == L.PARK_EWORKSPACE and "workspace too small" in msg
     # clusters out of range
-    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 0, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 0, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL and "n_clusters" in msg
-    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 1001, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 1001, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
-    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 4096, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 4096, 3, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
     # QRKC without a metric
-    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 1, None, 8, 3, 0, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 1, None, 8, 3, 0, 0, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL and "qmetric" in msg
     # bad init / side / iters
-    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 3, 5, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 3, 5, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
-    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 3, 0, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 3, 0, 0, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
-    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, -1, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, _ = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, -1, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
+    # the optional status word must be aligned
+    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 2, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, ODD, FAKE,
+                      1 << 40, None)
+    assert st == L.PARK_EINVAL and "status" in msg
     # labels required when iterating
-    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 2, 0, 0, 0, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None)
+    st, msg = _status(L, "park_cluster", bp(sh), FAKE, 0, None, 8, 2, 0, 0, 0, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL and "labels" in msg
     # top-p outside (0, 1]
     for p in (0.0, -0.1, 1.5, float("nan")):

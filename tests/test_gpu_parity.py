@@ -11,7 +11,7 @@ from gpu_helpers import (ATTN_MAX_ABS, ATTN_MEAN_ABS, LSE_ABS, MAP_ABS, SMALL, T
 
 pytestmark = pytest.mark.gpu
 
-WL = ["small", "small64", "tiny"]
+WL = ["small", "small64", "tiny", "small32"]
 
 
 def _bf(w):
@@ -336,3 +336,36 @@ def test_forward_free_running_vs_oracle_tiny():
     Od, _ = O.dense_attention(*(O.round_bf16(x) for x in (q, k, v)), w.scale)
     e = np.abs(to64(r1["out"][0]) - Od)
     assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS
+
+
+def test_seed_timeout_reaches_the_status_word():
+    """A cooperative seeding exchange that gives up must not pass as success: the device status word
+    carries PARK_DEVSTATUS_SEED_TIMEOUT. The failure is forced from the host (the launch starts with
+    its failure flag raised, so every bounded wait gives up at once and each kernel ends normally)."""
+    w = SMALL["small"]
+    Q, K, V = inputs(w)
+    M = bsa.park_qrkc_metric(Q)
+    bit = bsa.PARK_DEVSTATUS_SEED_TIMEOUT
+    ok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ref = bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, M, seed=3, side=bsa.PARK_SIDE_K, status=ok)
+    r_ok = bsa.park_forward(Q, K, V, w.cq, w.ck, 1, w.p, seed=3, outputs=("status",))
+    torch.cuda.synchronize()
+    assert int(ok.item()) == 0 and int(r_ok["status"].item()) == 0
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bsa.lib().park_debug_force_seed_timeout(1)
+    try:
+        bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, M, seed=3, side=bsa.PARK_SIDE_K, status=st)
+        r_bad = bsa.park_forward(Q, K, V, w.cq, w.ck, 1, w.p, seed=3, outputs=("status",))
+        torch.cuda.synchronize()
+    finally:
+        bsa.lib().park_debug_force_seed_timeout(0)
+    assert int(st.item()) & bit
+    assert int(r_bad["status"].item()) & bit
+    # the status word is or-ed into, never cleared: a later clean call leaves the bit set
+    bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, M, seed=3, side=bsa.PARK_SIDE_K, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & bit
+    # with the hook off again, a clean call is back to the reference result
+    again = bsa.park_cluster(K, w.ck, 1, bsa.PARK_QRKC, M, seed=3, side=bsa.PARK_SIDE_K)
+    torch.cuda.synchronize()
+    assert torch.equal(again["labels"], ref["labels"]) and torch.equal(again["centroids"], ref["centroids"])

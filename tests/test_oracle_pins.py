@@ -59,6 +59,19 @@ def test_round_bf16_matches_torch_rne():
     np.testing.assert_array_equal(O.round_bf16(x), want)
 
 
+def test_bf16_unit_roundoff_is_two_to_minus_eight():
+    """bf16 keeps 8 significant bits, so round-to-nearest errs by up to a relative 2^-8 (the bound the
+    attention's log-sum-exp tolerance is derived from): 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    and rounds to the even neighbour 1; just above it rounds up."""
+    x = 1.0 + 2.0 ** -8
+    assert O.round_bf16(x) == 1.0
+    assert abs(O.round_bf16(x) - x) / x == 2.0 ** -8 / (1.0 + 2.0 ** -8)
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    # no value is off by more than that
+    v = np.random.default_rng(4).uniform(0.5, 4.0, 200000)
+    assert (np.abs(O.round_bf16(v) - v) / v).max() <= 2.0 ** -8
+
+
 def test_round_f32_known_neighbours_and_ties():
     """Nearest float32, ties to even, on values worked out from the binary expansions."""
     # 0.1 lies between the float32 values 13421772 * 2^-27 and 13421773 * 2^-27 and is nearer
