@@ -18,7 +18,7 @@ __all__ = [
     "splitmix64_next", "splitmix64_first", "kpp_uniform",
     "round_f32", "round_bf16",
     "qrkc_metric", "metric_distance", "candidate_rows", "kmeanspp", "consumed_centroids",
-    "assign", "assign_near_tie", "cluster_order", "update", "lloyd", "cluster",
+    "assign", "assign_near_tie", "cluster_order", "update", "lloyd", "subset_rows", "lloyd_subset", "cluster",
     "pama", "select_topp", "topk_count", "select_topk", "key_runs", "sparse_attention", "dense_attention",
     "SIDE_SIP", "sip_uniform", "sip_probabilities", "select_sip", "weighted_sparse_attention",
     "recall", "density", "estimator_maps", "estimator_block_maps", "tv_to_full", "raw_key_mse", "qk_score_sq_error",
@@ -282,6 +282,36 @@ def lloyd(X, init, iters, metric=EUCLID, M=None, bf16=True, trace=None):
         if trace is not None:
             trace.append((labels, c))
     return labels, c
+
+
+def subset_rows(n: int, stride: int, phase: int):
+    """Tokens a subset update re-assigns: phase, phase + stride, phase + 2 stride, ... below n.
+
+    HyperVAttention page, abstract: between anchor steps only a subset of the tokens is updated.
+    Reading (the page does not say which subset): a strided one, so that successive steps with
+    phase = step mod stride cover every token once per stride steps, with the subset spread
+    evenly over the spatio-temporal grid.
+    """
+    return np.arange(phase, n, stride, dtype=np.int64)
+
+
+def lloyd_subset(X, init, labels, iters, stride, phase, metric=EUCLID, M=None, bf16=True):
+    """Subset update of a clustering (hybrid clustering between anchor steps, HyperVAttention page,
+    abstract): ``iters`` iterations, each re-assigning only the rows of ``subset_rows`` against the
+    consumed form of the current centroids (the other rows keep their labels, e.g. from the previous
+    denoising step), then setting every centroid to the mean of its members under the combined
+    labels, over the current values of all rows (empty clusters keep their centroid).
+    Returns (labels, centroids). stride = 1 is a full warm-started Lloyd iteration.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    lab = np.asarray(labels, dtype=np.int64).copy()
+    rows = subset_rows(X.shape[0], stride, phase)
+    c = round_f32(init)
+    for _ in range(iters):
+        g, b = consumed_centroids(c, metric, M, bf16)
+        lab[rows] = assign(X[rows], g, b)
+        c = update(X, lab, c.shape[0], c)
+    return lab.astype(np.int32), c
 
 
 def cluster(X, C, iters, metric=EUCLID, M=None, seed=0, head=0, side=SIDE_Q, bf16=True, init=None):

@@ -288,6 +288,49 @@ def test_lloyd_objective_non_increasing():
         assert all(b <= a * (1 + 1e-9) for a, b in zip(obj, obj[1:]))
 
 
+def test_subset_update_hand_worked():
+    c = _golden("subset_update_hand.json")
+    X, init = np.array(c["X"]), np.array(c["init"])
+    for case in c["cases"]:
+        lab, cent = O.lloyd_subset(X, init, np.array(c["labels"]), case["iters"], case["stride"], case["phase"],
+                                   bf16=False)
+        np.testing.assert_array_equal(lab, case["labels"])
+        np.testing.assert_allclose(cent, np.array(case["centroids"]), rtol=1e-7)  # centroids stored in fp32
+    np.testing.assert_array_equal(O.subset_rows(10, 4, 1), [1, 5, 9])
+    assert O.subset_rows(3, 4, 3).size == 0
+
+
+@pytest.mark.parametrize("metric", [O.EUCLID, O.QRKC])
+def test_subset_update_stride_one_is_lloyd_and_keeps_the_rest(metric):
+    rng = np.random.default_rng(29)
+    X, _ = _blobs(rng, 300, 6, 5, spread=1.0, scale=2.0)
+    M = O.qrkc_metric(rng.normal(size=(50, 6)) + 0.5) if metric == O.QRKC else None
+    init = X[rng.choice(300, 7, replace=False)]
+    prev, _ = O.lloyd(X, init, 2, metric, M, bf16=True)
+    # stride 1: every row is re-assigned, i.e. plain warm-started Lloyd iterations
+    l1, c1 = O.lloyd_subset(X, init, prev, 3, 1, 0, metric, M, bf16=True)
+    l2, c2 = O.lloyd(X, init, 3, metric, M, bf16=True)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(c1, c2)
+    # stride 4: rows off the subset keep their labels, rows on it take the fp64 argmin, the
+    # centroids are the member means, and the objective does not increase
+    scrambled = rng.integers(0, 7, 300).astype(np.int32)
+    c0 = O.update(X, scrambled, 7, O.round_f32(init))
+    lab, cent = O.lloyd_subset(X, c0, scrambled, 1, 4, 3, metric, M, bf16=True)
+    off = np.setdiff1d(np.arange(300), np.arange(3, 300, 4))
+    np.testing.assert_array_equal(lab[off], scrambled[off])
+    g, b = O.consumed_centroids(c0, metric, M, bf16=True)
+    np.testing.assert_array_equal(lab[3::4], O.assign(X[3::4], g, b))
+    np.testing.assert_array_equal(cent, O.update(X, lab, 7, c0))
+
+    # without the bf16 rounding of the consumed centroids the re-assignment is exact, so the
+    # objective cannot increase (the Lloyd argument, restricted to the re-assigned rows)
+    def objective(lb, cc):
+        return sum(O.metric_distance(X[lb == j], cc[j], M).sum() for j in range(7))
+    lab32, cent32 = O.lloyd_subset(X, c0, scrambled, 2, 4, 3, metric, M, bf16=False)
+    assert objective(lab32, cent32) <= objective(scrambled, c0) * (1 + 1e-12)
+
+
 def test_update_keeps_empty_clusters():
     X = np.array([[1.0, 2.0], [3.0, 4.0]])
     prev = np.array([[9.0, 9.0], [0.0, 0.0], [5.0, -5.0]])
