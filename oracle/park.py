@@ -19,7 +19,7 @@ __all__ = [
     "round_f32", "round_bf16",
     "qrkc_metric", "metric_distance", "candidate_rows", "kmeanspp", "consumed_centroids",
     "assign", "assign_near_tie", "cluster_order", "update", "lloyd", "subset_rows", "lloyd_subset", "cluster",
-    "pama", "select_topp", "topk_count", "select_topk", "key_runs", "sparse_attention", "dense_attention",
+    "pama", "select_topp", "topk_count", "select_topk", "merge_cost", "merge_clusters", "merged_order", "key_runs", "sparse_attention", "dense_attention",
     "SIDE_SIP", "sip_uniform", "sip_probabilities", "select_sip", "weighted_sparse_attention",
     "recall", "density", "estimator_maps", "estimator_block_maps", "tv_to_full", "raw_key_mse", "qk_score_sq_error",
     "centered_log_mass_error", "retrieve", "forward",
@@ -510,6 +510,88 @@ def select_sip(A, k_sizes, rho, seed=0, head=0):
     cols = [np.flatnonzero(mask[i]).astype(np.int32) for i in range(cq)]
     keys = (mask * k_sizes[None, :]).sum(axis=1).astype(np.int64)
     return mask, counts, cols, keys, log_w, pi
+
+
+def merge_cost(n_q, keys, bm: int):
+    """CTA-aligned cost of a query group (HyperVAttention page, abstract: clusters are processed in
+    fixed-size tiles, so a group of n_q queries occupies ceil(n_q / bm) tiles, each running over
+    every selected key): ceil(n_q / bm) * keys."""
+    return -(-int(n_q) // bm) * int(keys)
+
+
+def merge_clusters(q_sizes, cols, k_sizes, bm: int):
+    """Tile-aware merging of query clusters by parallel agglomeration (HyperVAttention page,
+    abstract: merging that lowers the CTA-aligned execution cost fills idle tile capacity and
+    makes every merged query attend to the union of the selections).
+
+    Reading (the page gives the idea only): groups start as the non-empty query clusters (empty ones
+    stay alone and select nothing). A group G has n(G) queries, selection S(G) = union of its
+    clusters' selections and cost merge_cost(n(G), L(S(G)), bm), L = total size of the key clusters.
+    Each round every group proposes the partner with the largest positive gain
+    cost(a) + cost(b) - cost(a u b) (ties to the lower index); pairs that propose each other merge
+    into the lower index. The gain is symmetric, so the pair of largest gain always proposes itself
+    and every round with a positive gain merges; the rounds stop when no pair gains.
+    Returns (group, sel): group[i] = the lowest cluster index of i's group, sel[r] = the sorted
+    union selection of the group with root r.
+    """
+    q_sizes = np.asarray(q_sizes, dtype=np.int64)
+    k_sizes = np.asarray(k_sizes, dtype=np.int64)
+    cq = q_sizes.size
+    parent = np.arange(cq)
+    n = {i: int(q_sizes[i]) for i in range(cq) if q_sizes[i] > 0}
+    S = {i: set(int(j) for j in cols[i]) for i in n}
+
+    def L(sel):
+        return int(sum(k_sizes[j] for j in sel))
+
+    def cost(i):
+        return merge_cost(n[i], L(S[i]), bm)
+
+    while True:
+        roots = sorted(n)
+        best = {}
+        for a in roots:
+            ba, bg = -1, 0
+            for b in roots:
+                if b == a:
+                    continue
+                g = cost(a) + cost(b) - merge_cost(n[a] + n[b], L(S[a] | S[b]), bm)
+                if g > bg:
+                    ba, bg = b, g
+            best[a] = ba
+        pairs = [(a, b) for a, b in best.items() if b > a and best.get(b) == a]
+        if not pairs:
+            break
+        for a, b in pairs:
+            n[a] += n.pop(b)
+            S[a] |= S.pop(b)
+            parent[parent == b] = a
+    group = parent.copy()
+    sel = {r: np.array(sorted(S.get(r, set())), dtype=np.int64) for r in set(group.tolist())}
+    for i in range(cq):
+        if q_sizes[i] == 0:
+            sel[i] = np.array([], dtype=np.int64)
+    return group, sel
+
+
+def merged_order(q_perm, q_offsets, group, sel):
+    """The merged groups as a query clustering: groups in increasing order of their lowest cluster,
+    each group's queries cluster by cluster in increasing cluster order (each cluster's queries in
+    their q_perm order). Returns (perm, offsets, cols) with cq slots: slot g < G holds the g-th
+    group, slots G .. cq - 1 are empty."""
+    q_perm = np.asarray(q_perm)
+    q_offsets = np.asarray(q_offsets)
+    cq = q_offsets.size - 1
+    roots = sorted(set(np.asarray(group).tolist()))
+    perm, offsets, cols = [], [0], [np.array([], dtype=np.int64) for _ in range(cq)]
+    for g, r in enumerate(roots):
+        for i in range(cq):
+            if group[i] == r:
+                perm.extend(q_perm[q_offsets[i]:q_offsets[i + 1]].tolist())
+        offsets.append(len(perm))
+        cols[g] = sel[r]
+    offsets += [len(perm)] * (cq + 1 - len(offsets))
+    return np.array(perm, dtype=np.int32), np.array(offsets, dtype=np.int32), cols
 
 
 def key_runs(cols, k_offsets):

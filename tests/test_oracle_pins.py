@@ -735,6 +735,70 @@ def test_full_full_topp_recall_reaches_p():
             np.testing.assert_allclose(A_fc[i], est["FC"][t].mean(0), atol=1e-13)
 
 
+def test_merge_clusters_hand_worked():
+    for c in _golden("merge_hand.json")["cases"]:
+        group, sel = O.merge_clusters(c["q_sizes"], c["cols"], c["k_sizes"], c["bm"])
+        np.testing.assert_array_equal(group, c["group"])
+        assert {str(r): v.tolist() for r, v in sel.items()} == c["sel"]
+
+
+def _merge_case(rng, cq=40, ck=60):
+    q_sizes = rng.integers(0, 700, cq) * (rng.random(cq) < 0.9)
+    k_sizes = rng.integers(0, 300, ck)
+    cols = [np.sort(rng.choice(ck, size=int(rng.integers(0, ck // 2)), replace=False)) for _ in range(cq)]
+    return q_sizes, k_sizes, cols
+
+
+@pytest.mark.parametrize("bm", [1, 32, 384])
+def test_merge_clusters_invariants(bm):
+    """Every cluster lands in exactly one group under its lowest member; a group selects the union
+    of its members' selections; the total cost does not increase; no two final groups gain by
+    merging; with bm = 1 no merge can gain (n_a L_a + n_b L_b <= (n_a + n_b) L(union))."""
+    rng = np.random.default_rng(bm)
+    for _ in range(3):
+        q_sizes, k_sizes, cols = _merge_case(rng)
+        group, sel = O.merge_clusters(q_sizes, cols, k_sizes, bm)
+        L = lambda s: int(k_sizes[np.asarray(list(s), dtype=np.int64)].sum()) if len(s) else 0
+        roots = sorted(set(group.tolist()))
+        assert all(group[r] == r and np.all(np.flatnonzero(group == r) >= r) for r in roots)
+        total0 = sum(O.merge_cost(q_sizes[i], L(cols[i]), bm) for i in range(len(q_sizes)) if q_sizes[i] > 0)
+        total = 0
+        for r in roots:
+            members = np.flatnonzero(group == r)
+            union = set().union(*(set(cols[i].tolist()) for i in members)) if q_sizes[r] > 0 else set()
+            assert sel[r].tolist() == sorted(union)
+            total += O.merge_cost(q_sizes[members].sum(), L(union), bm)
+        assert total <= total0
+        if bm == 1:
+            assert len(roots) == len(q_sizes)
+        live = [r for r in roots if q_sizes[r] > 0]
+        for a in live:
+            for b in live:
+                if a < b:
+                    na, nb = q_sizes[group == a].sum(), q_sizes[group == b].sum()
+                    g = (O.merge_cost(na, L(sel[a]), bm) + O.merge_cost(nb, L(sel[b]), bm)
+                         - O.merge_cost(na + nb, L(set(sel[a].tolist()) | set(sel[b].tolist())), bm))
+                    assert g <= 0, (a, b, g)
+
+
+def test_merged_order_is_a_clustering():
+    rng = np.random.default_rng(5)
+    q_sizes, k_sizes, cols = _merge_case(rng)
+    labels = np.repeat(np.arange(q_sizes.size), q_sizes)
+    rng.shuffle(labels)
+    q_perm, q_off = O.cluster_order(labels, q_sizes.size)
+    group, sel = O.merge_clusters(q_sizes, cols, k_sizes, 384)
+    perm, off, mcols = O.merged_order(q_perm, q_off, group, sel)
+    np.testing.assert_array_equal(np.sort(perm), np.arange(labels.size))
+    roots = sorted(set(group.tolist()))
+    assert off[-1] == labels.size and np.all(np.diff(off) >= 0) and np.all(np.diff(off)[len(roots):] == 0)
+    for g, r in enumerate(roots):
+        members = np.flatnonzero(group == r)
+        np.testing.assert_array_equal(perm[off[g]:off[g + 1]],
+                                      np.concatenate([q_perm[q_off[i]:q_off[i + 1]] for i in members]))
+        np.testing.assert_array_equal(mcols[g], sel[r])
+
+
 def test_key_runs_merge_adjacent_clusters():
     off = np.array([0, 3, 3, 7, 9, 12])
     assert O.key_runs([0, 1, 2], off) == [(0, 7)]
