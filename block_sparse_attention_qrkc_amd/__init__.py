@@ -16,7 +16,7 @@ import ctypes
 import torch
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PARK_BF16, PARK_EHIP, PARK_EINVAL, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_CLUSTER_Q,
+    EXPORTED, LIB_PATH, PARK_ENTRY_MERGE, PARK_INIT_SUBSET, STATS_FIELDS, PARK_BF16, PARK_EHIP, PARK_EINVAL, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_CLUSTER_Q,
     PARK_ENTRY_ESTIMATOR, PARK_ENTRY_FORWARD, PARK_ENTRY_METRIC, PARK_ENTRY_RETRIEVE_MAP, PARK_ENTRY_SELECT_TOPP,
     PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_SPARSE_ATTN_WEIGHTED, PARK_EST_CC, PARK_EST_CF, PARK_EST_FC, PARK_EST_FF,
     PARK_EUCLID, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_F32, PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_OK,
@@ -26,8 +26,8 @@ from ._lib import (  # noqa: F401
 from ._lib import _check, _ptr, _stream, _ws
 
 __all__ = [
-    "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
-    "park_select_topk", "park_sparse_attn",
+    "park_qrkc_metric", "park_cluster", "park_cluster_subset", "park_retrieve_map", "park_estimator_map", "park_select_topp",
+    "park_select_topk", "park_sparse_attn", "park_merge_clusters",
     "park_permute_rows", "park_unpermute_rows", "park_forward", "park_version", "ParkError", "lib",
 ]
 
@@ -68,6 +68,25 @@ def park_cluster(x, n_clusters, iters, metric=PARK_EUCLID, qmetric=None, init=PA
     _check(lib().park_cluster(ctypes.byref(sh), _ptr(x), int(metric), _ptr(qmetric), int(n_clusters), int(iters),
                               int(init), int(seed) & ((1 << 64) - 1), int(side), _ptr(centroids), _ptr(labels),
                               _ptr(perm), _ptr(offsets), _ptr(status), wp, wn, _stream(stream)))
+    return {"centroids": centroids, "labels": labels, "perm": perm, "offsets": offsets}
+
+
+def park_cluster_subset(x, n_clusters, iters, stride, phase, centroids, labels, metric=PARK_EUCLID, qmetric=None,
+                        ws=None, stream=None):
+    """Subset update between anchor steps: re-assign the tokens phase, phase + stride, ... and update
+    the centroids over all tokens. ``centroids`` [heads, C, d] float32 and ``labels`` [heads, n] int32
+    hold the previous step's state and are updated in place. Returns dict(centroids, labels, perm,
+    offsets)."""
+    sh = make_shape(x)
+    H, N = sh.heads, sh.n
+    perm = torch.empty(H, N, dtype=torch.int32, device=x.device)
+    offsets = torch.empty(H, n_clusters + 1, dtype=torch.int32, device=x.device)
+    prm = make_params(cq=n_clusters, ck=n_clusters, kmetric=metric)
+    entry = PARK_ENTRY_CLUSTER_K if metric == PARK_QRKC else PARK_ENTRY_CLUSTER_Q
+    wp, wn = _ws(entry, sh, prm, x.device, ws)
+    _check(lib().park_cluster_subset(ctypes.byref(sh), _ptr(x), int(metric), _ptr(qmetric), int(n_clusters),
+                                     int(iters), int(stride), int(phase), _ptr(centroids), _ptr(labels), _ptr(perm),
+                                     _ptr(offsets), wp, wn, _stream(stream)))
     return {"centroids": centroids, "labels": labels, "perm": perm, "offsets": offsets}
 
 
@@ -184,6 +203,28 @@ def park_sparse_attn_weighted(q, k, v, q_perm, q_offsets, k_perm, k_offsets, cou
     return o, L
 
 
+def park_merge_clusters(q_perm, q_offsets, k_offsets, counts, cols, bm=384, ws=None, stream=None):
+    """Tile-aware merging of the query clusters (CTA-aligned cost with bm-query tiles). Returns
+    dict(group, q_perm, q_offsets, counts, cols): the merged groups as a query clustering with the
+    same number of slots, ready for park_sparse_attn."""
+    H, N = q_perm.shape
+    cq = q_offsets.shape[1] - 1
+    ck = k_offsets.shape[1] - 1
+    dev = q_perm.device
+    group = torch.empty(H, cq, dtype=torch.int32, device=dev)
+    m_perm = torch.empty(H, N, dtype=torch.int32, device=dev)
+    m_off = torch.empty(H, cq + 1, dtype=torch.int32, device=dev)
+    m_cnt = torch.empty(H, cq, dtype=torch.int32, device=dev)
+    m_cols = torch.zeros(H, cq, ck, dtype=torch.int32, device=dev)
+    sh = park_shape(H, N, 128, PARK_BF16)
+    prm = make_params(cq=cq, ck=ck)
+    wp, wn = _ws(PARK_ENTRY_MERGE, sh, prm, dev, ws)
+    _check(lib().park_merge_clusters(H, N, cq, ck, int(bm), _ptr(q_perm), _ptr(q_offsets), _ptr(k_offsets),
+                                     _ptr(counts), _ptr(cols), _ptr(group), _ptr(m_perm), _ptr(m_off), _ptr(m_cnt),
+                                     _ptr(m_cols), wp, wn, _stream(stream)))
+    return {"group": group, "q_perm": m_perm, "q_offsets": m_off, "counts": m_cnt, "cols": m_cols}
+
+
 def park_permute_rows(x, perm, out=None, stream=None):
     """out[h, p] = x[h, perm[h, p]]."""
     sh = make_shape(x)
@@ -215,13 +256,18 @@ _FWD_FIELDS = {
     "sel_keys": lambda H, N, D, cq, ck: ((H, cq), torch.int64),
     "lse": lambda H, N, D, cq, ck: ((H, N), torch.float32),
     "status": lambda H, N, D, cq, ck: ((1,), torch.int32),
+    "stats": lambda H, N, D, cq, ck: ((8,), torch.int64),
 }
 
 
 def park_forward(q, k, v, cq, ck, iters, p, scale=0.0, seed=0, kmetric=PARK_QRKC, init=PARK_INIT_KMEANSPP,
-                 q_centroids=None, k_centroids=None, outputs=(), out=None, ws=None, stream=None):
+                 q_centroids=None, k_centroids=None, outputs=(), out=None, ws=None, stream=None, subset=(1, 0),
+                 q_labels=None, k_labels=None):
     """The whole path for one layer. ``outputs`` names intermediates to return (see
-    park_forward_outputs); q_centroids / k_centroids are caller state for warm starts."""
+    park_forward_outputs); q_centroids / k_centroids are caller state for warm starts. With
+    ``init=PARK_INIT_SUBSET``, ``subset`` = (stride, phase) and ``q_labels`` / ``k_labels`` (the
+    previous step's labels, updated in place) are required. ``"stats"`` in ``outputs`` returns the
+    park_stats totals as an int64 tensor (fields STATS_FIELDS)."""
     sh = make_shape(q)
     H, N, D = sh.heads, sh.n, sh.d
     dev = q.device
@@ -232,12 +278,19 @@ def park_forward(q, k, v, cq, ck, iters, p, scale=0.0, seed=0, kmetric=PARK_QRKC
     o = out if out is not None else torch.empty_like(q)
     res = {}
     fo = park_forward_outputs()
+    given = {"q_labels": q_labels, "k_labels": k_labels}
+    for name, t in given.items():
+        if t is not None:
+            res[name] = t
+            setattr(fo, name, t.data_ptr())
     for name in outputs:
+        if given.get(name) is not None:
+            continue
         shp, dt = _FWD_FIELDS[name](H, N, D, cq, ck)
         t = torch.zeros(shp, dtype=dt, device=dev) if name == "status" else torch.empty(shp, dtype=dt, device=dev)
         res[name] = t
         setattr(fo, name, t.data_ptr())
-    prm = make_params(cq, ck, iters, p, scale, seed, kmetric, init)
+    prm = make_params(cq, ck, iters, p, scale, seed, kmetric, init, subset[0], subset[1])
     wp, wn = _ws(PARK_ENTRY_FORWARD, sh, prm, dev, ws)
     _check(lib().park_forward(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(o), ctypes.byref(prm),
                               _ptr(q_centroids), _ptr(k_centroids), ctypes.byref(fo), wp, wn, _stream(stream)))

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libpark.so")
 PARK_OK, PARK_EINVAL, PARK_EUNSUPPORTED, PARK_EWORKSPACE, PARK_EHIP = range(5)
 PARK_F32, PARK_BF16 = 0, 1
 PARK_EUCLID, PARK_QRKC = 0, 1
-PARK_INIT_KMEANSPP, PARK_INIT_WARM = 0, 1
+PARK_INIT_KMEANSPP, PARK_INIT_WARM, PARK_INIT_SUBSET = 0, 1, 2
 PARK_SIDE_Q, PARK_SIDE_K = 0, 1
 PARK_EST_FC, PARK_EST_CC, PARK_EST_CF, PARK_EST_FF = range(4)
 (PARK_ENTRY_METRIC, PARK_ENTRY_CLUSTER_Q, PARK_ENTRY_CLUSTER_K, PARK_ENTRY_RETRIEVE_MAP,
  PARK_ENTRY_SELECT_TOPP, PARK_ENTRY_SPARSE_ATTN, PARK_ENTRY_FORWARD, PARK_ENTRY_ESTIMATOR,
- PARK_ENTRY_SPARSE_ATTN_WEIGHTED) = range(9)
+ PARK_ENTRY_SPARSE_ATTN_WEIGHTED, PARK_ENTRY_MERGE) = range(10)
 PARK_DEVSTATUS_SEED_TIMEOUT = 1
 
 EXPORTED = [
@@ -31,6 +31,7 @@ EXPORTED = [
     "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
     "park_select_topk", "park_select_sip", "park_sparse_attn", "park_sparse_attn_weighted",
     "park_permute_rows", "park_unpermute_rows", "park_forward", "park_debug_force_seed_timeout",
+    "park_cluster_subset", "park_merge_clusters",
 ]
 
 
@@ -51,7 +52,15 @@ class park_shape(ctypes.Structure):
 class park_params(ctypes.Structure):
     _fields_ = [("cq", ctypes.c_int32), ("ck", ctypes.c_int32), ("iters", ctypes.c_int32), ("p", ctypes.c_double),
                 ("scale", ctypes.c_float), ("seed", ctypes.c_uint64), ("kmetric", ctypes.c_int32),
-                ("init", ctypes.c_int32)]
+                ("init", ctypes.c_int32), ("subset_stride", ctypes.c_int32), ("subset_phase", ctypes.c_int32)]
+
+
+class park_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("pairs", "padded_pairs", "blocks", "live_blocks", "work_items",
+                                              "tokens", "reserved0", "reserved1")]
+
+
+STATS_FIELDS = ("pairs", "padded_pairs", "blocks", "live_blocks", "work_items", "tokens")
 
 
 _P = ctypes.c_void_p
@@ -60,7 +69,7 @@ _P = ctypes.c_void_p
 class park_forward_outputs(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("metric", "q_labels", "q_perm", "q_offsets", "k_labels", "k_perm", "k_offsets",
                                   "map", "mask", "counts", "cols", "sel_keys", "lse",
-                                  "status")]
+                                  "status", "stats")]
 
 
 _lib = None
@@ -88,6 +97,9 @@ def lib() -> ctypes.CDLL:
             "park_qrkc_metric": (i32, [SP, _P, _P, _P, sz, _P]),
             "park_cluster": (i32, [SP, _P, i32, _P, i32, i32, i32, u64, i32, _P, _P, _P, _P, _P, _P, sz, _P]),
             "park_debug_force_seed_timeout": (None, [i32]),
+            "park_cluster_subset": (i32, [SP, _P, i32, _P, i32, i32, i32, i32, _P, _P, _P, _P, _P, sz, _P]),
+            "park_merge_clusters": (i32, [i64, i64, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz,
+                                          _P]),
             "park_retrieve_map": (i32, [SP, _P, _P, _P, i32, _P, _P, i32, f32, _P, _P, sz, _P]),
             "park_estimator_map": (i32, [SP, _P, _P, _P, _P, i32, _P, _P, _P, i32, _P, i32, f32, _P, _P, sz, _P]),
             "park_select_topp": (i32, [_P, i64, i32, i32, _P, f64, _P, _P, _P, _P, _P]),
@@ -136,9 +148,10 @@ def make_shape(x: torch.Tensor) -> park_shape:
     return park_shape(x.shape[0], x.shape[1], x.shape[2], dt)
 
 
-def make_params(cq=1, ck=1, iters=1, p=0.9, scale=0.0, seed=0, kmetric=PARK_QRKC, init=PARK_INIT_KMEANSPP):
+def make_params(cq=1, ck=1, iters=1, p=0.9, scale=0.0, seed=0, kmetric=PARK_QRKC, init=PARK_INIT_KMEANSPP,
+                subset_stride=1, subset_phase=0):
     return park_params(int(cq), int(ck), int(iters), float(p), float(scale), int(seed) & ((1 << 64) - 1),
-                       int(kmetric), int(init))
+                       int(kmetric), int(init), int(subset_stride), int(subset_phase))
 
 
 class Workspace:

@@ -18,7 +18,8 @@ OUT = os.path.join(HERE, "libpark.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["metric.hip", "kmeans.hip", "pama.hip", "select.hip", "attn.hip", "permute.hip", "park_api.hip"]
+SOURCES = ["metric.hip", "kmeans.hip", "pama.hip", "select.hip", "attn.hip", "merge.hip", "permute.hip",
+           "park_api.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -74,19 +74,25 @@ __global__ __launch_bounds__(1024) void attn_order(const int32_t* __restrict__ q
   if (tid == 0) tb[cq] = total;
 }
 
-// Per (query cluster, head): the original key rows of the selected key clusters, concatenated in
-// selection order: gather[(h * cq + i) * N + v] for v < glen[h * cq + i]. Column entries outside
-// [0, ck) or with offsets outside [0, N] contribute nothing; the list is cut at N keys.
-__global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ counts,
-                                                   const int32_t* __restrict__ cols,
-                                                   const int32_t* __restrict__ k_offsets,
-                                                   const int32_t* __restrict__ k_perm, int64_t N, int cq, int ck,
-                                                   const float* __restrict__ log_w, float inv_scale,
-                                                   int32_t* __restrict__ gather, int32_t* __restrict__ glen,
-                                                   float* __restrict__ gbias) {
+// Per (query cluster i, head h): the keys of the selected key clusters, in selection order, form the
+// cluster's virtual key sequence. Key cluster j occupies the k_perm positions ko[j] .. ko[j+1]-1, so
+// the sequence is a list of runs of consecutive k_perm positions: consecutive selected clusters
+// whose ranges touch (every cluster between them empty) share one run. Virtual key v of run r
+// (rv[r] <= v < rv[r+1]) is the key at k_perm position v + rd[r]. Per (h, i) the region of
+// run_stride(ck) ints holds rv[0 .. R] (rv[R] = the sequence length), rd[0 .. R-1] and, for the
+// weighted form, rb[0 .. R-1] = the run's logit offset in raw-score units (runs then stay one per
+// cluster, since clusters carry their own weights). Column entries outside [0, ck) or with offsets
+// outside [0, N] contribute nothing; the sequence is cut at N keys (reached only when a cluster is
+// listed twice).
+__host__ __device__ constexpr int64_t run_stride(int ck) { return ((3 * (int64_t)ck + 1) + 3) & ~int64_t(3); }
+
+__global__ __launch_bounds__(256) void attn_runs(const int32_t* __restrict__ counts, const int32_t* __restrict__ cols,
+                                                 const int32_t* __restrict__ k_offsets, int64_t N, int cq, int ck,
+                                                 const float* __restrict__ log_w, float inv_scale,
+                                                 int32_t* __restrict__ runs, int32_t* __restrict__ nrun,
+                                                 int32_t* __restrict__ glen, int32_t* __restrict__ nblk) {
   __shared__ int scratch[17];
-  __shared__ int c_start[256], c_len[256], c_dst[256];
-  __shared__ float c_bias[256];
+  __shared__ int last_hi[4];  // per wave: end position of its last non-empty entry, -1 if none
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -96,72 +102,116 @@ __global__ __launch_bounds__(256) void attn_gather(const int32_t* __restrict__ c
   cnt = cnt < 0 ? 0 : (cnt > ck ? ck : cnt);
   const int32_t* crow = cols + ((int64_t)h * cq + i) * ck;
   const int32_t* ko = k_offsets + (int64_t)h * (ck + 1);
-  const int32_t* kp = k_perm + (int64_t)h * N;
-  int32_t* dst = gather + ((int64_t)h * cq + i) * N;
-  float* bdst = log_w ? gbias + ((int64_t)h * cq + i) * N : nullptr;
   const float* lwrow = log_w ? log_w + ((int64_t)h * cq + i) * ck : nullptr;
-  int64_t base = 0;
+  int32_t* rv = runs + ((int64_t)h * cq + i) * run_stride(ck);
+  int32_t* rd = rv + ck + 1;
+  float* rb = reinterpret_cast<float*>(rv + 2 * ck + 1);
+  int64_t base = 0;  // keys of the entries before this chunk
+  int R = 0;         // runs started before this chunk
+  int kept = 0;      // runs that start before N
+  int carry = -1;    // end position of the last non-empty entry before this chunk
+  int blocks = 0;    // selected non-empty key clusters
   for (int m0 = 0; m0 < cnt; m0 += 256) {
     const int m = m0 + tid;
-    int a = 0, len = 0;
+    int lo = 0, len = 0;
     float bias = 0.f;
     if (m < cnt) {
       const int j = crow[m];
       if (j >= 0 && j < ck) {
-        const int64_t lo = ko[j], hi = ko[j + 1];
-        if (lo >= 0 && hi > lo && hi <= N) {
-          a = (int)lo;
-          len = (int)(hi - lo);
+        const int64_t a = ko[j], b = ko[j + 1];
+        if (a >= 0 && b > a && b <= N) {
+          lo = (int)a;
+          len = (int)(b - a);
         }
         if (lwrow) bias = lwrow[j] * inv_scale;
       }
     }
-    int tot;
-    const int pre = block_exclusive_scan(len, scratch, &tot);
-    c_start[tid] = a;
-    c_len[tid] = len;
-    c_dst[tid] = (int)min<int64_t>(base + pre, N);
-    c_bias[tid] = bias;
+    const bool ne = len > 0;
+    // end position of the previous non-empty entry: within the wave from the nearest lower lane,
+    // else from the waves before, else from the chunks before
+    const uint64_t bal = __ballot(ne);
+    const uint64_t below = bal & ((1ull << l) - 1ull);
+    const int src = below ? 63 - __clzll((unsigned long long)below) : 0;
+    const int hi_below = __shfl(lo + len, src, kWave);
+    const int hi_last = __shfl(lo + len, bal ? 63 - __clzll((unsigned long long)bal) : 0, kWave);
+    if (l == 0) last_hi[w] = bal ? hi_last : -1;
     __syncthreads();
-    // each wave copies two clusters at a time, four 64-key rows of each in flight
-    const int nloc = min(256, cnt - m0);
-    for (int e0 = w; e0 < nloc; e0 += 8) {
-      int s0[2], d0[2], ln[2];
-      float cb[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int e = e0 + 4 * x;
-        s0[x] = e < nloc ? c_start[e] : 0;
-        d0[x] = e < nloc ? c_dst[e] : 0;
-        ln[x] = e < nloc ? (int)min<int64_t>(c_len[e], N - d0[x]) : 0;
-        cb[x] = e < nloc ? c_bias[e] : 0.f;
-      }
-      const int lmax = max(ln[0], ln[1]);
-      for (int u0 = 0; u0 < lmax; u0 += 4 * kWave) {
-        int v[2][4];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int u = u0 + k * kWave + l;
-            v[x][k] = kp[s0[x] + min(u, max(ln[x] - 1, 0))];  // clamped: every load is issued
-          }
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int u = u0 + k * kWave + l;
-            if (u < ln[x]) {
-              dst[d0[x] + u] = v[x][k];
-              if (bdst) bdst[d0[x] + u] = cb[x];
-            }
-          }
-      }
+    int prev = carry;
+    for (int q = 0; q < w; ++q) prev = last_hi[q] >= 0 ? last_hi[q] : prev;
+    if (below) prev = hi_below;
+    int chunk_last = carry;
+    for (int q = 0; q < 4; ++q) chunk_last = last_hi[q] >= 0 ? last_hi[q] : chunk_last;
+    const bool start = ne && (lwrow != nullptr || prev != lo);
+    int tot_len, tot_start;
+    const int pre_len = block_exclusive_scan(len, scratch, &tot_len);
+    const int pre_start = block_exclusive_scan(start ? 1 : 0, scratch, &tot_start);
+    const int64_t v0 = base + pre_len;
+    const bool write = start && v0 < N;
+    if (write) {
+      const int r = R + pre_start;
+      rv[r] = (int)v0;
+      rd[r] = lo - (int)v0;
+      if (lwrow) rb[r] = bias;
     }
-    base += tot;
-    __syncthreads();
+    kept += __syncthreads_count(write);
+    blocks += __syncthreads_count(ne);
+    base += tot_len;
+    R += tot_start;
+    carry = chunk_last;
   }
-  if (tid == 0) glen[(int64_t)h * cq + i] = (int)min<int64_t>(base, N);
+  if (tid == 0) {
+    const int L = (int)min<int64_t>(base, N);
+    rv[kept] = L;
+    nrun[(int64_t)h * cq + i] = kept;
+    glen[(int64_t)h * cq + i] = L;
+    nblk[(int64_t)h * cq + i] = blocks;
+  }
+}
+
+// Totals of the selection over all heads (park_stats): one work-group strides over the
+// (head, query cluster) pairs and the heads' key clusters; bn = keys per tile of the kernel.
+__global__ __launch_bounds__(1024) void attn_stats(const int32_t* __restrict__ q_offsets,
+                                                   const int32_t* __restrict__ k_offsets, int64_t H, int64_t N,
+                                                   int cq, int ck, const int32_t* __restrict__ glen,
+                                                   const int32_t* __restrict__ nblk,
+                                                   const int32_t* __restrict__ tile_base, int bn,
+                                                   int64_t* __restrict__ stats) {
+  __shared__ int64_t red[6][16];
+  int64_t acc[6] = {0, 0, 0, 0, 0, 0};  // pairs, padded, blocks, live q clusters x live k clusters, items
+  for (int64_t e = threadIdx.x; e < H * cq; e += 1024) {
+    const int64_t h = e / cq;
+    const int i = (int)(e % cq);
+    const int64_t nq = q_offsets[h * (cq + 1) + i + 1] - q_offsets[h * (cq + 1) + i];
+    const int64_t L = glen[e];
+    acc[0] += nq * L;
+    acc[1] += ((nq + 31) / 32) * 32 * ((L + bn - 1) / bn) * bn;
+    acc[2] += nq > 0 ? nblk[e] : 0;
+  }
+  for (int64_t h = threadIdx.x; h < H; h += 1024) {
+    int64_t lq = 0, lk = 0;
+    for (int i = 0; i < cq; ++i) lq += q_offsets[h * (cq + 1) + i + 1] > q_offsets[h * (cq + 1) + i];
+    for (int j = 0; j < ck; ++j) lk += k_offsets[h * (ck + 1) + j + 1] > k_offsets[h * (ck + 1) + j];
+    acc[3] += lq * lk;
+    acc[4] += tile_base[h * (2 * cq + 1) + cq];
+  }
+  const int l = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    int64_t v = acc[q];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    if (l == 0) red[q][w] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 5) {
+    int64_t v = 0;
+    for (int q = 0; q < 16; ++q) v += red[threadIdx.x][q];
+    stats[threadIdx.x] = v;
+  } else if (threadIdx.x == 5) {
+    stats[5] = H * N;
+  } else if (threadIdx.x < 8) {
+    stats[threadIdx.x] = 0;
+  }
 }
 
 __device__ __forceinline__ int find_tile(const int32_t* tb, int cq, int c) {
@@ -199,10 +249,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ q_perm,
                                                           const int32_t* __restrict__ q_off, int cq,
                                                           const int32_t* __restrict__ tile_base,
-                                                          const int32_t* __restrict__ gather,
-                                                          const int32_t* __restrict__ glen,
-                                                          const float* __restrict__ gbias, float scale,
-                                                          T* __restrict__ out, float* __restrict__ lse) {
+                                                          const int32_t* __restrict__ k_perm, int ck,
+                                                          const int32_t* __restrict__ runs,
+                                                          const int32_t* __restrict__ glen, int weighted,
+                                                          float scale, T* __restrict__ out,
+                                                          float* __restrict__ lse) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int KSTR = D + 8;
@@ -225,9 +276,12 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
   const int qbeg = qo[i] + (c - tb[ti]) * kAttnBM;
   const int qend = min(qbeg + kAttnBM, qo[i + 1]);
-  const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
-  const float* brow = gbias ? gbias + ((int64_t)h * cq + i) * N : nullptr;
+  const int32_t* rv = runs + ((int64_t)h * cq + i) * run_stride(ck);
+  const int32_t* rd = rv + ck + 1;
+  const float* brow = weighted ? reinterpret_cast<const float*>(rv + 2 * ck + 1) : nullptr;
+  const int32_t* kp = k_perm + (int64_t)h * N;
   const int L = glen[(int64_t)h * cq + i];
+  int cr = 0;  // run of this thread's key (threads < kBN; keys advance by kBN per tile)
   const T* Qh = Q + (int64_t)h * N * D;
   const T* Kh = K + (int64_t)h * N * D;
   const T* Vh = V + (int64_t)h * N * D;
@@ -258,8 +312,15 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   for (int v0 = 0; v0 < L; v0 += kBN) {
     if (tid < kBN) {
       const int v = v0 + tid;
-      krow[tid] = v < L ? rows[v] : -1;
-      kbias[tid] = (brow && v < L) ? brow[v] : 0.f;
+      int row = -1;
+      float bias = 0.f;
+      if (v < L) {
+        while (rv[cr + 1] <= v) ++cr;
+        row = kp[v + rd[cr]];
+        if (brow) bias = brow[cr];
+      }
+      krow[tid] = row;
+      kbias[tid] = bias;
     }
     __syncthreads();
     // K tile, row-major
@@ -500,6 +561,16 @@ __device__ __forceinline__ int lds_read_b32(uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
+// Two dwords.
+__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// One dword written (the counted waits and barriers order it).
+__device__ __forceinline__ void lds_write_b32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
 
 // W: every gather-list key carries a logit offset (the log weight of its block, in raw-score
 // units), copied into LDS with the tile and added to the scores
@@ -510,9 +581,10 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
                                                          const int32_t* __restrict__ q_perm,
                                                          const int32_t* __restrict__ q_off, int cq,
                                                          const int32_t* __restrict__ tile_base,
-                                                         const int32_t* __restrict__ gather,
-                                                         const int32_t* __restrict__ glen,
-                                                         const float* __restrict__ gbias, float scale,
+                                                         const int32_t* __restrict__ k_perm, int ck,
+                                                         const int32_t* __restrict__ runs,
+                                                         const int32_t* __restrict__ nrun,
+                                                         const int32_t* __restrict__ glen, float scale,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 12;
@@ -526,13 +598,19 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   constexpr int BN = D == 64 ? 64 : kBf16BN;
   constexpr int NSUB = BN / 32;                 // 32-key sub-tiles
   constexpr int TILEB = BN * ROWB;              // one K (or V) tile
-  constexpr int BIASB = W ? 256 : 0;            // per wave: the tile's key offsets (lanes l % BN)
-  constexpr int STAGEB = 2 * TILEB + NWC * BIASB;  // K, V, then the key offsets
+  constexpr int STAGEB = 2 * TILEB;              // K, then V
   constexpr int RPB = 1024 / ROWB;              // rows per 1 KB wave load
   constexpr int LOADS = TILEB / (1024 * NWC);    // 1 KB loads per wave per tile, for K and for V
   static_assert(LOADS >= 1, "tile smaller than one load per wave");
-  constexpr int CP = 2 * LOADS + (W ? 1 : 0);   // copies per wave per tile
+  constexpr int CP = 2 * LOADS;                 // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) uint8_t stages[NST * STAGEB];
+  // the query cluster's runs (see attn_runs), one record per run r: {rd[r], rv[r + 1]} (+ {rb[r], 0}
+  // in the weighted form), so that one LDS read gives a lane the run's offset and its end
+  constexpr int RREC = W ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) int32_t s_run[kMaxClusters * RREC];
+  // weighted form: per tile, the logit offset of each of the tile's keys (lane l: key l % BN),
+  // written when the tile's entries are loaded and read when it is computed
+  __shared__ __attribute__((aligned(16))) float bring[W ? 2 * NST : 1][kWave];
 
   int h, c;
   xcd_tile(h, c);
@@ -543,23 +621,31 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const bool copier = w < NWC;
+  const bool indexer = w == NWC;  // the first wave without copies resolves the tiles' key rows
   const int wc = copier ? w : NWC - 1;
   const int hl = l / 32;
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
   const int qbeg = qo[i] + (c - tb[ti]) * kBf16BM;
   const int qend = min(qbeg + kBf16BM, qo[i + 1]);
   const bool active = qbeg + w * 32 < qend;  // this wave has at least one query
-  const int32_t* rows = gather + ((int64_t)h * cq + i) * N;
   const int L = glen[(int64_t)h * cq + i];
+  const int R = nrun[(int64_t)h * cq + i];
+  {
+    const int32_t* rg = runs + ((int64_t)h * cq + i) * run_stride(ck);
+    for (int e = threadIdx.x; e < R; e += NW * kWave) {
+      s_run[e * RREC] = rg[ck + 1 + e];
+      s_run[e * RREC + 1] = rg[e + 1];
+      if constexpr (W) {
+        s_run[e * RREC + 2] = rg[2 * ck + 1 + e];
+        s_run[e * RREC + 3] = 0;
+      }
+    }
+  }
   const uint16_t* Qh = Q + (int64_t)h * N * D;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
-  // key offsets past the list end read as 0 (the range check of the buffer resource)
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W ? gbias + ((int64_t)h * cq + i) * N : nullptr), (short)0, (int)(uint32_t)(W ? L * 4 : 0),
-      kBufferFlags);
 
   const int qpos = qbeg + w * 32 + l % 32;
   const bool qok = qpos < qend;
@@ -586,19 +672,36 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   // read into a register at the end of iteration x - NST, ready for the copies of iteration
   // x - NST + 1.
   static_assert(LOADS == 1, "one 1 KB copy per wave and tile");
-  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][NWC][kWave];
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, (int)(uint32_t)(L * 4),
-                                                                       kBufferFlags);
+  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][kWave];
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k_perm + (int64_t)h * N), (short)0, (int)(uint32_t)(N * 4), kBufferFlags);
   constexpr int IL = 1;  // index loads per wave and tile
+  // Cursor of this lane's key through the runs: keys advance by BN per tile, so the run index only
+  // grows (the run record is read again per tile, which keeps the cursor to one register).
+  __syncthreads();  // run records in LDS
+  int cr = 0;
+  const uint32_t run_base = (uint32_t)(size_t)((PARK_LDS int32_t*)s_run);
+  const uint32_t bring_base = (uint32_t)(size_t)((PARK_LDS float*)&bring[0][0]);
   auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
-    if (!copier) return;
-    // entries past the list end read as 0 (a valid row; its scores are masked)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][wc][0], 4, (tile * BN + l % BN) * 4, 0, 0,
-                                             0);
+    if (!indexer) return;
+    const int v = tile * BN + l % BN;
+    int off = (int)(N * 4);  // past the buffer's range: reads 0 (a valid row; its scores are masked)
+    float bias = 0.f;
+    if (v < L) {
+      u32x2_t rec = lds_read_b64(run_base + (uint32_t)(cr * RREC) * 4u);
+      while (v >= (int)rec[1]) {  // rec[1]: first key after run cr (< L for every run but the last)
+        ++cr;
+        rec = lds_read_b64(run_base + (uint32_t)(cr * RREC) * 4u);
+      }
+      off = (v + (int)rec[0]) * 4;
+      if constexpr (W) bias = __int_as_float(lds_read_b32(run_base + (uint32_t)(cr * RREC + 2) * 4u));
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][0], 4, off, 0, 0, 0);
+    if constexpr (W) lds_write_b32(bring_base + (uint32_t)((tile % (2 * NST)) * kWave + l) * 4u, bias);
   };
-  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][wc][trow[0]]);
+  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][trow[0]]);
   auto read_idx = [&](int set) __attribute__((always_inline)) {
-    return lds_read_b32(ibase + (uint32_t)(set * NWC * kWave * 4));
+    return lds_read_b32(ibase + (uint32_t)(set * kWave * 4));
   };
   int nnext = 0;  // gather-list row of this lane's copy in the next issue
   auto issue = [&](int nrow0, int slot, int tile) __attribute__((always_inline)) {
@@ -611,11 +714,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
     }
-    if constexpr (W) {
-      const int boff = slot * STAGEB + 2 * TILEB + wc * BIASB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (PARK_LDS void*)(stages + boff), 4, (tile * BN + l % BN) * 4, 0,
-                                               0, 0);
-    }
+    (void)tile;
   };
 
   f32x16_t o[DT];
@@ -687,18 +786,14 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     }
   };
   // key offsets (weighted form) and the mask of keys past the list end
-  auto adjust = [&](auto OFFc, f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
+  auto adjust = [&](f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
     if constexpr (W) {
-      constexpr int OFF = decltype(OFFc)::value;  // the stage
+      const int tile = v0 / BN;
 #pragma unroll
       for (int st = 0; st < NSUB; ++st) {
         u32x4_t b[4];
-        const uint32_t ba = sbase + 2 * TILEB + (w % NWC) * BIASB + (st * 32 + hl * 16) * 4;
-        if constexpr (OFF + 48 <= 65535) {
-          lds_read4_b128<OFF>(b, ba);
-        } else {
-          lds_read4_b128<0>(b, ba + OFF);
-        }
+        const uint32_t ba = bring_base + (uint32_t)((tile % (2 * NST)) * kWave + st * 32 + hl * 16) * 4u;
+        lds_read4_b128<0>(b, ba);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -773,11 +868,15 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   };
 
   if (nt > 0) {
-    // prologue: entries of tiles 0 .. NST-1 (one wait), then those of tiles NST .. 2 NST-2 into the
-    // sets just read, then the copies of tiles 0 .. NST-2 into stages 0 .. NST-2
+    // prologue: entries of tiles 0 .. NST-1 (one wait of the indexer, then a barrier), then those
+    // of tiles NST .. 2 NST-2 into the sets just read, then the copies of tiles 0 .. NST-2 into
+    // stages 0 .. NST-2
 #pragma unroll
     for (int x = 0; x < NST; ++x) load_idx(x, x);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (indexer) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) & lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     int n0[NST];
 #pragma unroll
     for (int x = 0; x < NST; ++x) n0[x] = read_idx(x);
@@ -789,27 +888,27 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   }
   // Iteration t (stage SL = t % NST): wait until tile t landed, copy tile t + NST - 1 into the stage
   // tile t - 1 used, load the entries of tile t + 2 NST - 1, compute tile t, read the entries of
-  // tile t + NST. Tile t was copied in iteration t - NST + 1, after which each of the NST - 2
-  // iterations since issued CP + IL vector-memory operations (copies, then the index load), or in
-  // the prologue, after which at least NST - 2 tiles' CP copies were issued; the entries read at the
-  // end of iteration t were loaded before those copies. Copier waves only issue copies; the waits
-  // hold trivially for the others.
+  // tile t + NST. Copier waves: tile t was copied in iteration t - NST + 1 (or in the prologue),
+  // after which each of the NST - 2 iterations since issued CP copies. Indexer: the entries of tile
+  // t + NST were loaded in iteration t - NST + 1 (or in the prologue), after which NST - 2 index
+  // loads followed; its wait before the barrier lets every wave read them at the end of iteration
+  // t. The other waves issue no vector-memory operations in the loop.
   for (int t = 0; t < nt; t += NST) {
     const bool go_on = unroll_while<0, NST>([&](auto SLc) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLc)::value;
       constexpr int XS = (SL + NST - 1) % NST;
       const int tt = t + SL;
       if (tt >= nt) return false;
-      if (tt < NST - 1)
-        wait_barrier<(NST - 2) * CP>();
+      if (indexer)
+        wait_barrier<(NST - 2) * IL>();
       else
-        wait_barrier<(NST - 2) * (CP + IL)>();
+        wait_barrier<(NST - 2) * CP>();
       issue(nnext, XS, tt + NST - 1);
       load_idx(XS, tt + 2 * NST - 1);
       if (active) {
         f32x16_t sc[NSUB];
         s_tile(std::integral_constant<int, SL * STAGEB>{}, sc);
-        adjust(std::integral_constant<int, SL * STAGEB>{}, sc, tt * BN);
+        adjust(sc, tt * BN);
         if (tt == 0) m_ref = tile_max(sc);
         u32x4_t pb[NSUB][2];
         float ps = weights(sc, pb);
@@ -818,7 +917,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
           // live through the softmax
           f32x16_t s2[NSUB];
           s_tile(std::integral_constant<int, SL * STAGEB>{}, s2);
-          adjust(std::integral_constant<int, SL * STAGEB>{}, s2, tt * BN);
+          adjust(s2, tt * BN);
           const float m_new = fmaxf(m_ref, tile_max(s2));
           const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
           l_run *= alpha;
@@ -863,39 +962,46 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
 
 int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, s.bf16 ? kBf16BM : kAttnBM) + cq; }
 
-size_t attn_gather_ints(const Dims& s, int cq) { return (size_t)(s.H * cq) * (size_t)(s.N + 1); }
+size_t attn_run_ints(const Dims& s, int cq, int ck) {
+  return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq);
+}
 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
                               const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
                               int ck, const int32_t* counts, const int32_t* cols, const float* log_w, float scale,
-                              void* out, float* lse, int32_t* tile_base, int32_t* gather, float* gbias,
+                              void* out, float* lse, int32_t* tile_base, int32_t* runs, int64_t* stats,
                               hipStream_t st) {
-  int32_t* glen = gather + (size_t)(s.H * cq) * (size_t)s.N;
-  float* gb = log_w ? gbias : nullptr;
-  attn_gather<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, k_perm, s.N, cq, ck, log_w,
-                                                                1.f / scale, gather, glen, gb);
+  int32_t* nrun = runs + (size_t)(s.H * cq) * (size_t)run_stride(ck);
+  int32_t* glen = nrun + s.H * cq;
+  int32_t* nblk = glen + s.H * cq;
+  const int weighted = log_w != nullptr;
+  attn_runs<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, s.N, cq, ck, log_w,
+                                                               1.f / scale, runs, nrun, glen, nblk);
   attn_order<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, glen, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
+  if (stats)
+    attn_stats<<<1, 1024, 0, st>>>(q_offsets, k_offsets, s.H, s.N, cq, ck, glen, nblk, tile_base,
+                                   s.bf16 && s.D == 128 ? kBf16BN : kBN, stats);
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
 #define PARK_ATTN(T, D)                                                                                          \
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
                                                  static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, tile_base, \
-                                                 gather, glen, gb, scale, static_cast<T*>(out), lse);
-#define PARK_BF16ATTN(D, W)                                                                                            \
-  sparse_attn_bf16<D, W><<<grid, 768, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, gather, glen, gb, \
-                                             scale, oh, lse);
+                                                 k_perm, ck, runs, glen, weighted, scale, static_cast<T*>(out), lse);
+#define PARK_BF16ATTN(D, W)                                                                                         \
+  sparse_attn_bf16<D, W><<<grid, 768, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, k_perm, ck, runs, \
+                                             nrun, glen, scale, oh, lse);
   if (s.bf16) {
     const uint16_t* qh = static_cast<const uint16_t*>(q);
     const uint16_t* kh = static_cast<const uint16_t*>(k);
     const uint16_t* vh = static_cast<const uint16_t*>(v);
     uint16_t* oh = static_cast<uint16_t*>(out);
     if (s.D == 128) {
-      if (gb) {
+      if (weighted) {
         PARK_BF16ATTN(128, true)
       } else {
         PARK_BF16ATTN(128, false)
       }
     } else {
-      if (gb) {
+      if (weighted) {
         PARK_BF16ATTN(64, true)
       } else {
         PARK_BF16ATTN(64, false)

@@ -900,10 +900,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // tile only when that tile's best is larger in its top 20 bits, so equal scores keep the lower
 // centroid index across tiles. Registers are capped for three waves per SIMD, so that one wave's
 // MFMAs run while the others compare.
+// Rows: the M points phase + p * stride, p < M (every row: stride 1, phase 0, M = N); the labels of
+// the other rows are left as they are (subset updates).
 template <int D, int PT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void assign_bf16(const uint16_t* __restrict__ X, int64_t N, int C,
                                                    const uint16_t* __restrict__ G, const float* __restrict__ b,
-                                                   int32_t* __restrict__ labels) {
+                                                   int32_t* __restrict__ labels, int64_t M, int stride,
+                                                   int phase) {
   constexpr int KS = D / 16;
   constexpr int STR = D + 8;  // padded LDS row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t gl[kAsgChunk * STR];
@@ -921,10 +924,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
   for (int pt = 0; pt < PT; ++pt) {
     const int64_t p = p_base + pt * 32 + l % 32;
+    const int64_t row = phase + p * stride;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (p < N) v = *reinterpret_cast<const u32x4_t*>(Xh + p * D + kk * 16 + hl * 8);
+      if (p < M) v = *reinterpret_cast<const u32x4_t*>(Xh + row * D + kk * 16 + hl * 8);
       xb[pt][kk] = v;
     }
   }
@@ -1006,7 +1010,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int oi = __shfl_xor(bi, 32, kWave);
     if (ob > bestt[pt] || (ob == bestt[pt] && oi < bi)) bi = oi;
     const int64_t p = p_base + pt * 32 + l % 32;
-    if (hl == 0 && p < N) labels[(int64_t)h * N + p] = bi;
+    if (hl == 0 && p < M) labels[(int64_t)h * N + phase + p * stride] = bi;
   }
 }
 
@@ -1014,13 +1018,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 template <int D>
 __global__ __launch_bounds__(256) void assign_f32(const float* __restrict__ X, int64_t N, int C,
                                                   const float* __restrict__ G, const float* __restrict__ b,
-                                                  int32_t* __restrict__ labels) {
+                                                  int32_t* __restrict__ labels, int64_t M, int stride, int phase) {
   constexpr int CH = 32;
   __shared__ float gl[CH * D];
   __shared__ float bl[CH];
   const int h = blockIdx.y;
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const float* x = X + ((int64_t)h * N + (p < N ? p : 0)) * D;
+  const int64_t row = phase + (p < M ? p : 0) * stride;
+  const float* x = X + ((int64_t)h * N + row) * D;
   double best = INFINITY;
   int bi = 0;
   for (int c0 = 0; c0 < C; c0 += CH) {
@@ -1042,7 +1047,17 @@ __global__ __launch_bounds__(256) void assign_f32(const float* __restrict__ X, i
     }
     __syncthreads();
   }
-  if (p < N) labels[(int64_t)h * N + p] = bi;
+  if (p < M) labels[(int64_t)h * N + row] = bi;
+}
+
+// Labels outside [0, C) (a caller's stale buffer) become cluster 0, so that the sort and update
+// of a subset step never index outside their tables.
+__global__ void clamp_labels(int32_t* __restrict__ labels, int64_t n, int C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const int v = labels[i];
+    if (v < 0 || v >= C) labels[i] = 0;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1429,25 +1444,33 @@ hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* per
 }
 
 hipError_t launch_assign(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
-                         hipStream_t st) {
+                         hipStream_t st, int stride, int phase) {
+  const int64_t M = phase < s.N ? ceil_div(s.N - phase, stride) : 0;  // rows phase + p * stride < N
+  if (M == 0) return hipGetLastError();
   if (s.bf16) {
     constexpr int PT = 2;
-    const dim3 grid((unsigned)ceil_div(s.N, 4 * 32 * PT), (unsigned)s.H);
+    const dim3 grid((unsigned)ceil_div(M, 4 * 32 * PT), (unsigned)s.H);
     if (s.D == 128)
       assign_bf16<128, PT><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), s.N, C,
-                                                 static_cast<const uint16_t*>(g), b, labels);
+                                                 static_cast<const uint16_t*>(g), b, labels, M, stride, phase);
     else
       assign_bf16<64, PT><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), s.N, C,
-                                                static_cast<const uint16_t*>(g), b, labels);
+                                                static_cast<const uint16_t*>(g), b, labels, M, stride, phase);
   } else {
-    const dim3 grid((unsigned)ceil_div(s.N, 256), (unsigned)s.H);
+    const dim3 grid((unsigned)ceil_div(M, 256), (unsigned)s.H);
     if (s.D == 128)
       assign_f32<128><<<grid, 256, 0, st>>>(static_cast<const float*>(x), s.N, C, static_cast<const float*>(g), b,
-                                            labels);
+                                            labels, M, stride, phase);
     else
       assign_f32<64><<<grid, 256, 0, st>>>(static_cast<const float*>(x), s.N, C, static_cast<const float*>(g), b,
-                                           labels);
+                                           labels, M, stride, phase);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_clamp_labels(const Dims& s, int C, int32_t* labels, hipStream_t st) {
+  const int64_t n = s.H * s.N;
+  clamp_labels<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(labels, n, C);
   return hipGetLastError();
 }
 

@@ -173,14 +173,12 @@ size_t estimator_ws_bytes(const park::Dims& s, int cq, int ck) {
 
 struct AttnWs {
   int32_t* tile_base;
-  int32_t* gather;
-  float* gbias;  // per-key logit offsets of the gather lists (weighted attention only)
+  int32_t* runs;  // per (head, query cluster): the runs of its selected keys, run and key counts
 };
-AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck, bool weighted = false) {
+AttnWs plan_attn(Carver& cv, const park::Dims& s, int cq, int ck) {
   AttnWs w;
   w.tile_base = cv.take<int32_t>((size_t)(s.H * (2 * cq + 1)));
-  w.gather = cv.take<int32_t>(park::attn_gather_ints(s, cq));
-  w.gbias = weighted ? cv.take<float>((size_t)(s.H * cq) * (size_t)s.N) : nullptr;
+  w.runs = cv.take<int32_t>(park::attn_run_ints(s, cq, ck));
   return w;
 }
 
@@ -225,7 +223,11 @@ park_status check_params(const park::Dims& s, const park_params* p, bool need_it
     return fail(PARK_EINVAL, "iters must be in [%d, 100000], got %d", need_iters ? 1 : 0, p->iters);
   if (!(p->p > 0.0 && p->p <= 1.0)) return fail(PARK_EINVAL, "p must be in (0, 1], got %g", p->p);
   if (p->kmetric != PARK_EUCLID && p->kmetric != PARK_QRKC) return fail(PARK_EINVAL, "kmetric must be PARK_EUCLID or PARK_QRKC");
-  if (p->init != PARK_INIT_KMEANSPP && p->init != PARK_INIT_WARM) return fail(PARK_EINVAL, "init must be PARK_INIT_KMEANSPP or PARK_INIT_WARM");
+  if (p->init != PARK_INIT_KMEANSPP && p->init != PARK_INIT_WARM && p->init != PARK_INIT_SUBSET)
+    return fail(PARK_EINVAL, "init must be PARK_INIT_KMEANSPP, PARK_INIT_WARM or PARK_INIT_SUBSET");
+  if (p->init == PARK_INIT_SUBSET && (p->subset_stride < 1 || p->subset_phase < 0 || p->subset_phase >= p->subset_stride))
+    return fail(PARK_EINVAL, "subset updates need subset_stride >= 1 and 0 <= subset_phase < subset_stride, got %d, %d",
+                p->subset_stride, p->subset_phase);
   if (std::isnan(p->scale)) return fail(PARK_EINVAL, "scale is NaN");
   return PARK_OK;
 }
@@ -246,12 +248,16 @@ size_t forward_ws_bytes(const park::Dims& s, const park_params& p) {
 
 // Lloyd iterations shared by park_cluster and park_forward: (g, b) of the current centroids, then
 // per iteration assign -> stable sort -> update (which also prepares (g, b) for the next one).
+// With stride > 1 (a subset update) only the rows phase, phase + stride, ... are re-assigned; the
+// others keep the labels already in `labels`, which are first clamped into [0, C).
 hipError_t run_lloyd(const park::Dims& s, const void* x, const float* metric, int C, int iters, float* cent,
-                     int32_t* labels, int32_t* perm, int32_t* offsets, const ClusterWs& w, hipStream_t st) {
+                     int32_t* labels, int32_t* perm, int32_t* offsets, const ClusterWs& w, hipStream_t st,
+                     int stride = 1, int phase = 0) {
   if (iters == 0) return hipSuccess;
   hipError_t e = park::launch_update(s, x, C, nullptr, nullptr, cent, 0, metric, w.g, w.b, st);
+  if (e == hipSuccess && stride > 1) e = park::launch_clamp_labels(s, C, labels, st);
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
-    e = park::launch_assign(s, x, C, w.g, w.b, labels, st);
+    e = park::launch_assign(s, x, C, w.g, w.b, labels, st, stride, phase);
     if (e == hipSuccess) e = park::launch_sort(s, C, labels, w.table, perm, offsets, st);
     if (e == hipSuccess) e = park::launch_update(s, x, C, perm, offsets, cent, 1, metric, w.g, w.b, st);
   }
@@ -343,7 +349,7 @@ size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_p
         return cv.off;
       case PARK_ENTRY_SPARSE_ATTN_WEIGHTED:
         if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
-        plan_attn(cv, s, params->cq, params->ck, true);
+        plan_attn(cv, s, params->cq, params->ck);
         return cv.off;
       case PARK_ENTRY_ESTIMATOR:
         if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || check_clusters(s, params->ck, "ck") != PARK_OK) return 0;
@@ -351,6 +357,12 @@ size_t park_workspace_bytes(int32_t entry, const park_shape* shape, const park_p
       case PARK_ENTRY_FORWARD:
         if (check_params(s, params, true) != PARK_OK) return 0;
         return forward_ws_bytes(s, *params);
+      case PARK_ENTRY_MERGE:
+        if (!params || check_clusters(s, params->cq, "cq") != PARK_OK || params->ck < 1 ||
+            params->ck > park::kMaxClusters)
+          return 0;
+        cv.take<int32_t>(park::merge_ws_ints(s.H, params->cq, params->ck));
+        return cv.off;
       default:
         return 0;
     }
@@ -414,6 +426,37 @@ park_status park_cluster(const park_shape* shape, const void* x, int32_t metric,
     return hip_check(e, "park_cluster");
   } catch (...) {
     return fail(PARK_EHIP, "park_cluster: internal error");
+  }
+}
+
+park_status park_cluster_subset(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
+                                int32_t n_clusters, int32_t iters, int32_t stride, int32_t phase, float* centroids,
+                                int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                                void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_ptr(x, "x", 16));
+    PARK_TRY(check_clusters(s, n_clusters, "n_clusters"));
+    if (metric != PARK_EUCLID && metric != PARK_QRKC) return fail(PARK_EINVAL, "metric must be PARK_EUCLID or PARK_QRKC");
+    if (metric == PARK_QRKC) PARK_TRY(check_ptr(qmetric, "qmetric", 4));
+    if (iters < 1 || iters > 100000) return fail(PARK_EINVAL, "iters must be in [1, 100000], got %d", iters);
+    if (stride < 1 || phase < 0 || phase >= stride)
+      return fail(PARK_EINVAL, "need stride >= 1 and 0 <= phase < stride, got %d, %d", stride, phase);
+    PARK_TRY(check_ptr(centroids, "centroids", 4));
+    PARK_TRY(check_ptr(labels, "labels", 4));
+    PARK_TRY(check_ptr(perm, "perm", 4));
+    PARK_TRY(check_ptr(offsets, "offsets", 4));
+    Carver meas(nullptr);
+    plan_cluster(meas, s, n_clusters, metric == PARK_QRKC);
+    PARK_TRY(check_ws(ws, ws_bytes, meas.off));
+    Carver cv(ws);
+    ClusterWs w = plan_cluster(cv, s, n_clusters, metric == PARK_QRKC);
+    return hip_check(run_lloyd(s, x, metric == PARK_QRKC ? qmetric : nullptr, n_clusters, iters, centroids, labels,
+                               perm, offsets, w, (hipStream_t)stream, stride, phase),
+                     "park_cluster_subset");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_cluster_subset: internal error");
   }
 }
 
@@ -595,15 +638,14 @@ park_status sparse_attn_impl(const char* name, const park_shape* shape, const vo
   PARK_TRY(check_clusters(s, cq, "cq"));
   PARK_TRY(check_clusters(s, ck, "ck"));
   if (std::isnan(scale)) return fail(PARK_EINVAL, "scale is NaN");
-  const bool weighted = log_w != nullptr;
   Carver meas(nullptr);
-  plan_attn(meas, s, cq, ck, weighted);
+  plan_attn(meas, s, cq, ck);
   PARK_TRY(check_ws(ws, ws_bytes, meas.off));
   Carver cv(ws);
-  AttnWs w = plan_attn(cv, s, cq, ck, weighted);
+  AttnWs w = plan_attn(cv, s, cq, ck);
   return hip_check(park::launch_sparse_attn(s, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck, counts, cols,
-                                            log_w, resolve_scale(scale, s.D), out, lse, w.tile_base, w.gather,
-                                            w.gbias, (hipStream_t)stream),
+                                            log_w, resolve_scale(scale, s.D), out, lse, w.tile_base, w.runs,
+                                            nullptr, (hipStream_t)stream),
                    name);
 }
 }  // namespace
@@ -631,6 +673,38 @@ park_status park_sparse_attn_weighted(const park_shape* shape, const void* q, co
                             ck, counts, cols, log_w, scale, out, lse, ws, ws_bytes, stream);
   } catch (...) {
     return fail(PARK_EHIP, "park_sparse_attn_weighted: internal error");
+  }
+}
+
+park_status park_merge_clusters(int64_t heads, int64_t n, int32_t cq, int32_t ck, int32_t bm, const int32_t* q_perm,
+                                const int32_t* q_offsets, const int32_t* k_offsets, const int32_t* counts,
+                                const int32_t* cols, int32_t* group, int32_t* m_perm, int32_t* m_offsets,
+                                int32_t* m_counts, int32_t* m_cols, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (heads < 1 || heads > 65535) return fail(PARK_EINVAL, "heads must be in [1, 65535]");
+    if (n < 1 || n >= (int64_t(1) << 24)) return fail(PARK_EINVAL, "n must be in [1, 2^24), got %lld", (long long)n);
+    if (cq < 1 || cq > park::kMaxClusters || cq > n) return fail(PARK_EINVAL, "cq must be in [1, min(n, %d)]", park::kMaxClusters);
+    if (ck < 1 || ck > park::kMaxClusters) return fail(PARK_EINVAL, "ck must be in [1, %d]", park::kMaxClusters);
+    if (bm < 1) return fail(PARK_EINVAL, "bm must be >= 1, got %d", bm);
+    PARK_TRY(check_ptr(q_perm, "q_perm", 4));
+    PARK_TRY(check_ptr(q_offsets, "q_offsets", 4));
+    PARK_TRY(check_ptr(k_offsets, "k_offsets", 4));
+    PARK_TRY(check_ptr(counts, "counts", 4));
+    PARK_TRY(check_ptr(cols, "cols", 4));
+    PARK_TRY(check_ptr(group, "group", 4));
+    PARK_TRY(check_ptr(m_perm, "m_perm", 4));
+    PARK_TRY(check_ptr(m_offsets, "m_offsets", 4));
+    PARK_TRY(check_ptr(m_counts, "m_counts", 4));
+    PARK_TRY(check_ptr(m_cols, "m_cols", 4));
+    if (m_perm == q_perm || m_cols == cols || m_offsets == q_offsets || m_counts == counts)
+      return fail(PARK_EINVAL, "the merged clustering must not overlap its inputs");
+    const size_t need = park::merge_ws_ints(heads, cq, ck) * sizeof(int32_t);
+    PARK_TRY(check_ws(ws, ws_bytes, need));
+    return hip_check(park::launch_merge(heads, n, cq, ck, bm, q_perm, q_offsets, k_offsets, counts, cols, group, m_perm,
+                                        m_offsets, m_counts, m_cols, static_cast<int32_t*>(ws), (hipStream_t)stream),
+                     "park_merge_clusters");
+  } catch (...) {
+    return fail(PARK_EHIP, "park_merge_clusters: internal error");
   }
 }
 
@@ -683,7 +757,11 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
     for (const void* ptr : opt)
       if (ptr && !aligned(ptr, 4)) return fail(PARK_EINVAL, "forward outputs must be 4-byte aligned");
     if (o.sel_keys && !aligned(o.sel_keys, 8)) return fail(PARK_EINVAL, "sel_keys must be 8-byte aligned");
+    if (o.stats && !aligned(o.stats, 8)) return fail(PARK_EINVAL, "stats must be 8-byte aligned");
     const park_params& p = *params;
+    const bool subset = p.init == PARK_INIT_SUBSET;
+    if (subset && (!o.q_labels || !o.k_labels))
+      return fail(PARK_EINVAL, "PARK_INIT_SUBSET needs outputs->q_labels and outputs->k_labels (the previous labels)");
     PARK_TRY(check_ws(ws, ws_bytes, forward_ws_bytes(s, p)));
     Carver cv(ws);
     ForwardWs w = plan_forward(cv, s, p);
@@ -717,10 +795,12 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
       e = side_stream(lock, &ss);
       if (e == hipSuccess) e = hipEventRecord(ss->fork, st);
       if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
-      if (e == hipSuccess) e = run_lloyd(s, q, nullptr, p.cq, p.iters, q_centroids, ql, qp, qo, w.qc, ss->stream);
+      const int stride = subset ? p.subset_stride : 1, phase = subset ? p.subset_phase : 0;
+      if (e == hipSuccess)
+        e = run_lloyd(s, q, nullptr, p.cq, p.iters, q_centroids, ql, qp, qo, w.qc, ss->stream, stride, phase);
       if (e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
       if (e == hipSuccess)
-        e = run_lloyd(s, k, qrkc ? M : nullptr, p.ck, p.iters, k_centroids, kl, kp, ko, w.kc, st);
+        e = run_lloyd(s, k, qrkc ? M : nullptr, p.ck, p.iters, k_centroids, kl, kp, ko, w.kc, st, stride, phase);
       if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
     }
     if (e == hipSuccess)
@@ -730,7 +810,7 @@ park_status park_forward(const park_shape* shape, const void* q, const void* k, 
       e = park::launch_select_topp(map, s.H, p.cq, p.ck, ko, p.p, o.mask, counts, cols, sk, st);
     if (e == hipSuccess)
       e = park::launch_sparse_attn(s, q, k, v, qp, qo, p.cq, kp, ko, p.ck, counts, cols, nullptr, scale, out, o.lse,
-                                   w.aw.tile_base, w.aw.gather, nullptr, st);
+                                   w.aw.tile_base, w.aw.runs, reinterpret_cast<int64_t*>(o.stats), st);
     return hip_check(e, "park_forward");
   } catch (...) {
     return fail(PARK_EHIP, "park_forward: internal error");

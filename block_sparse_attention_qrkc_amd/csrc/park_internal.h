@@ -55,8 +55,11 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
 // Centroid means (do_update) and the consumed form (g, b) of the centroids for the next assignment.
 hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets, float* cent,
                          int do_update, const float* metric, void* g, float* b, hipStream_t st);
+// Assignment of the rows phase, phase + stride, ... (all rows by default); other labels untouched.
 hipError_t launch_assign(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
-                         hipStream_t st);
+                         hipStream_t st, int stride = 1, int phase = 0);
+// Labels outside [0, C) become 0 (caller-provided labels of a subset update).
+hipError_t launch_clamp_labels(const Dims& s, int C, int32_t* labels, hipStream_t st);
 hipError_t launch_sort(const Dims& s, int C, const int32_t* labels, int32_t* table, int32_t* perm,
                        int32_t* offsets, hipStream_t st);
 size_t sort_table_ints(const Dims& s, int C);
@@ -94,11 +97,22 @@ hipError_t launch_select_sip(const float* map, int64_t H, int cq, int ck, const 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
                               const int32_t* q_offsets, int cq, const int32_t* k_perm, const int32_t* k_offsets,
                               int ck, const int32_t* counts, const int32_t* cols, const float* log_w, float scale,
-                              void* out, float* lse, int32_t* tile_base, int32_t* gather, float* gbias,
+                              void* out, float* lse, int32_t* tile_base, int32_t* runs, int64_t* stats,
                               hipStream_t st);
 int64_t attn_max_tiles(const Dims& s, int cq);
-// ints of the gather workspace: [H, cq, N] key rows + [H, cq] lengths
-size_t attn_gather_ints(const Dims& s, int cq);
+// ints of the run workspace: per (head, query cluster) the runs of its selected keys (at most ck,
+// three ints each) + [H, cq] run counts + [H, cq] key counts + [H, cq] non-empty selected blocks.
+// stats (device, may be NULL): the eight int64 of park_stats.
+size_t attn_run_ints(const Dims& s, int cq, int ck);
+
+// merge.hip
+// Tile-aware merging of query clusters (cost ceil(n / bm) * selected keys per group); outputs a
+// query clustering with cq slots. Workspace: merge_ws_ints(H, cq, ck) int32.
+size_t merge_ws_ints(int64_t H, int cq, int ck);
+hipError_t launch_merge(int64_t H, int64_t N, int cq, int ck, int bm, const int32_t* q_perm, const int32_t* q_offsets,
+                        const int32_t* k_offsets, const int32_t* counts, const int32_t* cols, int32_t* group,
+                        int32_t* m_perm, int32_t* m_offsets, int32_t* m_counts, int32_t* m_cols, int32_t* ws,
+                        hipStream_t st);
 
 // permute.hip
 hipError_t launch_permute(const Dims& s, const void* x, const int32_t* perm, void* out, int inverse,

@@ -40,7 +40,7 @@ typedef enum {
 
 typedef enum { PARK_F32 = 0, PARK_BF16 = 1 } park_dtype;
 typedef enum { PARK_EUCLID = 0, PARK_QRKC = 1 } park_metric;
-typedef enum { PARK_INIT_KMEANSPP = 0, PARK_INIT_WARM = 1 } park_init;
+typedef enum { PARK_INIT_KMEANSPP = 0, PARK_INIT_WARM = 1, PARK_INIT_SUBSET = 2 } park_init;
 typedef enum { PARK_SIDE_Q = 0, PARK_SIDE_K = 1 } park_side;
 /* Query/key representations of a block map (PARK, thelatestinai.com page, Table 1): F = full
  * (every original query or key), C = centroid. FC is the PAMA map. */
@@ -62,7 +62,10 @@ typedef struct {
   uint64_t seed;   /* k-means++ seed */
   int32_t kmetric; /* park_metric of the key clustering: PARK_QRKC (default) or PARK_EUCLID */
   int32_t init;    /* park_init: PARK_INIT_KMEANSPP, or PARK_INIT_WARM to start from the
-                      centroids already in the caller's centroid buffers */
+                      centroids already in the caller's centroid buffers, or PARK_INIT_SUBSET: a
+                      warm start that re-assigns only a subset of the tokens (see park_forward) */
+  int32_t subset_stride; /* PARK_INIT_SUBSET: every subset_stride-th token is re-assigned, */
+  int32_t subset_phase;  /* starting at token subset_phase (0 <= phase < stride); else unused */
 } park_params;
 
 /* Entry identifiers for park_workspace_bytes. */
@@ -75,7 +78,8 @@ enum {
   PARK_ENTRY_SPARSE_ATTN = 5,
   PARK_ENTRY_FORWARD = 6,
   PARK_ENTRY_ESTIMATOR = 7,  /* park_estimator_map, any mode */
-  PARK_ENTRY_SPARSE_ATTN_WEIGHTED = 8
+  PARK_ENTRY_SPARSE_ATTN_WEIGHTED = 8,
+  PARK_ENTRY_MERGE = 9 /* park_merge_clusters: shape->heads, params->cq, params->ck */
 };
 
 /* Workspace bytes an entry needs for this shape and these parameters (0 on invalid input). */
@@ -146,6 +150,29 @@ park_status park_cluster(const park_shape* shape, const void* x, int32_t metric,
                          int32_t n_clusters, int32_t iters, int32_t init, uint64_t seed, int32_t side,
                          float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Subset update of a clustering between anchor steps (HyperVAttention page, abstract: hybrid
+ * clustering runs the full clustering only at anchor steps and updates a subset of the tokens at
+ * the steps in between). Reading of the subset: the tokens phase, phase + stride, phase + 2 stride,
+ * ...; a caller that advances phase by one per denoising step refreshes every token once per stride
+ * steps. Each of the `iters` iterations re-assigns the subset's tokens against the consumed form of
+ * the current centroids (as park_cluster), keeps the other tokens' labels, and sets every centroid
+ * to the mean of its members under the combined labels over the current values of all tokens
+ * (empty clusters keep their value).
+ *   x, metric, qmetric, n_clusters  as park_cluster
+ *   iters      >= 1
+ *   stride     >= 1 (1: every token, i.e. warm-started Lloyd iterations); 0 <= phase < stride
+ *   centroids  [heads, C, d] float32, input and output (the previous step's centroids)
+ *   labels     [heads, n] int32, input and output (the previous step's labels; values outside
+ *              [0, C) are taken as cluster 0)
+ *   perm, offsets  outputs as park_cluster
+ * Workspace: park_workspace_bytes(PARK_ENTRY_CLUSTER_Q or _K, ...) as park_cluster.
+ */
+park_status park_cluster_subset(const park_shape* shape, const void* x, int32_t metric, const float* qmetric,
+                                int32_t n_clusters, int32_t iters, int32_t stride, int32_t phase,
+                                float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /*
  * PAMA block-importance map (PARK page, Figure 2 caption and abstract: each original query keeps
@@ -274,6 +301,33 @@ park_status park_sparse_attn_weighted(const park_shape* shape, const void* q, co
                                       void* stream);
 
 /*
+ * Tile-aware merging of query clusters (HyperVAttention page, abstract: merging clusters so as to
+ * lower the CTA-aligned execution cost puts idle tile capacity to use, and the merged queries attend
+ * to the union of the selections). Reading of the cost: a group of n queries whose selection holds
+ * L keys costs ceil(n / bm) * L (its tiles of bm queries, each over every selected key). Parallel
+ * agglomeration: each round every group proposes the partner of largest positive gain
+ * cost(a) + cost(b) - cost(a u b) (ties to the lower index) and mutual proposals merge into the
+ * lower index; the rounds end when no pair gains. Empty query clusters stay alone.
+ *   q_perm [heads, n], q_offsets [heads, cq + 1]  the query clustering (park_cluster)
+ *   k_offsets [heads, ck + 1]                     key cluster sizes
+ *   counts [heads, cq], cols [heads, cq, ck]      the selection (park_select_topp / _topk)
+ *   bm        queries per tile of the cost (the attention's work item: 384 for bf16 data)
+ *   group     [heads, cq] output: merged slot of every query cluster
+ *   m_perm, m_offsets, m_counts, m_cols  outputs, the merged groups as a query clustering and its
+ *             selection with cq slots: slot g < G is the g-th group in increasing order of its
+ *             lowest cluster, its queries cluster by cluster in increasing cluster order (each
+ *             in q_perm order), its selection the ascending union; slots G .. cq - 1 are empty.
+ *             Pass them to park_sparse_attn in place of q_perm, q_offsets, counts, cols.
+ * Workspace: park_workspace_bytes(PARK_ENTRY_MERGE, ...): a selection bitset per cluster and head.
+ * Cost: per round, cq^2 bitset intersections of ck / 32 words per head.
+ */
+park_status park_merge_clusters(int64_t heads, int64_t n, int32_t cq, int32_t ck, int32_t bm,
+                                const int32_t* q_perm, const int32_t* q_offsets, const int32_t* k_offsets,
+                                const int32_t* counts, const int32_t* cols, int32_t* group, int32_t* m_perm,
+                                int32_t* m_offsets, int32_t* m_counts, int32_t* m_cols, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
  * Cluster-contiguous gather and its inverse (the "Clustered" token ordering of PARK Tables 1/10).
  *   park_permute_rows:   out[h, p, :] = x[h, perm[h, p], :]
  *   park_unpermute_rows: out[h, perm[h, p], :] = x[h, p, :]
@@ -300,13 +354,38 @@ typedef struct {
   int64_t* sel_keys;   /* [heads, cq] */
   float* lse;          /* [heads, n] */
   int32_t* status;     /* one int32: PARK_DEVSTATUS_* bits or-ed in (see park_cluster) */
+  struct park_stats* stats; /* selection and work statistics of the call (see park_stats) */
 } park_forward_outputs;
 
+/* Statistics of one park_forward call, written to device memory (totals over all heads). Token
+ * density = pairs / (heads n^2); block density = blocks / live_blocks; the attention computes
+ * 4 d FLOPs per pair and its matrix cores 4 d per padded pair. */
+typedef struct park_stats {
+  int64_t pairs;        /* selected (query, key) pairs: sum over query clusters of n_q(i) * L(i) */
+  int64_t padded_pairs; /* pairs the matrix cores run: queries of a cluster rounded up to the 32 of a
+                           wave, its selected keys to whole key tiles */
+  int64_t blocks;       /* selected (query cluster, key cluster) blocks, both clusters non-empty */
+  int64_t live_blocks;  /* non-empty query clusters x non-empty key clusters */
+  int64_t work_items;   /* attention work items (tiles of up to 384 queries of one cluster) */
+  int64_t tokens;       /* heads * n */
+  int64_t reserved[2];
+} park_stats;
+
 /*
- * The whole path for one layer: QRKC metric, both clusterings (seeded or warm), PAMA map, top-p,
- * block-sparse attention. q_centroids [heads, cq, d] and k_centroids [heads, ck, d] are caller
- * state: outputs, and inputs for PARK_INIT_WARM (a later denoising step reusing the previous
- * step's centroids). The query side uses side stream PARK_SIDE_Q, the key side PARK_SIDE_K.
+ * The whole path for one layer (PARK page, abstract: retrieve the important blocks of each head's
+ * attention, then compute attention only within them; Figure 2 caption: Euclidean K-means on the
+ * queries, K-means under the query-derived metric on the keys, the PAMA map, top-p): QRKC metric,
+ * both clusterings, PAMA map, top-p, block-sparse attention. q_centroids [heads, cq, d] and
+ * k_centroids [heads, ck, d] are caller state, outputs of every call and inputs of the warm modes:
+ *   PARK_INIT_KMEANSPP  seeded k-means++ on both sides, then params->iters Lloyd iterations;
+ *   PARK_INIT_WARM      params->iters Lloyd iterations from the caller's centroids (a later
+ *                       denoising step reusing the previous step's clustering: PARK,
+ *                       thelatestinai.com page, Table 9 recomputes the retrieval only at some steps);
+ *   PARK_INIT_SUBSET    params->iters subset updates (park_cluster_subset) from the caller's
+ *                       centroids and labels: outputs->q_labels and outputs->k_labels are then
+ *                       required and hold the previous step's labels on entry.
+ * The query side uses random stream PARK_SIDE_Q, the key side PARK_SIDE_K. The query-side
+ * iterations run on a helper stream forked from and joined back into `stream` by events.
  */
 park_status park_forward(const park_shape* shape, const void* q, const void* k, const void* v, void* out,
                          const park_params* params, float* q_centroids, float* k_centroids,

@@ -152,14 +152,14 @@ def test_validation_errors(L):
     st, msg = _status(L, "park_sparse_attn", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE,
                       0.0, FAKE, None, FAKE, 8, None)
     assert st == L.PARK_EWORKSPACE
-    # weighted attention: log weights required; its workspace also holds the per-key offsets
+    # weighted attention: log weights required; a workspace one byte short is refused
     st, msg = _status(L, "park_sparse_attn_weighted", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE,
                       FAKE, None, 0.0, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL and "log_w" in msg
     prm = L.make_params(10, 20, 1, 0.9)
-    plain = L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, sh, prm)
+    need = L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN_WEIGHTED, sh, prm)
     st, _ = _status(L, "park_sparse_attn_weighted", bp(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE,
-                    FAKE, FAKE, 0.0, FAKE, None, FAKE, plain, None)
+                    FAKE, FAKE, 0.0, FAKE, None, FAKE, need - 1, None)
     assert st == L.PARK_EWORKSPACE
     # forward: iters must be >= 1, p in range
     prm = L.make_params(10, 20, 0, 0.9)
@@ -184,7 +184,15 @@ def test_workspace_bytes(L):
     assert L.workspace_bytes(L.PARK_ENTRY_FORWARD, L.park_shape(40, 75600, 96, 1), prm) == 0
     assert L.workspace_bytes(L.PARK_ENTRY_FORWARD, wan, L.make_params(100, 500, 0, 0.9)) == 0
     assert L.workspace_bytes(L.PARK_ENTRY_CLUSTER_K, wan, prm) > L.workspace_bytes(L.PARK_ENTRY_CLUSTER_Q, wan, prm)
-    # the weighted attention adds one float32 offset per gather-list slot, [heads, cq, n]
-    extra = (L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN_WEIGHTED, wan, prm)
-             - L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, wan, prm))
-    assert 40 * 100 * 75600 * 4 <= extra <= 40 * 100 * 75600 * 4 + 1024
+    # the attention keeps per (head, query cluster) at most ck runs of its selected keys (three ints
+    # each), so its workspace scales with the selection's own size [heads, cq, ck], not with n
+    attn = L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, wan, prm)
+    assert attn <= 40 * 100 * (3 * 500 + 4 + 3) * 4 + 40 * (2 * 100 + 1) * 4 + 1024
+    assert L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN_WEIGHTED, wan, prm) == attn
+    assert L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, L.park_shape(40, 219600, 128, 1), prm) == attn
+    # the long clip's whole forward pass fits in 2 GB of workspace (the per-token int arrays, the
+    # candidate products of the seeding, the map, sort and map partials)
+    long_fwd = L.workspace_bytes(L.PARK_ENTRY_FORWARD, L.park_shape(40, 219600, 128, 1),
+                                 L.make_params(200, 1000, 10, 0.9))
+    assert 0 < long_fwd <= 2 * 1024 ** 3, long_fwd
+    print(f"workspace: Wan attention {attn / 2**20:.1f} MiB, long-clip forward {long_fwd / 2**30:.2f} GiB")

@@ -296,6 +296,30 @@ def test_full_weighted_attention_sampled(full):
     print(f"[full weighted attention] max-abs {worst:.2e} mean-abs {tot / n:.2e}")
 
 
+def test_full_stats(full):
+    """The device-side statistics of park_forward (park_stats) against the same totals computed on
+    the host from the returned clusterings and selection (exact integers)."""
+    w, Q, K, V, r, ws = full
+    r2 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=("stats",), ws=ws)
+    got = dict(zip(bsa.STATS_FIELDS, np_i(r2["stats"]).tolist()))
+    qo, ko = np_i(r["q_offsets"]), np_i(r["k_offsets"])
+    counts, cols = np_i(r["counts"]), np_i(r["cols"])
+    nq = np.diff(qo, axis=1)
+    nk = np.diff(ko, axis=1)
+    L = np_i(r["sel_keys"])
+    want = {"pairs": int((nq * L).sum()),
+            "padded_pairs": int((((nq + 31) // 32) * 32 * ((L + 31) // 32) * 32).sum()),
+            "blocks": int(sum(int((nk[h][cols[h, i, :counts[h, i]]] > 0).sum())
+                              for h in range(w.heads) for i in range(w.cq) if nq[h, i] > 0)),
+            "live_blocks": int(((nq > 0).sum(1) * (nk > 0).sum(1)).sum()),
+            "work_items": int(((nq + 383) // 384).sum()),
+            "tokens": w.heads * w.n}
+    assert got == want, (got, want)
+    print(f"[full stats] token density {got['pairs'] / (w.heads * w.n ** 2):.4f}, block density "
+          f"{got['blocks'] / got['live_blocks']:.4f}, padded / computed {got['padded_pairs'] / got['pairs']:.4f}, "
+          f"work items {got['work_items']}")
+
+
 def test_full_output_everywhere(full):
     """Every token of every head gets a finite output (every live query block selects at least one
     non-empty key block at p < 1), and a second call is bitwise identical."""
@@ -351,3 +375,69 @@ def test_long_warm_step():
     assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS
     assert np.abs(to64(r1["lse"][h])[tt] - Lo[tt]).max() <= LSE_ABS
     print(f"[long warm step] sampled near-ties {n_near}")
+
+
+def test_long_reuse_and_subset_steps():
+    """Three drifted steps of the long clip after a full anchor step, under the two cheaper policies
+    between anchors. Reuse keeps the anchor's clusterings and selection and recomputes only the
+    attention on the current inputs (PARK, thelatestinai.com page, Table 9: the retrieval is
+    recomputed only at some steps): sampled blocks against the fp64 masked softmax on the drifted
+    inputs. Subset updates re-assign every fourth token, phase = step mod 4 (HyperVAttention page,
+    abstract): the first iteration in lock-step against the oracle on sampled tokens, and the fused
+    entry's key side equal to the subset entry's."""
+    w = synth.WORKLOADS["long"]
+    print(f"\n[full] long reuse / subset steps: H={w.heads} N={w.n}", flush=True)
+    Q, K, V, Qm, Km = synth.make_qkv(w, seed=0, device="cuda", keep_fp32=True)
+    ws = bsa.Workspace()
+    r0 = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=ALL_OUT, ws=ws)
+    anchor = {n: r0[n] for n in ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols")}
+    qc, kc = r0["q_centroids"].clone(), r0["k_centroids"].clone()
+    ql, kl = r0["q_labels"].clone(), r0["k_labels"].clone()
+    h = w.heads - 1
+    rng = np.random.default_rng(23)
+    qp, qo = np_i(anchor["q_perm"][h]), np_i(anchor["q_offsets"][h])
+    kp, ko = np_i(anchor["k_perm"][h]), np_i(anchor["k_offsets"][h])
+    sel = cols_list(np_i(anchor["counts"][h]), np_i(anchor["cols"][h]))
+    near = 0
+    for step in (1, 2, 3):
+        Q = synth.drift_step(w, Qm, 0, step, 0)
+        K = synth.drift_step(w, Km, 0, step, 1)
+        # reuse: the anchor's selection on the drifted inputs
+        out, lse = bsa.park_sparse_attn(Q, K, V, anchor["q_perm"], anchor["q_offsets"], anchor["k_perm"],
+                                        anchor["k_offsets"], anchor["counts"], anchor["cols"], ws=ws)
+        rows = _sample_blocks(qo, rng)[:1]
+        q, x, v = to64(Q[h]), to64(K[h]), to64(V[h])
+        Oo, Lo = O.sparse_attention(q, x, v, qp, qo, kp, ko, sel, w.scale, rows=rows)
+        t = qp[qo[rows[0]]:qo[rows[0] + 1]]
+        e = np.abs(to64(out[h])[t] - Oo[t])
+        assert e.max() <= ATTN_MAX_ABS and e.mean() <= ATTN_MEAN_ABS, (step, e.max(), e.mean())
+        assert np.abs(to64(lse[h])[t] - Lo[t]).max() <= LSE_ABS
+        # subset update of the key side, one iteration, against the oracle on sampled tokens
+        M = bsa.park_qrkc_metric(Q)
+        phase = step % 4
+        prev_c, prev_l = kc.clone(), kl.clone()
+        one = bsa.park_cluster_subset(K, w.ck, 1, 4, phase, prev_c.clone(), prev_l.clone(), bsa.PARK_QRKC, M, ws=ws)
+        lab1 = np_i(one["labels"][h])
+        lab0 = np_i(prev_l[h])
+        subset = O.subset_rows(w.n, 4, phase)
+        keep = np.setdiff1d(np.arange(w.n), subset)
+        np.testing.assert_array_equal(lab1[keep], lab0[keep])
+        g, b = O.consumed_centroids(to64(prev_c[h]), O.QRKC, to64(M[h]), bf16=True)
+        tt = rng.choice(subset, size=SAMPLE_TOKENS, replace=False)
+        n_near, bad = O.assign_near_tie(x[tt], g, b, lab1[tt], TAU)
+        assert bad.size == 0, (step, bad.size)
+        near += n_near
+        co = O.update(x, lab1, w.ck, to64(prev_c[h]))
+        assert np.abs(to64(one["centroids"][h]) - co).max() <= 1e-6 * np.abs(x).max()
+        po, oo = O.cluster_order(lab1, w.ck)
+        np.testing.assert_array_equal(np_i(one["perm"][h]), po)
+        # the fused entry in subset mode (state carried in qc / kc and ql / kl)
+        r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.warm_iters, w.p, seed=0, init=bsa.PARK_INIT_SUBSET,
+                             subset=(4, phase), q_centroids=qc, k_centroids=kc, q_labels=ql, k_labels=kl,
+                             outputs=("k_perm", "counts", "lse"), ws=ws)
+        two = bsa.park_cluster_subset(K, w.ck, w.warm_iters, 4, phase, prev_c.clone(), prev_l.clone(),
+                                      bsa.PARK_QRKC, M, ws=ws)
+        assert torch.equal(two["centroids"], r["k_centroids"]) and torch.equal(two["labels"], kl)
+        assert torch.equal(two["perm"], r["k_perm"])
+        assert torch.isfinite(r["lse"]).all()
+    print(f"[long reuse / subset] sampled subset near-ties: {near}")

@@ -90,6 +90,56 @@ def test_lloyd_lockstep(case, side):
     print(f"[lloyd {side}] assignment near-ties over 3 iterations: {near}")
 
 
+@pytest.mark.parametrize("side", ["q", "k"])
+@pytest.mark.parametrize("stride,phase", [(3, 1), (4, 0), (1, 0)])
+def test_subset_update_lockstep(case, side, stride, phase):
+    """Subset updates (hybrid clustering between anchor steps): the rows phase, phase + stride, ...
+    are re-assigned against the consumed centroids (near-ties counted), every other row keeps its
+    label bit for bit, the order is the stable sort of the labels, and the centroids are the fp64
+    member means. The labels start from a clustering with some rows scrambled, a few of them
+    outside [0, C) (taken as cluster 0)."""
+    w, Q, K, V, M = case
+    X = Q if side == "q" else K
+    C = w.cq if side == "q" else w.ck
+    metric = bsa.PARK_EUCLID if side == "q" else bsa.PARK_QRKC
+    sd = bsa.PARK_SIDE_Q if side == "q" else bsa.PARK_SIDE_K
+    Mp = M if side == "k" else None
+    base = bsa.park_cluster(X, C, 2, metric, Mp, seed=7, side=sd)
+    rng = np.random.default_rng(stride * 10 + phase)
+    lab0 = np_i(base["labels"])
+    scr = rng.random(lab0.shape) < 0.1
+    lab0[scr] = rng.integers(0, C, int(scr.sum()))
+    lab0[:, 5] = C + 3
+    lab0[:, 11] = -2
+    labels = torch.tensor(lab0, dtype=torch.int32, device="cuda")
+    prev = base["centroids"].clone()
+    res = bsa.park_cluster_subset(X, C, 1, stride, phase, base["centroids"], labels, metric, Mp)
+    lab, perm, off, new = np_i(res["labels"]), np_i(res["perm"]), np_i(res["offsets"]), to64(res["centroids"])
+    start = np.where((lab0 < 0) | (lab0 >= C), 0, lab0)
+    rows = O.subset_rows(w.n, stride, phase)
+    keep = np.setdiff1d(np.arange(w.n), rows)
+    xmax = 0.0
+    near = 0
+    for h in range(w.heads):
+        x = to64(X[h])
+        xmax = max(xmax, np.abs(x).max())
+        np.testing.assert_array_equal(lab[h][keep], start[h][keep])
+        Mh = to64(M[h]) if side == "k" else None
+        g, b = O.consumed_centroids(to64(prev[h]), metric, Mh, bf16=_bf(w))
+        n_near, bad = O.assign_near_tie(x[rows], g, b, lab[h][rows], TAU)
+        assert bad.size == 0, f"head {h}: {bad.size} subset labels differ beyond near-ties"
+        near += n_near
+        po, oo = O.cluster_order(lab[h], C)
+        np.testing.assert_array_equal(perm[h], po)
+        np.testing.assert_array_equal(off[h], oo)
+        # the oracle's subset update from the same start (a near-tie would only move a centroid)
+        lo, co = O.lloyd_subset(x, to64(prev[h]), start[h], 1, stride, phase, metric, Mh, bf16=_bf(w))
+        if n_near == 0:
+            np.testing.assert_array_equal(lab[h], lo)
+        assert np.abs(new[h] - O.update(x, lab[h], C, to64(prev[h]))).max() <= 1e-6 * xmax
+    print(f"[subset {side} stride={stride} phase={phase}] near-ties: {near}")
+
+
 @pytest.fixture(scope="module")
 def clustered(case):
     w, Q, K, V, M = case
@@ -140,6 +190,38 @@ def test_select_topp(clustered, p):
             if p >= 1 and Ag[h, i].sum() > 0:
                 assert np.array_equal(c, np.flatnonzero(sizes > 0))
     print(f"[top-p {p}] near-ties: {near}")
+
+
+@pytest.mark.parametrize("bm", [64, 384])
+def test_merge_clusters(clustered, bm):
+    """Tile-aware merging of the query clusters on the top-p selection: groups, merged order,
+    offsets and union selections bit-exact against the oracle's merge; attention over the merged
+    groups against the fp64 masked softmax over each group's union selection."""
+    w, Q, K, V, M, qc, kc = clustered
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    sel = bsa.park_select_topp(A, kc["offsets"], w.p)
+    mg = bsa.park_merge_clusters(qc["perm"], qc["offsets"], kc["offsets"], sel["counts"], sel["cols"], bm=bm)
+    groups = 0
+    for h in range(w.heads):
+        qo = np_i(qc["offsets"][h])
+        sizes = np.diff(np_i(kc["offsets"][h]))
+        cl = cols_list(np_i(sel["counts"][h]), np_i(sel["cols"][h]))
+        group, gsel = O.merge_clusters(np.diff(qo), cl, sizes, bm)
+        perm, off, mcols = O.merged_order(np_i(qc["perm"][h]), qo, group, gsel)
+        roots = sorted(set(group.tolist()))
+        rank = {r: g for g, r in enumerate(roots)}
+        np.testing.assert_array_equal(np_i(mg["group"][h]), [rank[r] for r in group])
+        np.testing.assert_array_equal(np_i(mg["q_perm"][h]), perm)
+        np.testing.assert_array_equal(np_i(mg["q_offsets"][h]), off)
+        cnt = np_i(mg["counts"][h])
+        for g in range(w.cq):
+            np.testing.assert_array_equal(np_i(mg["cols"][h, g, :cnt[g]]), mcols[g])
+        groups += len(roots)
+    out, lse = bsa.park_sparse_attn(Q, K, V, mg["q_perm"], mg["q_offsets"], kc["perm"], kc["offsets"], mg["counts"],
+                                    mg["cols"])
+    worst, mean = _attn_check(w, Q, K, V, mg["q_perm"], mg["q_offsets"], kc["perm"], kc["offsets"], mg["counts"],
+                              mg["cols"], out, lse)
+    print(f"[merge bm={bm}] {w.heads * w.cq} clusters -> {groups} groups; attention max-abs {worst:.2e}")
 
 
 def test_select_topp_hand_fixture():
