@@ -2,9 +2,11 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan] [--no-cpu] [--no-stages]
 python bench.py --sweep        # p x Ck grid on the Wan-shaped layer (one JSON document)
-python bench.py --schedule     # the long clip's 10-step schedule: full K-means at anchors, warm starts
+python bench.py --schedule     # the long clip's 10-step schedule: warm / subset / reuse between anchors
 python bench.py --estimators   # FC / CC / CF / FF block maps: recall and density of top-p / top-k
 python bench.py --sip          # top-k truncation vs SIP sampling with inverse-probability weights
+python bench.py --merge        # tile-aware merging of query clusters: attention time, recall, density
+python bench.py --ablation     # QRKC against Euclidean key clustering (the "w/o QRKC" row)
 
 A step is one park_forward call (QRKC metric, seeded K-means on queries and keys, PAMA map, top-p,
 block-sparse attention) over one synthetic layer already resident in HBM. Prints one JSON line.
@@ -244,75 +246,187 @@ def run_sweep(args, bsa, w0, dev, log):
 
 def run_schedule(args, bsa, w, dev, log):
     """The long clip's denoising schedule (PARK-p2 Table 9: how often the retrieval is recomputed).
-    Inputs drift every step. Two policies on the same inputs:
-    * warm: full K-means (k-means++ and ``iters`` iterations) at the anchor steps, warm start from the
-      previous centroids with ``warm_iters`` iterations otherwise (HyperVAttention's anchor/subset
-      idea, with every token updated);
-    * reuse: the anchor step's clustering and block selection are kept until the next anchor; the
-      steps in between run the sparse attention only.
+    Inputs drift every step. Full K-means (k-means++ and ``iters`` iterations) at the anchor steps;
+    three policies between anchors, each carrying its own state from the last anchor:
+    * warm: warm start from the previous centroids with ``warm_iters`` iterations over every token;
+    * subset: hybrid clustering (HyperVAttention page, abstract): ``warm_iters`` subset updates of
+      every fourth token (phase = step mod 4) from the previous centroids and labels;
+    * reuse: the anchor's clustering and block selection are kept; the step runs the attention only.
     Each step reports ms, token density and recall (from the kernel's log-sum-exp against dense
     attention of the same step)."""
     Q, K, V, Qm, Km = synth.make_qkv(w, seed=args.seed, device=dev, keep_fp32=True)
     ws = bsa.Workspace()
-    qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
-    kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
-    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse")
+    stride = 4
+    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse", "stats")
+    shape_c = lambda c: torch.empty(w.heads, c, w.d, dtype=torch.float32, device=dev)
+    st = {k: {"qc": shape_c(w.cq), "kc": shape_c(w.ck),
+              "ql": torch.zeros(w.heads, w.n, dtype=torch.int32, device=dev),
+              "kl": torch.zeros(w.heads, w.n, dtype=torch.int32, device=dev)} for k in ("warm", "subset")}
+    cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+    cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+
+    def timed(fn, state=None):
+        """fn() twice from the same state (a warm-up call, then the timed one); returns (result, ms)."""
+        saved = {k: v.clone() for k, v in state.items()} if state else None
+        fn()
+        torch.cuda.synchronize()
+        if saved:
+            for k, v in saved.items():
+                state[k].copy_(v)
+        a, b = _events()
+        a.record()
+        r = fn()
+        b.record()
+        torch.cuda.synchronize()
+        return r, a.elapsed_time(b)
+
+    def quality(r, ld, ms):
+        rec = torch.exp(r["lse"] - ld).mean(dim=1)
+        stats = dict(zip(bsa.STATS_FIELDS, r["stats"].tolist()))
+        return {"ms": round(ms, 3), "token_density": round(stats["pairs"] / (w.heads * w.n * w.n), 5),
+                "recall_mean": round(rec.mean().item(), 4), "recall_worst": round(rec.min().item(), 4)}
+
     steps, kept = [], None
     for t in range(w.steps):
         if t > 0:
             Q.copy_(synth.drift_step(w, Qm, args.seed, t, 0))
             K.copy_(synth.drift_step(w, Km, args.seed, t, 1))
         full = t in w.anchors
-        init = bsa.PARK_INIT_KMEANSPP if full else bsa.PARK_INIT_WARM
-        iters = w.iters if full else w.warm_iters
-        fn = lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, iters, w.p, seed=args.seed, init=init,
-                                      q_centroids=qcent, k_centroids=kcent, outputs=outs, ws=ws)
-        qs, ks = qcent.clone(), kcent.clone()
-        fn()  # warm-up call; the timed call repeats it from the same centroids
-        torch.cuda.synchronize()
-        qcent.copy_(qs)
-        kcent.copy_(ks)
-        a, b = _events()
-        a.record()
-        r = fn()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b)
+        entry = {"step": t, "full_kmeans": full}
         if full:
-            kept = {k: r[k].clone() for k in ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols",
-                                                "sel_keys")}
-        # dense log-sum-exp of this step: every key cluster selected
-        cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
-        cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
-        _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
-                                     cols_all, ws=ws)
-        rec = torch.exp(r["lse"] - ld).mean(dim=1)
-        computed, padded, dense = selection_stats(w, r)
-        entry = {"step": t, "full_kmeans": full, "iters": iters,
-                 "warm": {"ms": round(ms, 3), "token_density": round(computed / dense, 5),
-                          "recall_mean": round(rec.mean().item(), 4), "recall_worst": round(rec.min().item(), 4)}}
-        if full:
-            entry["reuse"] = dict(entry["warm"])
+            s0 = st["warm"]
+            r, ms = timed(lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed,
+                                                   q_centroids=s0["qc"], k_centroids=s0["kc"], q_labels=s0["ql"],
+                                                   k_labels=s0["kl"], outputs=outs, ws=ws), s0)
+            for k in ("qc", "kc", "ql", "kl"):
+                st["subset"][k].copy_(s0[k])
+            kept = {k: r[k].clone() for k in ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols")}
+            _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
+                                         cols_all, ws=ws)
+            q = quality(r, ld, ms)
+            entry.update(warm=q, subset=dict(q), reuse=dict(q))
         else:
+            for name, init, sub in (("warm", bsa.PARK_INIT_WARM, (1, 0)),
+                                    ("subset", bsa.PARK_INIT_SUBSET, (stride, t % stride))):
+                s0 = st[name]
+                r, ms = timed(lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, w.warm_iters, w.p, seed=args.seed,
+                                                       init=init, subset=sub, q_centroids=s0["qc"],
+                                                       k_centroids=s0["kc"], q_labels=s0["ql"], k_labels=s0["kl"],
+                                                       outputs=outs, ws=ws), s0)
+                _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"],
+                                             cnt_all, cols_all, ws=ws)
+                entry[name] = quality(r, ld, ms)
             fa = lambda: bsa.park_sparse_attn(Q, K, V, kept["q_perm"], kept["q_offsets"], kept["k_perm"],
                                               kept["k_offsets"], kept["counts"], kept["cols"], ws=ws)
-            fa()
-            torch.cuda.synchronize()
-            a, b = _events()
-            a.record()
-            _, lr = fa()
-            b.record()
-            torch.cuda.synchronize()
+            (_, lr), ms = timed(fa)
+            _, ld = bsa.park_sparse_attn(Q, K, V, kept["q_perm"], kept["q_offsets"], kept["k_perm"],
+                                         kept["k_offsets"], cnt_all, cols_all, ws=ws)
+            qsz = torch.diff(kept["q_offsets"], dim=1).double()
+            ksz = torch.diff(kept["k_offsets"], dim=1).double()
+            # cols is row-padded: entries past counts are not written, so they are masked before lookup
+            valid = torch.arange(w.ck, device=dev)[None, None, :] < kept["counts"][:, :, None]
+            idx = torch.where(valid, kept["cols"].long(), torch.zeros_like(kept["cols"], dtype=torch.long))
+            keys = (torch.gather(ksz, 1, idx.view(w.heads, -1)).view(w.heads, w.cq, w.ck) * valid).sum(-1)
+            pairs = float((qsz * keys).sum())
             rr = torch.exp(lr - ld).mean(dim=1)
-            c2, _, d2 = selection_stats(w, kept)
-            entry["reuse"] = {"ms": round(a.elapsed_time(b), 3), "token_density": round(c2 / d2, 5),
+            entry["reuse"] = {"ms": round(ms, 3), "token_density": round(pairs / (w.heads * w.n * w.n), 5),
                               "recall_mean": round(rr.mean().item(), 4), "recall_worst": round(rr.min().item(), 4)}
         steps.append(entry)
         log(f"schedule {entry}")
-    tot = {k: round(sum(x[k]["ms"] for x in steps), 3) for k in ("warm", "reuse")}
+    pol = ("warm", "subset", "reuse")
+    tot = {k: round(sum(x[k]["ms"] for x in steps), 3) for k in pol}
     print(json.dumps({"schedule": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "p": w.p,
-                      "anchors": list(w.anchors), "steps": steps, "total_ms": tot,
+                      "anchors": list(w.anchors), "warm_iters": w.warm_iters, "subset_stride": stride,
+                      "steps": steps, "total_ms": tot,
                       "ms_per_step": {k: round(v / len(steps), 3) for k, v in tot.items()}}), flush=True)
+
+
+def run_merge(args, bsa, w, dev, log):
+    """Tile-aware merging of query clusters (HyperVAttention page, abstract) on one layer: the top-p
+    selection's attention as is, and after merging the query clusters under the CTA-aligned cost with
+    the attention's 384-query work items (and, for comparison, 32-query tiles): groups, work items,
+    token density (computed pairs), recall against dense attention, merge and attention ms."""
+    Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
+    ws = bsa.Workspace()
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed,
+                         outputs=("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys",
+                                  "stats"), ws=ws)
+    cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+    cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+    _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
+                                 cols_all, ws=ws)
+    ksz = torch.diff(r["k_offsets"], dim=1).double()
+
+    def measure(qp, qo, counts, cols):
+        o, lse = bsa.park_sparse_attn(Q, K, V, qp, qo, r["k_perm"], r["k_offsets"], counts, cols, ws=ws)
+        ms = time_call(lambda: bsa.park_sparse_attn(Q, K, V, qp, qo, r["k_perm"], r["k_offsets"], counts, cols,
+                                                    out=o, lse=lse, ws=ws), 3)
+        rec = torch.exp(lse - ld).mean(dim=1).double()
+        qsz = torch.diff(qo, dim=1).double()
+        # cols is row-padded: entries past counts are not written, so they are masked before any lookup
+        valid = torch.arange(w.ck, device=dev)[None, None, :] < counts[:, :, None]
+        idx = torch.where(valid, cols.long(), torch.zeros_like(cols, dtype=torch.long))
+        keys = (torch.gather(ksz, 1, idx.view(w.heads, -1)).view(w.heads, w.cq, w.ck) * valid).sum(-1)
+        pairs = float((qsz * keys).sum())
+        items = int(((qsz + 383) // 384).sum())
+        return {"attn_ms": round(ms, 3), "token_density": round(pairs / (w.heads * w.n * w.n), 5),
+                "computed_tflops": round(4 * w.d * pairs / (ms * 1e9), 1), "work_items": items,
+                "groups": int((qsz > 0).sum()),
+                "recall_mean": round(float(rec.mean()), 4), "recall_p05": round(float(torch.quantile(rec, 0.05)), 4),
+                "recall_worst": round(float(rec.min()), 4)}
+
+    out = {"merge": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "p": w.p,
+           "base": measure(r["q_perm"], r["q_offsets"], r["counts"], r["cols"])}
+    log(f"merge base {out['base']}")
+    for bm in (384, 32):
+        mg = bsa.park_merge_clusters(r["q_perm"], r["q_offsets"], r["k_offsets"], r["counts"], r["cols"], bm=bm, ws=ws)
+        ms = time_call(lambda: bsa.park_merge_clusters(r["q_perm"], r["q_offsets"], r["k_offsets"], r["counts"],
+                                                       r["cols"], bm=bm, ws=ws), 3)
+        pt = measure(mg["q_perm"], mg["q_offsets"], mg["counts"], mg["cols"])
+        pt["merge_ms"] = round(ms, 3)
+        out[f"merged_bm{bm}"] = pt
+        log(f"merge bm={bm} {pt}")
+    print(json.dumps(out), flush=True)
+
+
+def run_ablation(args, bsa, w, dev, log):
+    """QRKC against Euclidean key clustering (PARK-p2 Table 3 ablation rows, Table 5) on one layer:
+    for each key metric, the recall of the top-p selection (mean, P05, worst over heads), token and
+    block density at p, and on one sampled head (head 0) the QK-score squared error
+    mean_{t,u} (q_t.k_u - q_t.c(u))^2 over 4096 sampled queries and the raw-key squared error
+    mean_u |k_u - c(u)|^2 (c(u) = the key's cluster centroid)."""
+    Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
+    ws = bsa.Workspace()
+    cols_all = torch.arange(w.ck, dtype=torch.int32, device=dev).expand(w.heads, w.cq, w.ck).contiguous()
+    cnt_all = torch.full((w.heads, w.cq), w.ck, dtype=torch.int32, device=dev)
+    out = {"ablation": w.name, "heads": w.heads, "n": w.n, "cq": w.cq, "ck": w.ck, "p": w.p, "metrics": {}}
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed + 77)
+    tq = torch.randperm(w.n, generator=g, device=dev)[:4096]
+    for name, km in (("qrkc", bsa.PARK_QRKC), ("euclid", bsa.PARK_EUCLID)):
+        r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed, kmetric=km,
+                             outputs=("q_perm", "q_offsets", "k_perm", "k_offsets", "k_labels", "lse", "stats"),
+                             ws=ws)
+        ms = time_call(lambda: bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=args.seed, kmetric=km,
+                                                ws=ws), 2)
+        _, ld = bsa.park_sparse_attn(Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], cnt_all,
+                                     cols_all, ws=ws)
+        rec = torch.exp(r["lse"] - ld).mean(dim=1).double()
+        stats = dict(zip(bsa.STATS_FIELDS, r["stats"].tolist()))
+        k0 = K[0].double()
+        c0 = r["k_centroids"][0].double()[r["k_labels"][0].long()]
+        diff = k0 - c0
+        qk = Q[0].double()[tq] @ diff.T
+        entry = {"forward_ms": round(ms, 3),
+                 "recall_mean": round(float(rec.mean()), 4), "recall_p05": round(float(torch.quantile(rec, 0.05)), 4),
+                 "recall_worst": round(float(rec.min()), 4),
+                 "token_density": round(stats["pairs"] / (w.heads * w.n * w.n), 5),
+                 "block_density": round(stats["blocks"] / stats["live_blocks"], 5),
+                 "qk_score_sq_error_head0": round(float((qk * qk).mean()), 4),
+                 "raw_key_sq_error_head0": round(float((diff * diff).sum(1).mean()), 4)}
+        out["metrics"][name] = entry
+        log(f"ablation {name} {entry}")
+    print(json.dumps(out), flush=True)
 
 
 def run_estimators(args, bsa, w, dev, log):
@@ -429,7 +543,11 @@ def main():
     ap.add_argument("--sip", action="store_true",
                     help="top-k truncation vs SIP sampling with inverse-probability weights at equal budgets")
     ap.add_argument("--schedule", action="store_true",
-                    help="the long clip's multi-step schedule with warm starts (own JSON document)")
+                    help="the long clip's multi-step schedule: warm / subset / reuse between anchors (own JSON)")
+    ap.add_argument("--merge", action="store_true",
+                    help="tile-aware merging of query clusters: attention time, recall and density (own JSON)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="QRKC against Euclidean key clustering: recall, density, QK-score error (own JSON)")
     ap.add_argument("--kernel-only", choices=["sparse_attn", "assign", "pama"], default=None,
                     help="profiling aid: prepare one layer, then launch only this stage --steps times, followed "
                          "by a 1 GiB device copy (reference for byte counters); prints no JSON line")
@@ -458,13 +576,20 @@ def main():
     if args.sip:
         run_sip(args, bsa, w, dev, log)
         return
+    if args.merge:
+        run_merge(args, bsa, w, dev, log)
+        return
+    if args.ablation:
+        run_ablation(args, bsa, w, dev, log)
+        return
     Q, K, V = synth.make_qkv(w, seed=args.seed, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready: {w.name} H={w.heads} N={w.n} d={w.d}")
     ws = bsa.Workspace()
     qcent = torch.empty(w.heads, w.cq, w.d, dtype=torch.float32, device=dev)
     kcent = torch.empty(w.heads, w.ck, w.d, dtype=torch.float32, device=dev)
-    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse", "map", "metric")
+    outs = ("q_perm", "q_offsets", "k_perm", "k_offsets", "counts", "cols", "sel_keys", "lse", "map", "metric",
+            "stats")
     if args.kernel_only:
         outs = outs + ("k_labels",)
 
@@ -494,9 +619,12 @@ def main():
     per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (median {per[len(per) // 2]:.3f}, min {per[0]:.3f})")
 
-    # selection statistics of the last step
+    # selection statistics of the last step (park_stats, written by the library on the device)
     n = w.n
-    computed_flops, padded_flops, dense_flops = selection_stats(w, r)
+    stats = dict(zip(bsa.STATS_FIELDS, r["stats"].tolist()))
+    computed_flops = 4.0 * w.d * stats["pairs"]
+    padded_flops = 4.0 * w.d * stats["padded_pairs"]
+    dense_flops = 4.0 * w.d * w.n * w.n * w.heads
     density = computed_flops / dense_flops
 
     res = {"metric": METRIC, "value": round(ms_step, 3), "unit": "ms/layer", "n_gpus": 1, "steps": args.steps,
@@ -509,6 +637,7 @@ def main():
     res["step_ms_min"] = round(per[0], 3)
     res["token_density"] = round(density, 5)
     res["padded_over_computed_flops"] = round(padded_flops / computed_flops, 4)
+    res["work_items"] = stats["work_items"]
 
     if not args.no_stages:
         M = r["metric"]
@@ -547,9 +676,7 @@ def main():
         res["retrieval_over_dense"] = round(retrieval / st["dense_attn"], 4)
         # the same ratio against dense attention at the bf16 matrix-core peak (the ideal kernel)
         res["retrieval_over_dense_at_peak"] = round(retrieval / (dense_flops / (PEAK_BF16_TFLOPS * 1e9)), 4)
-        live_q = (torch.diff(qc["offsets"], dim=1) > 0).sum(1).double()
-        live_k = (torch.diff(kc["offsets"], dim=1) > 0).sum(1).double()
-        res["block_density"] = round(float(sel["counts"].double().sum() / (live_q * live_k).sum()), 5)
+        res["block_density"] = round(stats["blocks"] / stats["live_blocks"], 5)
         res["effective_tflops_dense_equiv"] = round(dense_flops / (ms_step * 1e9), 2)
         res["computed_tflops"] = round(computed_flops / (ms_step * 1e9), 2)
         res["mfma_frac_whole_path"] = round(computed_flops / (ms_step * 1e9) / PEAK_BF16_TFLOPS, 4)
