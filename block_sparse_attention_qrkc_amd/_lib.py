@@ -31,7 +31,7 @@ EXPORTED = [
     "park_qrkc_metric", "park_cluster", "park_retrieve_map", "park_estimator_map", "park_select_topp",
     "park_select_topk", "park_select_sip", "park_sparse_attn", "park_sparse_attn_weighted",
     "park_permute_rows", "park_unpermute_rows", "park_forward", "park_debug_force_seed_timeout",
-    "park_cluster_subset", "park_merge_clusters",
+    "park_cluster_subset", "park_merge_clusters", "park_sparse_attn_noalloc",
 ]
 
 
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
             "park_sparse_attn": (i32, [SP, _P, _P, _P, _P, _P, i32, _P, _P, i32, _P, _P, f32, _P, _P, _P, sz, _P]),
             "park_sparse_attn_weighted": (i32, [SP, _P, _P, _P, _P, _P, i32, _P, _P, i32, _P, _P, _P, f32, _P, _P, _P,
                                                 sz, _P]),
+            "park_sparse_attn_noalloc": (i32, [SP, _P, _P, _P, _P, _P, i32, _P, _P, i32, _P, _P, f32, _P, _P, _P]),
             "park_permute_rows": (i32, [SP, _P, _P, _P, _P]),
             "park_unpermute_rows": (i32, [SP, _P, _P, _P, _P]),
             "park_forward": (i32, [SP, _P, _P, _P, _P, PP, _P, _P, ctypes.POINTER(park_forward_outputs), _P, sz,

@@ -295,6 +295,31 @@ hipError_t side_stream(std::unique_lock<std::mutex>& lock, SideStream** out) {
   return hipSuccess;
 }
 
+// Scratch of park_sparse_attn_noalloc: static device memory of a fixed size, one copy per GPU,
+// held until the process ends. Host code never uses the array's name as an address: on each device
+// its address comes from hipGetSymbolAddress once (with that device current) and is kept here.
+constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+// The current device's scratch address (nullptr and an error on failure).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 park::KppArgs kpp_args(const void* x, const float* metric, int C, int side, float* cent, const ClusterWs& w) {
   return park::KppArgs{x, metric, C, side, cent, w.cand_norm, w.cand_y, w.kpp_psum, w.kpp_sync};
 }
@@ -659,6 +684,31 @@ park_status park_sparse_attn(const park_shape* shape, const void* q, const void*
                             cols, nullptr, scale, out, lse, ws, ws_bytes, stream);
   } catch (...) {
     return fail(PARK_EHIP, "park_sparse_attn: internal error");
+  }
+}
+
+park_status park_sparse_attn_noalloc(const park_shape* shape, const void* q, const void* k, const void* v,
+                                     const int32_t* q_perm, const int32_t* q_offsets, int32_t cq, const int32_t* k_perm,
+                                     const int32_t* k_offsets, int32_t ck, const int32_t* counts, const int32_t* cols,
+                                     float scale, void* out, float* lse, void* stream) {
+  try {
+    park::Dims s;
+    PARK_TRY(check_shape(shape, &s));
+    PARK_TRY(check_clusters(s, cq, "cq"));
+    PARK_TRY(check_clusters(s, ck, "ck"));
+    Carver meas(nullptr);
+    plan_attn(meas, s, cq, ck);
+    if (meas.off > kNoAllocScratchBytes)
+      return fail(PARK_EWORKSPACE,
+                  "park_sparse_attn_noalloc: this shape needs %zu bytes of scratch, more than the %zu bytes it holds "
+                  "(use park_sparse_attn with a workspace)",
+                  meas.off, kNoAllocScratchBytes);
+    void* ptr = nullptr;
+    PARK_TRY(hip_check(scratch_address(&ptr), "park_sparse_attn_noalloc: scratch address"));
+    return sparse_attn_impl("park_sparse_attn_noalloc", shape, q, k, v, q_perm, q_offsets, cq, k_perm, k_offsets, ck,
+                            counts, cols, nullptr, scale, out, lse, ptr, kNoAllocScratchBytes, stream);
+  } catch (...) {
+    return fail(PARK_EHIP, "park_sparse_attn_noalloc: internal error");
   }
 }
 

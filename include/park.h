@@ -283,6 +283,24 @@ park_status park_sparse_attn(const park_shape* shape, const void* q, const void*
                              float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * park_sparse_attn without a workspace argument and without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it). Arguments, results and errors as park_sparse_attn. Its scratch (the per-cluster key runs and
+ * the work order) is a static device array of 96 MiB on every GPU the library runs on, held until
+ * the process ends; shapes that need more (park_workspace_bytes(PARK_ENTRY_SPARSE_ATTN, ...) above
+ * 96 MiB, e.g. heads * cq * (3 ck + 7) * 4 bytes at large cq and ck) are refused with
+ * PARK_EWORKSPACE before anything is enqueued. Every call overwrites what it reads of the scratch
+ * before reading it (nothing needs clearing), and all calls on one GPU share it: calls that overlap
+ * on one GPU (on different streams, or from different threads) race and must be serialised by the
+ * caller.
+ */
+park_status park_sparse_attn_noalloc(const park_shape* shape, const void* q, const void* k, const void* v,
+                                     const int32_t* q_perm, const int32_t* q_offsets, int32_t cq,
+                                     const int32_t* k_perm, const int32_t* k_offsets, int32_t ck,
+                                     const int32_t* counts, const int32_t* cols, float scale, void* out,
+                                     float* lse, void* stream);
+
+/*
  * Block-weighted attention over the selected blocks (AB-Attention page, SIP paragraph: sampled blocks
  * reweighted by the inverse of their inclusion probability). As park_sparse_attn, except that every
  * key of selected block j of row i enters the softmax with weight w = exp(log_w[h, i, j]):

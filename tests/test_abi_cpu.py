@@ -168,6 +168,12 @@ def test_validation_errors(L):
     prm = L.make_params(10, 20, 3, 0.0)
     st, _ = _status(L, "park_forward", bp(sh), FAKE, FAKE, FAKE, FAKE, bp(prm), FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == L.PARK_EINVAL
+    # the allocation-free attention refuses a shape whose scratch would exceed its 96 MiB (checked
+    # before any pointer is touched or anything is enqueued)
+    big = L.park_shape(40, 219600, 128, 1)
+    st, msg = _status(L, "park_sparse_attn_noalloc", bp(big), FAKE, FAKE, FAKE, FAKE, FAKE, 1000, FAKE, FAKE, 2000,
+                      FAKE, FAKE, 0.0, FAKE, None, None)
+    assert st == L.PARK_EWORKSPACE and "scratch" in msg
     # permutation: in place is rejected
     st, msg = _status(L, "park_permute_rows", bp(sh), FAKE, FAKE, FAKE, None)
     assert st == L.PARK_EINVAL and "overlap" in msg
