@@ -57,6 +57,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_decide(const int32_t* __r
   __shared__ int64_t gl[kMaxClusters];   // keys the group rooted at i selects
   __shared__ int parent[kMaxClusters];   // parent[i] == i: i is a root
   __shared__ int best[kMaxClusters];     // proposal of root i this round (-1: none)
+  __shared__ unsigned long long bkey[kMaxClusters];  // (gain << 12) | (4095 - partner), 0: none
   __shared__ int slot[kMaxClusters];     // merged slot of root i
   __shared__ int gq[kMaxClusters];       // queries of slot g
   __shared__ int scratch[17];
@@ -96,25 +97,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_decide(const int32_t* __r
   }
   __syncthreads();
   for (;;) {
-    // proposals: every non-empty root against every other non-empty root
-    for (int a = tid; a < cq; a += kMergeThreads) {
-      int ba = -1;
-      int64_t bg = 0;
-      if (parent[a] == a && nq[a] > 0) {
-        const int64_t ca = tile_cost(nq[a], gl[a], bm);
-        for (int b = 0; b < cq; ++b) {
-          if (b == a || parent[b] != b || nq[b] == 0) continue;
-          const int64_t un = gl[a] + gl[b] - weighted_and(B + (int64_t)a * W, B + (int64_t)b * W, W, nk);
-          const int64_t g = ca + tile_cost(nq[b], gl[b], bm) - tile_cost((int64_t)nq[a] + nq[b], un, bm);
-          if (g > bg) {
-            bg = g;
-            ba = b;
-          }
-        }
-      }
-      best[a] = ba;
-    }
+    // proposals, one pair (a < b) of non-empty roots per thread at a time: each side keeps its
+    // largest positive gain, ties to the lower partner, by a 64-bit max on (gain, 4095 - partner)
+    // (gains stay below 2^50: at most N^2 with N < 2^24; partners below 2048)
+    for (int i = tid; i < cq; i += kMergeThreads) bkey[i] = 0ull;
     if (tid == 0) merged = 0;
+    __syncthreads();
+    for (int64_t e = tid; e < (int64_t)cq * cq; e += kMergeThreads) {
+      const int a = (int)(e / cq), b = (int)(e % cq);
+      if (b <= a || parent[a] != a || parent[b] != b || nq[a] == 0 || nq[b] == 0) continue;
+      const int64_t un = gl[a] + gl[b] - weighted_and(B + (int64_t)a * W, B + (int64_t)b * W, W, nk);
+      const int64_t g = tile_cost(nq[a], gl[a], bm) + tile_cost(nq[b], gl[b], bm) -
+                        tile_cost((int64_t)nq[a] + nq[b], un, bm);
+      if (g > 0) {
+        atomicMax(&bkey[a], ((unsigned long long)g << 12) | (unsigned long long)(4095 - b));
+        atomicMax(&bkey[b], ((unsigned long long)g << 12) | (unsigned long long)(4095 - a));
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < cq; i += kMergeThreads) best[i] = bkey[i] ? 4095 - (int)(bkey[i] & 4095ull) : -1;
     __syncthreads();
     // mutual proposals merge into the lower index (pairs are disjoint: one proposal per root)
     for (int a = tid; a < cq; a += kMergeThreads) {
