@@ -168,32 +168,30 @@ __global__ __launch_bounds__(256) void attn_runs(const int32_t* __restrict__ cou
   }
 }
 
-// Totals of the selection over all heads (park_stats): one work-group strides over the
-// (head, query cluster) pairs and the heads' key clusters; bn = keys per tile of the kernel.
-__global__ __launch_bounds__(1024) void attn_stats(const int32_t* __restrict__ q_offsets,
-                                                   const int32_t* __restrict__ k_offsets, int64_t H, int64_t N,
-                                                   int cq, int ck, const int32_t* __restrict__ glen,
-                                                   const int32_t* __restrict__ nblk,
-                                                   const int32_t* __restrict__ tile_base, int bn,
-                                                   int64_t* __restrict__ stats) {
-  __shared__ int64_t red[6][16];
-  int64_t acc[6] = {0, 0, 0, 0, 0, 0};  // pairs, padded, blocks, live q clusters x live k clusters, items
-  for (int64_t e = threadIdx.x; e < H * cq; e += 1024) {
-    const int64_t h = e / cq;
-    const int i = (int)(e % cq);
-    const int64_t nq = q_offsets[h * (cq + 1) + i + 1] - q_offsets[h * (cq + 1) + i];
-    const int64_t L = glen[e];
+// Totals of the selection (park_stats). attn_stats_head: one work-group per head writes the head's
+// five partial totals (pairs, padded pairs, blocks, live query clusters x live key clusters, work
+// items) to part[h * 8 ..]; attn_stats_sum adds them over the heads in head order (deterministic).
+// bn = keys per tile of the kernel.
+__global__ __launch_bounds__(256) void attn_stats_head(const int32_t* __restrict__ q_offsets,
+                                                       const int32_t* __restrict__ k_offsets, int cq, int ck,
+                                                       const int32_t* __restrict__ glen,
+                                                       const int32_t* __restrict__ nblk,
+                                                       const int32_t* __restrict__ tile_base, int bn,
+                                                       int64_t* __restrict__ part) {
+  __shared__ int64_t red[5][4];
+  const int h = blockIdx.x;
+  const int32_t* qo = q_offsets + (int64_t)h * (cq + 1);
+  const int32_t* ko = k_offsets + (int64_t)h * (ck + 1);
+  int64_t acc[5] = {0, 0, 0, 0, 0};  // pairs, padded, blocks, live query clusters, live key clusters
+  for (int i = threadIdx.x; i < cq; i += 256) {
+    const int64_t nq = qo[i + 1] - qo[i];
+    const int64_t L = glen[(int64_t)h * cq + i];
     acc[0] += nq * L;
     acc[1] += ((nq + 31) / 32) * 32 * ((L + bn - 1) / bn) * bn;
-    acc[2] += nq > 0 ? nblk[e] : 0;
+    acc[2] += nq > 0 ? nblk[(int64_t)h * cq + i] : 0;
+    acc[3] += nq > 0;
   }
-  for (int64_t h = threadIdx.x; h < H; h += 1024) {
-    int64_t lq = 0, lk = 0;
-    for (int i = 0; i < cq; ++i) lq += q_offsets[h * (cq + 1) + i + 1] > q_offsets[h * (cq + 1) + i];
-    for (int j = 0; j < ck; ++j) lk += k_offsets[h * (ck + 1) + j + 1] > k_offsets[h * (ck + 1) + j];
-    acc[3] += lq * lk;
-    acc[4] += tile_base[h * (2 * cq + 1) + cq];
-  }
+  for (int j = threadIdx.x; j < ck; j += 256) acc[4] += ko[j + 1] > ko[j];
   const int l = lane_id(), w = threadIdx.x / kWave;
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
@@ -203,14 +201,29 @@ __global__ __launch_bounds__(1024) void attn_stats(const int32_t* __restrict__ q
     if (l == 0) red[q][w] = v;
   }
   __syncthreads();
-  if (threadIdx.x < 5) {
+  if (threadIdx.x == 0) {
+    int64_t t[5];
+    for (int q = 0; q < 5; ++q) t[q] = ((red[q][0] + red[q][1]) + red[q][2]) + red[q][3];
+    int64_t* o = part + (int64_t)h * 8;
+    o[0] = t[0];
+    o[1] = t[1];
+    o[2] = t[2];
+    o[3] = t[3] * t[4];
+    o[4] = tile_base[(int64_t)h * (2 * cq + 1) + cq];
+  }
+}
+
+__global__ __launch_bounds__(64) void attn_stats_sum(const int64_t* __restrict__ part, int64_t H, int64_t N,
+                                                     int64_t* __restrict__ stats) {
+  const int q = threadIdx.x;
+  if (q < 5) {
     int64_t v = 0;
-    for (int q = 0; q < 16; ++q) v += red[threadIdx.x][q];
-    stats[threadIdx.x] = v;
-  } else if (threadIdx.x == 5) {
+    for (int64_t h = 0; h < H; ++h) v += part[h * 8 + q];
+    stats[q] = v;
+  } else if (q == 5) {
     stats[5] = H * N;
-  } else if (threadIdx.x < 8) {
-    stats[threadIdx.x] = 0;
+  } else if (q < 8) {
+    stats[q] = 0;
   }
 }
 
@@ -963,7 +976,8 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
 int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, s.bf16 ? kBf16BM : kAttnBM) + cq; }
 
 size_t attn_run_ints(const Dims& s, int cq, int ck) {
-  return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq);
+  // + per-head partial statistics: 8 int64 per head, after an alignment of up to 4 bytes
+  return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq) + 16 * (size_t)s.H + 1;
 }
 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
@@ -974,13 +988,17 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
   int32_t* nrun = runs + (size_t)(s.H * cq) * (size_t)run_stride(ck);
   int32_t* glen = nrun + s.H * cq;
   int32_t* nblk = glen + s.H * cq;
+  // per-head partial statistics: 8 int64 per head after the counts, aligned up to 8 bytes
+  int64_t* spart = reinterpret_cast<int64_t*>((reinterpret_cast<uintptr_t>(nblk + s.H * cq) + 7) & ~uintptr_t(7));
   const int weighted = log_w != nullptr;
   attn_runs<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, s.N, cq, ck, log_w,
                                                                1.f / scale, runs, nrun, glen, nblk);
   attn_order<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, glen, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
-  if (stats)
-    attn_stats<<<1, 1024, 0, st>>>(q_offsets, k_offsets, s.H, s.N, cq, ck, glen, nblk, tile_base,
-                                   s.bf16 && s.D == 128 ? kBf16BN : kBN, stats);
+  if (stats) {
+    attn_stats_head<<<(unsigned)s.H, 256, 0, st>>>(q_offsets, k_offsets, cq, ck, glen, nblk, tile_base,
+                                                   s.bf16 && s.D == 128 ? kBf16BN : kBN, spart);
+    attn_stats_sum<<<1, 64, 0, st>>>(spart, s.H, s.N, stats);
+  }
   const dim3 grid((unsigned)attn_max_tiles(s, cq), (unsigned)s.H);
 #define PARK_ATTN(T, D)                                                                                          \
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \

@@ -193,7 +193,7 @@ def test_workspace_bytes(L):
     # the attention keeps per (head, query cluster) at most ck runs of its selected keys (three ints
     # each), so its workspace scales with the selection's own size [heads, cq, ck], not with n
     attn = L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, wan, prm)
-    assert attn <= 40 * 100 * (3 * 500 + 4 + 3) * 4 + 40 * (2 * 100 + 1) * 4 + 1024
+    assert attn <= 40 * 100 * (3 * 500 + 4 + 3) * 4 + 40 * (2 * 100 + 1) * 4 + 40 * 64 + 1024
     assert L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN_WEIGHTED, wan, prm) == attn
     assert L.workspace_bytes(L.PARK_ENTRY_SPARSE_ATTN, L.park_shape(40, 219600, 128, 1), prm) == attn
     # the long clip's whole forward pass fits in 2 GB of workspace (the per-token int arrays, the
