@@ -30,9 +30,10 @@ CFLAGS = [
 ]
 
 
-# Per-file flags. kmeans.hip: MFMA results in ordinary VGPRs (the assignment's argmax reads every
-# accumulator with VALU instructions, which cannot take AGPR operands).
-FILE_FLAGS = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags. kmeans.hip and pama.hip: MFMA results in ordinary VGPRs (the assignment's argmax
+# and the map's exponentials read every accumulator with VALU instructions, which cannot take AGPR
+# operands, so AGPR results would cost a copy each).
+FILE_FLAGS = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "pama.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -52,6 +52,8 @@ __global__ __launch_bounds__(256) void pama_prep(const float* __restrict__ k_cen
   }
 }
 
+constexpr int kPamaTW = 4;  // 16-query tiles per MFMA group of a wave
+
 __device__ __forceinline__ int find_item(const int32_t* cb, int cq, int c) {
   // largest i with cb[i] <= c and cb[i+1] > c
   int lo = 0, hi = cq;  // cb[lo] <= c < cb[hi]
@@ -65,35 +67,12 @@ __device__ __forceinline__ int find_item(const int32_t* cb, int cq, int c) {
   return lo;
 }
 
-// B operand fragments of centroid tile ct (centroid ct * 16 + l % 16, dims kk * 32 + g * 8 .. +7) and
-// its log-size weight. Loads are unconditional (row clamped to ck - 1) so that they stay in flight;
-// columns past ck get weight -inf.
-template <int KS>
-__device__ __forceinline__ void fetch_centroids(const uint16_t* kh, const float* lnh, int ck, int ct, int l, int g,
-                                                u32x4_t* bv, float* ln) {
-  const int j = ct * 16 + l % 16;
-  const int jc = min(j, ck - 1);
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk)
-    bv[kk] = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)jc * (KS * 32) + kk * 32 + g * 8);
-  const float v = lnh[jc];
-  *ln = j < ck ? v : -INFINITY;
-}
-
-// B operand fragments of key tile ct in cluster order (key k_perm[ct * 16 + l % 16], dims kk * 32 +
-// g * 8 .. +7): log-weight 0, -inf past the last key (row clamped).
-template <int KS>
-__device__ __forceinline__ void fetch_keys(const uint16_t* Kh, const int32_t* kp, int64_t nk, int ct, int l, int g,
-                                          u32x4_t* bv, float* ln) {
-  const int64_t p = (int64_t)ct * 16 + l % 16;
-  const int64_t row = kp[p < nk ? p : nk - 1];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk)
-    bv[kk] = *reinterpret_cast<const u32x4_t*>(Kh + row * (KS * 32) + kk * 32 + g * 8);
-  *ln = p < nk ? 0.f : -INFINITY;
-}
-
-template <int D, bool FULL>
+// Work item = up to 256 consecutive cluster-ordered queries (four waves of 64). Column tiles (16
+// key centroids, or with FULL 16 keys in cluster order) pass through LDS: each tile is fetched from
+// memory once per work-group, one 16-byte piece per thread, into a ring of two buffers (one barrier
+// per tile), and every wave reads its MFMA B fragments from there. Rows of a staged tile are
+// padded by 16 bytes, so that the 16 column lanes of a fragment read hit distinct banks.
+template <int D, bool FULL, int TW>
 __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q, int64_t N,
                                                  const int32_t* __restrict__ q_perm,
                                                  const int32_t* __restrict__ q_off, int cq,
@@ -104,9 +83,14 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
                                                  const int32_t* __restrict__ k_perm,
                                                  const int32_t* __restrict__ k_off) {
   constexpr int KS = D / 32;
-  constexpr int TW = 4;  // 16-query tiles per wave: each centroid fragment feeds TW MFMAs
+  // a wave's 64 rows run as 4 / TW groups of TW 16-query tiles (each B fragment feeds TW MFMAs)
+  static_assert(TW == 1 || TW == 2 || TW == 4, "tiles per group");
+  constexpr int RS = D + 8;      // staged row stride in bf16 elements (16 bytes of padding)
+  constexpr int PPR = D / 8;     // 16-byte pieces per row
   __shared__ float colsum[4][kMaxClusters];
+  __shared__ float lns[FULL ? 1 : kMaxClusters];
   __shared__ int koff[FULL ? kMaxClusters + 1 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t btile[2][16 * RS];
   const int h = blockIdx.y;
   const int c = blockIdx.x;
   const int32_t* cb = chunk_base + (int64_t)h * (cq + 1);
@@ -115,31 +99,77 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
   const int32_t* off = q_off + (int64_t)h * (cq + 1);
   const int row0 = off[i] + (c - cb[i]) * kPamaRows;
   const int row_end = min(row0 + kPamaRows, off[i + 1]);
+  const int tid = threadIdx.x;
   const int l = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = tid / kWave;
   const int g = l / 16;  // lane group: rows g*4 .. g*4+3 of a tile
   const uint16_t* Qh = Q + (int64_t)h * N * D;
   const int32_t* ph = q_perm + (int64_t)h * N;
   const uint16_t* kh = khat + (int64_t)h * ck * D;
-  const float* lnh = FULL ? nullptr : logn + (int64_t)h * ck;
   const uint16_t* Kh = FULL ? K + (int64_t)h * Nk * D : nullptr;
   const int32_t* kph = FULL ? k_perm + (int64_t)h * Nk : nullptr;
   // columns: the key centroids, or (FULL) every key in cluster order, whose weights are summed per
   // key cluster
-  const int nct = FULL ? (int)((Nk + 15) / 16) : (ck + 15) / 16;
-  auto fetch = [&](int ct, u32x4_t* bv, float* ln) __attribute__((always_inline)) {
-    if constexpr (FULL)
-      fetch_keys<KS>(Kh, kph, Nk, ct, l, g, bv, ln);
-    else
-      fetch_centroids<KS>(kh, lnh, ck, ct, l, g, bv, ln);
+  const int64_t ncol = FULL ? Nk : ck;
+  const int nct = (int)((ncol + 15) / 16);
+  for (int j = tid; j < 4 * kMaxClusters; j += 256) (&colsum[0][0])[j] = 0.f;
+  if constexpr (FULL) {
+    for (int j = tid; j <= ck; j += 256) koff[j] = k_off[(int64_t)h * (ck + 1) + j];
+  } else {
+    for (int j = tid; j < ck; j += 256) lns[j] = logn[(int64_t)h * ck + j];
+  }
+  // staging: thread tid < 16 * PPR fetches piece tid % PPR of row tid / PPR of a column tile (rows
+  // past the last column are clamped; their weight is -inf)
+  const bool stager = tid < 16 * PPR;
+  const int sr = tid / PPR, sp = tid % PPR;
+  auto gload = [&](int ct) __attribute__((always_inline)) {
+    const int64_t j = min((int64_t)ct * 16 + sr, ncol - 1);
+    const uint16_t* src = FULL ? Kh + (int64_t)kph[j] * D : kh + j * D;
+    return *reinterpret_cast<const u32x4_t*>(src + sp * 8);
   };
-  for (int j = threadIdx.x; j < 4 * kMaxClusters; j += 256) (&colsum[0][0])[j] = 0.f;
-  if constexpr (FULL)
-    for (int j = threadIdx.x; j <= ck; j += 256) koff[j] = k_off[(int64_t)h * (ck + 1) + j];
-  __syncthreads();
+  auto sstore = [&](int buf, u32x4_t v) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4_t*>(&btile[buf][sr * RS + sp * 8]) = v;
+  };
+  // the weight of this lane's column in tile ct (log2 n_j; FULL: 0), -inf past the last column
+  auto weight = [&](int ct) __attribute__((always_inline)) {
+    const int64_t j = (int64_t)ct * 16 + l % 16;
+    if constexpr (FULL)
+      return j < ncol ? 0.f : -INFINITY;
+    else
+      return j < ncol ? lns[j] : -INFINITY;
+  };
+  // One sweep over the column tiles; body(ct, bv, ln) runs on the waves that hold rows. Every wave
+  // takes part in the staging and the barriers.
+  auto sweep = [&](bool active, auto&& body) __attribute__((always_inline)) {
+    u32x4_t nxt = {0u, 0u, 0u, 0u};
+    if (stager) {
+      sstore(0, gload(0));
+      nxt = gload(min(1, nct - 1));
+    }
+    for (int ct = 0; ct < nct; ++ct) {
+      // tile ct is in buffer ct & 1; every wave is done with tile ct - 1, whose buffer is refilled
+      __syncthreads();
+      if (stager && ct + 1 < nct) {
+        sstore((ct + 1) & 1, nxt);
+        nxt = gload(min(ct + 2, nct - 1));
+      }
+      if (active) {
+        u32x4_t bv[KS];
+        const uint16_t* bt = &btile[ct & 1][(l % 16) * RS + g * 8];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) bv[kk] = *reinterpret_cast<const u32x4_t*>(bt + kk * 32);
+        body(ct, bv, weight(ct));
+      }
+    }
+    __syncthreads();  // the buffers are free for the next sweep
+  };
 
-  const int w0 = row0 + w * 16 * TW;  // this wave's first row
-  if (w0 < row_end) {
+  constexpr float kRaise = 16.f;
+  const float c1 = scale * 1.4426950408889634f;
+  int cl = 0;  // FULL: the key cluster of this lane's column (advances with the tiles)
+  for (int grp = 0; grp < 4 / TW; ++grp) {
+    const int w0 = row0 + w * 64 + grp * 16 * TW;  // this group's first row
+    const bool active = w0 < row_end;
     // A operands: query row w0 + t*16 + l%16, dims kk*32 + g*8 .. +7
     u32x4_t qa[TW][KS];
 #pragma unroll
@@ -155,11 +185,9 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       }
     }
     // Logits in base 2: lg2 = acc * scale * log2(e) + log2(n_j). Pass 1 keeps, per lane and row, a
-    // reference r and the sum of 2^(lg2 - r) over this lane's centroid columns. r is raised only
-    // when a logit exceeds it by more than 2^kRaise (first tile, or rarely later), so the common
-    // step is one fma, one subtraction, one exp2 and one add per logit.
-    constexpr float kRaise = 16.f;
-    const float c1 = scale * 1.4426950408889634f;
+    // reference r and the sum of 2^(lg2 - r) over this lane's columns. r is raised only when a
+    // logit exceeds it by more than kRaise (first tile, or rarely later), so the common step is
+    // one fma, one subtraction, one exp2 and one add per logit.
     float r[TW][4], s[TW][4];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
@@ -168,13 +196,7 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
         r[t][e] = -1e30f;  // finite, so that an empty column (-inf) never meets -inf - -inf
         s[t][e] = 0.f;
       }
-    u32x4_t bv[KS];
-    float ln;
-    fetch(0, bv, &ln);
-    for (int ct = 0; ct < nct; ++ct) {
-      u32x4_t bn[KS];
-      float lnn;
-      fetch(min(ct + 1, nct - 1), bn, &lnn);
+    sweep(active, [&](int ct, const u32x4_t* bv, float ln) __attribute__((always_inline)) {
       float lg[TW][4], dmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
@@ -201,10 +223,7 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       for (int t = 0; t < TW; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[t][e] += __builtin_amdgcn_exp2f(lg[t][e] - r[t][e]);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) bv[kk] = bn[kk];
-      ln = lnn;
-    }
+    });
     // merge (reference, sum) across the 16 lanes (columns) of each group; the row's offset
     // off = r + log2(sum) makes 2^(lg2 - off) its normalised weight (off = +inf for rows that are
     // out of range, whose weights are then 0)
@@ -226,13 +245,9 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       }
     }
     // pass 2: accumulate normalised weights 2^(lg2 - off) into the wave's column sums
-    fetch(0, bv, &ln);
-    int cl = 0;  // FULL: the key cluster of this lane's column (advances with the tiles)
-    for (int ct = 0; ct < nct; ++ct) {
-      const int j = ct * 16 + l % 16;
-      u32x4_t bn[KS];
-      float lnn;
-      fetch(min(ct + 1, nct - 1), bn, &lnn);
+    cl = 0;
+    sweep(active, [&](int ct, const u32x4_t* bv, float ln) __attribute__((always_inline)) {
+      const int64_t j = (int64_t)ct * 16 + l % 16;
       float cs = 0.f;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
@@ -246,18 +261,14 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
       cs += __shfl_xor(cs, 32, kWave);
       if constexpr (FULL) {
         while (cl < ck && koff[cl + 1] <= j) ++cl;
-        if (g == 0 && j < Nk) atomicAdd(&colsum[w][cl], cs);
+        if (g == 0 && j < ncol) atomicAdd(&colsum[w][cl], cs);
       } else {
-        if (g == 0 && j < ck) colsum[w][j] = cs;
+        if (g == 0 && j < ncol) colsum[w][j] += cs;
       }
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) bv[kk] = bn[kk];
-      ln = lnn;
-    }
+    });
   }
-  __syncthreads();
   float* out = partial + ((int64_t)h * max_chunks + c) * ck;
-  for (int j = threadIdx.x; j < ck; j += 256) out[j] = ((colsum[0][j] + colsum[1][j]) + colsum[2][j]) + colsum[3][j];
+  for (int j = tid; j < ck; j += 256) out[j] = ((colsum[0][j] + colsum[1][j]) + colsum[2][j]) + colsum[3][j];
 }
 
 // fp32 data: one thread per query row, fp64 logits and weights, block-wide column sums.
@@ -340,11 +351,11 @@ hipError_t launch_pama(const Dims& s, const void* q, const int32_t* q_perm, cons
     const dim3 pg((unsigned)ceil_div((int64_t)ck * s.D, 256), (unsigned)s.H);
     pama_prep<<<pg, 256, 0, st>>>(k_cent, k_offsets, ck, (int)s.D, static_cast<uint16_t*>(khat), logn);
     if (s.D == 128)
-      pama_bf16<128, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+      pama_bf16<128, false, kPamaTW><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
                                                   static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base,
                                                   maxc, partial, nullptr, 0, nullptr, nullptr);
     else
-      pama_bf16<64, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
+      pama_bf16<64, false, kPamaTW><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q), s.N, q_perm, q_offsets, cq,
                                                  static_cast<const uint16_t*>(khat), logn, ck, scale, chunk_base,
                                                  maxc, partial, nullptr, 0, nullptr, nullptr);
   } else {
@@ -405,10 +416,10 @@ hipError_t launch_block_mass(const Dims& s, const void* q, const int32_t* q_perm
   const uint16_t* qh = static_cast<const uint16_t*>(q);
   const uint16_t* kh = static_cast<const uint16_t*>(k);
   if (s.D == 128)
-    pama_bf16<128, true><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
+    pama_bf16<128, true, kPamaTW><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
                                                maxc, partial, kh, nk, k_perm, k_offsets);
   else
-    pama_bf16<64, true><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
+    pama_bf16<64, true, kPamaTW><<<grid, 256, 0, st>>>(qh, s.N, q_perm, q_offsets, cq, nullptr, nullptr, ck, scale, chunk_base,
                                               maxc, partial, kh, nk, k_perm, k_offsets);
   pama_reduce<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(partial, q_offsets, chunk_base, cq, ck, maxc, map);
   return hipGetLastError();
