@@ -569,19 +569,19 @@ __device__ __forceinline__ void tr_read8(u32x2_t (&r)[8], const uint32_t (&a)[8]
       : "memory");
 }
 // One dword.
-__device__ __forceinline__ int lds_read_b32(uint32_t addr) {
+[[maybe_unused]] __device__ __forceinline__ int lds_read_b32(uint32_t addr) {
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
 // Two dwords.
-__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
+[[maybe_unused]] __device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
   u32x2_t v;
   asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
 // One dword written (the counted waits and barriers order it).
-__device__ __forceinline__ void lds_write_b32(uint32_t addr, float v) {
+[[maybe_unused]] __device__ __forceinline__ void lds_write_b32(uint32_t addr, float v) {
   asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
