@@ -30,10 +30,11 @@ CFLAGS = [
 ]
 
 
-# Per-file flags. kmeans.hip and pama.hip: MFMA results in ordinary VGPRs (the assignment's argmax
-# and the map's exponentials read every accumulator with VALU instructions, which cannot take AGPR
-# operands, so AGPR results would cost a copy each).
-FILE_FLAGS = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "pama.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags. kmeans.hip, pama.hip and metric.hip: MFMA results in ordinary VGPRs (the
+# assignment's argmax, the map's exponentials and the metric's fp64 flushes read every accumulator
+# with VALU instructions, which cannot take AGPR operands, so AGPR results would cost a copy each).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+FILE_FLAGS = {"kmeans.hip": _VGPR_FORM, "pama.hip": _VGPR_FORM, "metric.hip": _VGPR_FORM}
 
 
 def _compile(src: str) -> str:

@@ -165,4 +165,28 @@ __device__ __forceinline__ uint64_t splitmix_first(uint64_t seed) {
   return z ^ (z >> 31);
 }
 
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+#define PARK_LDS __attribute__((address_space(3)))
+
+// Chunk swizzle of LDS row r. Two read patterns must be bank-conflict free:
+//  - K (ds_read_b128): a 16-lane group reads one logical chunk of rows {0-3, 16-19, 4-7, 20-23}
+//    (or the same set + 8), so those 16 rows need distinct swizzles (and, for 8-lane phases,
+//    distinct low 3 bits within {0-3, 16-19} and within {4-7, 20-23});
+//  - V (ds_read_b64_tr_b16): a half-wave reads an aligned group of four chunks from four
+//    consecutive rows 4a..4a+3 (a quarter-wave: two chunks), so bits 2-3 (and bits 1-2) of the
+//    swizzle must differ across those four rows.
+// D = 128 (16 chunks per row): sw = 2 (g ^ 2g) ^ ((r >> 2) & 1) * 2 ^ ((r >> 4) & 1), g = r & 3,
+// i.e. {0, 6, 12, 10} by r & 3 with the bit-0/bit-1 flips separating the row quartets.
+// D = 64 (8 chunks, two rows per 256-byte bank sweep): rows of equal parity in a K group need
+// distinct swizzles, rows r and r + 2 of a V quartet need different bit 2.
+template <int CPR>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (CPR == 16) {
+    const int g = r & 3;
+    return (2 * (g ^ (g << 1))) ^ (((r >> 2) & 1) << 1) ^ ((r >> 4) & 1);
+  } else {
+    return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+  }
+}
+
 }  // namespace park
