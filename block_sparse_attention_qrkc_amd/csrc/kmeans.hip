@@ -1050,6 +1050,246 @@ __global__ __launch_bounds__(256) void assign_f32(const float* __restrict__ X, i
   if (p < M) labels[(int64_t)h * N + row] = bi;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Fused Euclidean Lloyd step (bf16 data, at most 128 clusters): the assignment and the per-cluster
+// sums of the members in one pass over the points
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kFuseT = 128;        // points per tile
+constexpr int kFuseThreads = 512;  // eight waves
+
+// Work-group (g, h) takes the tiles [g nt / P, (g + 1) nt / P) of head h (nt tiles of 128 points,
+// P work-groups per head), staged in LDS in two buffers (rows XOR-swizzled by 16-byte chunk,
+// chunk_swz; the loads of a tile are issued two tiles ahead). Per tile:
+//  A. the assignment exactly as assign_bf16 computes it (same MFMAs, accumulators started at
+//     -b_j/2, the same packed-key argmax): wave w takes the 32 points 32 (w % 4) .. and the
+//     clusters 64 (w / 4) .. + 63; the two cluster halves of a point are merged in LDS (larger top
+//     20 bits of the score, ties to the lower index, as the sequential scan over tiles gives);
+//  B. the member sums S[c][d] += sum_p [label_p == c] x_p[d]: 32x32x16 MFMAs of a 0/1 matrix built
+//     from the labels and the points (transposing LDS reads, eight consecutive points of one
+//     dimension per lane for both factors); wave w owns the clusters 32 (w / 2) .. + 31 and the
+//     dimensions (D / 2) (w % 2) .. ; each tile's fp32 sums (at most 128 terms) are added into
+//     fp64 accumulators in tile order, so the sums do not depend on scheduling.
+// Outputs: the labels, and per work-group the fp64 sums [C][D] and the member counts [C].
+template <int D>
+__global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __restrict__ X, int64_t N, int C,
+                                                            const uint16_t* __restrict__ G,
+                                                            const float* __restrict__ b,
+                                                            int32_t* __restrict__ labels, double* __restrict__ psum,
+                                                            int32_t* __restrict__ pcnt, int P) {
+  constexpr int KS = D / 16;               // 16-dimension MFMA steps of the assignment
+  constexpr int STR = D + 8;               // padded centroid row (bf16 elements)
+  constexpr int CPR = D / 8;               // 16-byte chunks per point row
+  constexpr int DTW = D / 64;              // 32-dimension tiles per wave in the sums
+  constexpr int LOADS = kFuseT * CPR / kFuseThreads;  // 16-byte loads per thread and tile
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][kFuseT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t gl[kFuseT * STR];
+  __shared__ float hb[kFuseT];
+  __shared__ float hbt[2][kFuseT];  // per cluster half: best top-20-bit score of each point
+  __shared__ int hbi[2][kFuseT];    // and its cluster
+  __shared__ __attribute__((aligned(16))) int lab[kFuseT];
+  __shared__ int cnt[kFuseT];
+  const int h = blockIdx.y;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hl = l / 32;
+  const int g16 = l / 16, i16 = l % 16;
+  const int64_t nt = (N + kFuseT - 1) / kFuseT;
+  const int64_t tb = (int64_t)g * nt / P, te = (int64_t)(g + 1) * nt / P;
+  const uint16_t* Xh = X + (int64_t)h * N * D;
+
+  // centroids (rows past C: zero, score -FLT_MAX) and counts
+  for (int e = tid; e < kFuseT * (D / 8); e += kFuseThreads) {
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < C) v = *reinterpret_cast<const u32x4_t*>(G + ((int64_t)h * C + r) * D + c8 * 8);
+    *reinterpret_cast<u32x4_t*>(&gl[r * STR + c8 * 8]) = v;
+  }
+  for (int r = tid; r < kFuseT; r += kFuseThreads) {
+    hb[r] = r < C ? -0.5f * b[(int64_t)h * C + r] : -FLT_MAX;
+    cnt[r] = 0;
+  }
+
+  // staging of tile t: pieces e = tid + 512 q: point row e / CPR, chunk e % CPR (rows past N: zero)
+  auto gload = [&](u32x4_t(&pre)[LOADS], int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const int e = tid + q * kFuseThreads;
+      const int64_t row = min(t * kFuseT + e / CPR, N - 1);
+      pre[q] = *reinterpret_cast<const u32x4_t*>(Xh + row * D + (e % CPR) * 8);
+    }
+  };
+  auto sstore = [&](const u32x4_t(&pre)[LOADS], int buf, int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const int e = tid + q * kFuseThreads;
+      const int r = e / CPR, c = e % CPR;
+      u32x4_t v = pre[q];
+      if (t * kFuseT + r >= N) v = u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(&xt[buf][r * D + (c ^ chunk_swz<CPR>(r)) * 8]) = v;
+    }
+  };
+
+  // phase A: this lane's point (rows permuted so that each 16-lane group reads distinct swizzles)
+  const int pw = w & 3, ch = w >> 2;
+  const int r32 = l % 32;
+  const int prow = pw * 32 + ((r32 / 4) % 2) * 16 + (r32 / 8) * 4 + r32 % 4;
+  const int pswz = chunk_swz<CPR>(prow);
+  // phase B: transposing-read offsets (bf16 elements) of dimension tile dt, sub-tile st, half kh,
+  // rows z
+  const int cw = w >> 1, dt0 = (w & 1) * DTW;
+  int tofs[DTW][4][2][2];
+#pragma unroll
+  for (int x = 0; x < DTW; ++x) {
+    const int D0 = (dt0 + x) * 32 + 16 * (g16 & 1);
+    const int cc = (D0 + 4 * (i16 % 4)) / 8;
+    const int half = (i16 % 4) & 1;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const int R = st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4 + 4 * z;
+          tofs[x][st][kh][z] = R * D + (cc ^ chunk_swz<CPR>(R)) * 8 + half * 4;
+        }
+  }
+  f32x16_t sacc[DTW];
+  double s64[DTW][16];
+#pragma unroll
+  for (int x = 0; x < DTW; ++x)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s64[x][i] = 0.0;
+
+  auto tile = [&](u32x4_t(&pre)[LOADS], int buf, int64_t t) __attribute__((always_inline)) {
+    // tile t into buffer buf (read two tiles ago, before the previous tile's last barrier)
+    sstore(pre, buf, t);
+    __syncthreads();
+    if (t + 2 < te) gload(pre, t + 2);
+    // ---- A: scores of this lane's point against the clusters 64 ch .. + 63
+    float best = -FLT_MAX, bestt = -FLT_MAX;
+    int btile = 2 * ch;
+#pragma unroll
+    for (int cti = 0; cti < 2; ++cti) {
+      const int ct = 2 * ch + cti;
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = hb[ct * 32 + (i / 4) * 8 + hl * 4 + i % 4];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&gl[(ct * 32 + l % 32) * STR + kk * 16 + hl * 8]);
+        const u32x4_t xb = *reinterpret_cast<const u32x4_t*>(&xt[buf][prow * D + ((2 * kk + hl) ^ pswz) * 8]);
+        acc = mfma32(a, xb, acc);
+      }
+      float tk = max3f(asg_key(acc[0], 15u), asg_key(acc[1], 14u), asg_key(acc[2], 13u));
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) tk = max3f(tk, asg_key(acc[i], 15u - i), asg_key(acc[i + 1], 14u - i));
+      tk = max3f(tk, asg_key(acc[15], 0u), asg_key(acc[15], 0u));
+      const float tt = asg_trunc(tk);
+      if (tt > bestt) {
+        best = tk;
+        bestt = tt;
+        btile = ct;
+      }
+    }
+    {
+      const int slot = 15 - (int)(__float_as_uint(best) & 15u);
+      int bi = btile * 32 + (slot / 4) * 8 + hl * 4 + slot % 4;
+      const float ob = __shfl_xor(bestt, 32, kWave);
+      const int oi = __shfl_xor(bi, 32, kWave);
+      if (ob > bestt || (ob == bestt && oi < bi)) bi = oi;
+      if (hl == 0) {
+        hbt[ch][prow] = fmaxf(bestt, ob);
+        hbi[ch][prow] = bi;
+      }
+    }
+    __syncthreads();
+    // merge the cluster halves (the second only when strictly better: ties keep the lower index)
+    if (tid < kFuseT) {
+      const int64_t p = t * kFuseT + tid;
+      int lb = hbt[1][tid] > hbt[0][tid] ? hbi[1][tid] : hbi[0][tid];
+      if (p < N) {
+        labels[(int64_t)h * N + p] = lb;
+        atomicAdd(&cnt[lb], 1);
+      } else {
+        lb = -1;
+      }
+      lab[tid] = lb;
+    }
+    __syncthreads();
+    // ---- B: member sums of this tile
+#pragma unroll
+    for (int x = 0; x < DTW; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[x][i] = 0.f;
+    const int cme = cw * 32 + l % 32;
+    const PARK_LDS uint16_t* xs = (const PARK_LDS uint16_t*)&xt[buf][0];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int base = st * 32 + 16 * hl + 8 * kh;
+        const u32x4_t la = *reinterpret_cast<const u32x4_t*>(&lab[base]);
+        const u32x4_t lb = *reinterpret_cast<const u32x4_t*>(&lab[base + 4]);
+        const uint32_t one = 0x3F80u;  // bf16 1.0
+        u32x4_t oh;
+        oh[0] = ((int)la[0] == cme ? one : 0u) | (((int)la[1] == cme ? one : 0u) << 16);
+        oh[1] = ((int)la[2] == cme ? one : 0u) | (((int)la[3] == cme ? one : 0u) << 16);
+        oh[2] = ((int)lb[0] == cme ? one : 0u) | (((int)lb[1] == cme ? one : 0u) << 16);
+        oh[3] = ((int)lb[2] == cme ? one : 0u) | (((int)lb[3] == cme ? one : 0u) << 16);
+#pragma unroll
+        for (int x = 0; x < DTW; ++x) {
+          const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(xs + tofs[x][st][kh][0]));
+          const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(xs + tofs[x][st][kh][1]));
+          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, r0), u1 = __builtin_bit_cast(u32x2_t, r1);
+          sacc[x] = mfma32(oh, u32x4_t{u0[0], u0[1], u1[0], u1[1]}, sacc[x]);
+        }
+      }
+#pragma unroll
+    for (int x = 0; x < DTW; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s64[x][i] += (double)sacc[x][i];
+  };
+
+  u32x4_t pa[LOADS], pb[LOADS];
+  if (tb < te) gload(pa, tb);
+  if (tb + 1 < te) gload(pb, tb + 1);
+  for (int64_t t = tb; t < te; t += 2) {
+    tile(pa, 0, t);
+    if (t + 1 < te) tile(pb, 1, t + 1);
+  }
+  __syncthreads();  // counts complete
+  // element i of lane l in sums tile (cw, dt): cluster cw * 32 + (i / 4) * 8 + (l / 32) * 4 + i % 4,
+  // dimension dt * 32 + l % 32
+  double* ps = psum + ((int64_t)h * P + g) * C * D;
+#pragma unroll
+  for (int x = 0; x < DTW; ++x)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = cw * 32 + (i / 4) * 8 + (l / 32) * 4 + i % 4;
+      if (c < C) ps[(int64_t)c * D + (dt0 + x) * 32 + l % 32] = s64[x][i];
+    }
+  for (int c = tid; c < C; c += kFuseThreads) pcnt[((int64_t)h * P + g) * C + c] = cnt[c];
+}
+
+// Per (cluster j, head): the member mean from the work-groups' sums (added in work-group order);
+// empty clusters keep their centroid.
+__global__ __launch_bounds__(128) void lloyd_fused_means(const double* __restrict__ psum,
+                                                         const int32_t* __restrict__ pcnt, int C, int D, int P,
+                                                         float* __restrict__ cent) {
+  const int j = blockIdx.x, h = blockIdx.y;
+  int n = 0;
+  for (int g = 0; g < P; ++g) n += pcnt[((int64_t)h * P + g) * C + j];
+  if (n == 0) return;
+  for (int d = threadIdx.x; d < D; d += 128) {
+    double s = 0.0;
+    for (int g = 0; g < P; ++g) s += psum[(((int64_t)h * P + g) * C + j) * D + d];
+    cent[((int64_t)h * C + j) * D + d] = (float)(s / (double)n);
+  }
+}
+
 // Labels outside [0, C) (a caller's stale buffer) become cluster 0, so that the sort and update
 // of a subset step never index outside their tables.
 __global__ void clamp_labels(int32_t* __restrict__ labels, int64_t n, int C) {
@@ -1465,6 +1705,31 @@ hipError_t launch_assign(const Dims& s, const void* x, int C, const void* g, con
       assign_f32<64><<<grid, 256, 0, st>>>(static_cast<const float*>(x), s.N, C, static_cast<const float*>(g), b,
                                            labels, M, stride, phase);
   }
+  return hipGetLastError();
+}
+
+int fused_parts(const Dims& s, int C) {
+  if (!s.bf16 || (s.D != 128 && s.D != 64) || C > kFuseT || C < 1) return 0;
+  const int64_t nt = ceil_div(s.N, kFuseT);
+  int64_t P = kFuseCUs / s.H;
+  if (P < 1) P = 1;
+  if (P > kFuseMaxParts) P = kFuseMaxParts;
+  if (P > nt) P = nt;
+  return (int)P;
+}
+
+hipError_t launch_lloyd_fused(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
+                              double* psum, int32_t* pcnt, float* cent, hipStream_t st) {
+  const int P = fused_parts(s, C);
+  if (P == 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)P, (unsigned)s.H);
+  if (s.D == 128)
+    lloyd_fused<128><<<grid, kFuseThreads, 0, st>>>(static_cast<const uint16_t*>(x), s.N, C,
+                                                    static_cast<const uint16_t*>(g), b, labels, psum, pcnt, P);
+  else
+    lloyd_fused<64><<<grid, kFuseThreads, 0, st>>>(static_cast<const uint16_t*>(x), s.N, C,
+                                                   static_cast<const uint16_t*>(g), b, labels, psum, pcnt, P);
+  lloyd_fused_means<<<dim3((unsigned)C, (unsigned)s.H), 128, 0, st>>>(psum, pcnt, C, (int)s.D, P, cent);
   return hipGetLastError();
 }
 

@@ -103,9 +103,18 @@ struct ClusterWs {
   int32_t* table;
   void* g;
   float* b;
+  double* fuse_sum = nullptr;   // fused Euclidean Lloyd step: per work-group member sums
+  int32_t* fuse_cnt = nullptr;  // and member counts (NULL: the step runs unfused)
 };
 ClusterWs plan_cluster(Carver& cv, const park::Dims& s, int C, bool qrkc) {
   ClusterWs w;
+  if (!qrkc) {
+    const int P = park::fused_parts(s, C);
+    if (P > 0) {
+      w.fuse_sum = cv.take<double>((size_t)s.H * P * C * s.D);
+      w.fuse_cnt = cv.take<int32_t>((size_t)s.H * P * C);
+    }
+  }
   const size_t S = (size_t)park::kpp_candidates(s.N, C);
   w.cand_norm = cv.take<double>((size_t)s.H * S);
   w.cand_y = qrkc ? cv.take<float>((size_t)s.H * S * s.D) : nullptr;
@@ -247,7 +256,9 @@ size_t forward_ws_bytes(const park::Dims& s, const park_params& p) {
 }
 
 // Lloyd iterations shared by park_cluster and park_forward: (g, b) of the current centroids, then
-// per iteration assign -> stable sort -> update (which also prepares (g, b) for the next one).
+// per iteration assign -> stable sort -> update (which also prepares (g, b) for the next one). A
+// Euclidean bf16 side with at most 128 clusters runs the fused step instead (same labels; means
+// from per-tile fp32 sums added in fp64) and sorts once at the end.
 // With stride > 1 (a subset update) only the rows phase, phase + stride, ... are re-assigned; the
 // others keep the labels already in `labels`, which are first clamped into [0, C).
 hipError_t run_lloyd(const park::Dims& s, const void* x, const float* metric, int C, int iters, float* cent,
@@ -255,6 +266,16 @@ hipError_t run_lloyd(const park::Dims& s, const void* x, const float* metric, in
                      int stride = 1, int phase = 0) {
   if (iters == 0) return hipSuccess;
   hipError_t e = park::launch_update(s, x, C, nullptr, nullptr, cent, 0, metric, w.g, w.b, st);
+  if (metric == nullptr && stride == 1 && w.fuse_sum != nullptr) {
+    // Euclidean side with few clusters: assignment and member means in one pass per iteration,
+    // the cluster order once after the last
+    for (int it = 0; it < iters && e == hipSuccess; ++it) {
+      e = park::launch_lloyd_fused(s, x, C, w.g, w.b, labels, w.fuse_sum, w.fuse_cnt, cent, st);
+      if (e == hipSuccess) e = park::launch_update(s, x, C, nullptr, nullptr, cent, 0, nullptr, w.g, w.b, st);
+    }
+    if (e == hipSuccess) e = park::launch_sort(s, C, labels, w.table, perm, offsets, st);
+    return e;
+  }
   if (e == hipSuccess && stride > 1) e = park::launch_clamp_labels(s, C, labels, st);
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
     e = park::launch_assign(s, x, C, w.g, w.b, labels, st, stride, phase);

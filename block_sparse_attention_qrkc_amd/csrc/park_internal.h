@@ -52,6 +52,15 @@ struct KppArgs {
 // k-means++ seeding of one or two sides in a single launch.
 // status (device, may be NULL): kSeedTimeout is or-ed in when a cooperative exchange timed out.
 hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t seed, int* status, hipStream_t st);
+// Fused Euclidean Lloyd step (bf16, D = 64 or 128, at most 128 clusters): labels of every point
+// and the member means into cent (empty clusters keep theirs); the consumed form (g, b) is then
+// recomputed by launch_update. fused_parts gives the work-groups per head (0: not applicable);
+// psum holds H * parts * C * D doubles, pcnt H * parts * C ints.
+constexpr int kFuseCUs = 256;      // work-groups per layer the split aims at (one per CU)
+constexpr int kFuseMaxParts = 32;  // work-groups per head at most
+int fused_parts(const Dims& s, int C);
+hipError_t launch_lloyd_fused(const Dims& s, const void* x, int C, const void* g, const float* b, int32_t* labels,
+                              double* psum, int32_t* pcnt, float* cent, hipStream_t st);
 // Centroid means (do_update) and the consumed form (g, b) of the centroids for the next assignment.
 hipError_t launch_update(const Dims& s, const void* x, int C, const int32_t* perm, const int32_t* offsets, float* cent,
                          int do_update, const float* metric, void* g, float* b, hipStream_t st);
