@@ -90,6 +90,36 @@ def test_lloyd_lockstep(case, side):
     print(f"[lloyd {side}] assignment near-ties over 3 iterations: {near}")
 
 
+@pytest.mark.parametrize("name", ["small", "small64"])
+def test_fused_step_empty_cluster(name):
+    """Euclidean bf16 sides with at most 128 clusters run the fused step (assignment and member sums
+    in one pass). A centroid moved far from every point draws no members and keeps its value; the
+    labels are the assignment against the consumed centroids (near-ties counted) and every other
+    centroid is the fp64 mean of its members."""
+    w = SMALL[name]
+    Q, K, V = inputs(w)
+    C = w.cq
+    cent = bsa.park_cluster(Q, C, 0, bsa.PARK_EUCLID, seed=3, side=bsa.PARK_SIDE_Q)["centroids"]
+    cent[:, 5] = 1.0e3
+    prev = to64(cent)
+    res = bsa.park_cluster(Q, C, 1, bsa.PARK_EUCLID, init=bsa.PARK_INIT_WARM, side=bsa.PARK_SIDE_Q, centroids=cent)
+    lab, perm, off, new = np_i(res["labels"]), np_i(res["perm"]), np_i(res["offsets"]), to64(res["centroids"])
+    near = 0
+    for h in range(w.heads):
+        x = to64(Q[h])
+        assert not np.any(lab[h] == 5)
+        np.testing.assert_array_equal(new[h][5], prev[h][5])
+        g, b = O.consumed_centroids(prev[h], O.EUCLID, None, bf16=True)
+        n_near, bad = O.assign_near_tie(x, g, b, lab[h], TAU)
+        assert bad.size == 0, f"head {h}: {bad.size} labels differ beyond near-ties"
+        near += n_near
+        po, oo = O.cluster_order(lab[h], C)
+        np.testing.assert_array_equal(perm[h], po)
+        np.testing.assert_array_equal(off[h], oo)
+        assert np.abs(new[h] - O.update(x, lab[h], C, prev[h])).max() <= 1e-6 * np.abs(x).max()
+    print(f"[fused step {name}] near-ties: {near}")
+
+
 @pytest.mark.parametrize("side", ["q", "k"])
 @pytest.mark.parametrize("stride,phase", [(3, 1), (4, 0), (1, 0)])
 def test_subset_update_lockstep(case, side, stride, phase):
