@@ -153,6 +153,82 @@ __global__ __launch_bounds__(256) void kpp_prep_tiled(const T* __restrict__ X, i
   }
 }
 
+// The same products for bf16 data on the matrix cores, 256 candidates per block: M (fp32) is split
+// exactly into three bf16 parts (Mh = bf16(M), Mm = bf16(M - Mh), Ml = bf16(M - Mh - Mm); each
+// difference is exact in fp32), staged in LDS, and y = Mh x + Mm x + Ml x accumulates the exact
+// products in fp32 (32x32x16 MFMAs: dimensions of M as A rows, candidates as B columns; wave w
+// takes 32 candidates). xx = x . y: fp64 sums of fp64 products, per lane over its outputs in tile
+// order, then over the two half-waves.
+template <int D>
+__global__ __launch_bounds__(512) void kpp_prep_mfma(const uint16_t* __restrict__ X, int64_t N, int S,
+                                                     const float* __restrict__ M, double* __restrict__ xx,
+                                                     float* __restrict__ y) {
+  constexpr int STR = D + 8;  // padded LDS row (bf16 elements)
+  constexpr int KS = D / 16;  // 16-dimension MFMA steps
+  constexpr int AT = D / 32;  // 32-dimension output tiles
+  __shared__ __attribute__((aligned(16))) uint16_t ms[3][D * STR];
+  const int h = blockIdx.y;
+  const int l = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int hl = l / 32;
+  const float* Mh = M + (int64_t)h * D * D;
+  for (int e = threadIdx.x; e < D * D / 4; e += 512) {
+    const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(Mh + e * 4);
+    const int r = (e * 4) / D, c = (e * 4) % D;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float m = m4[q];
+      const uint32_t b0 = f32_to_bf16_bits(m);
+      const float r1 = m - bf16_bits_to_f32(b0);
+      const uint32_t b1 = f32_to_bf16_bits(r1);
+      const float r2 = r1 - bf16_bits_to_f32(b1);
+      ms[0][r * STR + c + q] = (uint16_t)b0;
+      ms[1][r * STR + c + q] = (uint16_t)b1;
+      ms[2][r * STR + c + q] = (uint16_t)f32_to_bf16_bits(r2);
+    }
+  }
+  __syncthreads();
+  const int cand = blockIdx.x * 256 + w * 32 + l % 32;  // this lane's candidate (B column)
+  const bool ok = cand < S;
+  const uint16_t* xr = X + ((int64_t)h * N + cand_row(min(cand, S - 1), S, N)) * D;
+  f32x16_t acc[AT];
+#pragma unroll
+  for (int at = 0; at < AT; ++at)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[at][i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(xr + kk * 16 + hl * 8);
+#pragma unroll
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&ms[sp][(at * 32 + l % 32) * STR + kk * 16 + hl * 8]);
+        acc[at] = mfma32(a, b, acc[at]);
+      }
+  }
+  // element i of tile at: dimension at * 32 + (i / 4) * 8 + hl * 4 + i % 4 of this lane's candidate
+  double part = 0.0;
+  float* yr = y + ((int64_t)h * S + min(cand, S - 1)) * D;
+#pragma unroll
+  for (int at = 0; at < AT; ++at)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int a0 = at * 32 + g4 * 8 + hl * 4;
+      const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(xr + a0);
+      const float xs[4] = {bf16_bits_to_f32(xv[0] & 0xFFFFu), bf16_bits_to_f32(xv[0] >> 16),
+                           bf16_bits_to_f32(xv[1] & 0xFFFFu), bf16_bits_to_f32(xv[1] >> 16)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part += (double)xs[q] * (double)acc[at][g4 * 4 + q];
+      if (ok) {
+        const f32x4_t v = {acc[at][g4 * 4], acc[at][g4 * 4 + 1], acc[at][g4 * 4 + 2], acc[at][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4_t*>(yr + a0) = v;
+      }
+    }
+  part += __shfl_xor(part, 32, kWave);
+  if (hl == 0 && ok) xx[(int64_t)h * S + cand] = part;
+}
+
 struct KppSide {
   const void* x;      // [H, N, D] data of this side
   const double* xx;   // [H, S] candidate norms
@@ -1592,10 +1668,17 @@ hipError_t launch_kpp(const Dims& s, const KppArgs* sides, int nsides, uint64_t 
   else                                                                                                      \
     kpp_prep<T, D><<<g1, 256, 0, st>>>(static_cast<const T*>(a.x), s.N, S, a.xx);
     if (s.bf16) {
+      const dim3 g2((unsigned)ceil_div(S, 256), (unsigned)s.H);
       if (s.D == 128) {
-        PARK_PREP(uint16_t, 128)
+        if (a.metric)
+          kpp_prep_mfma<128><<<g2, 512, 0, st>>>(static_cast<const uint16_t*>(a.x), s.N, S, a.metric, a.xx, a.y);
+        else
+          kpp_prep<uint16_t, 128><<<g1, 256, 0, st>>>(static_cast<const uint16_t*>(a.x), s.N, S, a.xx);
       } else {
-        PARK_PREP(uint16_t, 64)
+        if (a.metric)
+          kpp_prep_mfma<64><<<g2, 512, 0, st>>>(static_cast<const uint16_t*>(a.x), s.N, S, a.metric, a.xx, a.y);
+        else
+          kpp_prep<uint16_t, 64><<<g1, 256, 0, st>>>(static_cast<const uint16_t*>(a.x), s.N, S, a.xx);
       }
     } else {
       if (s.D == 128) {
