@@ -468,15 +468,30 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
   c = L - h * nx;
 }
 
-// 384-query tiles: twelve waves x 32 queries share one work-group per CU (three waves per SIMD,
-// 168 registers each), so each key/value tile copied to LDS serves 384 queries and each SIMD has
-// three waves to interleave matrix-core, vector and LDS work. Tiles of 32 keys (d = 128; 64 for
-// d = 64) are copied by eight of the waves, 1 KB of K and of V each, through a ring of four stages
-// three tiles ahead; a wave waits only for the copies of the tile it is about to read (a counted
-// vmcnt, then a plain barrier: a fenced barrier would also wait for the copies still in flight).
-constexpr int kBf16BM = 384;  // queries per work item
-[[maybe_unused]] constexpr int kBf16BN = 32;   // keys per tile for d = 128
-[[maybe_unused]] constexpr int kBf16NST = 4;   // LDS stages of one tile (K and V)
+// 384-query work items: twelve waves x 32 queries share one work-group per CU (three waves per
+// SIMD, 168 registers each), so each key/value tile copied to LDS serves up to 384 queries and each
+// SIMD has three waves to interleave matrix-core, vector and LDS work. Tiles (32 keys for d = 128,
+// 64 for d = 64) are copied by eight of the waves (1 KB of K and of V per wave and copy) through a
+// ring of four stages three tiles ahead; a wave waits only for the copies of the tile it is about to
+// read (a counted vmcnt, then a plain barrier: a fenced barrier would also wait for the copies still
+// in flight). A d = 128 work item of at most 192 queries (the ragged last item of a query cluster)
+// runs a second form: 64-key tiles, and two groups of six waves on the same queries, each group
+// one 32-key half of every tile; the second group's partial output, reference and sum are merged
+// into the first's at the end. The busiest SIMD of such an item then computes half the sub-tiles it
+// would compute alone (one wave per SIMD runs at well under a third of three waves' rate).
+constexpr int kBf16BM = 384;                      // queries per work item
+[[maybe_unused]] constexpr int kBf16BN = 32;      // keys per matrix-core sub-tile for d = 128
+[[maybe_unused]] constexpr int kBf16TK = 64;      // keys per copied tile in the split form (and for d = 64)
+[[maybe_unused]] constexpr int kBf16NST = 4;      // LDS stages of the ring
+[[maybe_unused]] constexpr int kBf16SplitQ = 192; // d = 128 items of at most this many queries split their keys
+
+// The lane id through an opaque read, which the compiler can neither reuse across nor hoist out of
+// the code that needs it.
+__device__ __forceinline__ int lane_id_opaque() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
 
 // vmcnt(n) & lgkmcnt(0), then a plain workgroup barrier
 template <int VM>
@@ -584,22 +599,24 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   constexpr int DT = D / 32;
   constexpr int CPR = D / 8;
   constexpr int ROWB = D * 2;
-  constexpr int BN = D == 64 ? 64 : kBf16BN;
-  constexpr int NSUB = BN / 32;                 // 32-key sub-tiles
-  constexpr int TILEB = BN * ROWB;              // one K (or V) tile
-  constexpr int STAGEB = 2 * TILEB;              // K, then V
+  constexpr int NSC = D == 64 ? 2 : 1;          // 32-key sub-tiles a wave computes at once
+  constexpr bool SPLIT = D == 128;              // ragged items may split their keys over two wave groups
   constexpr int RPB = 1024 / ROWB;              // rows per 1 KB wave load
-  constexpr int LOADS = TILEB / (1024 * NWC);    // 1 KB loads per wave per tile, for K and for V
-  static_assert(LOADS >= 1, "tile smaller than one load per wave");
-  constexpr int CP = 2 * LOADS;                 // copies per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t stages[NST * STAGEB];
-  // the query cluster's runs (see attn_runs), one record per run r: {rd[r], rv[r + 1]} (+ {rb[r], 0}
-  // in the weighted form), so that one LDS read gives a lane the run's offset and its end
-  constexpr int RREC = W ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) int32_t s_run[kMaxClusters * RREC];
+  // the ring (K and V) for the largest tiles (64 keys); the split form's merge reuses it: 17 KB per
+  // wave of the second group (its 64 output accumulators, then reference and sum, as one 16-byte
+  // row per lane each)
+  constexpr int MERGEB = SPLIT ? 6 * 17 * 1024 : 0;
+  constexpr int RINGB = 2 * NST * 64 * ROWB > MERGEB ? 2 * NST * 64 * ROWB : MERGEB;
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[RINGB];
+  // the query cluster's runs (see attn_runs), one record per run r: {rd[r], rv[r + 1]}, so that one
+  // LDS read gives a lane the run's offset and its end; the weighted form keeps rb[r] apart
+  __shared__ __attribute__((aligned(16))) int32_t s_run[kMaxClusters * 2];
+  __shared__ __attribute__((aligned(16))) int32_t s_rb[W ? kMaxClusters : 1];
   // weighted form: per tile, the logit offset of each of the tile's keys (lane l: key l % BN),
   // written when the tile's entries are loaded and read when it is computed
   __shared__ __attribute__((aligned(16))) float bring[W ? 2 * NST : 1][kWave];
+  // gather-list entries of the tiles in flight (see load_idx)
+  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][kWave];
 
   int h, c;
   xcd_tile(h, c);
@@ -616,18 +633,19 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   const int32_t* qo = q_off + (int64_t)h * (cq + 1);
   const int qbeg = qo[i] + (c - tb[ti]) * kBf16BM;
   const int qend = min(qbeg + kBf16BM, qo[i + 1]);
-  const bool active = qbeg + w * 32 < qend;  // this wave has at least one query
+  // split form: wave 6 g + j takes query group j and sub-tile g of every tile
+  const bool split = SPLIT && qend - qbeg <= kBf16SplitQ;
+  const int grp = split ? w / 6 : 0;
+  const int qw = split ? w - 6 * grp : w;
+  const bool active = qbeg + qw * 32 < qend;  // this wave has at least one query
   const int L = glen[(int64_t)h * cq + i];
   const int R = nrun[(int64_t)h * cq + i];
   {
     const int32_t* rg = runs + ((int64_t)h * cq + i) * run_stride(ck);
     for (int e = threadIdx.x; e < R; e += NW * kWave) {
-      s_run[e * RREC] = rg[ck + 1 + e];
-      s_run[e * RREC + 1] = rg[e + 1];
-      if constexpr (W) {
-        s_run[e * RREC + 2] = rg[2 * ck + 1 + e];
-        s_run[e * RREC + 3] = 0;
-      }
+      s_run[e * 2] = rg[ck + 1 + e];
+      s_run[e * 2 + 1] = rg[e + 1];
+      if constexpr (W) s_rb[e] = rg[2 * ck + 1 + e];
     }
   }
   const uint16_t* Qh = Q + (int64_t)h * N * D;
@@ -636,7 +654,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + (int64_t)h * N * D), (short)0, (int)(uint32_t)(N * ROWB), kBufferFlags);
 
-  const int qpos = qbeg + w * 32 + l % 32;
+  const int qpos = qbeg + qw * 32 + l % 32;
   const bool qok = qpos < qend;
   const int qrow = q_perm[(int64_t)h * N + min(qpos, qend - 1)];
   u32x4_t qb[KS];
@@ -646,65 +664,6 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     const u32x4_t z = {0u, 0u, 0u, 0u};
     qb[kk] = qok ? v : z;
   }
-
-  // load slots: slot q of this lane copies tile row trow[q], logical chunk (l % CPR) ^ swizzle, into
-  // physical chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
-  int trow[LOADS], lbyte[LOADS];
-#pragma unroll
-  for (int q = 0; q < LOADS; ++q) {
-    trow[q] = (wc * LOADS + q) * RPB + l / CPR;
-    lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
-  }
-  const int nt = (L + BN - 1) / BN;
-  // Gather-list entries of tile x reach LDS (set x % NST, one 256-byte region per wave, lane l
-  // holding entry x * BN + l % BN) by a direct load in iteration x - 2 NST + 1; the lane's entry is
-  // read into a register at the end of iteration x - NST, ready for the copies of iteration
-  // x - NST + 1.
-  static_assert(LOADS == 1, "one 1 KB copy per wave and tile");
-  __shared__ __attribute__((aligned(16))) int32_t idxs[NST][kWave];
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k_perm + (int64_t)h * N), (short)0, (int)(uint32_t)(N * 4), kBufferFlags);
-  constexpr int IL = 1;  // index loads per wave and tile
-  // Cursor of this lane's key through the runs: keys advance by BN per tile, so the run index only
-  // grows (the run record is read again per tile, which keeps the cursor to one register).
-  __syncthreads();  // run records in LDS
-  int cr = 0;
-  const uint32_t run_base = (uint32_t)(size_t)((PARK_LDS int32_t*)s_run);
-  const uint32_t bring_base = (uint32_t)(size_t)((PARK_LDS float*)&bring[0][0]);
-  auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
-    if (!indexer) return;
-    const int v = tile * BN + l % BN;
-    int off = (int)(N * 4);  // past the buffer's range: reads 0 (a valid row; its scores are masked)
-    float bias = 0.f;
-    if (v < L) {
-      u32x2_t rec = lds_read_b64(run_base + (uint32_t)(cr * RREC) * 4u);
-      while (v >= (int)rec[1]) {  // rec[1]: first key after run cr (< L for every run but the last)
-        ++cr;
-        rec = lds_read_b64(run_base + (uint32_t)(cr * RREC) * 4u);
-      }
-      off = (v + (int)rec[0]) * 4;
-      if constexpr (W) bias = __int_as_float(lds_read_b32(run_base + (uint32_t)(cr * RREC + 2) * 4u));
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][0], 4, off, 0, 0, 0);
-    if constexpr (W) lds_write_b32(bring_base + (uint32_t)((tile % (2 * NST)) * kWave + l) * 4u, bias);
-  };
-  const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][trow[0]]);
-  auto read_idx = [&](int set) __attribute__((always_inline)) {
-    return lds_read_b32(ibase + (uint32_t)(set * kWave * 4));
-  };
-  int nnext = 0;  // gather-list row of this lane's copy in the next issue
-  auto issue = [&](int nrow0, int slot, int tile) __attribute__((always_inline)) {
-    if (!copier) return;
-    const int nrow[1] = {nrow0};
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-      const int boff = slot * STAGEB + (w * LOADS + q) * 1024;
-      const int voff = (int)((uint32_t)nrow[q] * ROWB + lbyte[q]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + boff + TILEB), 16, voff, 0, 0, 0);
-    }
-    (void)tile;
-  };
 
   f32x16_t o[DT];
 #pragma unroll
@@ -718,230 +677,370 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   constexpr float kRaise = 1099511627776.0f;  // 2^40
   float m_ref = -INFINITY;
   float l_run = 0.f;
-  const int r = l % 32;
-  const int prow = ((r / 4) % 2) * 16 + (r / 8) * 4 + r % 4;
-  const int g16 = l / 16, i16 = l % 16;
-  const bf16x2_t ones = as_bf16x2(0x3F803F80u);
 
-  // per-lane byte offsets of the LDS operand reads within a K (V) tile, computed once
-  int kofs[NSUB][KS], vofs[DT][NSUB][2][2];
+  // The tile loop for tiles of TK keys: 32 for d = 128 outside the split form, 64 in it (each group
+  // of waves one half) and for d = 64.
+  auto run = [&](auto TKc) __attribute__((always_inline)) {
+    constexpr int BN = decltype(TKc)::value;
+    // the lane-derived values are derived again in each form (an opaque read of the lane id), so
+    // that the two forms' copies are not kept live across both: the 168-register budget is tight
+    const int l = lane_id_opaque();
+    const int hl = l / 32;
+    constexpr int NSUB = BN / 32;                 // 32-key sub-tiles per tile
+    static_assert(NSUB == NSC || (SPLIT && NSUB == 2), "a wave computes all sub-tiles, or one in the split form");
+    constexpr int TILEB = BN * ROWB;              // one K (or V) tile
+    // K and V of a stage side by side while every stage offset fits the LDS reads' 16-bit offset
+    // field, else the K ring followed by the V ring
+    constexpr bool INTER = 2 * NST * TILEB <= 65536;
+    constexpr int KSTR = INTER ? 2 * TILEB : TILEB;  // bytes from one stage's K to the next
+    constexpr int VOFF = INTER ? TILEB : NST * TILEB; // a stage's V past its K
+    constexpr int LOADS = TILEB / (1024 * NWC);    // 1 KB loads per wave per tile, for K and for V
+    static_assert(LOADS >= 1, "tile smaller than one load per wave");
+    constexpr int CP = 2 * LOADS;                 // copies per wave per tile
+    // load slots: slot q of this lane copies tile row trow[q], logical chunk (l % CPR) ^ swizzle, into
+    // physical chunk l % CPR of the wave's 1 KB block (w * LOADS + q)
+    int trow[LOADS], lbyte[LOADS];
 #pragma unroll
-  for (int st = 0; st < NSUB; ++st) {
-    const int R = st * 32 + prow;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kofs[st][kk] = R * ROWB + ((2 * kk + hl) ^ chunk_swz<CPR>(R)) * 16;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int D0 = dt * 32 + 16 * (g16 & 1);
-    const int cc = (D0 + 4 * (i16 % 4)) / 8;
-    const int half = (i16 % 4) & 1;
-#pragma unroll
-    for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int R1 = st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4;
-        const int R2 = R1 + 4;
-        vofs[dt][st][kh][0] = R1 * ROWB + (cc ^ chunk_swz<CPR>(R1)) * 16 + half * 8;
-        vofs[dt][st][kh][1] = R2 * ROWB + (cc ^ chunk_swz<CPR>(R2)) * 16 + half * 8;
+    for (int q = 0; q < LOADS; ++q) {
+      trow[q] = (wc * LOADS + q) * RPB + l / CPR;
+      lbyte[q] = ((l % CPR) ^ chunk_swz<CPR>(trow[q])) * 16;
+    }
+    const int nt = (L + BN - 1) / BN;
+    // Gather-list entries of tile x reach LDS (set x % NST, one 256-byte region per wave, lane l
+    // holding entry x * BN + l % BN) by a direct load in iteration x - 2 NST + 1; the lane's entry is
+    // read into a register at the end of iteration x - NST, ready for the copies of iteration
+    // x - NST + 1.
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(k_perm + (int64_t)h * N), (short)0, (int)(uint32_t)(N * 4), kBufferFlags);
+    constexpr int IL = 1;  // index loads per wave and tile
+    // Cursor of this lane's key through the runs: keys advance by BN per tile, so the run index only
+    // grows (the run record is read again per tile, which keeps the cursor to one register).
+    __syncthreads();  // run records in LDS
+    int cr = 0;
+    const uint32_t run_base = (uint32_t)(size_t)((PARK_LDS int32_t*)s_run);
+    const uint32_t rb_base = (uint32_t)(size_t)((PARK_LDS int32_t*)s_rb);
+    const uint32_t bring_base = (uint32_t)(size_t)((PARK_LDS float*)&bring[0][0]);
+    auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
+      if (!indexer) return;
+      const int v = tile * BN + l % BN;
+      int off = (int)(N * 4);  // past the buffer's range: reads 0 (a valid row; its scores are masked)
+      float bias = 0.f;
+      if (v < L) {
+        u32x2_t rec = lds_read_b64(run_base + (uint32_t)cr * 8u);
+        while (v >= (int)rec[1]) {  // rec[1]: first key after run cr (< L for every run but the last)
+          ++cr;
+          rec = lds_read_b64(run_base + (uint32_t)cr * 8u);
+        }
+        off = (v + (int)rec[0]) * 4;
+        if constexpr (W) bias = __int_as_float(lds_read_b32(rb_base + (uint32_t)cr * 4u));
       }
-  }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][0], 4, off, 0, 0, 0);
+      if constexpr (W) lds_write_b32(bring_base + (uint32_t)((tile % (2 * NST)) * kWave + l) * 4u, bias);
+    };
+    // entries of this lane's copy rows trow[q] = trow[0] + q RPB
+    const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][trow[0]]);
+    auto read_idx = [&](int set, int(&nr)[LOADS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) nr[q] = lds_read_b32(ibase + (uint32_t)((set * kWave + q * RPB) * 4));
+    };
+    int nnext[LOADS];  // gather-list rows of this lane's copies in the next issue
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) nnext[q] = 0;
+    auto issue = [&](const int(&nrow)[LOADS], int slot, int tile) __attribute__((always_inline)) {
+      if (!copier) return;
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) {
+        const int boff = slot * KSTR + (w * LOADS + q) * 1024;
+        const int voff = (int)((uint32_t)nrow[q] * ROWB + lbyte[q]);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PARK_LDS void*)(stages + boff), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PARK_LDS void*)(stages + VOFF + boff), 16, voff, 0, 0, 0);
+      }
+      (void)tile;
+    };
 
-  static_assert((NST - 1) * STAGEB + TILEB + 64 <= 65535, "stage offsets fit the LDS reads' 16-bit offset field");
-  // scores of one tile: its eight K operand reads in two blocks of four, each followed by its MFMAs
-  const uint32_t sbase = (uint32_t)(size_t)((PARK_LDS uint8_t*)stages);
-  static_assert(KS * NSUB == 8, "eight K reads per tile");
-  auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
-    constexpr int OFF = decltype(OFFc)::value;
+    const int r = l % 32;
+    const int prow = ((r / 4) % 2) * 16 + (r / 8) * 4 + r % 4;
+    const int g16 = l / 16, i16 = l % 16;
+    const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+
+    // per-lane byte offsets of the LDS operand reads within a stage (K, and V past VOFF), computed
+    // once; a wave of the split form's second group reads the second sub-tile of every tile
+    const int sub0 = grp * 32;
+    int kofs[NSC][KS], vofs[DT][NSC][2][2];
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st)
+    for (int st = 0; st < NSC; ++st) {
+      const int R = sub0 + st * 32 + prow;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint32_t a[4];
-      u32x4_t ka[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = hh * 4 + j;
-        a[j] = sbase + kofs[idx / KS][idx % KS];
-      }
-      lds_read4x_b128<OFF>(ka, a);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = hh * 4 + j;
-        sa[idx / KS] = mfma32(ka[j], qb[idx % KS], sa[idx / KS]);
-      }
+      for (int kk = 0; kk < KS; ++kk) kofs[st][kk] = R * ROWB + ((2 * kk + hl) ^ chunk_swz<CPR>(R)) * 16;
     }
-  };
-  // key offsets (weighted form) and the mask of keys past the list end
-  auto adjust = [&](f32x16_t(&sa)[NSUB], int v0) __attribute__((always_inline)) {
-    if constexpr (W) {
-      const int tile = v0 / BN;
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st) {
-        u32x4_t b[4];
-        const uint32_t ba = bring_base + (uint32_t)((tile % (2 * NST)) * kWave + st * 32 + hl * 16) * 4u;
-        lds_read4_b128<0>(b, ba);
+    for (int dt = 0; dt < DT; ++dt) {
+      const int D0 = dt * 32 + 16 * (g16 & 1);
+      const int cc = (D0 + 4 * (i16 % 4)) / 8;
+      const int half = (i16 % 4) & 1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+      for (int st = 0; st < NSC; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += __uint_as_float(b[q][e]);
-      }
-    }
-    const int nvalid = L - v0;
-    if (__builtin_expect(nvalid < BN, 0)) {
-      const int lim = nvalid - hl * 16;  // accumulator e of sub-tile st is key st * 32 + hl * 16 + e
-#pragma unroll
-      for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (st * 32 + e >= lim) sa[st][e] = -INFINITY;
-    }
-  };
-  auto tile_max = [&](const f32x16_t(&sa)[NSUB]) __attribute__((always_inline)) {
-    float mx = sa[0][0];
-#pragma unroll
-    for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[st][e]);
-    return fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  };
-  auto weights = [&](const f32x16_t(&sa)[NSUB], u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
-    const float mb = m_ref * sl2;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-      float pv[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[st][e], sl2, -mb));
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t pk = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
-          pb[st][kh][q] = pk;
-          s4[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, s4[q], false);
+        for (int kh = 0; kh < 2; ++kh) {
+          const int R1 = sub0 + st * 32 + 16 * (g16 >> 1) + 8 * kh + i16 / 4;
+          const int R2 = R1 + 4;
+          vofs[dt][st][kh][0] = VOFF + R1 * ROWB + (cc ^ chunk_swz<CPR>(R1)) * 16 + half * 8;
+          vofs[dt][st][kh][1] = VOFF + R2 * ROWB + (cc ^ chunk_swz<CPR>(R2)) * 16 + half * 8;
         }
     }
-    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  };
-  // V^T operands of a tile: two blocks of eight reads, each followed by its P V MFMAs
-  auto pv_tile = [&](auto OFFc, const u32x4_t(&pb)[NSUB][2]) __attribute__((always_inline)) {
-    constexpr int OFF = decltype(OFFc)::value;
-    constexpr int DG = 2 / NSUB;
+
+    static_assert((NST - 1) * KSTR <= 65535, "stage offsets fit the LDS reads' 16-bit offset field");
+    // scores of one tile: its eight K operand reads in two blocks of four, each followed by its MFMAs
+    const uint32_t sbase = (uint32_t)(size_t)((PARK_LDS uint8_t*)stages);
+    static_assert(KS * NSC == 8, "eight K reads per computed sub-tile set");
+    auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSC]) __attribute__((always_inline)) {
+      constexpr int OFF = decltype(OFFc)::value;
 #pragma unroll
-    for (int d0 = 0; d0 < DT; d0 += DG) {
-      uint32_t a[8];
-      u32x2_t r[8];
+      for (int st = 0; st < NSC; ++st)
 #pragma unroll
-      for (int x = 0; x < DG; ++x)
+        for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
 #pragma unroll
-        for (int st = 0; st < NSUB; ++st)
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t a[4];
+        u32x4_t ka[4];
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+        for (int j = 0; j < 4; ++j) {
+          const int idx = hh * 4 + j;
+          a[j] = sbase + kofs[idx / KS][idx % KS];
+        }
+        lds_read4x_b128<OFF>(ka, a);
 #pragma unroll
-            for (int z = 0; z < 2; ++z) a[((x * NSUB + st) * 2 + kh) * 2 + z] = sbase + vofs[d0 + x][st][kh][z];
-      tr_read8<OFF>(r, a);
+        for (int j = 0; j < 4; ++j) {
+          const int idx = hh * 4 + j;
+          sa[idx / KS] = mfma32(ka[j], qb[idx % KS], sa[idx / KS]);
+        }
+      }
+    };
+    // key offsets (weighted form) and the mask of keys past the list end; v0 = the first key
+    auto adjust = [&](f32x16_t(&sa)[NSC], int v0) __attribute__((always_inline)) {
+      if constexpr (W) {
+        const int tile = v0 / BN, sub = v0 % BN;
 #pragma unroll
-      for (int x = 0; x < DG; ++x)
+        for (int st = 0; st < NSC; ++st) {
+          u32x4_t b[4];
+          const uint32_t ba = bring_base + (uint32_t)((tile % (2 * NST)) * kWave + sub + st * 32 + hl * 16) * 4u;
+          lds_read4_b128<0>(b, ba);
 #pragma unroll
-        for (int st = 0; st < NSUB; ++st)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const int j = ((x * NSUB + st) * 2 + kh) * 2;
-            const u32x4_t va = u32x4_t{r[j][0], r[j][1], r[j + 1][0], r[j + 1][1]};
-            o[d0 + x] = mfma32(va, pb[st][kh], o[d0 + x]);
+            for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += __uint_as_float(b[q][e]);
+        }
+      }
+      const int nvalid = L - v0;
+      if (__builtin_expect(nvalid < NSC * 32, 0)) {
+        const int lim = nvalid - hl * 16;  // accumulator e of sub-tile st is key v0 + st * 32 + hl * 16 + e
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (st * 32 + e >= lim) sa[st][e] = -INFINITY;
+      }
+    };
+    auto tile_max = [&](const f32x16_t(&sa)[NSC]) __attribute__((always_inline)) {
+      float mx = sa[0][0];
+#pragma unroll
+      for (int st = 0; st < NSC; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[st][e]);
+      return fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    };
+    auto weights = [&](const f32x16_t(&sa)[NSC], u32x4_t(&pb)[NSC][2]) __attribute__((always_inline)) {
+      const float mb = m_ref * sl2;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NSC; ++st) {
+        float pv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[st][e], sl2, -mb));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t pk = pack_bf16x2(pv[kh * 8 + 2 * q], pv[kh * 8 + 2 * q + 1]);
+            pb[st][kh][q] = pk;
+            s4[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, s4[q], false);
           }
+      }
+      return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    // V^T operands of a tile: two blocks of eight reads, each followed by its P V MFMAs
+    auto pv_tile = [&](auto OFFc, const u32x4_t(&pb)[NSC][2]) __attribute__((always_inline)) {
+      constexpr int OFF = decltype(OFFc)::value;
+      constexpr int DG = 2 / NSC;
+#pragma unroll
+      for (int d0 = 0; d0 < DT; d0 += DG) {
+        uint32_t a[8];
+        u32x2_t r[8];
+#pragma unroll
+        for (int x = 0; x < DG; ++x)
+#pragma unroll
+          for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int z = 0; z < 2; ++z) a[((x * NSC + st) * 2 + kh) * 2 + z] = sbase + vofs[d0 + x][st][kh][z];
+        tr_read8<OFF>(r, a);
+#pragma unroll
+        for (int x = 0; x < DG; ++x)
+#pragma unroll
+          for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+              const int j = ((x * NSC + st) * 2 + kh) * 2;
+              const u32x4_t va = u32x4_t{r[j][0], r[j][1], r[j + 1][0], r[j + 1][1]};
+              o[d0 + x] = mfma32(va, pb[st][kh], o[d0 + x]);
+            }
+      }
+    };
+
+    // one sub-tile set of the stage at LDS offset OFF (its V past VOFF), first key v0; `first`: the
+    // wave's first set, which sets the softmax reference
+    auto compute = [&](auto OFFc, int v0, bool first) __attribute__((always_inline)) {
+      f32x16_t sc[NSC];
+      s_tile(OFFc, sc);
+      adjust(sc, v0);
+      if (first) m_ref = tile_max(sc);
+      u32x4_t pb[NSC][2];
+      float ps = weights(sc, pb);
+      if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
+        // rare: the scores are computed again (the tile is still in LDS), so they need not stay
+        // live through the softmax
+        f32x16_t s2[NSC];
+        s_tile(OFFc, s2);
+        adjust(s2, v0);
+        const float m_new = fmaxf(m_ref, tile_max(s2));
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        m_ref = m_new;
+        ps = weights(s2, pb);
+      }
+      l_run += ps;
+      pv_tile(OFFc, pb);
+    };
+
+    if (nt > 0) {
+      // prologue: entries of tiles 0 .. NST-1 (one wait of the indexer, then a barrier), then those
+      // of tiles NST .. 2 NST-2 into the sets just read, then the copies of tiles 0 .. NST-2 into
+      // stages 0 .. NST-2
+#pragma unroll
+      for (int x = 0; x < NST; ++x) load_idx(x, x);
+      if (indexer) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) & lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      int n0[NST][LOADS];
+#pragma unroll
+      for (int x = 0; x < NST; ++x) read_idx(x, n0[x]);
+#pragma unroll
+      for (int x = NST; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
+#pragma unroll
+      for (int x = 0; x < NST - 1; ++x) issue(n0[x], x, x);
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) nnext[q] = n0[NST - 1][q];
+    }
+    // Iteration t (stage SL = t % NST): wait until tile t landed, copy tile t + NST - 1 into the stage
+    // tile t - 1 used, load the entries of tile t + 2 NST - 1, compute tile t, read the entries of
+    // tile t + NST. Copier waves: tile t was copied in iteration t - NST + 1 (or in the prologue),
+    // after which each of the NST - 2 iterations since issued CP copies. Indexer: the entries of tile
+    // t + NST were loaded in iteration t - NST + 1 (or in the prologue), after which NST - 2 index
+    // loads followed; its wait before the barrier lets every wave read them at the end of iteration
+    // t. The other waves issue no vector-memory operations in the loop.
+    for (int t = 0; t < nt; t += NST) {
+      const bool go_on = unroll_while<0, NST>([&](auto SLc) __attribute__((always_inline)) {
+        constexpr int SL = decltype(SLc)::value;
+        constexpr int XS = (SL + NST - 1) % NST;
+        const int tt = t + SL;
+        if (tt >= nt) return false;
+        if (indexer)
+          wait_barrier<(NST - 2) * IL>();
+        else
+          wait_barrier<(NST - 2) * CP>();
+        issue(nnext, XS, tt + NST - 1);
+        load_idx(XS, tt + 2 * NST - 1);
+        // the tile's sub-tiles (split form: this wave's half, if it holds a key of the list)
+        const int v0 = tt * BN + sub0;
+        if (active && v0 < L) compute(std::integral_constant<int, SL * KSTR>{}, v0, tt == 0);
+        read_idx(SL, nnext);
+        return true;
+      });
+      if (!go_on) break;
     }
   };
-
-  if (nt > 0) {
-    // prologue: entries of tiles 0 .. NST-1 (one wait of the indexer, then a barrier), then those
-    // of tiles NST .. 2 NST-2 into the sets just read, then the copies of tiles 0 .. NST-2 into
-    // stages 0 .. NST-2
-#pragma unroll
-    for (int x = 0; x < NST; ++x) load_idx(x, x);
-    if (indexer) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) & lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int n0[NST];
-#pragma unroll
-    for (int x = 0; x < NST; ++x) n0[x] = read_idx(x);
-#pragma unroll
-    for (int x = NST; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
-#pragma unroll
-    for (int x = 0; x < NST - 1; ++x) issue(n0[x], x, x);
-    nnext = n0[NST - 1];
+  if constexpr (D == 64) {
+    run(std::integral_constant<int, 64>{});
+  } else {
+    if (split)
+      run(std::integral_constant<int, 64>{});
+    else
+      run(std::integral_constant<int, 32>{});
   }
-  // Iteration t (stage SL = t % NST): wait until tile t landed, copy tile t + NST - 1 into the stage
-  // tile t - 1 used, load the entries of tile t + 2 NST - 1, compute tile t, read the entries of
-  // tile t + NST. Copier waves: tile t was copied in iteration t - NST + 1 (or in the prologue),
-  // after which each of the NST - 2 iterations since issued CP copies. Indexer: the entries of tile
-  // t + NST were loaded in iteration t - NST + 1 (or in the prologue), after which NST - 2 index
-  // loads followed; its wait before the barrier lets every wave read them at the end of iteration
-  // t. The other waves issue no vector-memory operations in the loop.
-  for (int t = 0; t < nt; t += NST) {
-    const bool go_on = unroll_while<0, NST>([&](auto SLc) __attribute__((always_inline)) {
-      constexpr int SL = decltype(SLc)::value;
-      constexpr int XS = (SL + NST - 1) % NST;
-      const int tt = t + SL;
-      if (tt >= nt) return false;
-      if (indexer)
-        wait_barrier<(NST - 2) * IL>();
-      else
-        wait_barrier<(NST - 2) * CP>();
-      issue(nnext, XS, tt + NST - 1);
-      load_idx(XS, tt + 2 * NST - 1);
-      if (active) {
-        f32x16_t sc[NSUB];
-        s_tile(std::integral_constant<int, SL * STAGEB>{}, sc);
-        adjust(sc, tt * BN);
-        if (tt == 0) m_ref = tile_max(sc);
-        u32x4_t pb[NSUB][2];
-        float ps = weights(sc, pb);
-        if (__builtin_amdgcn_ballot_w64(!(ps <= kRaise))) {
-          // rare: the scores are computed again (the tile is still in LDS), so they need not stay
-          // live through the softmax
-          f32x16_t s2[NSUB];
-          s_tile(std::integral_constant<int, SL * STAGEB>{}, s2);
-          adjust(s2, tt * BN);
-          const float m_new = fmaxf(m_ref, tile_max(s2));
-          const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-          m_ref = m_new;
-          ps = weights(s2, pb);
-        }
-        l_run += ps;
-        pv_tile(std::integral_constant<int, SL * STAGEB + TILEB>{}, pb);
-      }
-      nnext = read_idx(SL);
-      return true;
-    });
-    if (!go_on) break;
-  }
-  // drain the copies still in flight before the work-group's LDS can be handed to another
+  // drain the copies still in flight before the ring is reused or the work-group's LDS handed to
+  // another
   __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (qok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = out + ((int64_t)h * N + qrow) * D;
+  // lane-derived values derived again rather than kept live through the tile loop
+  {
+    const int l = lane_id_opaque();
+    const int hl = l / 32;
+    const int qpos = qbeg + qw * 32 + l % 32;
+    const bool qok = qpos < qend;
+    if (split) {
+      // merge the second group's (O, reference, sum) into the first's: with m = max(m0, m1),
+      // O = O0 2^(sl2 (m0 - m)) + O1 2^(sl2 (m1 - m)) and the same for the sums; a group that met
+      // no key of the list has m = -inf and weight 0
+      f32x4_t* mrow = reinterpret_cast<f32x4_t*>(stages) + qw * 17 * kWave + l;
+      __syncthreads();  // every wave is done with the ring
+      if (grp == 1 && active) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = dt * 32 + g4 * 8 + hl * 4;
-        store_out4<uint16_t>(orow + d0, o[dt][g4 * 4] * inv, o[dt][g4 * 4 + 1] * inv, o[dt][g4 * 4 + 2] * inv,
-                             o[dt][g4 * 4 + 3] * inv);
+          for (int g4 = 0; g4 < 4; ++g4)
+            mrow[(dt * 4 + g4) * kWave] = f32x4_t{o[dt][g4 * 4], o[dt][g4 * 4 + 1], o[dt][g4 * 4 + 2], o[dt][g4 * 4 + 3]};
+        mrow[16 * kWave] = f32x4_t{m_ref, l_run, 0.f, 0.f};
       }
-    if (lse != nullptr && hl == 0)
-      lse[(int64_t)h * N + qrow] = l_tot > 0.f ? m_ref * scale + logf(l_tot) : -INFINITY;
+      __syncthreads();
+      if (grp == 0 && active) {
+        const f32x4_t ml = mrow[16 * kWave];
+        const float m = fmaxf(m_ref, ml[0]);
+        const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m) * sl2);
+        const float a1 = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml[0] - m) * sl2);
+        l_run = l_run * a0 + ml[1] * a1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4_t v = mrow[(dt * 4 + g4) * kWave];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dt][g4 * 4 + e] = o[dt][g4 * 4 + e] * a0 + v[e] * a1;
+          }
+        m_ref = m;
+      }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    if (qok && grp == 0) {
+      const int qrow = q_perm[(int64_t)h * N + qpos];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = out + ((int64_t)h * N + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = dt * 32 + g4 * 8 + hl * 4;
+          store_out4<uint16_t>(orow + d0, o[dt][g4 * 4] * inv, o[dt][g4 * 4 + 1] * inv, o[dt][g4 * 4 + 2] * inv,
+                               o[dt][g4 * 4 + 3] * inv);
+        }
+      if (lse != nullptr && hl == 0)
+        lse[(int64_t)h * N + qrow] = l_tot > 0.f ? m_ref * scale + logf(l_tot) : -INFINITY;
+    }
   }
 #endif
 }

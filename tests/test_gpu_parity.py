@@ -379,6 +379,41 @@ def test_sparse_attention_many_clusters():
     _attn_check(w, Q, K, V, qp, qo, kp, ko, counts, cols, out, lse)
 
 
+def test_sparse_attention_split_items():
+    """Work items of at most 192 queries split their keys over two wave groups (each group one
+    32-key half of every 64-key tile, merged at the end): query clusters just below, at and above
+    that size and at the 384-query item boundary, against selections whose key counts fall just
+    below, at and above the 32- and 64-key tile edges (a second group that meets no key included)."""
+    w = SMALL["small"]
+    rng = np.random.default_rng(5)
+    Q, K, V = inputs(w)
+    H, N = w.heads, w.n
+    qsz = [1, 31, 32, 33, 64, 96, 160, 191, 192, 193, 250, 384, 385, 576]
+    qsz.append(N - sum(qsz))
+    ksz = [1, 31, 32, 33, 63, 64, 65, 97, 128, 129, 300]
+    ksz.append(N - sum(ksz))
+    cq, ck = len(qsz), len(ksz)
+    combos = [[0, 2, 5], list(range(ck)), [1, 3], [4, 10]]
+    qps, qos, kps, kos, cnts, colss = [], [], [], [], [], []
+    for h in range(H):
+        ql = rng.permutation(np.repeat(np.arange(cq), qsz))
+        kl = rng.permutation(np.repeat(np.arange(ck), ksz))
+        qp, qo = O.cluster_order(ql, cq)
+        kp, ko = O.cluster_order(kl, ck)
+        cols = np.zeros((cq, ck), dtype=np.int32)
+        cnt = np.zeros(cq, dtype=np.int32)
+        for i in range(cq):
+            sel = np.array([(i + 5 * h) % 11]) if i < 11 else np.array(combos[i - 11])
+            cnt[i] = sel.size
+            cols[i, :sel.size] = np.sort(sel)
+        qps.append(qp); qos.append(qo); kps.append(kp); kos.append(ko); cnts.append(cnt); colss.append(cols)
+    T = lambda a: torch.tensor(np.stack(a), dtype=torch.int32, device="cuda").contiguous()
+    qp, qo, kp, ko, counts, cols = map(T, (qps, qos, kps, kos, cnts, colss))
+    out, lse = bsa.park_sparse_attn(Q, K, V, qp, qo, kp, ko, counts, cols)
+    worst, mean = _attn_check(w, Q, K, V, qp, qo, kp, ko, counts, cols, out, lse)
+    print(f"[attention split items] max-abs {worst:.2e} mean-abs {mean:.2e}")
+
+
 def test_permute_roundtrip(case):
     """P12: gather then scatter is the identity; the gather matches the permutation."""
     w, Q, K, V, M = case
