@@ -165,7 +165,10 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
   };
 
   constexpr float kRaise = 16.f;
-  const float c1 = scale * 1.4426950408889634f;
+  // logit scale in base 2 (kept above 1e-30 so that its reciprocal is finite; below that every
+  // logit is log2 n_j to within 1e-28 anyway)
+  const float c1 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
+  const float ic1 = 1.f / c1;
   int cl = 0;  // FULL: the key cluster of this lane's column (advances with the tiles)
   for (int grp = 0; grp < 4 / TW; ++grp) {
     const int w0 = row0 + w * 64 + grp * 16 * TW;  // this group's first row
@@ -184,78 +187,89 @@ __global__ __launch_bounds__(256) void pama_bf16(const uint16_t* __restrict__ Q,
         qa[t][kk] = v;
       }
     }
-    // Logits in base 2: lg2 = acc * scale * log2(e) + log2(n_j). Pass 1 keeps, per lane and row, a
-    // reference r and the sum of 2^(lg2 - r) over this lane's columns. r is raised only when a
-    // logit exceeds it by more than kRaise (first tile, or rarely later), so the common step is
-    // one fma, one subtraction, one exp2 and one add per logit.
-    float r[TW][4], s[TW][4];
+    // Logits in base 2: lg2 = acc * c1 + log2(n_j), acc = q . c_j. Pass 1 keeps, per lane and row,
+    // a reference r and the sum of 2^(lg2 - r) over this lane's columns; the row's accumulators
+    // start at nr = -r / c1 instead of 0, so that acc * c1 + log2(n_j) is already lg2 - r: one
+    // fma, one exp2 and one add per logit. r is raised only when a logit exceeds it by more than
+    // kRaise (the first tile, or rarely later); the raised rows then take their logit computed
+    // again from zero accumulators, so that the new reference is exact. nr starts at 1e30: every
+    // finite logit raises it, and an empty column (-inf) never meets inf - inf.
+    float nr[TW][4], s[TW][4];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        r[t][e] = -1e30f;  // finite, so that an empty column (-inf) never meets -inf - -inf
+        nr[t][e] = 1e30f;
         s[t][e] = 0.f;
       }
     sweep(active, [&](int ct, const u32x4_t* bv, float ln) __attribute__((always_inline)) {
-      float lg[TW][4], dmax = -INFINITY;
+      float d[TW][4], dmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = {nr[t][0], nr[t][1], nr[t][2], nr[t][3]};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lg[t][e] = __builtin_fmaf(acc[e], c1, ln);
-          dmax = fmaxf(dmax, lg[t][e] - r[t][e]);
+          d[t][e] = __builtin_fmaf(acc[e], c1, ln);
+          dmax = fmaxf(dmax, d[t][e]);
         }
       }
       if (__builtin_expect(__ballot(dmax > kRaise) != 0, 0)) {
 #pragma unroll
-        for (int t = 0; t < TW; ++t)
+        for (int t = 0; t < TW; ++t) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (lg[t][e] - r[t][e] > kRaise) {
-              s[t][e] *= __builtin_amdgcn_exp2f(r[t][e] - lg[t][e]);
-              r[t][e] = lg[t][e];
+            if (d[t][e] > kRaise) {
+              const float lg = __builtin_fmaf(acc[e], c1, ln);
+              s[t][e] *= __builtin_amdgcn_exp2f(-__builtin_fmaf(nr[t][e], c1, lg));  // 2^(r - lg2)
+              nr[t][e] = -lg * ic1;
+              d[t][e] = 0.f;
             }
+        }
       }
 #pragma unroll
       for (int t = 0; t < TW; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[t][e] += __builtin_amdgcn_exp2f(lg[t][e] - r[t][e]);
+        for (int e = 0; e < 4; ++e) s[t][e] += __builtin_amdgcn_exp2f(d[t][e]);
     });
     // merge (reference, sum) across the 16 lanes (columns) of each group; the row's offset
     // off = r + log2(sum) makes 2^(lg2 - off) its normalised weight (off = +inf for rows that are
-    // out of range, whose weights are then 0)
+    // out of range, whose weights are then 0); pass 2 starts its accumulators at -off / c1
     float roff[TW][4];
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        float rr = -nr[t][e] * c1;
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-          const float ro = __shfl_xor(r[t][e], o, kWave);
+          const float ro = __shfl_xor(rr, o, kWave);
           const float so = __shfl_xor(s[t][e], o, kWave);
-          const float rn = fmaxf(r[t][e], ro);
-          s[t][e] = s[t][e] * __builtin_amdgcn_exp2f(r[t][e] - rn) + so * __builtin_amdgcn_exp2f(ro - rn);
-          r[t][e] = rn;
+          const float rn = fmaxf(rr, ro);
+          s[t][e] = s[t][e] * __builtin_amdgcn_exp2f(rr - rn) + so * __builtin_amdgcn_exp2f(ro - rn);
+          rr = rn;
         }
         const bool ok = (w0 + t * 16 + g * 4 + e) < row_end && s[t][e] > 0.f;
-        roff[t][e] = ok ? r[t][e] + log2f(s[t][e]) : INFINITY;
+        roff[t][e] = ok ? -(rr + log2f(s[t][e])) * ic1 : -INFINITY;
       }
     }
-    // pass 2: accumulate normalised weights 2^(lg2 - off) into the wave's column sums
+    // pass 2: accumulate normalised weights 2^(lg2 - off) into the wave's column sums (the
+    // accumulators start at roff = -off / c1, -inf for rows out of range)
     cl = 0;
     sweep(active, [&](int ct, const u32x4_t* bv, float ln) __attribute__((always_inline)) {
       const int64_t j = (int64_t)ct * 16 + l % 16;
       float cs = 0.f;
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = {roff[t][0], roff[t][1], roff[t][2], roff[t][3]};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[t][kk], bv[kk], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cs += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], c1, ln) - roff[t][e]);
+        for (int e = 0; e < 4; ++e) cs += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], c1, ln));
       }
       cs += __shfl_xor(cs, 16, kWave);
       cs += __shfl_xor(cs, 32, kWave);
