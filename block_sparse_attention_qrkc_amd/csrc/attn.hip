@@ -239,6 +239,27 @@ __device__ __forceinline__ int find_tile(const int32_t* tb, int cq, int c) {
   return lo;
 }
 
+// The bf16 attention's work queue: hpre[h] = work items of the heads before h (hpre[H] = all), and
+// the eight per-XCD queue counters cleared.
+__global__ __launch_bounds__(1024) void attn_queue_prep(const int32_t* __restrict__ tile_base, int64_t H, int cq,
+                                                        int64_t* __restrict__ hpre,
+                                                        unsigned long long* __restrict__ qctr) {
+  __shared__ int64_t scratch[17];
+  const int tid = threadIdx.x;
+  const int64_t per = (H + 1023) / 1024;
+  const int64_t h0 = tid * per, h1 = min(h0 + per, H);
+  int64_t local = 0;
+  for (int64_t h = h0; h < h1; ++h) local += tile_base[h * (2 * cq + 1) + cq];
+  int64_t total;
+  int64_t run = block_exclusive_scan(local, scratch, &total);
+  for (int64_t h = h0; h < h1; ++h) {
+    hpre[h] = run;
+    run += tile_base[h * (2 * cq + 1) + cq];
+  }
+  if (tid == 0) hpre[H] = total;
+  if (tid < 8) qctr[tid] = 0ull;
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out4(T* p, float a, float b, float c, float d);
 template <>
@@ -589,7 +610,9 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
                                                          const int32_t* __restrict__ runs,
                                                          const int32_t* __restrict__ nrun,
                                                          const int32_t* __restrict__ glen, float scale,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
+                                                         uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                         const int64_t* __restrict__ hpre,
+                                                         unsigned long long* __restrict__ qctr, int64_t H) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 12;
   constexpr int NWC = 8;  // copier waves
@@ -618,13 +641,45 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   // gather-list entries of the tiles in flight (see load_idx)
   __shared__ __attribute__((aligned(16))) int32_t idxs[NST][kWave];
 
-  int h, c;
-  xcd_tile(h, c);
+  // Persistent work-groups, one per CU, take work items from eight queues, one per XCD (work-groups
+  // are dealt to the XCDs in turn): queue q holds the work items of heads qH/8 .. (q+1)H/8 - 1, each
+  // head's longest first, so consecutive items of a head (the same key/value rows) stay on one
+  // XCD's L2. A work-group takes its own queue's items from the front, then other queues' items from
+  // the back (their shortest). Front and back counts share one 64-bit counter per queue (front in
+  // the low half): a claim that finds front + back >= the queue's length gets nothing, so every
+  // item is claimed exactly once.
+  __shared__ int64_t s_item;
+  const int xq = blockIdx.x & 7;
+  for (;;) {
+  if (threadIdx.x == 0) {
+    int64_t got = -1;
+    for (int k = 0; k < 8 && got < 0; ++k) {
+      const int q = (xq + k) & 7;
+      const int64_t lo = hpre[q * H / 8], n = hpre[(q + 1) * H / 8] - lo;
+      if (n <= 0) continue;
+      const unsigned long long v = atomicAdd(&qctr[q], k == 0 ? 1ull : (1ull << 32));
+      const int64_t f = (int64_t)(v & 0xFFFFFFFFull), b = (int64_t)(v >> 32);
+      if (f + b < n) got = k == 0 ? lo + f : lo + n - 1 - b;
+    }
+    s_item = got;
+  }
+  __syncthreads();
+  const int64_t gi = __builtin_amdgcn_readfirstlane(s_item);
+  if (gi < 0) break;
+  int hlo = 0, hhi = (int)H;  // the item's head: the largest h with hpre[h] <= gi
+  while (hhi - hlo > 1) {
+    const int mid = (hlo + hhi) >> 1;
+    if (hpre[mid] <= gi)
+      hlo = mid;
+    else
+      hhi = mid;
+  }
+  const int h = hlo;
+  const int c = (int)(gi - hpre[h]);
   const int32_t* tb = tile_base + (int64_t)h * (2 * cq + 1);
-  if (c >= tb[cq]) return;
   const int ti = find_tile(tb, cq, c);
   const int i = tb[cq + 1 + ti];
-  const int l = lane_id();
+  const int l = lane_id_opaque();  // derived per item, not kept live across the item loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const bool copier = w < NWC;
   const bool indexer = w == NWC;  // the first wave without copies resolves the tiles' key rows
@@ -722,7 +777,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     const uint32_t bring_base = (uint32_t)(size_t)((PARK_LDS float*)&bring[0][0]);
     auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
       if (!indexer) return;
-      const int v = tile * BN + l % BN;
+      const int v = tile * BN + lane_id_opaque() % BN;  // the lane id read again: no register held for it
       int off = (int)(N * 4);  // past the buffer's range: reads 0 (a valid row; its scores are masked)
       float bias = 0.f;
       if (v < L) {
@@ -833,7 +888,8 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
       }
       const int nvalid = L - v0;
       if (__builtin_expect(nvalid < NSC * 32, 0)) {
-        const int lim = nvalid - hl * 16;  // accumulator e of sub-tile st is key v0 + st * 32 + hl * 16 + e
+        // accumulator e of sub-tile st is key v0 + st * 32 + hl * 16 + e (hl read again: no register held)
+      const int lim = nvalid - (lane_id_opaque() / 32) * 16;
 #pragma unroll
         for (int st = 0; st < NSC; ++st)
 #pragma unroll
@@ -1042,6 +1098,8 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
         lse[(int64_t)h * N + qrow] = l_tot > 0.f ? m_ref * scale + logf(l_tot) : -INFINITY;
     }
   }
+  __syncthreads();  // the item's LDS is free for the next one
+  }
 #endif
 }
 
@@ -1051,8 +1109,10 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
 int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, s.bf16 ? kBf16BM : kAttnBM) + cq; }
 
 size_t attn_run_ints(const Dims& s, int cq, int ck) {
-  // + per-head partial statistics: 8 int64 per head, after an alignment of up to 4 bytes
-  return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq) + 16 * (size_t)s.H + 1;
+  // + per-head partial statistics: 8 int64 per head, after an alignment of up to 4 bytes; then the
+  // work queue: H + 1 int64 head offsets and 8 uint64 counters
+  return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq) + 16 * (size_t)s.H + 1 +
+         2 * ((size_t)s.H + 1) + 16;
 }
 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
@@ -1069,6 +1129,9 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
   attn_runs<<<dim3((unsigned)cq, (unsigned)s.H), 256, 0, st>>>(counts, cols, k_offsets, s.N, cq, ck, log_w,
                                                                1.f / scale, runs, nrun, glen, nblk);
   attn_order<<<(unsigned)s.H, 1024, 0, st>>>(q_offsets, glen, cq, s.bf16 ? kBf16BM : kAttnBM, tile_base);
+  int64_t* hpre = spart + 8 * s.H;
+  unsigned long long* qctr = reinterpret_cast<unsigned long long*>(hpre + s.H + 1);
+  if (s.bf16) attn_queue_prep<<<1, 1024, 0, st>>>(tile_base, s.H, cq, hpre, qctr);
   if (stats) {
     attn_stats_head<<<(unsigned)s.H, 256, 0, st>>>(q_offsets, k_offsets, cq, ck, glen, nblk, tile_base,
                                                    s.bf16 && s.D == 128 ? kBf16BN : kBN, spart);
@@ -1079,10 +1142,16 @@ hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const
   sparse_attn_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),            \
                                                  static_cast<const T*>(v), s.N, q_perm, q_offsets, cq, tile_base, \
                                                  k_perm, ck, runs, glen, weighted, scale, static_cast<T*>(out), lse);
-#define PARK_BF16ATTN(D, W)                                                                                         \
-  sparse_attn_bf16<D, W><<<grid, 768, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, k_perm, ck, runs, \
-                                             nrun, glen, scale, oh, lse);
+#define PARK_BF16ATTN(D, W)                                                                                  \
+  sparse_attn_bf16<D, W><<<ncu, 768, 0, st>>>(qh, kh, vh, s.N, q_perm, q_offsets, cq, tile_base, k_perm, ck, runs, \
+                                            nrun, glen, scale, oh, lse, hpre, qctr, s.H);
   if (s.bf16) {
+    // one persistent work-group per CU
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu < 1) ncu = 1;
     const uint16_t* qh = static_cast<const uint16_t*>(q);
     const uint16_t* kh = static_cast<const uint16_t*>(k);
     const uint16_t* vh = static_cast<const uint16_t*>(v);
