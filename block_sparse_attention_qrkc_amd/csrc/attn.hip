@@ -777,7 +777,8 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     const uint32_t bring_base = (uint32_t)(size_t)((PARK_LDS float*)&bring[0][0]);
     auto load_idx = [&](int set, int tile) __attribute__((always_inline)) {
       if (!indexer) return;
-      const int v = tile * BN + lane_id_opaque() % BN;  // the lane id read again: no register held for it
+      const int li = lane_id_opaque();  // the lane id read again: no register held for it
+      const int v = tile * BN + li % BN;
       int off = (int)(N * 4);  // past the buffer's range: reads 0 (a valid row; its scores are masked)
       float bias = 0.f;
       if (v < L) {
@@ -790,7 +791,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
         if constexpr (W) bias = __int_as_float(lds_read_b32(rb_base + (uint32_t)cr * 4u));
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (PARK_LDS void*)&idxs[set][0], 4, off, 0, 0, 0);
-      if constexpr (W) lds_write_b32(bring_base + (uint32_t)((tile % (2 * NST)) * kWave + l) * 4u, bias);
+      if constexpr (W) lds_write_b32(bring_base + (uint32_t)((tile % (2 * NST)) * kWave + li) * 4u, bias);
     };
     // entries of this lane's copy rows trow[q] = trow[0] + q RPB
     const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][trow[0]]);
@@ -848,12 +849,32 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     // scores of one tile: its eight K operand reads in two blocks of four, each followed by its MFMAs
     const uint32_t sbase = (uint32_t)(size_t)((PARK_LDS uint8_t*)stages);
     static_assert(KS * NSC == 8, "eight K reads per computed sub-tile set");
-    auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSC]) __attribute__((always_inline)) {
+    // The accumulators start at 0, or (weighted form) at the keys' logit offsets, which the tile's
+    // entries brought into LDS: accumulator e of sub-tile st is key v0 + st * 32 + hl * 16 + e.
+    auto s_tile = [&](auto OFFc, f32x16_t(&sa)[NSC], int v0) __attribute__((always_inline)) {
       constexpr int OFF = decltype(OFFc)::value;
+      if constexpr (W) {
+        const int tile = v0 / BN, sub = v0 % BN;
 #pragma unroll
-      for (int st = 0; st < NSC; ++st)
+        for (int st = 0; st < NSC; ++st) {
+          u32x4_t b[4];
+          const uint32_t ba =
+              bring_base + (uint32_t)((tile % (2 * NST)) * kWave + sub + st * 32 + (lane_id_opaque() / 32) * 16) * 4u;
+          lds_read4_b128<0>(b, ba);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t u = b[q][e];
+              sa[st][q * 4 + e] = __uint_as_float(u);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sa[st][e] = 0.f;
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         uint32_t a[4];
@@ -871,25 +892,12 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
         }
       }
     };
-    // key offsets (weighted form) and the mask of keys past the list end; v0 = the first key
+    // the mask of keys past the list end; v0 = the first key
     auto adjust = [&](f32x16_t(&sa)[NSC], int v0) __attribute__((always_inline)) {
-      if constexpr (W) {
-        const int tile = v0 / BN, sub = v0 % BN;
-#pragma unroll
-        for (int st = 0; st < NSC; ++st) {
-          u32x4_t b[4];
-          const uint32_t ba = bring_base + (uint32_t)((tile % (2 * NST)) * kWave + sub + st * 32 + hl * 16) * 4u;
-          lds_read4_b128<0>(b, ba);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sa[st][q * 4 + e] += __uint_as_float(b[q][e]);
-        }
-      }
       const int nvalid = L - v0;
       if (__builtin_expect(nvalid < NSC * 32, 0)) {
         // accumulator e of sub-tile st is key v0 + st * 32 + hl * 16 + e (hl read again: no register held)
-      const int lim = nvalid - (lane_id_opaque() / 32) * 16;
+        const int lim = nvalid - (lane_id_opaque() / 32) * 16;
 #pragma unroll
         for (int st = 0; st < NSC; ++st)
 #pragma unroll
@@ -958,7 +966,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     // wave's first set, which sets the softmax reference
     auto compute = [&](auto OFFc, int v0, bool first) __attribute__((always_inline)) {
       f32x16_t sc[NSC];
-      s_tile(OFFc, sc);
+      s_tile(OFFc, sc, v0);
       adjust(sc, v0);
       if (first) m_ref = tile_max(sc);
       u32x4_t pb[NSC][2];
@@ -967,7 +975,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
         // rare: the scores are computed again (the tile is still in LDS), so they need not stay
         // live through the softmax
         f32x16_t s2[NSC];
-        s_tile(OFFc, s2);
+        s_tile(OFFc, s2, v0);
         adjust(s2, v0);
         const float m_new = fmaxf(m_ref, tile_max(s2));
         const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
