@@ -240,7 +240,7 @@ __device__ __forceinline__ int find_tile(const int32_t* tb, int cq, int c) {
 }
 
 // The bf16 attention's work queue: hpre[h] = work items of the heads before h (hpre[H] = all), and
-// the eight per-XCD queue counters cleared.
+// the queue counter cleared.
 __global__ __launch_bounds__(1024) void attn_queue_prep(const int32_t* __restrict__ tile_base, int64_t H, int cq,
                                                         int64_t* __restrict__ hpre,
                                                         unsigned long long* __restrict__ qctr) {
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(1024) void attn_queue_prep(const int32_t* __restric
     run += tile_base[h * (2 * cq + 1) + cq];
   }
   if (tid == 0) hpre[H] = total;
-  if (tid < 8) qctr[tid] = 0ull;
+  if (tid == 0) qctr[0] = 0ull;
 }
 
 template <typename T>
@@ -641,27 +641,17 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
   // gather-list entries of the tiles in flight (see load_idx)
   __shared__ __attribute__((aligned(16))) int32_t idxs[NST][kWave];
 
-  // Persistent work-groups, one per CU, take work items from eight queues, one per XCD (work-groups
-  // are dealt to the XCDs in turn): queue q holds the work items of heads qH/8 .. (q+1)H/8 - 1, each
-  // head's longest first, so consecutive items of a head (the same key/value rows) stay on one
-  // XCD's L2. A work-group takes its own queue's items from the front, then other queues' items from
-  // the back (their shortest). Front and back counts share one 64-bit counter per queue (front in
-  // the low half): a claim that finds front + back >= the queue's length gets nothing, so every
-  // item is claimed exactly once.
+  // Persistent work-groups, one per CU, take the work items in order from one queue: the heads one
+  // after the other, each head's items longest-first. All CUs then work on about one head at a
+  // time, whose key/value rows (39 MB at the Wan shape) stay in the 256 MB memory-side cache;
+  // eight per-XCD queues of five heads each (consecutive items of a head sharing an XCD's L2)
+  // measured 2 % slower. The last items are the last head's shortest.
   __shared__ int64_t s_item;
-  const int xq = blockIdx.x & 7;
+  const int64_t T = hpre[H];
   for (;;) {
   if (threadIdx.x == 0) {
-    int64_t got = -1;
-    for (int k = 0; k < 8 && got < 0; ++k) {
-      const int q = (xq + k) & 7;
-      const int64_t lo = hpre[q * H / 8], n = hpre[(q + 1) * H / 8] - lo;
-      if (n <= 0) continue;
-      const unsigned long long v = atomicAdd(&qctr[q], k == 0 ? 1ull : (1ull << 32));
-      const int64_t f = (int64_t)(v & 0xFFFFFFFFull), b = (int64_t)(v >> 32);
-      if (f + b < n) got = k == 0 ? lo + f : lo + n - 1 - b;
-    }
-    s_item = got;
+    const int64_t v = (int64_t)atomicAdd(&qctr[0], 1ull);
+    s_item = v < T ? v : -1;
   }
   __syncthreads();
   const int64_t gi = __builtin_amdgcn_readfirstlane(s_item);
@@ -1118,9 +1108,9 @@ int64_t attn_max_tiles(const Dims& s, int cq) { return ceil_div(s.N, s.bf16 ? kB
 
 size_t attn_run_ints(const Dims& s, int cq, int ck) {
   // + per-head partial statistics: 8 int64 per head, after an alignment of up to 4 bytes; then the
-  // work queue: H + 1 int64 head offsets and 8 uint64 counters
+  // work queue: H + 1 int64 head offsets and a uint64 counter
   return (size_t)(s.H * cq) * (size_t)run_stride(ck) + 3 * (size_t)(s.H * cq) + 16 * (size_t)s.H + 1 +
-         2 * ((size_t)s.H + 1) + 16;
+         2 * ((size_t)s.H + 1) + 2;
 }
 
 hipError_t launch_sparse_attn(const Dims& s, const void* q, const void* k, const void* v, const int32_t* q_perm,
