@@ -476,19 +476,6 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const T* __restrict__ 
 // from the transposing LDS read (each lane of a 16-lane group receives 4 keys of one column).
 // ------------------------------------------------------------------------------------------------
 
-// Work-group -> tile mapping that keeps neighbouring tiles (the tiles of one query cluster read
-// the same key/value rows) on one XCD: work-groups are dealt to the 8 XCDs round-robin, so XCD x
-// receives ids x, x + 8, ...; those are given the x-th contiguous range of tiles.
-[[maybe_unused]] __device__ __forceinline__ void xcd_tile(int& h, int& c) {
-  const int nx = gridDim.x;
-  const int G = nx * gridDim.y;
-  const int b = blockIdx.x + blockIdx.y * nx;
-  const int x = b & 7, per = G >> 3, rem = G & 7;
-  const int L = x * per + min(x, rem) + (b >> 3);
-  h = L / nx;
-  c = L - h * nx;
-}
-
 // 384-query work items: twelve waves x 32 queries share one work-group per CU (three waves per
 // SIMD, 168 registers each), so each key/value tile copied to LDS serves up to 384 queries and each
 // SIMD has three waves to interleave matrix-core, vector and LDS work. Tiles (32 keys for d = 128,
