@@ -773,6 +773,7 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     // entries of this lane's copy rows trow[q] = trow[0] + q RPB
     const uint32_t ibase = (uint32_t)(size_t)((PARK_LDS int32_t*)&idxs[0][trow[0]]);
     auto read_idx = [&](int set, int(&nr)[LOADS]) __attribute__((always_inline)) {
+      if (!copier) return;  // only the copier waves use the entries
 #pragma unroll
       for (int q = 0; q < LOADS; ++q) nr[q] = lds_read_b32(ibase + (uint32_t)((set * kWave + q * RPB) * 4));
     };
