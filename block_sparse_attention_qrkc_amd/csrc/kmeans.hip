@@ -486,11 +486,14 @@ __device__ __forceinline__ int spin_nonzero(int* p, int* fail) {
   return v;
 }
 
-// The same for a 64-bit slot.
-__device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
+// The same for two 64-bit slots written by one lane: both are polled in every round, so that the
+// second costs no round trip of its own.
+__device__ __forceinline__ void spin_slots(uint64_t* p, uint64_t* q, int* fail, uint64_t& a, uint64_t& c) {
   long long n = 0;
-  uint64_t v;
-  while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+  for (;;) {
+    a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a != 0 && c != 0) break;
     if (__hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
     if (++n >= kSpinLimit) {
       __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -498,7 +501,39 @@ __device__ __forceinline__ uint64_t spin_slot(uint64_t* p, int* fail) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// One DPP move of a double (both halves with the same control); lanes whose source lies outside
+// the pattern, or whose row is masked off, read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// Inclusive sum over lanes 0..l of the wave: within each row of 16 by shifts of 1, 2, 4 and 8
+// lanes, then the end of row 0 into row 1 and of row 2 into row 3, then the end of row 1 into
+// rows 2 and 3 (register moves only, no LDS round trips).
+__device__ __forceinline__ double wave_scan_dpp(double v) {
+  v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
+}
+
+// The value of lane l - 1 (0 in lane 0): an inclusive scan turned exclusive without a subtraction.
+__device__ __forceinline__ double wave_shr1(double v) { return dpp_f64<0x138, 0xF>(v); }  // wave_shr:1
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // H heads from head h0 on: the side pointers start at head h0, the draws use the head's own index.
@@ -513,10 +548,11 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
   __shared__ __attribute__((aligned(16))) uint32_t yhi[D / 2];
   __shared__ __attribute__((aligned(16))) uint32_t ylo[D / 2];
   constexpr int CPR = D / 8;           // 16-byte pieces per row
-  __shared__ double wred[kCoopWaves];   // per wave: D^2 total of its register rows
-  __shared__ double wred2[kCoopWaves];  // per wave: D^2 total of its LDS rows
-  __shared__ int wmin[kCoopWaves];
-  __shared__ int wfirst[2][kCoopWaves], wlast[2][kCoopWaves];
+  // per wave slot (register rows of waves 0.., then LDS rows of waves 0..): D^2 total, and its
+  // exclusive prefix within the part in candidate order
+  __shared__ double wsum[2 * kCoopWaves], wpre[2 * kCoopWaves];
+  __shared__ int wmin[kCoopWaves];      // per wave: its first untaken candidate
+  __shared__ int first_s, last_s;       // owner part: first candidate past the draw, last one with mass
   __shared__ double pre_s, v_s, cc_s;
   __shared__ int owner_s, pick_s;
 
@@ -588,64 +624,65 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
       t = t0 < S ? t0 : S - 1;
     } else {
       // ---- running D^2 sums inside each wave (candidate order: register rows of waves 0..7, then
-      // LDS rows of waves 0..7), the wave totals, and this part's first untaken candidate
-      const double incr = wave_inclusive_scan(d2r);
-      const double incl = wave_inclusive_scan(d2l);
-      int fu = has_r && !taken_r ? c0 + tid : (has_l && !taken_l ? c0 + NT + tid : 0x7FFFFFFF);
-      // lowest untaken: reg candidates precede LDS ones in candidate order
-      const int fu_r = has_r && !taken_r ? c0 + tid : 0x7FFFFFFF;
-      const int fu_l = has_l && !taken_l ? c0 + NT + tid : 0x7FFFFFFF;
-      fu = fu_r < fu_l ? fu_r : fu_l;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const int f2 = __shfl_xor(fu, o, kWave);
-        fu = f2 < fu ? f2 : fu;
-      }
+      // LDS rows of waves 0..7), the wave totals, and each wave's first untaken candidate (register
+      // rows precede LDS rows in candidate order)
+      const double incr = wave_scan_dpp(d2r);
+      const double incl = wave_scan_dpp(d2l);
+      const uint64_t ur = __ballot(has_r && !taken_r);
+      const uint64_t ul = __ballot(has_l && !taken_l);
       if (l == kWave - 1) {
-        wred[w] = incr;
-        wred2[w] = incl;
+        wsum[w] = incr;
+        wsum[kCoopWaves + w] = incl;
       }
-      if (l == 0) wmin[w] = fu;
+      if (l == 0) {
+        wmin[w] = ur ? c0 + w * kWave + __ffsll((unsigned long long)ur) - 1
+                     : (ul ? c0 + NT + w * kWave + __ffsll((unsigned long long)ul) - 1 : 0x7FFFFFFF);
+        if (w == 0) {
+          first_s = 0x7FFFFFFF;
+          last_s = -1;
+        }
+      }
       __syncthreads();
       if (w == 0) {
         // slots of step m: [part][0] = D^2 sum with its sign bit set, [part][1] = first untaken + 1
         uint64_t* slots = psum + (int64_t)m * kCoopMaxParts * 2;
+        const double u = kpp_uniform(seed, h0 + h, sd.side, m);
+        // the wave slots' exclusive prefixes (for the search, if this part owns the draw), the
+        // part's total and its first untaken candidate
+        const double ws = l < 2 * kCoopWaves ? wsum[l] : 0.0;
+        const double wi = wave_scan_dpp(ws);
+        const double wx = wave_shr1(wi);
+        if (l < 2 * kCoopWaves) wpre[l] = wx;
+        const double pt = readlane_f64(wi, 2 * kCoopWaves - 1);
+        int pf = l < kCoopWaves ? wmin[l] : 0x7FFFFFFF;
+        // kCoopWaves <= 16: the minimum over row 0 by rotations of 1, 2, 4 and 8 lanes (row_ror)
+        pf = min(pf, __builtin_amdgcn_update_dpp(pf, pf, 0x121, 0xF, 0xF, false));
+        pf = min(pf, __builtin_amdgcn_update_dpp(pf, pf, 0x122, 0xF, 0xF, false));
+        pf = min(pf, __builtin_amdgcn_update_dpp(pf, pf, 0x124, 0xF, 0xF, false));
+        pf = min(pf, __builtin_amdgcn_update_dpp(pf, pf, 0x128, 0xF, 0xF, false));
+        pf = __builtin_amdgcn_readfirstlane(pf);
         if (l == 0) {
-          double pt = 0.0;
-          int pf = 0x7FFFFFFF;
-          for (int q = 0; q < kCoopWaves; ++q) {
-            pt += wred[q];
-            pf = wmin[q] < pf ? wmin[q] : pf;
-          }
-          for (int q = 0; q < kCoopWaves; ++q) pt += wred2[q];
           __hip_atomic_store(&slots[part * 2], (uint64_t)__double_as_longlong(pt) | (1ull << 63), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(&slots[part * 2 + 1], (uint64_t)(uint32_t)pf + 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         }
-        // the G part sums are read at once (lane q: part q) and folded in the same order by every
-        // part (a lane scan); a failed wait reads as an empty part
+        // the G part sums are read at once (lane q: part q) and scanned in the same order by every
+        // part; a failed wait reads as an empty part
         double pq = 0.0;
         int fq = 0x7FFFFFFF;
         if (l < G) {
-          const uint64_t a = spin_slot(&slots[l * 2], fail);
-          const uint64_t c = spin_slot(&slots[l * 2 + 1], fail);
+          uint64_t a, c;
+          spin_slots(&slots[l * 2], &slots[l * 2 + 1], fail, a, c);
           pq = __longlong_as_double((long long)(a & ~(1ull << 63)));
           fq = c != 0 ? (int)(c - 1u) : 0x7FFFFFFF;
         }
-        double run = pq;  // inclusive prefix over parts (lanes < kCoopMaxParts)
-#pragma unroll
-        for (int o = 1; o < kCoopMaxParts; o <<= 1) {
-          const double u = __shfl_up(run, o, kWave);
-          if (l >= o) run += u;
-        }
-        const double total = __shfl(run, G - 1, kWave);
-        const double run_prev = __shfl_up(run, 1, kWave);
-        const double pre_q = l == 0 ? 0.0 : run_prev;  // exclusive prefix of part l
+        const double run = wave_scan_dpp(pq);  // inclusive prefix over parts
+        const double total = readlane_f64(run, G - 1);
         int owner = -1;
-        double v = 0.0;
+        double v = 0.0, pre = 0.0;
         if (total > 0.0) {
-          v = kpp_uniform(seed, h0 + h, sd.side, m) * total;
+          v = u * total;
           const uint64_t over = __ballot(l < G && run > v);
           if (over) {
             owner = __ffsll((unsigned long long)over) - 1;
@@ -654,51 +691,49 @@ __global__ __launch_bounds__(NT) void kpp_coop(CoopSide s0, CoopSide s1, int H, 
             owner = 63 - __clzll((unsigned long long)mass);
           }
         }
-        int best = fq;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const int f2 = __shfl_xor(best, o, kWave);
-          best = f2 < best ? f2 : best;
-        }
-        const double pre = owner >= 0 ? __shfl(pre_q, owner, kWave) : 0.0;
+        const double rx = wave_shr1(run);  // exclusive prefix over parts
+        if (owner >= 0) pre = readlane_f64(rx, owner);
         if (l == 0) {
           owner_s = owner;
           pre_s = pre;
           v_s = v;
+        }
+        if (owner < 0) {
           // every D^2 is zero: the lowest candidate not chosen yet, over all parts
-          pick_s = owner < 0 ? (best < S ? best : 0) : -1;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) {
+            const int f2 = __shfl_xor(fq, o, kWave);
+            fq = f2 < fq ? f2 : fq;
+          }
+          if (l == 0) pick_s = fq < S ? fq : 0;
         }
       }
       __syncthreads();
       const int owner = owner_s;
       if (owner >= 0) {
         if (owner == part) {
-          // running sums in candidate order (pre: the parts before this one); per wave, the first
-          // candidate whose running sum exceeds v, and the last one with mass (rounding fallback)
+          // per wave, the first candidate whose running sum exceeds v and the last one with mass
+          // (rounding fallback), folded over the waves by LDS min / max
           const double v = v_s;
-          double pr = pre_s, pl = pre_s;
-          for (int q = 0; q < w; ++q) pr += wred[q];
-          for (int q = 0; q < kCoopWaves; ++q) pl += wred[q];
-          for (int q = 0; q < w; ++q) pl += wred2[q];
+          const double pr = pre_s + wpre[w];
+          const double pl = pre_s + wpre[kCoopWaves + w];
           const uint64_t hr = __ballot(d2r > 0.0 && pr + incr > v);
           const uint64_t hq = __ballot(d2l > 0.0 && pl + incl > v);
           const uint64_t mr = __ballot(d2r > 0.0);
           const uint64_t mq = __ballot(d2l > 0.0);
           if (l == 0) {
             const int rb = c0 + w * kWave, lb = c0 + NT + w * kWave;
-            wfirst[0][w] = hr ? rb + __ffsll((unsigned long long)hr) - 1 : 0x7FFFFFFF;
-            wfirst[1][w] = hq ? lb + __ffsll((unsigned long long)hq) - 1 : 0x7FFFFFFF;
-            wlast[0][w] = mr ? rb + 63 - __clzll((unsigned long long)mr) : -1;
-            wlast[1][w] = mq ? lb + 63 - __clzll((unsigned long long)mq) : -1;
+            const int f = hr ? rb + __ffsll((unsigned long long)hr) - 1
+                             : (hq ? lb + __ffsll((unsigned long long)hq) - 1 : 0x7FFFFFFF);
+            const int la = mq ? lb + 63 - __clzll((unsigned long long)mq)
+                              : (mr ? rb + 63 - __clzll((unsigned long long)mr) : -1);
+            if (f != 0x7FFFFFFF) atomicMin(&first_s, f);
+            if (la >= 0) atomicMax(&last_s, la);
           }
           __syncthreads();
           if (tid == 0) {
-            int best = 0x7FFFFFFF, last = -1;
-            for (int k2 = 0; k2 < 2 && best == 0x7FFFFFFF; ++k2)  // register rows precede LDS rows
-              for (int q = 0; q < kCoopWaves; ++q) best = wfirst[k2][q] < best ? wfirst[k2][q] : best;
-            for (int k2 = 0; k2 < 2; ++k2)
-              for (int q = 0; q < kCoopWaves; ++q) last = wlast[k2][q] > last ? wlast[k2][q] : last;
-            if (best == 0x7FFFFFFF) best = last >= 0 ? last : c0;
+            int best = first_s;
+            if (best == 0x7FFFFFFF) best = last_s >= 0 ? last_s : c0;
             // the flag carries the pick (+1, so that 0 means not yet)
             __hip_atomic_store(&sync[m * 3 + 2], best + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pick_s = best;
