@@ -970,9 +970,9 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
     };
 
     if (nt > 0) {
-      // prologue: entries of tiles 0 .. NST-1 (one wait of the indexer, then a barrier), then those
-      // of tiles NST .. 2 NST-2 into the sets just read, then the copies of tiles 0 .. NST-2 into
-      // stages 0 .. NST-2
+      // prologue: entries of tiles 0 .. NST-1 (one wait of the indexer, then a barrier), then, once
+      // every copier has read them, those of tiles NST .. 2 NST-2 into the sets just read, then the
+      // copies of tiles 0 .. NST-2 into stages 0 .. NST-2
 #pragma unroll
       for (int x = 0; x < NST; ++x) load_idx(x, x);
       if (indexer) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) & lgkmcnt(0)
@@ -982,6 +982,11 @@ __global__ __launch_bounds__(768, 1) void sparse_attn_bf16(const uint16_t* __res
       int n0[NST][LOADS];
 #pragma unroll
       for (int x = 0; x < NST; ++x) read_idx(x, n0[x]);
+      // the indexer's next loads land in sets 0 .. NST-2: every copier has read them first (the
+      // reads wait for their data), else a late copier could take a later tile's entries
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int x = NST; x < 2 * NST - 1; ++x) load_idx(x % NST, x);
 #pragma unroll

@@ -414,6 +414,34 @@ def test_sparse_attention_split_items():
     print(f"[attention split items] max-abs {worst:.2e} mean-abs {mean:.2e}")
 
 
+def test_sparse_attention_repeatable():
+    """Repeated launches give bitwise-identical outputs (each work item is computed by one work-group
+    in a fixed order): thousands of work items, so that many work-groups start items at once, with
+    unrelated matrix products between the launches; no oracle is needed for this property."""
+    H, N, D, cq, ck = 8, 40000, 128, 160, 200
+    g = torch.Generator(device="cuda").manual_seed(3)
+    Q, K, V = (torch.randn(H, N, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    rng = np.random.default_rng(13)
+    qps, qos, kps, kos, cnts, colss = [], [], [], [], [], []
+    for h in range(H):
+        qp, qo = O.cluster_order(rng.integers(0, cq, N), cq)
+        kp, ko = O.cluster_order(rng.integers(0, ck, N), ck)
+        cols = np.zeros((cq, ck), dtype=np.int32)
+        cnt = rng.integers(1, ck // 2, cq).astype(np.int32)
+        for i in range(cq):
+            cols[i, :cnt[i]] = np.sort(rng.choice(ck, size=int(cnt[i]), replace=False))
+        qps.append(qp); qos.append(qo); kps.append(kp); kos.append(ko); cnts.append(cnt); colss.append(cols)
+    T = lambda a: torch.tensor(np.stack(a), dtype=torch.int32, device="cuda").contiguous()
+    qp, qo, kp, ko, counts, cols = map(T, (qps, qos, kps, kos, cnts, colss))
+    ref_out, ref_lse = bsa.park_sparse_attn(Q, K, V, qp, qo, kp, ko, counts, cols)
+    a = torch.randn(2048, 2048, device="cuda", generator=g)
+    for rep in range(6):
+        _ = a @ a
+        out, lse = bsa.park_sparse_attn(Q, K, V, qp, qo, kp, ko, counts, cols)
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), rep
+    assert torch.isfinite(ref_out.float()).all() and torch.isfinite(ref_lse).all()
+
+
 def test_permute_roundtrip(case):
     """P12: gather then scatter is the identity; the gather matches the permutation."""
     w, Q, K, V, M = case
