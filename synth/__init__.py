@@ -60,6 +60,9 @@ WORKLOADS = {
     "wan": Workload("wan", 40, (21, 45, 80), 128, "bf16", 64, 8.0, (3, 5, 5), 0.2, 100, 500, 10, 0.9),
     # HunyuanVideo-shaped layer: 24 heads, 33x45x80 = 118,800 tokens, Cq=128, Ck=512.
     "hunyuan": Workload("hunyuan", 24, (33, 45, 80), 128, "bf16", 64, 8.0, (3, 5, 5), 0.2, 128, 512, 10, 0.9),
+    # One GPU's share of the Wan-shaped layer when its 40 heads are split over eight GPUs (heads are
+    # independent, so a head shard runs the same path): heads 0-4 of the Wan layer.
+    "wan_shard8": Workload("wan_shard8", 5, (21, 45, 80), 128, "bf16", 64, 8.0, (3, 5, 5), 0.2, 100, 500, 10, 0.9),
     # Long clip: 40 heads, 61x45x80 = 219,600 tokens, Cq=200, Ck=1000, 10 drifting steps,
     # full K-means at steps 0 and 5, two warm-started iterations otherwise.
     "long": Workload("long", 40, (61, 45, 80), 128, "bf16", 64, 8.0, (3, 5, 5), 0.2, 200, 1000, 10, 0.9,
