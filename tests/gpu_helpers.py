@@ -37,6 +37,9 @@ SMALL = {
     "small64": synth.custom("small64", heads=2, grid=(5, 12, 31), d=64, dtype="bf16", centres=16, norm=6.0,
                             patch=(2, 4, 8), cq=16, ck=40, iters=4, p=0.9),
     "tiny": synth.WORKLOADS["tiny"],
+    # both sides at the ABI's cluster limit (2048), two tokens per cluster on average
+    "maxc": synth.custom("maxc", heads=1, grid=(4, 32, 32), d=128, dtype="bf16", centres=24, norm=8.0,
+                         patch=(2, 4, 8), cq=2048, ck=2048, iters=1, p=0.9),
     # fp32 data at d = 128 (fp32 assignment and map kernels, 128-query fp32 attention work items)
     "small32": synth.custom("small32", heads=2, grid=(5, 13, 29), d=128, dtype="f32", centres=16, norm=8.0,
                             patch=(2, 4, 8), cq=20, ck=60, iters=4, p=0.9),

@@ -442,6 +442,52 @@ def test_sparse_attention_repeatable():
     assert torch.isfinite(ref_out.float()).all() and torch.isfinite(ref_lse).all()
 
 
+def test_pipeline_at_the_cluster_limit():
+    """Both sides at the ABI's cluster limit (2048 query and 2048 key clusters over 4096 tokens, so
+    most clusters hold one to a few tokens): k-means++ step by step, one Lloyd step of each side in
+    lock-step, the map, the top-p rows and the attention (thousands of tiny work items) against the
+    oracle."""
+    w = SMALL["maxc"]
+    Q, K, V = inputs(w)
+    M = bsa.park_qrkc_metric(Q)
+    res = {}
+    for side, X, C, metric, sd, Mp in (("q", Q, w.cq, bsa.PARK_EUCLID, bsa.PARK_SIDE_Q, None),
+                                       ("k", K, w.ck, bsa.PARK_QRKC, bsa.PARK_SIDE_K, M)):
+        cent = bsa.park_cluster(X, C, 0, metric, Mp, seed=7, side=sd)["centroids"]
+        x = to64(X[0])
+        Mh = to64(Mp[0]) if Mp is not None else None
+        co, chosen, margins = O.kmeanspp(x, C, Mh, seed=7, head=0, side=sd, return_trace=True)
+        diff = np.flatnonzero(np.any(to64(cent)[0] != co, axis=1))
+        if diff.size:
+            assert margins[diff[0]] <= TAU, f"{side}: seeding differs at step {diff[0]}"
+        prev = to64(cent)
+        r = bsa.park_cluster(X, C, 1, metric, Mp, init=bsa.PARK_INIT_WARM, side=sd, centroids=cent)
+        lab, perm, off = np_i(r["labels"]), np_i(r["perm"]), np_i(r["offsets"])
+        g, b = O.consumed_centroids(prev[0], metric, Mh, bf16=True)
+        _, bad = O.assign_near_tie(x, g, b, lab[0], TAU)
+        assert bad.size == 0, f"{side}: {bad.size} labels differ beyond near-ties"
+        po, oo = O.cluster_order(lab[0], C)
+        np.testing.assert_array_equal(perm[0], po)
+        np.testing.assert_array_equal(off[0], oo)
+        assert np.abs(to64(r["centroids"])[0] - O.update(x, lab[0], C, prev[0])).max() <= 1e-6 * np.abs(x).max()
+        res[side] = r
+    qc, kc = res["q"], res["k"]
+    A = bsa.park_retrieve_map(Q, qc["perm"], qc["offsets"], kc["centroids"], kc["offsets"])
+    sizes = np.diff(np_i(kc["offsets"][0]))
+    Ao = O.pama(to64(Q[0]), np_i(qc["perm"][0]), np_i(qc["offsets"][0]), O.round_bf16(to64(kc["centroids"][0])),
+                sizes, w.scale)
+    assert np.abs(to64(A)[0] - Ao).max() <= MAP_ABS
+    sel = bsa.park_select_topp(A, kc["offsets"], w.p)
+    _, bad = check_topp_rows(to64(A)[0], sizes, w.p, np_i(sel["counts"][0]), np_i(sel["cols"][0]),
+                             np_i(sel["sel_keys"][0]))
+    assert not bad, bad[:5]
+    out, lse = bsa.park_sparse_attn(Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"], sel["counts"],
+                                    sel["cols"])
+    worst, mean = _attn_check(w, Q, K, V, qc["perm"], qc["offsets"], kc["perm"], kc["offsets"], sel["counts"],
+                              sel["cols"], out, lse)
+    print(f"[cluster limit] attention max-abs {worst:.2e} mean-abs {mean:.2e}")
+
+
 def test_permute_roundtrip(case):
     """P12: gather then scatter is the identity; the gather matches the permutation."""
     w, Q, K, V, M = case
