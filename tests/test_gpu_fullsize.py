@@ -441,3 +441,66 @@ def test_long_reuse_and_subset_steps():
         assert torch.equal(two["perm"], r["k_perm"])
         assert torch.isfinite(r["lse"]).all()
     print(f"[long reuse / subset] sampled subset near-ties: {near}")
+
+
+def test_max_tokens_one_head():
+    """One head at the token limit of the ABI (N = 2^24 - 1 = 4095 x 4097 tokens, d = 128, bf16; a
+    row's element offset reaches 2^31 - 128 and its byte offset 2^32 - 256): the forward ends with a
+    clear status and finite outputs, the orders are the stable counting sorts of the labels, a warm
+    Lloyd step of each side matches the fp64 assignment on sampled tokens and the member means on
+    sampled clusters, a query cluster's map row matches the oracle, and sampled queries' outputs
+    match the fp64 softmax over their selected keys."""
+    w = synth.custom("max_tokens", heads=1, grid=(4095, 1, 4097), d=128, dtype="bf16", centres=64, norm=8.0,
+                     patch=(3, 5, 5), cq=100, ck=500, iters=2, p=0.5)
+    assert w.n == (1 << 24) - 1
+    Q, K, V = synth.make_qkv(w, seed=0, device="cuda")
+    outs = ("metric", "q_labels", "q_perm", "q_offsets", "k_labels", "k_perm", "k_offsets", "map", "counts",
+            "cols", "lse", "status")
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=0, outputs=outs)
+    torch.cuda.synchronize()
+    assert int(r["status"][0]) == 0
+    assert torch.isfinite(r["out"].float()).all() and torch.isfinite(r["lse"]).all()
+    rng = np.random.default_rng(23)
+    dev = Q.device
+    for side, X, C, metric, sd in (("q", Q, w.cq, bsa.PARK_EUCLID, bsa.PARK_SIDE_Q),
+                                   ("k", K, w.ck, bsa.PARK_QRKC, bsa.PARK_SIDE_K)):
+        po, oo = O.cluster_order(np_i(r[f"{side}_labels"][0]), C)
+        np.testing.assert_array_equal(np_i(r[f"{side}_perm"][0]), po)
+        np.testing.assert_array_equal(np_i(r[f"{side}_offsets"][0]), oo)
+        M = r["metric"] if side == "k" else None
+        prev = r[f"{side}_centroids"].clone()
+        res = bsa.park_cluster(X, C, 1, metric, M, init=bsa.PARK_INIT_WARM, side=sd, centroids=prev.clone())
+        t = np.sort(rng.choice(w.n, size=16384, replace=False))
+        xt = to64(X[0][torch.as_tensor(t, device=dev)])
+        g, b = O.consumed_centroids(to64(prev)[0], metric, to64(M[0]) if M is not None else None, bf16=True)
+        _, bad = O.assign_near_tie(xt, g, b, np_i(res["labels"][0])[t], TAU)
+        assert bad.size == 0, f"{side}: {bad.size} sampled labels differ beyond near-ties"
+        off = np_i(res["offsets"][0])
+        new = to64(res["centroids"])[0]
+        for c in rng.choice(np.flatnonzero(np.diff(off) > 0), size=3, replace=False):
+            xm = to64(X[0][res["perm"][0][off[c]:off[c + 1]].long()])
+            assert np.abs(new[c] - xm.mean(0)).max() <= 1e-6 * np.abs(xm).max(), (side, c)
+    qo, ko = np_i(r["q_offsets"][0]), np_i(r["k_offsets"][0])
+    qp, kp = r["q_perm"][0].long(), r["k_perm"][0].long()
+    live = np.flatnonzero(np.diff(qo) > 0)
+    # one query cluster's map row (its members passed in cluster order)
+    i = int(rng.choice(live))
+    members = qp[qo[i]:qo[i + 1]]
+    n_i = int(members.numel())
+    khat = O.round_bf16(to64(r["k_centroids"])[0])
+    Ao = O.pama(to64(Q[0][members]), np.arange(n_i), np.array([0, n_i]), khat, np.diff(ko), w.scale)
+    assert np.abs(to64(r["map"])[0][i] - Ao[0]).max() <= MAP_ABS
+    # sampled queries of four query clusters against the fp64 softmax over their selected keys
+    counts, cols = np_i(r["counts"][0]), np_i(r["cols"][0])
+    worst, tot, n = 0.0, 0.0, 0
+    for i in rng.choice(live, size=4, replace=False):
+        sel = cols[i, :counts[i]]
+        keys = torch.cat([kp[ko[j]:ko[j + 1]] for j in sel])
+        q = qp[qo[i]:qo[i + 1]]
+        q = q[torch.as_tensor(rng.choice(q.numel(), size=min(64, q.numel()), replace=False), device=dev)]
+        Oo, Lo = O.dense_attention(to64(Q[0][q]), to64(K[0][keys]), to64(V[0][keys]), w.scale)
+        e = np.abs(to64(r["out"][0][q]) - Oo)
+        worst, tot, n = max(worst, e.max()), tot + e.sum(), n + e.size
+        assert np.abs(to64(r["lse"][0][q]) - Lo).max() <= LSE_ABS
+    assert worst <= ATTN_MAX_ABS and tot / n <= ATTN_MEAN_ABS, (worst, tot / n)
+    print(f"[max tokens] attention max-abs {worst:.2e} mean-abs {tot / n:.2e}")
