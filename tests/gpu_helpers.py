@@ -37,6 +37,10 @@ SMALL = {
     "small64": synth.custom("small64", heads=2, grid=(5, 12, 31), d=64, dtype="bf16", centres=16, norm=6.0,
                             patch=(2, 4, 8), cq=16, ck=40, iters=4, p=0.9),
     "tiny": synth.WORKLOADS["tiny"],
+    # more heads than the cooperative seeding can hold on the CUs (the single-work-group seeding
+    # runs for every head and side)
+    "many_heads": synth.custom("many_heads", heads=1000, grid=(4, 32, 32), d=64, dtype="bf16", centres=16,
+                               norm=6.0, patch=(2, 4, 8), cq=32, ck=64, iters=2, p=0.9),
     # both sides at the ABI's cluster limit (2048), two tokens per cluster on average
     "maxc": synth.custom("maxc", heads=1, grid=(4, 32, 32), d=128, dtype="bf16", centres=24, norm=8.0,
                          patch=(2, 4, 8), cq=2048, ck=2048, iters=1, p=0.9),

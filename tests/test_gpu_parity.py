@@ -488,6 +488,43 @@ def test_pipeline_at_the_cluster_limit():
     print(f"[cluster limit] attention max-abs {worst:.2e} mean-abs {mean:.2e}")
 
 
+def test_many_heads():
+    """1000 heads of 4096 tokens: more heads than the cooperative seeding can keep on the CUs, so each
+    (head, side) is seeded by one work-group; seeding step by step, the forward's orders on every head,
+    and map, top-p and attention of sampled heads against the oracle."""
+    w = SMALL["many_heads"]
+    Q, K, V = inputs(w)
+    M = bsa.park_qrkc_metric(Q)
+    heads = [0, 511, 999]
+    for X, C, metric, sd, Mp in ((Q, w.cq, bsa.PARK_EUCLID, bsa.PARK_SIDE_Q, None),
+                                 (K, w.ck, bsa.PARK_QRKC, bsa.PARK_SIDE_K, M)):
+        cg = to64(bsa.park_cluster(X, C, 0, metric, Mp, seed=9, side=sd)["centroids"])
+        for h in heads:
+            co, _, margins = O.kmeanspp(to64(X[h]), C, to64(Mp[h]) if Mp is not None else None, seed=9, head=h,
+                                        side=sd, return_trace=True)
+            diff = np.flatnonzero(np.any(cg[h] != co, axis=1))
+            if diff.size:
+                assert margins[diff[0]] <= TAU, f"head {h}: seeding differs at step {diff[0]}"
+    r = bsa.park_forward(Q, K, V, w.cq, w.ck, w.iters, w.p, seed=9, outputs=ALL_OUT)
+    for side, C in (("q", w.cq), ("k", w.ck)):
+        lab, perm, off = np_i(r[f"{side}_labels"]), np_i(r[f"{side}_perm"]), np_i(r[f"{side}_offsets"])
+        for h in range(w.heads):
+            po, oo = O.cluster_order(lab[h], C)
+            np.testing.assert_array_equal(perm[h], po)
+            np.testing.assert_array_equal(off[h], oo)
+    for h in heads:
+        sizes = np.diff(np_i(r["k_offsets"][h]))
+        Ao = O.pama(to64(Q[h]), np_i(r["q_perm"][h]), np_i(r["q_offsets"][h]),
+                    O.round_bf16(to64(r["k_centroids"][h])), sizes, w.scale)
+        assert np.abs(to64(r["map"][h]) - Ao).max() <= MAP_ABS
+        _, bad = check_topp_rows(to64(r["map"][h]), sizes, w.p, np_i(r["counts"][h]), np_i(r["cols"][h]),
+                                 np_i(r["sel_keys"][h]))
+        assert not bad
+    _attn_check(w, Q, K, V, r["q_perm"], r["q_offsets"], r["k_perm"], r["k_offsets"], r["counts"], r["cols"],
+                r["out"], r["lse"], heads=heads)
+    assert torch.isfinite(r["out"].float()).all()
+
+
 def test_permute_roundtrip(case):
     """P12: gather then scatter is the identity; the gather matches the permutation."""
     w, Q, K, V, M = case
