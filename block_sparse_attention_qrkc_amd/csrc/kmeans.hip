@@ -1176,9 +1176,11 @@ constexpr int kFuseThreads = 512;  // eight waves
 //     -b_j/2, the same packed-key argmax): wave w takes the 32 points 32 (w % 4) .. and the
 //     clusters 64 (w / 4) .. + 63; the two cluster halves of a point are merged in LDS (larger top
 //     20 bits of the score, ties to the lower index, as the sequential scan over tiles gives);
-//  B. the member sums S[c][d] += sum_p [label_p == c] x_p[d]: 32x32x16 MFMAs of a 0/1 matrix built
-//     from the labels and the points (transposing LDS reads, eight consecutive points of one
-//     dimension per lane for both factors); wave w owns the clusters 32 (w / 2) .. + 31 and the
+//  B. the member sums S[c][d] += sum_p [label_p == c] x_p[d]: 32x32x16 MFMAs of a 0/1 matrix and
+//     the points (transposing LDS reads, eight consecutive points of one dimension per lane for both
+//     factors). The 0/1 factor comes from a per-tile membership bit mask of every cluster (set by
+//     LDS atomics when the labels are merged): eight bits of it select one 16-byte entry of a
+//     256-entry table of bf16 0/1 patterns; wave w owns the clusters 32 (w / 2) .. + 31 and the
 //     dimensions (D / 2) (w % 2) .. ; each tile's fp32 sums (at most 128 terms) are added into
 //     fp64 accumulators in tile order, so the sums do not depend on scheduling.
 // Outputs: the labels, and per work-group the fp64 sums [C][D] and the member counts [C].
@@ -1198,7 +1200,9 @@ __global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __re
   __shared__ float hb[kFuseT];
   __shared__ float hbt[2][kFuseT];  // per cluster half: best top-20-bit score of each point
   __shared__ int hbi[2][kFuseT];    // and its cluster
-  __shared__ __attribute__((aligned(16))) int lab[kFuseT];
+  __shared__ __attribute__((aligned(16))) uint32_t mbits[kFuseT][kFuseT / 32];  // [cluster][point / 32]
+  __shared__ __attribute__((aligned(16))) u32x4_t ohlut[256];  // bit i of e -> element i is bf16 1.0
+  static_assert(kFuseT * kFuseT / 32 == kFuseThreads, "one membership word per thread");
   __shared__ int cnt[kFuseT];
   const int h = blockIdx.y;
   const int g = blockIdx.x;
@@ -1221,6 +1225,12 @@ __global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __re
   for (int r = tid; r < kFuseT; r += kFuseThreads) {
     hb[r] = r < C ? -0.5f * b[(int64_t)h * C + r] : -FLT_MAX;
     cnt[r] = 0;
+  }
+  for (int e = tid; e < 256; e += kFuseThreads) {
+    u32x4_t v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = ((e >> (2 * j)) & 1 ? 0x3F80u : 0u) | ((e >> (2 * j + 1)) & 1 ? 0x3F800000u : 0u);
+    ohlut[e] = v;
   }
 
   // staging of tile t: pieces e = tid + 512 q: point row e / CPR, chunk e % CPR (rows past N: zero)
@@ -1279,6 +1289,7 @@ __global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __re
     sstore(pre, buf, t);
     __syncthreads();
     if (t + 2 < te) gload(pre, t + 2);
+    (&mbits[0][0])[tid] = 0u;  // the previous tile's masks were read before the barrier above
     // ---- A: scores of this lane's point against the clusters 64 ch .. + 63
     float best = -FLT_MAX, bestt = -FLT_MAX;
     int btile = 2 * ch;
@@ -1324,10 +1335,8 @@ __global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __re
       if (p < N) {
         labels[(int64_t)h * N + p] = lb;
         atomicAdd(&cnt[lb], 1);
-      } else {
-        lb = -1;
+        atomicOr(&mbits[lb][tid / 32], 1u << (tid % 32));
       }
-      lab[tid] = lb;
     }
     __syncthreads();
     // ---- B: member sums of this tile
@@ -1335,21 +1344,15 @@ __global__ __launch_bounds__(kFuseThreads) void lloyd_fused(const uint16_t* __re
     for (int x = 0; x < DTW; ++x)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[x][i] = 0.f;
-    const int cme = cw * 32 + l % 32;
     const PARK_LDS uint16_t* xs = (const PARK_LDS uint16_t*)&xt[buf][0];
+    // membership of this lane's cluster in the tile: bit i of word st = point 32 st + i
+    const u32x4_t mw = *reinterpret_cast<const u32x4_t*>(&mbits[cw * 32 + l % 32][0]);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const int base = st * 32 + 16 * hl + 8 * kh;
-        const u32x4_t la = *reinterpret_cast<const u32x4_t*>(&lab[base]);
-        const u32x4_t lb = *reinterpret_cast<const u32x4_t*>(&lab[base + 4]);
-        const uint32_t one = 0x3F80u;  // bf16 1.0
-        u32x4_t oh;
-        oh[0] = ((int)la[0] == cme ? one : 0u) | (((int)la[1] == cme ? one : 0u) << 16);
-        oh[1] = ((int)la[2] == cme ? one : 0u) | (((int)la[3] == cme ? one : 0u) << 16);
-        oh[2] = ((int)lb[0] == cme ? one : 0u) | (((int)lb[1] == cme ? one : 0u) << 16);
-        oh[3] = ((int)lb[2] == cme ? one : 0u) | (((int)lb[3] == cme ? one : 0u) << 16);
+        // the 0/1 factor of the points 32 st + 16 hl + 8 kh .. + 7 (two points per word)
+        const u32x4_t oh = ohlut[(mw[st] >> (16 * hl + 8 * kh)) & 0xFFu];
 #pragma unroll
         for (int x = 0; x < DTW; ++x) {
           const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PARK_LDS s16x4_t*)(xs + tofs[x][st][kh][0]));
