@@ -120,6 +120,38 @@ def test_fused_step_empty_cluster(name):
     print(f"[fused step {name}] near-ties: {near}")
 
 
+def test_fused_step_full_tiles_and_128_clusters():
+    """The fused step at its cluster limit (128 clusters: every 32-cluster tile of the assignment
+    live) on 3000 tokens (a ragged last 128-token tile), where the first five tiles belong to one
+    cluster (every bit of that cluster's per-tile membership mask set) and the other tokens spread
+    over all clusters; labels, order and means against the oracle as in the test above."""
+    g = torch.Generator().manual_seed(11)
+    H, N, D, C = 2, 3000, 128, 128
+    dirs = torch.randn(C, D, generator=g)
+    dirs = dirs / dirs.norm(dim=1, keepdim=True) * 8.0
+    cen = torch.randint(0, C, (H, N), generator=g)
+    cen[:, :640] = 7
+    Q = (dirs[cen] + 0.3 * torch.randn(H, N, D, generator=g)).to(torch.bfloat16).cuda().contiguous()
+    cent = dirs.unsqueeze(0).repeat(H, 1, 1).float().cuda().contiguous()
+    prev = to64(cent)
+    res = bsa.park_cluster(Q, C, 1, bsa.PARK_EUCLID, init=bsa.PARK_INIT_WARM, side=bsa.PARK_SIDE_Q, centroids=cent)
+    lab, perm, off, new = np_i(res["labels"]), np_i(res["perm"]), np_i(res["offsets"]), to64(res["centroids"])
+    near = 0
+    for h in range(H):
+        x = to64(Q[h])
+        assert np.all(lab[h][:640] == 7)
+        assert len(np.unique(lab[h])) > 100
+        gg, b = O.consumed_centroids(prev[h], O.EUCLID, None, bf16=True)
+        n_near, bad = O.assign_near_tie(x, gg, b, lab[h], TAU)
+        assert bad.size == 0, f"head {h}: {bad.size} labels differ beyond near-ties"
+        near += n_near
+        po, oo = O.cluster_order(lab[h], C)
+        np.testing.assert_array_equal(perm[h], po)
+        np.testing.assert_array_equal(off[h], oo)
+        assert np.abs(new[h] - O.update(x, lab[h], C, prev[h])).max() <= 1e-6 * np.abs(x).max()
+    print(f"[fused step, 128 clusters] near-ties: {near}")
+
+
 @pytest.mark.parametrize("side", ["q", "k"])
 @pytest.mark.parametrize("stride,phase", [(3, 1), (4, 0), (1, 0)])
 def test_subset_update_lockstep(case, side, stride, phase):
